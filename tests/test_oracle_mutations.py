@@ -1,0 +1,171 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check a pin catches each.
+
+Each mutant replaces one oracle function with a version carrying a typical bug
+(a dropped term, a wrong sign or index, a transposed operand, a lost tie rule);
+at least one of the listed pin tests must then fail.
+"""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+import tests.test_oracle_gate as TG
+import tests.test_oracle_permute as TP
+import tests.test_oracle_ffn_combine as TF
+import tests.test_oracle_stats as TS
+
+_orig = {name: getattr(O, name) for name in ("gate", "permute", "grouped_ffn", "combine", "stats",
+                                              "silu_product", "assignment_groups")}
+
+
+def _gate_unstable(logits, k, renormalize=True):
+    lg = np.asarray(logits, dtype=np.float32)
+    key = np.where(np.isnan(lg), -np.inf, lg).astype(np.float64)
+    # ties resolved towards the higher id
+    order = np.array([sorted(range(lg.shape[1]), key=lambda e: (-row[e], -e)) for row in key])
+    ids = order[:, :k].astype(np.int32)
+    return ids, _orig["gate"](logits, k, renormalize)[1]
+
+
+def _gate_nan_high(logits, k, renormalize=True):
+    lg = np.asarray(logits, dtype=np.float32).copy()
+    lg[np.isnan(lg)] = np.inf
+    return _orig["gate"](lg, k, renormalize)
+
+
+def _gate_no_renorm(logits, k, renormalize=True):
+    return _orig["gate"](logits, k, False)
+
+
+def _permute_unstable(topk_ids, E, n_shared=0, n_priority=0, x=None):
+    p = _orig["permute"](topk_ids, E, n_shared, n_priority, x)
+    offs = p["group_offsets"]
+    s2f = p["sorted_to_flat"].copy()
+    for g in range(len(offs) - 1):                  # reverse inside each group
+        s2f[offs[g]:offs[g + 1]] = s2f[offs[g]:offs[g + 1]][::-1]
+    f2s = np.empty_like(s2f)
+    f2s[s2f] = np.arange(len(s2f))
+    p.update(sorted_to_flat=s2f, flat_to_sorted=f2s)
+    if x is not None:
+        T, k = np.asarray(topk_ids).shape
+        tok = np.where(s2f < T * k, s2f // k, (s2f - T * k) % T)
+        p["x_sorted"] = np.asarray(x)[tok]
+    return p
+
+
+def _assign_shared_wrong(topk_ids, E, n_shared=0, n_priority=0):
+    g, t, G, nseg = _orig["assignment_groups"](topk_ids, E, n_shared, n_priority)
+    T, k = np.asarray(topk_ids).shape
+    t = t.copy()
+    t[T * k:] = t[T * k:][::-1]                     # shared rows of the wrong tokens
+    return g, t, G, nseg
+
+
+def _silu_wrong_sign(g, u):
+    return u * g / (1.0 + np.exp(g))
+
+
+def _silu_drops_gate(g, u):
+    return u / (1.0 + np.exp(-g))
+
+
+def _ffn_transposed_down(x_sorted, group_offsets, E, n_shared, nseg, w_gate, w_up, w_down,
+                         dtype, rows=None):
+    wd = np.ascontiguousarray(np.swapaxes(w_down, 1, 2)[:, :, :]) if w_down.shape[1] == w_down.shape[2] \
+        else w_down[:, ::-1, :]
+    return _orig["grouped_ffn"](x_sorted, group_offsets, E, n_shared, nseg, w_gate, w_up, wd, dtype, rows)
+
+
+def _ffn_gate_up_swapped(x_sorted, group_offsets, E, n_shared, nseg, w_gate, w_up, w_down,
+                         dtype, rows=None):
+    return _orig["grouped_ffn"](x_sorted, group_offsets, E, n_shared, nseg, w_up, w_gate, w_down, dtype, rows)
+
+
+def _combine_no_shared(h_sorted, flat_to_sorted, topk_w, T, k, n_shared, tokens=None, row_of_sorted=None):
+    return _orig["combine"](h_sorted, flat_to_sorted, topk_w, T, k, 0, tokens, row_of_sorted)
+
+
+def _combine_weight_index(h_sorted, flat_to_sorted, topk_w, T, k, n_shared, tokens=None, row_of_sorted=None):
+    return _orig["combine"](h_sorted, flat_to_sorted, np.asarray(topk_w)[:, ::-1], T, k, n_shared,
+                            tokens, row_of_sorted)
+
+
+def _stats_no_diag(topk_ids, E, req_offsets=None, idf=None):
+    st = _orig["stats"](topk_ids, E, req_offsets, idf)
+    for l in range(st["affinity"].shape[0]):
+        np.fill_diagonal(st["affinity"][l], 0)
+    return st
+
+
+def _stats_idf_inverted(topk_ids, E, req_offsets=None, idf=None):
+    st = _orig["stats"](topk_ids, E, req_offsets, idf)
+    if req_offsets is not None and idf is None:
+        R = len(req_offsets) - 1
+        df = st["df"].astype(np.float64)
+        st["idf"] = np.where(df > 0, np.log(np.maximum(df, 1) / R), 0.0)
+        st["signature"] = (st["req_counts"] * st["idf"][None]).astype(np.float32)
+    return st
+
+
+def _stats_union_off_by_one(topk_ids, E, req_offsets=None, idf=None):
+    st = _orig["stats"](topk_ids, E, req_offsets, idf)
+    st["union_mask"] = (st["counts"] > 1).astype(np.uint8)
+    st["union_size"] = st["union_mask"].sum(axis=1).astype(np.int32)
+    return st
+
+
+def _run_pins(pins):
+    failures = 0
+    for fn, args in pins:
+        try:
+            fn(*args)
+        except AssertionError:
+            failures += 1
+        except Exception:           # a crash is a detection too
+            failures += 1
+    return failures
+
+
+def _gate_cases():
+    return [(TG.test_gate_golden, (c,)) for c in TG._golden_cases()] + [(TG.test_gate_bruteforce_tiny_E, ())]
+
+
+MUTANTS = {
+    "gate_ties_to_higher_id": ("gate", _gate_unstable, _gate_cases),
+    "gate_nan_as_plus_inf": ("gate", _gate_nan_high, _gate_cases),
+    "gate_skips_renormalisation": ("gate", _gate_no_renorm,
+                                   lambda: [(TG.test_gate_weights_sum_to_one_and_k1_is_exactly_one, ())]),
+    "permute_unstable_within_group": ("permute", _permute_unstable,
+                                      lambda: [(TP.test_permute_golden, (c,)) for c in TP._cases()]),
+    "permute_shared_rows_wrong_token": ("assignment_groups", _assign_shared_wrong,
+                                        lambda: [(TP.test_permute_invariants, (s,)) for s in range(2)]),
+    "silu_wrong_sign": ("silu_product", _silu_wrong_sign,
+                        lambda: [(TF.test_ffn_golden, (c,)) for c in TF._golden()["ffn_cases"]]),
+    "silu_drops_gate_factor": ("silu_product", _silu_drops_gate,
+                               lambda: [(TF.test_ffn_single_expert_is_dense_swiglu, ())]),
+    "ffn_down_misindexed": ("grouped_ffn", _ffn_transposed_down,
+                            lambda: [(TF.test_ffn_single_expert_is_dense_swiglu, ())]),
+    "ffn_gate_up_swapped": ("grouped_ffn", _ffn_gate_up_swapped,
+                            lambda: [(TF.test_ffn_golden, (c,)) for c in TF._golden()["ffn_cases"]]),
+    "combine_drops_shared": ("combine", _combine_no_shared,
+                             lambda: [(TF.test_combine_golden, (c,)) for c in TF._golden()["combine_cases"]]),
+    "combine_weight_slots_reversed": ("combine", _combine_weight_index,
+                                      lambda: [(TF.test_combine_golden, (c,)) for c in TF._golden()["combine_cases"]]),
+    "affinity_without_diagonal": ("stats", _stats_no_diag,
+                                  lambda: [(TS.test_stats_golden, (c,)) for c in TS._cases()]),
+    "idf_inverted": ("stats", _stats_idf_inverted,
+                     lambda: [(TS.test_stats_golden, (c,)) for c in TS._cases()]),
+    "union_needs_two_hits": ("stats", _stats_union_off_by_one,
+                             lambda: [(TS.test_stats_golden, (c,)) for c in TS._cases()]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, mutant, pins = MUTANTS[name]
+    monkeypatch.setattr(O, attr, mutant)
+    assert _run_pins(pins()) > 0, f"no pin caught mutant {name}"
+
+
+def test_pins_pass_on_unmutated_oracle():
+    for name in sorted(MUTANTS):
+        assert _run_pins(MUTANTS[name][2]()) == 0, name

@@ -1,0 +1,207 @@
+/*
+ * libmoe - one Mixture-of-Experts layer's expert path on one AMD Instinct
+ * MI355X (gfx950): softmax top-k gate, dispatch permutation, grouped SwiGLU
+ * expert FFN, gate-weighted combine, and the expert-activation statistics.
+ *
+ * Where the operations come from (three web summaries of 2026 MoE-serving
+ * papers):
+ *   ELDR page ("Expert-Locality-Aware Decode Routing for PD-Disaggregated MoE
+ *   Serving"), section "What it solves": a decode step reads the weights of
+ *   every distinct expert that any token of the batch selected; section "Core
+ *   idea / structure / operation": the gate is standard top-k gating, left
+ *   unchanged, and each request is summarised by its per-expert top-k
+ *   activation counts reweighted by IDF over a subset of layers.
+ *   GRACE-MoE page, section 1: every MoE layer dispatches tokens to their
+ *   experts and combines the results back; sections 3-4: expert co-activation
+ *   (affinity) and per-expert load are read off recorded top-k selections.
+ *   ExpertPlex page, "Instance vs module disaggregation": the expert FFN is the
+ *   bulk (~95 %) of a MoE layer; "Adaptive Persistent Kernels": expert work is
+ *   cut into tiles served from a device-side queue, decode tiles first.
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer to a dense, row-major,
+ *     contiguous array, 16-byte aligned.  The caller owns all memory; the
+ *     library never allocates or frees device memory and keeps no pointer after
+ *     the work it enqueued has completed.  Outputs must not alias inputs.
+ *   - Each call checks its arguments on the host, enqueues kernels on `stream`
+ *     and returns.  No call synchronises, copies device->host or reads device
+ *     data on the host; device faults surface at the caller's next sync.
+ *   - Errors are returned synchronously as moe_status and nothing is enqueued:
+ *       MOE_ERR_INVALID_ARG  negative sizes, k < 1, k > E, n_priority > T,
+ *                            NULL required pointer, misaligned pointer
+ *       MOE_ERR_UNSUPPORTED  E > 512, d or I not a multiple of 8, unknown dtype,
+ *                            sizes whose element counts overflow int32
+ *       MOE_ERR_WORKSPACE    workspace smaller than the queried size
+ *       MOE_ERR_HIP          a HIP launch reported an error (after enqueueing)
+ *   - T = 0 (no tokens) is valid: outputs with zero elements are untouched;
+ *     fixed-size outputs (group offsets, counts, ...) receive their empty-batch
+ *     values.
+ *   - Workspace query: when `workspace` is NULL, the call stores the number of
+ *     bytes it needs in *workspace_bytes, returns MOE_OK and enqueues nothing.
+ *     The size depends only on the scalar arguments.  Otherwise
+ *     *workspace_bytes is the size of the caller's buffer.
+ *   - Calls are reentrant; the library holds no mutable global state.  Two calls
+ *     that share a workspace must not overlap in time.
+ *   - Expert ids outside [0, E) in an input id array are a precondition
+ *     violation: kernels clamp them into range to stay memory safe, the
+ *     results are then unspecified.
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Largest expert count the kernels accept. */
+#define MOE_MAX_EXPERTS 512
+
+/*
+ * moe_gate - softmax top-k gate over fp32 router logits.
+ * (ELDR page, "Core idea / structure / operation": standard top-k gating.)
+ *
+ *   logits   [T][E] fp32, read only.
+ *   topk_ids [T][k] int32, written: the k largest logits of each row in
+ *            descending order; equal logits go to the lower expert id; -0.0
+ *            equals +0.0; NaN ranks as -inf.
+ *   topk_w   [T][k] fp32, written: renormalize = 1 -> softmax over the k chosen
+ *            logits (the full softmax renormalised over the chosen experts);
+ *            renormalize = 0 -> the full-E softmax probability of each chosen
+ *            expert.  Weights are computed in double and rounded once.
+ *   Requires 1 <= k <= E <= 512, T >= 0.
+ */
+moe_status moe_gate(const float* logits, int32_t T, int32_t E, int32_t k,
+                    int32_t renormalize, int32_t* topk_ids, float* topk_w,
+                    hipStream_t stream);
+
+/*
+ * moe_permute - dispatch as a stable counting sort of token->expert
+ * assignments into contiguous per-expert groups (histogram, prefix scan,
+ * scatter, row gather).  (GRACE-MoE page, section 1: the dispatch exchange.)
+ *
+ *   Assignments: routed f = t*k + j (expert topk_ids[t][j]) and, for the
+ *   n_shared always-on experts, f = T*k + s*T + t (expert E + s).
+ *   Group of an assignment: routed g = seg(t)*E + e with seg(t) = 1 when
+ *   n_priority > 0 and t >= n_priority, else 0 (the first n_priority tokens form
+ *   a priority segment whose groups come first: ExpertPlex page, "Adaptive
+ *   Persistent Kernels"); shared g = nseg*E + s with nseg = (n_priority > 0 ? 2
+ *   : 1).  G = nseg*E + n_shared groups, N = T*(k + n_shared) assignments.
+ *   Assignments are ordered by (g, f).
+ *
+ *   topk_ids       [T][k] int32, read only, ids in [0, E).
+ *   x              [T][d] of `dtype`, or NULL (then no row gather; x_sorted
+ *                  is ignored and may be NULL).
+ *   group_offsets  [G+1] int32, written: exclusive scan of the group sizes.
+ *   sorted_to_flat [N] int32, written: f of the assignment at sorted row n.
+ *   flat_to_sorted [N] int32, written: its inverse.
+ *   x_sorted       [N][d] of `dtype`, written: x_sorted[n] = x[token(f)]
+ *                  bit for bit.
+ *   workspace      device scratch of the queried size.
+ *   Requires 0 <= n_priority <= T, 1 <= k <= E <= 512, n_shared >= 0, d % 8 == 0
+ *   when x is given.
+ */
+moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
+                       int32_t n_shared, int32_t n_priority,
+                       const void* x, moe_dtype dtype, int32_t d,
+                       int32_t* group_offsets, int32_t* sorted_to_flat,
+                       int32_t* flat_to_sorted, void* x_sorted,
+                       void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_ffn - grouped SwiGLU expert FFN over the sorted rows.
+ * (ExpertPlex page, "Instance vs module disaggregation": the expert FFN;
+ * "Adaptive Persistent Kernels": tiles served from a device-side queue with
+ * the priority segment's tiles ahead of the rest.)
+ *
+ *   For sorted row n of group g (expert e = g mod E for g < nseg*E, else
+ *   E + g - nseg*E):
+ *     h[n] = W_down[e] . ( silu(W_gate[e] . xs[n]) * (W_up[e] . xs[n]) ).
+ *   x_sorted       [n_rows][d] of `dtype`.
+ *   group_offsets  [G+1] int32 with G = nseg*E + n_shared, non-decreasing,
+ *                  group_offsets[G] == n_rows (device data: never read on the
+ *                  host; the tile list is built on the device).
+ *   w_gate, w_up   [E+n_shared][I][d] of `dtype` (nn.Linear [out][in] layout).
+ *   w_down         [E+n_shared][d][I] of `dtype`.
+ *   h_sorted       [n_rows][d] of `dtype`, written.
+ *   Only experts with at least one row are read.  bf16: bf16 operands, fp32
+ *   accumulation, the SwiGLU product rounded to bf16 (round to nearest even)
+ *   before the down projection.  f32: fp32 throughout.
+ *   Requires d % 8 == 0, I % 8 == 0, nseg in {1, 2}, 1 <= E <= 512.
+ */
+moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* group_offsets,
+                           int32_t n_rows, int32_t E, int32_t n_shared, int32_t nseg,
+                           int32_t d, int32_t I,
+                           const void* w_gate, const void* w_up, const void* w_down,
+                           moe_dtype dtype, void* h_sorted,
+                           void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_combine - gate-weighted combine back to token order.
+ * (GRACE-MoE page, section 1: the combine exchange.)
+ *
+ *   y[t] = sum_{j<k} topk_w[t][j] * h[flat_to_sorted[t*k+j]]
+ *        + sum_{s<n_shared} h[flat_to_sorted[T*k+s*T+t]],
+ *   accumulated in fp32 in that order and rounded once to `dtype`.
+ *   h_sorted       [T*(k+n_shared)][d] of `dtype`.
+ *   flat_to_sorted [T*(k+n_shared)] int32.
+ *   topk_w         [T][k] fp32.
+ *   y              [T][d] of `dtype`, written.
+ *   Requires k >= 1, n_shared >= 0, d % 8 == 0.
+ */
+moe_status moe_combine(const void* h_sorted, const int32_t* flat_to_sorted,
+                       const float* topk_w, int32_t T, int32_t k, int32_t n_shared,
+                       int32_t d, moe_dtype dtype, void* y, hipStream_t stream);
+
+/*
+ * moe_stats - per-batch expert-activation statistics over a stack of L layers.
+ * (ELDR page, "What it solves": the distinct-expert union; "Core idea /
+ * structure / operation": count x IDF request signatures over a layer subset;
+ * GRACE-MoE page, sections 3-4: co-activation (affinity) and load.)
+ *
+ *   topk_ids    [L][T][k] int32 routed ids (no shared experts).
+ *   With M_l[t][e] = number of slots j with ids[l][t][j] == e:
+ *   counts      [L][E] int32, written: column sums of M_l.
+ *   union_size  [L] int32, written: number of experts with a nonzero count.
+ *   union_mask  [L][E] uint8 or NULL, written: 1 where the count is nonzero.
+ *   affinity    [L][E][E] int32 or NULL, written: M_l^T M_l (symmetric, the
+ *               diagonal equals counts for distinct ids per token).
+ *   req_offsets [R+1] int32 or NULL: request r owns tokens
+ *               [req_offsets[r], req_offsets[r+1]) (0 <= ... <= T, non
+ *               decreasing; a request may be a KV block).
+ *   req_counts  [R][L][E] int32 or NULL, written: column sums of M_l over the
+ *               request's tokens.
+ *   idf         [L][E] fp32 or NULL.  NULL: idf = ln(R / df) from this batch,
+ *               df = number of requests with a nonzero count, idf = 0 where
+ *               df = 0 (computed in double).
+ *   signature   [R][L][E] fp32 or NULL, written: req_counts * idf (double,
+ *               rounded once).
+ *   req_counts and signature need req_offsets.  R >= 0.
+ */
+moe_status moe_stats(const int32_t* topk_ids, int32_t L, int32_t T, int32_t k, int32_t E,
+                     const int32_t* req_offsets, int32_t R, const float* idf,
+                     int32_t* counts, int32_t* union_size, uint8_t* union_mask,
+                     int32_t* affinity, int32_t* req_counts, float* signature,
+                     void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_H */

@@ -1,0 +1,132 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching a GPU (CPU-only; no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_expert_routing_amd as m
+from top_expert_routing_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmoe.h")
+
+INV, UNS, WS = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED, _lib.MOE_ERR_WORKSPACE
+FAKE = 1 << 20          # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return m.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_five_calls():
+    assert _declared() == sorted(["moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_stats",
+                                  "moe_status_string"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert tuple(sorted(_lib.EXPORTS)) == tuple(_declared())
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.moe_status_string(code).decode() == name
+    assert lib.moe_status_string(99).decode() == "MOE_ERR_UNKNOWN"
+
+
+def test_gate_validation(lib):
+    g = lib.moe_gate
+    assert g(FAKE, 4, 8, 9, 1, FAKE, FAKE, None) == INV          # k > E
+    assert g(FAKE, 4, 8, 0, 1, FAKE, FAKE, None) == INV          # k < 1
+    assert g(FAKE, -1, 8, 2, 1, FAKE, FAKE, None) == INV         # T < 0
+    assert g(FAKE, 4, 8, 2, 2, FAKE, FAKE, None) == INV          # renormalize not 0/1
+    assert g(FAKE, 4, 513, 2, 1, FAKE, FAKE, None) == UNS        # E > 512
+    assert g(None, 4, 8, 2, 1, FAKE, FAKE, None) == INV          # NULL logits
+    assert g(FAKE + 2, 4, 8, 2, 1, FAKE, FAKE, None) == INV      # misaligned
+    assert g(None, 0, 8, 2, 1, None, None, None) == 0            # T = 0 is a no-op
+
+
+def _perm(lib, T=4, E=8, k=2, S=0, P=0, x=FAKE, dt=1, d=64, ws=FAKE, nbytes=1 << 30, **kw):
+    n = ctypes.c_size_t(nbytes)
+    ptrs = dict(ids=FAKE, go=FAKE, s2f=FAKE, f2s=FAKE, xs=FAKE)
+    ptrs.update(kw)
+    return lib.moe_permute(ptrs["ids"], T, E, k, S, P, x, dt, d, ptrs["go"], ptrs["s2f"], ptrs["f2s"],
+                           ptrs["xs"], ws, ctypes.byref(n), None), n.value
+
+
+def test_permute_validation_and_query(lib):
+    assert _perm(lib, k=9)[0] == INV
+    assert _perm(lib, P=5)[0] == INV                 # n_priority > T
+    assert _perm(lib, S=-1)[0] == INV
+    assert _perm(lib, d=12)[0] == UNS                # d % 8
+    assert _perm(lib, dt=7)[0] == UNS                # unknown dtype
+    assert _perm(lib, go=None)[0] == INV
+    assert _perm(lib, xs=None)[0] == INV             # x given without x_sorted
+    assert _perm(lib, xs=FAKE + 8)[0] == INV         # misaligned x_sorted
+    st, need = _perm(lib, T=8192, E=128, k=8, ws=None, nbytes=0)
+    assert st == 0 and need > 0
+    assert _perm(lib, T=8192, E=128, k=8, nbytes=need - 1)[0] == WS
+    st, need_small = _perm(lib, T=4, ws=None, nbytes=0)
+    assert st == 0 and need_small > 0
+
+
+def _ffn(lib, N=64, E=8, S=0, nseg=1, d=64, I=128, dt=1, ws=FAKE, nbytes=1 << 40, **kw):
+    n = ctypes.c_size_t(nbytes)
+    p = dict(xs=FAKE, go=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, h=FAKE)
+    p.update(kw)
+    return lib.moe_grouped_ffn(p["xs"], p["go"], N, E, S, nseg, d, I, p["wg"], p["wu"], p["wd"], dt, p["h"],
+                               ws, ctypes.byref(n), None), n.value
+
+
+def test_ffn_validation_and_query(lib):
+    assert _ffn(lib, nseg=3)[0] == INV
+    assert _ffn(lib, E=0)[0] == INV
+    assert _ffn(lib, d=100)[0] == UNS
+    assert _ffn(lib, I=12)[0] == UNS
+    assert _ffn(lib, dt=5)[0] == UNS
+    assert _ffn(lib, E=600)[0] == UNS
+    assert _ffn(lib, wd=None)[0] == INV
+    assert _ffn(lib, wg=FAKE + 4)[0] == INV
+    st, need = _ffn(lib, N=65536, E=128, d=2048, I=768, ws=None, nbytes=0)
+    assert st == 0 and need >= 65536 * 768 * 2           # holds the bf16 intermediate
+    assert _ffn(lib, N=65536, E=128, d=2048, I=768, nbytes=need - 1)[0] == WS
+    assert _ffn(lib, N=0, ws=FAKE)[0] == 0               # no rows: no-op
+
+
+def test_combine_validation(lib):
+    c = lib.moe_combine
+    assert c(FAKE, FAKE, FAKE, 4, 0, 0, 64, 1, FAKE, None) == INV
+    assert c(FAKE, FAKE, FAKE, 4, 2, 0, 60, 1, FAKE, None) == UNS
+    assert c(FAKE, FAKE, FAKE, 4, 2, 0, 64, 3, FAKE, None) == UNS
+    assert c(None, FAKE, FAKE, 4, 2, 0, 64, 1, FAKE, None) == INV
+    assert c(FAKE, FAKE, FAKE, 4, 2, 0, 64, 1, FAKE + 4, None) == INV
+    assert c(None, None, None, 0, 2, 0, 64, 1, None, None) == 0
+
+
+def _stats(lib, L=1, T=8, k=2, E=8, req=FAKE, R=2, ws=FAKE, nbytes=1 << 30, **kw):
+    n = ctypes.c_size_t(nbytes)
+    p = dict(ids=FAKE, idf=None, counts=FAKE, usize=FAKE, umask=FAKE, aff=FAKE, rc=FAKE, sig=FAKE)
+    p.update(kw)
+    return lib.moe_stats(p["ids"], L, T, k, E, req, R, p["idf"], p["counts"], p["usize"], p["umask"], p["aff"],
+                         p["rc"], p["sig"], ws, ctypes.byref(n), None), n.value
+
+
+def test_stats_validation_and_query(lib):
+    assert _stats(lib, k=9)[0] == INV
+    assert _stats(lib, R=-1)[0] == INV
+    assert _stats(lib, E=1000, k=2)[0] == UNS
+    assert _stats(lib, req=None)[0] == INV           # signature without requests
+    assert _stats(lib, counts=None)[0] == INV
+    st, need = _stats(lib, L=8, T=8192, k=8, E=128, R=128, ws=None, nbytes=0)
+    assert st == 0 and need >= 128 * 8 * 128 * 4
+    assert _stats(lib, L=8, T=8192, k=8, E=128, R=128, nbytes=need - 1)[0] == WS
+    assert _stats(lib, L=0)[0] == 0

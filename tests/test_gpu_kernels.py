@@ -1,0 +1,274 @@
+"""GPU parity of each libmoe call against the CPU oracle, through the C ABI.
+
+Integer outputs (ids, permutation, offsets, counts, union, affinity, request
+counts) must match bit for bit; gate weights within 1e-6 absolute; FFN and
+combine within 1e-2 (bf16) / 1e-5 (fp32) of max |reference|; signatures within
+1e-6 relative.  Inputs are small enough for the oracle to finish in seconds
+but span several tiles and ragged tails; edge cases cover empty batches,
+empty groups, one hot expert, k = E, E = 1, E = 512 and priority segments.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import moe_oracle as O
+from helpers import GATE_W_ATOL, SIG_RTOL, TOL, announce, f64_of, np_of, rel_max_err, require_gpu
+
+import top_expert_routing_amd as moe
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _poison(shape, dtype):
+    t = torch.empty(shape, dtype=dtype, device=DEV)
+    t.view(torch.uint8).fill_(0xFF) if t.numel() else None
+    return t
+
+
+# ------------------------------------------------------------------ gate
+GATE_CASES = [
+    # (T, E, k, renormalize, kind)
+    (1, 8, 2, 1, "normal"), (300, 64, 8, 1, "normal"), (257, 128, 8, 1, "normal"),
+    (64, 8, 8, 1, "normal"), (33, 1, 1, 1, "normal"), (100, 512, 16, 1, "normal"),
+    (129, 96, 5, 0, "normal"), (50, 16, 16, 0, "normal"), (200, 64, 6, 1, "ties"),
+    (200, 130, 7, 1, "ties"), (64, 32, 4, 1, "zeros_nan"), (77, 512, 512, 1, "ties"),
+]
+
+
+def _gate_logits(T, E, kind, seed):
+    g = torch.Generator().manual_seed(seed)
+    lg = torch.randn((T, E), generator=g)
+    if kind == "ties":
+        lg = torch.floor(lg * 2) / 2
+    if kind == "zeros_nan":
+        lg = torch.floor(lg)
+        lg[lg == 0] = -0.0
+        lg[:, ::3] = 0.0
+        lg[::5, 1] = float("nan")
+        lg[::7, 2] = float("-inf")
+    return lg
+
+
+@pytest.mark.parametrize("T,E,k,renorm,kind", GATE_CASES)
+def test_gate_parity(T, E, k, renorm, kind):
+    announce(f"gate T={T} E={E} k={k} renorm={renorm} {kind}")
+    lg = _gate_logits(T, E, kind, seed=T * 1000 + E + k)
+    ids_ref, w_ref = O.gate(lg.numpy(), k, bool(renorm))
+    ids = _poison((T, k), torch.int32)
+    w = _poison((T, k), torch.float32)
+    moe.gate(lg.to(DEV), k, bool(renorm), ids, w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(np_of(ids), ids_ref)
+    got = np_of(w)
+    finite = np.isfinite(w_ref)
+    assert np.abs(got[finite].astype(np.float64) - w_ref[finite]).max(initial=0.0) <= GATE_W_ATOL
+
+
+def test_gate_config_logits_bit_exact():
+    for name in ("tiny", "olmoe_decode", "qwen3_prefill", "dsv2_decode_t256", "gptoss_mixed"):
+        wl = workloads.make(name, DEV, with_weights=False)
+        announce(f"gate {name}")
+        for l in range(wl.stats_logits.shape[0]):
+            lg = wl.stats_logits[l].contiguous()
+            ids, w = moe.gate(lg, wl.spec.k)
+            ids_ref, w_ref = O.gate(np_of(lg), wl.spec.k)
+            np.testing.assert_array_equal(np_of(ids), ids_ref)
+            assert np.abs(np_of(w).astype(np.float64) - w_ref).max() <= GATE_W_ATOL
+
+
+def test_gate_empty_batch():
+    ids = torch.empty((0, 2), dtype=torch.int32, device=DEV)
+    w = torch.empty((0, 2), dtype=torch.float32, device=DEV)
+    moe.gate(torch.empty((0, 8), device=DEV), 2, True, ids, w)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ permute
+PERM_CASES = [
+    # (T, E, k, S, P, d, dtype, kind)
+    (3, 3, 2, 0, 0, 8, torch.float32, "random"),
+    (128, 64, 8, 0, 0, 2048, torch.bfloat16, "random"),
+    (256, 64, 6, 2, 0, 64, torch.bfloat16, "zipf"),
+    (600, 32, 8, 0, 0, 72, torch.float32, "random"),        # 4800 assignments: two chunks, ragged
+    (4160, 128, 4, 0, 64, 40, torch.bfloat16, "zipf"),     # priority segment, five chunks
+    (5000, 16, 2, 1, 5000, 16, torch.bfloat16, "random"),  # every token in the priority segment
+    (777, 8, 1, 0, 1, 24, torch.float32, "one_hot"),       # all tokens to one expert
+    (1100, 512, 4, 3, 0, 8, torch.bfloat16, "random"),
+    (2, 4, 4, 0, 0, 8, torch.float32, "random"),           # k = E
+    (10, 1, 1, 0, 0, 8, torch.float32, "random"),          # E = 1
+    (9000, 8, 8, 0, 0, 0, None, "random"),                 # no row gather, k = E, 18 chunks
+]
+
+
+def _ids(T, E, k, kind, seed):
+    if kind == "one_hot":
+        return torch.full((T, k), E // 2, dtype=torch.int32)
+    if kind == "zipf":
+        lg = torch.randn((T, E), generator=torch.Generator().manual_seed(seed)) - 1.5 * torch.log(
+            torch.arange(1, E + 1, dtype=torch.float32))
+        return torch.topk(lg, k, dim=1).indices.to(torch.int32)
+    return workloads.random_ids(T, E, k, seed)[0]
+
+
+@pytest.mark.parametrize("T,E,k,S,P,d,dtype,kind", PERM_CASES)
+def test_permute_parity(T, E, k, S, P, d, dtype, kind):
+    announce(f"permute T={T} E={E} k={k} S={S} P={P} d={d} {kind}")
+    ids = _ids(T, E, k, kind, seed=T + 7 * E).contiguous()
+    x = None
+    if dtype is not None:
+        x = torch.randn((T, d), generator=torch.Generator().manual_seed(T)).to(dtype)
+    ref = O.permute(ids.numpy(), E, S, P, np_of(x) if x is not None else None)
+    N = T * (k + S)
+    G = (2 if P > 0 else 1) * E + S
+    out = {"group_offsets": _poison(G + 1, torch.int32), "sorted_to_flat": _poison(N, torch.int32),
+           "flat_to_sorted": _poison(N, torch.int32)}
+    if x is not None:
+        out["x_sorted"] = _poison((N, d), dtype)
+    got = moe.permute(ids.to(DEV), E, S, P, x.to(DEV) if x is not None else None, out=out)
+    torch.cuda.synchronize()
+    for key in ("group_offsets", "sorted_to_flat", "flat_to_sorted"):
+        np.testing.assert_array_equal(np_of(got[key]), ref[key], err_msg=key)
+    if x is not None:
+        assert np.array_equal(np_of(got["x_sorted"]), ref["x_sorted"])
+
+
+def test_permute_empty_batch_writes_zero_offsets():
+    out = {"group_offsets": _poison(2 * 8 + 1 + 1, torch.int32),
+           "sorted_to_flat": torch.empty(0, dtype=torch.int32, device=DEV),
+           "flat_to_sorted": torch.empty(0, dtype=torch.int32, device=DEV)}
+    moe.permute(torch.empty((0, 2), dtype=torch.int32, device=DEV), 8, 1, 0, None, out=out)
+    torch.cuda.synchronize()
+    assert (np_of(out["group_offsets"])[:9 + 1] == 0).all()
+
+
+def test_permute_deterministic():
+    ids = workloads.random_ids(8192, 128, 8, seed=11)[0].to(DEV)
+    a = moe.permute(ids, 128, 0, 0)
+    b = moe.permute(ids, 128, 0, 0)
+    torch.cuda.synchronize()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+# ------------------------------------------------------------------ grouped FFN
+FFN_CASES = [
+    # (T, E, k, S, P, d, I, dtype, kind)
+    (64, 8, 2, 0, 0, 128, 256, "f32", "random"),          # the tiny config's shape
+    (40, 6, 2, 1, 9, 40, 24, "f32", "random"),            # tails in d and I, shared + priority
+    (96, 16, 4, 0, 0, 136, 200, "bf16", "random"),        # K and N tails (136 = 2*64 + 8)
+    (300, 8, 2, 0, 0, 256, 192, "bf16", "random"),        # groups far above one tile
+    (50, 64, 8, 2, 0, 128, 88, "bf16", "zipf"),           # hot/cold, empty groups, shared
+    (33, 4, 1, 0, 1, 64, 64, "bf16", "one_hot"),          # one expert takes everything
+    (17, 128, 4, 0, 5, 72, 136, "bf16", "random"),        # priority segment, mostly empty groups
+]
+
+
+def _ffn_inputs(T, E, k, S, P, d, I, dtype, kind, seed):
+    wl = workloads.custom(T=T, E=E, k=k, d=d, I=I, dtype=dtype, S=S, n_priority=P, seed=seed, device="cpu",
+                          w_std=0.08)
+    ids = _ids(T, E, k, kind, seed).contiguous()
+    return wl, ids
+
+
+@pytest.mark.parametrize("T,E,k,S,P,d,I,dtype,kind", FFN_CASES)
+def test_grouped_ffn_parity(T, E, k, S, P, d, I, dtype, kind):
+    announce(f"ffn T={T} E={E} k={k} S={S} P={P} d={d} I={I} {dtype} {kind}")
+    wl, ids = _ffn_inputs(T, E, k, S, P, d, I, dtype, kind, seed=T + E)
+    nseg = 2 if P > 0 else 1
+    p_ref = O.permute(ids.numpy(), E, S, P, np_of(wl.x))
+    h_ref = O.grouped_ffn(p_ref["x_sorted"], p_ref["group_offsets"], E, S, nseg, np_of(wl.w_gate),
+                          np_of(wl.w_up), np_of(wl.w_down), dtype)
+    xs = torch.from_numpy(p_ref["x_sorted"].view(np.int16) if dtype == "bf16" else p_ref["x_sorted"])
+    xs = (xs.view(torch.bfloat16) if dtype == "bf16" else xs).to(DEV)
+    offs = torch.from_numpy(p_ref["group_offsets"]).to(DEV)
+    h = moe.grouped_ffn(xs, offs, E, S, nseg, wl.w_gate.to(DEV), wl.w_up.to(DEV), wl.w_down.to(DEV),
+                        h_sorted=_poison((xs.shape[0], d), xs.dtype))
+    torch.cuda.synchronize()
+    err = rel_max_err(f64_of(h), h_ref)
+    assert err <= TOL[dtype], err
+
+
+# ------------------------------------------------------------------ combine
+COMBINE_CASES = [
+    (64, 2, 0, 128, "f32"), (128, 8, 0, 2048, "bf16"), (256, 6, 2, 2048, "bf16"),
+    (4160, 4, 0, 2880, "bf16"), (7, 3, 1, 24, "f32"), (1, 1, 0, 8, "bf16"),
+]
+
+
+@pytest.mark.parametrize("T,k,S,d,dtype", COMBINE_CASES)
+def test_combine_parity(T, k, S, d, dtype):
+    announce(f"combine T={T} k={k} S={S} d={d} {dtype}")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    gen = torch.Generator().manual_seed(T * 31 + d)
+    N = T * (k + S)
+    h = torch.randn((N, d), generator=gen).to(tdt)
+    f2s = torch.randperm(N, generator=gen).to(torch.int32)
+    w = torch.rand((T, k), generator=gen)
+    y_ref = O.combine(O.to_f64(np_of(h), dtype), f2s.numpy(), w.numpy(), T, k, S)
+    y = moe.combine(h.to(DEV), f2s.to(DEV), w.to(DEV), S, y=_poison((T, d), tdt))
+    torch.cuda.synchronize()
+    assert rel_max_err(f64_of(y), y_ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_combine_identity_experts_k1_returns_input(dtype):
+    """k = 1 and h_sorted := x_sorted: y equals x bit for bit."""
+    announce(f"combine identity {dtype}")
+    T, E, d = 300, 16, 64
+    x = torch.randn((T, d), generator=torch.Generator().manual_seed(5)).to(dtype).to(DEV)
+    lg = torch.randn((T, E), generator=torch.Generator().manual_seed(6)).to(DEV)
+    ids, w = moe.gate(lg, 1)
+    p = moe.permute(ids, E, 0, 0, x)
+    y = moe.combine(p["x_sorted"], p["flat_to_sorted"], w, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(y, x)
+
+
+# ------------------------------------------------------------------ stats
+STATS_CASES = [
+    # (L, T, E, k, req_len, with_idf)
+    (1, 64, 8, 2, 0, False), (8, 8192, 128, 8, 64, False), (1, 128, 64, 8, 1, False),
+    (2, 300, 256, 4, 7, False), (1, 1000, 512, 6, 100, True), (3, 50, 5, 5, 3, False),
+    (1, 0, 16, 2, 1, False),
+]
+
+
+@pytest.mark.parametrize("L,T,E,k,req_len,with_idf", STATS_CASES)
+def test_stats_parity(L, T, E, k, req_len, with_idf):
+    announce(f"stats L={L} T={T} E={E} k={k} req_len={req_len} idf={with_idf}")
+    ids = workloads.random_ids(T, E, k, seed=T + E, L=L)
+    if req_len:
+        offs = list(range(0, T, req_len)) + [T]
+        if T == 0:
+            offs = [0, 0]
+    else:
+        offs = [0, T]
+    req = torch.tensor(offs, dtype=torch.int32)
+    idf = torch.rand((L, E), generator=torch.Generator().manual_seed(3)) if with_idf else None
+    ref = O.stats(ids.numpy(), E, req.numpy(), idf.numpy() if idf is not None else None)
+    R = len(offs) - 1
+    out = {"counts": _poison((L, E), torch.int32), "union_size": _poison(L, torch.int32),
+           "union_mask": _poison((L, E), torch.uint8), "affinity": _poison((L, E, E), torch.int32),
+           "req_counts": _poison((R, L, E), torch.int32), "signature": _poison((R, L, E), torch.float32)}
+    got = moe.stats(ids.to(DEV), E, req.to(DEV), idf.to(DEV) if idf is not None else None, out=out)
+    torch.cuda.synchronize()
+    for key in ("counts", "union_size", "union_mask", "affinity", "req_counts"):
+        np.testing.assert_array_equal(np_of(got[key]), ref[key], err_msg=key)
+    sig, sref = np_of(got["signature"]).astype(np.float64), ref["signature"].astype(np.float64)
+    assert np.all(np.abs(sig - sref) <= SIG_RTOL * np.abs(sref))
+
+
+def test_stats_without_optional_outputs():
+    ids = workloads.random_ids(200, 32, 4, seed=9, L=2)
+    ref = O.stats(ids.numpy(), 32)
+    got = moe.stats(ids.to(DEV), 32, None, affinity=False)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(np_of(got["counts"]), ref["counts"])
+    np.testing.assert_array_equal(np_of(got["union_size"]), ref["union_size"])

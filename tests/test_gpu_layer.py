@@ -1,0 +1,90 @@
+"""End-to-end parity of the whole expert path at the five workload shapes.
+
+The GPU runs the layer exactly as the benchmark does (MoeLayer: gate ->
+permute -> grouped FFN -> combine, plus statistics).  Integer outputs are
+compared with the oracle in full, bit for bit.  x_sorted is checked through
+the property x_sorted[n] == x[token(sorted_to_flat[n])] at full size.  The FFN
+and the layer output are compared on a sample of tokens that the oracle
+computes one by one (every sorted row those tokens need).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import moe_oracle as O
+from helpers import GATE_W_ATOL, SIG_RTOL, TOL, announce, f64_of, np_of, rel_max_err, require_gpu
+
+import top_expert_routing_amd as moe
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+CONFIGS = ["tiny", "olmoe_decode", "olmoe_decode_local", "qwen3_prefill", "dsv2_decode_t16",
+           "dsv2_decode_t64", "dsv2_decode_t128", "dsv2_decode_t256", "gptoss_mixed"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _sample_tokens(T, P, n=12):
+    picks = {0, T - 1, T // 2}
+    if P:
+        picks |= {0, P - 1, P, min(T - 1, P + 1)}
+    rng = np.random.default_rng(T)
+    picks |= set(rng.integers(0, T, size=n).tolist())
+    return np.array(sorted(picks))
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_layer_parity(name):
+    announce(f"layer {name}")
+    wl = workloads.make(name, DEV)
+    s = wl.spec
+    layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, wl.w_gate, wl.w_up, wl.w_down,
+                         n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize),
+                         stats_layers=s.stats_layers, req_offsets=wl.req_offsets, device=DEV)
+    stats_ids = torch.empty((s.stats_layers, s.T, s.k), dtype=torch.int32, device=DEV)
+    for l in range(1, s.stats_layers):
+        moe.gate(wl.stats_logits[l].contiguous(), s.k, True, stats_ids[l], torch.empty((s.T, s.k), device=DEV))
+    layer.forward(wl.logits, wl.x)
+    stats_ids[0].copy_(layer.topk_ids)
+    layer.stats(stats_ids)
+    torch.cuda.synchronize()
+
+    logits = np_of(wl.logits)
+    ids_ref, w_ref = O.gate(logits, s.k, bool(s.renormalize))
+    np.testing.assert_array_equal(np_of(layer.topk_ids), ids_ref)
+    assert np.abs(np_of(layer.topk_w).astype(np.float64) - w_ref).max() <= GATE_W_ATOL
+
+    p_ref = O.permute(ids_ref, s.E, s.S, s.n_priority)
+    for key in ("group_offsets", "sorted_to_flat", "flat_to_sorted"):
+        np.testing.assert_array_equal(np_of(layer.perm[key]), p_ref[key], err_msg=key)
+    s2f = layer.perm["sorted_to_flat"].long()
+    Nr = s.T * s.k
+    tok = torch.where(s2f < Nr, s2f // s.k, (s2f - Nr) % s.T)
+    assert torch.equal(layer.perm["x_sorted"], wl.x.index_select(0, tok))
+
+    # statistics over the layer stack, in full
+    all_ids = np.stack([ids_ref] + [O.gate(np_of(wl.stats_logits[l]), s.k)[0]
+                                    for l in range(1, s.stats_layers)])
+    np.testing.assert_array_equal(np_of(stats_ids), all_ids)
+    st_ref = O.stats(all_ids, s.E, np_of(wl.req_offsets))
+    for key in ("counts", "union_size", "union_mask", "affinity", "req_counts"):
+        np.testing.assert_array_equal(np_of(layer.stats_out[key]), st_ref[key], err_msg=key)
+    sig, sref = np_of(layer.stats_out["signature"]).astype(np.float64), st_ref["signature"].astype(np.float64)
+    assert np.all(np.abs(sig - sref) <= SIG_RTOL * np.abs(sref))
+
+    # FFN rows and outputs for a sample of tokens
+    toks = _sample_tokens(s.T, s.n_priority)
+    ref = O.moe_layer(logits, np_of(wl.x), np_of(wl.w_gate), np_of(wl.w_up), np_of(wl.w_down), s.k,
+                      s.dtype, n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize),
+                      tokens=toks)
+    rows = torch.from_numpy(ref["h_rows"]).to(DEV)
+    h_err = rel_max_err(f64_of(layer.h_sorted.index_select(0, rows)), ref["h"])
+    y_err = rel_max_err(f64_of(layer.y[torch.from_numpy(toks).to(DEV)]), ref["y"])
+    announce(f"layer {name}: h err {h_err:.2e}, y err {y_err:.2e}, union {np_of(layer.stats_out['union_size'])}")
+    assert h_err <= TOL[s.dtype], h_err
+    assert y_err <= TOL[s.dtype], y_err

@@ -1,0 +1,274 @@
+"""Thin torch wrappers over the five libmoe calls.
+
+Argument marshalling only: shapes, dtypes and contiguity are checked, outputs
+and workspaces are allocated with torch on the input's device, and the call is
+enqueued on torch's current stream.  Every step of the path runs in libmoe's
+HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib
+from ._lib import MOE_BF16, MOE_F32, check
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def _workspace(fn, args_before_ws, dev) -> torch.Tensor:
+    """Query a call's workspace size (NULL workspace) and allocate it."""
+    n = ctypes.c_size_t(0)
+    check(fn.__name__, fn(*args_before_ws, None, ctypes.byref(n), None))
+    return torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
+
+
+def gate(logits: torch.Tensor, k: int, renormalize: bool = True,
+         topk_ids: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None):
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    dev = logits.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    check("moe_gate", lib.moe_gate(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(topk_ids),
+                                   _ptr(topk_w), _stream(dev)))
+    return topk_ids, topk_w
+
+
+def permute_workspace_bytes(T, E, k, n_shared=0, n_priority=0) -> int:
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    check("moe_permute", lib.moe_permute(None, T, E, k, n_shared, n_priority, None, MOE_BF16, 8,
+                                         None, None, None, None, None, ctypes.byref(n), None))
+    return int(n.value)
+
+
+def permute(topk_ids: torch.Tensor, E: int, n_shared: int = 0, n_priority: int = 0,
+            x: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None,
+            workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    nseg = 2 if n_priority > 0 else 1
+    G = nseg * E + n_shared
+    N = T * (k + n_shared)
+    d = 8
+    dt = MOE_BF16
+    if x is not None:
+        _need(x, "x", None, 2)
+        d = x.shape[1]
+        dt = _dtype_code(x)
+    o = {} if out is None else out
+    if "group_offsets" not in o:
+        o["group_offsets"] = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    if "sorted_to_flat" not in o:
+        o["sorted_to_flat"] = torch.empty(N, dtype=torch.int32, device=dev)
+    if "flat_to_sorted" not in o:
+        o["flat_to_sorted"] = torch.empty(N, dtype=torch.int32, device=dev)
+    if x is not None and "x_sorted" not in o:
+        o["x_sorted"] = torch.empty((N, d), dtype=x.dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(permute_workspace_bytes(T, E, k, n_shared, n_priority), 256),
+                                dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    nbytes = ctypes.c_size_t(workspace.numel())
+    check("moe_permute", lib.moe_permute(
+        _ptr(topk_ids), T, E, k, n_shared, n_priority, _ptr(x), dt, d,
+        _ptr(o["group_offsets"]), _ptr(o["sorted_to_flat"]), _ptr(o["flat_to_sorted"]),
+        _ptr(o.get("x_sorted")) if x is not None else None,
+        _ptr(workspace), ctypes.byref(nbytes), _stream(dev)))
+    return o
+
+
+def ffn_workspace_bytes(n_rows, E, n_shared, nseg, d, I, dtype=torch.bfloat16) -> int:
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    code = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    check("moe_grouped_ffn", lib.moe_grouped_ffn(None, None, n_rows, E, n_shared, nseg, d, I, None, None,
+                                                 None, code, None, None, ctypes.byref(n), None))
+    return int(n.value)
+
+
+def grouped_ffn(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_shared: int, nseg: int,
+                w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                h_sorted: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(x_sorted, "x_sorted", None, 2)
+    _need(group_offsets, "group_offsets", torch.int32, 1)
+    for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(w, name, x_sorted.dtype, 3)
+    N, d = x_sorted.shape
+    I = w_gate.shape[1]
+    if w_gate.shape != (E + n_shared, I, d) or w_up.shape != w_gate.shape or w_down.shape != (E + n_shared, d, I):
+        raise ValueError("expert weight shapes do not match [E+S][I][d] / [E+S][d][I]")
+    if group_offsets.numel() != nseg * E + n_shared + 1:
+        raise ValueError("group_offsets must have nseg*E + n_shared + 1 entries")
+    dev = x_sorted.device
+    if h_sorted is None:
+        h_sorted = torch.empty((N, d), dtype=x_sorted.dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(ffn_workspace_bytes(N, E, n_shared, nseg, d, I, x_sorted.dtype), 256),
+                                dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    nbytes = ctypes.c_size_t(workspace.numel())
+    check("moe_grouped_ffn", lib.moe_grouped_ffn(
+        _ptr(x_sorted), _ptr(group_offsets), N, E, n_shared, nseg, d, I, _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _dtype_code(x_sorted), _ptr(h_sorted), _ptr(workspace), ctypes.byref(nbytes),
+        _stream(dev)))
+    return h_sorted
+
+
+def combine(h_sorted: torch.Tensor, flat_to_sorted: torch.Tensor, topk_w: torch.Tensor, n_shared: int = 0,
+            y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(h_sorted, "h_sorted", None, 2)
+    _need(flat_to_sorted, "flat_to_sorted", torch.int32, 1)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    T, k = topk_w.shape
+    d = h_sorted.shape[1]
+    if flat_to_sorted.numel() != T * (k + n_shared) or h_sorted.shape[0] != T * (k + n_shared):
+        raise ValueError("h_sorted / flat_to_sorted must have T*(k+n_shared) rows")
+    dev = h_sorted.device
+    if y is None:
+        y = torch.empty((T, d), dtype=h_sorted.dtype, device=dev)
+    lib = _lib.load()
+    check("moe_combine", lib.moe_combine(_ptr(h_sorted), _ptr(flat_to_sorted), _ptr(topk_w), T, k, n_shared,
+                                         d, _dtype_code(h_sorted), _ptr(y), _stream(dev)))
+    return y
+
+
+def stats_workspace_bytes(L, T, k, E, R) -> int:
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    check("moe_stats", lib.moe_stats(None, L, T, k, E, None, R, None, None, None, None, None, None, None,
+                                     None, ctypes.byref(n), None))
+    return int(n.value)
+
+
+def stats(topk_ids: torch.Tensor, E: int, req_offsets: Optional[torch.Tensor] = None,
+          idf: Optional[torch.Tensor] = None, affinity: bool = True, signature: bool = True,
+          out: Optional[Dict[str, torch.Tensor]] = None,
+          workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    _need(topk_ids, "topk_ids", torch.int32, 3)
+    L, T, k = topk_ids.shape
+    dev = topk_ids.device
+    R = 0
+    if req_offsets is not None:
+        _need(req_offsets, "req_offsets", torch.int32, 1)
+        R = req_offsets.numel() - 1
+    if idf is not None:
+        _need(idf, "idf", torch.float32, 2)
+    o = {} if out is None else out
+    o.setdefault("counts", torch.empty((L, E), dtype=torch.int32, device=dev))
+    o.setdefault("union_size", torch.empty(L, dtype=torch.int32, device=dev))
+    o.setdefault("union_mask", torch.empty((L, E), dtype=torch.uint8, device=dev))
+    if affinity:
+        o.setdefault("affinity", torch.empty((L, E, E), dtype=torch.int32, device=dev))
+    if R > 0:
+        o.setdefault("req_counts", torch.empty((R, L, E), dtype=torch.int32, device=dev))
+        if signature:
+            o.setdefault("signature", torch.empty((R, L, E), dtype=torch.float32, device=dev))
+    if workspace is None:
+        workspace = torch.empty(max(stats_workspace_bytes(L, T, k, E, R), 256), dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    nbytes = ctypes.c_size_t(workspace.numel())
+    check("moe_stats", lib.moe_stats(
+        _ptr(topk_ids), L, T, k, E, _ptr(req_offsets), R, _ptr(idf), _ptr(o["counts"]),
+        _ptr(o["union_size"]), _ptr(o["union_mask"]), _ptr(o.get("affinity")), _ptr(o.get("req_counts")),
+        _ptr(o.get("signature")), _ptr(workspace), ctypes.byref(nbytes), _stream(dev)))
+    return o
+
+
+class MoeLayer:
+    """One MoE layer's expert path with every buffer allocated up front.
+
+    `forward()` enqueues gate -> permute -> grouped FFN -> combine and, when
+    `stats_ids` is given, the statistics over that [L][T][k] id stack (the
+    routing layer's own ids are written into stats_ids[0] by the gate).
+    Nothing is allocated per call.
+    """
+
+    def __init__(self, E, k, d, I, T, dtype, w_gate, w_up, w_down, n_shared=0, n_priority=0,
+                 renormalize=True, stats_layers=0, req_offsets=None, device="cuda"):
+        dev = torch.device(device)
+        self.E, self.k, self.d, self.I, self.T = E, k, d, I, T
+        self.S, self.P = n_shared, n_priority
+        self.nseg = 2 if n_priority > 0 else 1
+        self.renormalize = renormalize
+        self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
+        N = T * (k + n_shared)
+        G = self.nseg * E + n_shared
+        self.N, self.G = N, G
+        self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.perm = {"group_offsets": torch.empty(G + 1, dtype=torch.int32, device=dev),
+                     "sorted_to_flat": torch.empty(N, dtype=torch.int32, device=dev),
+                     "flat_to_sorted": torch.empty(N, dtype=torch.int32, device=dev),
+                     "x_sorted": torch.empty((N, d), dtype=dtype, device=dev)}
+        self.perm_ws = torch.empty(max(permute_workspace_bytes(T, E, k, n_shared, n_priority), 256),
+                                   dtype=torch.uint8, device=dev)
+        self.h_sorted = torch.empty((N, d), dtype=dtype, device=dev)
+        self.ffn_ws = torch.empty(max(ffn_workspace_bytes(N, E, n_shared, self.nseg, d, I, dtype), 256),
+                                  dtype=torch.uint8, device=dev)
+        self.y = torch.empty((T, d), dtype=dtype, device=dev)
+        self.stats_out = None
+        self.req_offsets = req_offsets
+        if stats_layers:
+            R = 0 if req_offsets is None else req_offsets.numel() - 1
+            self.stats_out = {}
+            self.stats_ws = torch.empty(max(stats_workspace_bytes(stats_layers, T, k, E, R), 256),
+                                        dtype=torch.uint8, device=dev)
+
+    def gate(self, logits):
+        return gate(logits, self.k, self.renormalize, self.topk_ids, self.topk_w)
+
+    def permute(self, x):
+        return permute(self.topk_ids, self.E, self.S, self.P, x, out=self.perm, workspace=self.perm_ws)
+
+    def ffn(self):
+        return grouped_ffn(self.perm["x_sorted"], self.perm["group_offsets"], self.E, self.S, self.nseg,
+                           self.w_gate, self.w_up, self.w_down, self.h_sorted, self.ffn_ws)
+
+    def combine(self):
+        return combine(self.h_sorted, self.perm["flat_to_sorted"], self.topk_w, self.S, self.y)
+
+    def stats(self, stats_ids):
+        return stats(stats_ids, self.E, self.req_offsets, out=self.stats_out, workspace=self.stats_ws)
+
+    def forward(self, logits, x, stats_ids=None):
+        self.gate(logits)
+        self.permute(x)
+        self.ffn()
+        self.combine()
+        if stats_ids is not None and self.stats_out is not None:
+            self.stats(stats_ids)
+        return self.y

@@ -1,0 +1,197 @@
+// libmoe C ABI: host-side argument checks, workspace queries and launches.
+// Every check happens before anything is enqueued; no call synchronises or
+// reads device memory on the host.
+#include <stdint.h>
+
+#include "../../include/libmoe.h"
+#include "launch.h"
+
+namespace {
+
+constexpr long long kIntMax = 0x7fffffffLL;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool fits_int(long long v) { return v >= 0 && v <= kIntMax; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int elem_bytes(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+bool known_dtype(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+// workspace protocol: NULL buffer -> report the size; else check it is enough
+moe_status workspace_check(void* workspace, size_t* workspace_bytes, size_t need, bool* query) {
+  *query = false;
+  if (workspace_bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  if (workspace == nullptr) {
+    *workspace_bytes = need;
+    *query = true;
+    return MOE_OK;
+  }
+  if (*workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+moe_status moe_gate(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renormalize, int32_t* topk_ids,
+                    float* topk_w, hipStream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if (!fits_int(static_cast<long long>(T) * E)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned4(logits) || !aligned4(topk_ids) || !aligned4(topk_w)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_gate(logits, T, E, k, renormalize, topk_ids, topk_w, stream));
+}
+
+moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k, int32_t n_shared,
+                       int32_t n_priority, const void* x, moe_dtype dtype, int32_t d, int32_t* group_offsets,
+                       int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted, void* workspace,
+                       size_t* workspace_bytes, hipStream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || n_shared < 0 || n_priority < 0 || n_priority > T)
+    return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  const long long N = static_cast<long long>(T) * (k + n_shared);
+  if (!fits_int(N)) return MOE_ERR_UNSUPPORTED;
+  if (x != nullptr) {
+    if (!known_dtype(dtype)) return MOE_ERR_UNSUPPORTED;
+    if (d < 1) return MOE_ERR_INVALID_ARG;
+    if (d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  }
+  bool query;
+  moe_status st = workspace_check(workspace, workspace_bytes,
+                                  moe::permute_workspace_bytes(T, E, k, n_shared, n_priority), &query);
+  if (st != MOE_OK || query) return st;
+  if (!group_offsets || !aligned4(group_offsets)) return MOE_ERR_INVALID_ARG;
+  if (N > 0) {
+    if (!topk_ids || !sorted_to_flat || !flat_to_sorted) return MOE_ERR_INVALID_ARG;
+    if (!aligned4(topk_ids) || !aligned4(sorted_to_flat) || !aligned4(flat_to_sorted)) return MOE_ERR_INVALID_ARG;
+    if (x != nullptr && (!x_sorted || !aligned16(x) || !aligned16(x_sorted))) return MOE_ERR_INVALID_ARG;
+  }
+  moe::PermuteArgs a;
+  a.topk_ids = topk_ids;
+  a.T = T;
+  a.E = E;
+  a.k = k;
+  a.n_shared = n_shared;
+  a.n_priority = n_priority;
+  a.x = N > 0 ? x : nullptr;
+  a.elem_bytes = elem_bytes(dtype);
+  a.d = d;
+  a.group_offsets = group_offsets;
+  a.sorted_to_flat = sorted_to_flat;
+  a.flat_to_sorted = flat_to_sorted;
+  a.x_sorted = x_sorted;
+  return hip_status(moe::launch_permute(a, workspace, stream));
+}
+
+moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* group_offsets, int32_t n_rows, int32_t E,
+                           int32_t n_shared, int32_t nseg, int32_t d, int32_t I, const void* w_gate,
+                           const void* w_up, const void* w_down, moe_dtype dtype, void* h_sorted, void* workspace,
+                           size_t* workspace_bytes, hipStream_t stream) {
+  if (n_rows < 0 || E < 1 || n_shared < 0 || (nseg != 1 && nseg != 2) || d < 1 || I < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if (!known_dtype(dtype) || d % 8 != 0 || I % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
+    return MOE_ERR_UNSUPPORTED;
+  bool query;
+  moe_status st = workspace_check(
+      workspace, workspace_bytes,
+      moe::ffn_workspace_bytes(n_rows, E, n_shared, nseg, d, I, dtype == MOE_BF16 ? 1 : 0), &query);
+  if (st != MOE_OK || query) return st;
+  if (n_rows == 0) return MOE_OK;
+  if (!x_sorted || !group_offsets || !w_gate || !w_up || !w_down || !h_sorted) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_sorted) || !aligned4(group_offsets) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(h_sorted))
+    return MOE_ERR_INVALID_ARG;
+  moe::FfnArgs a;
+  a.x_sorted = x_sorted;
+  a.group_offsets = group_offsets;
+  a.n_rows = n_rows;
+  a.E = E;
+  a.n_shared = n_shared;
+  a.nseg = nseg;
+  a.d = d;
+  a.I = I;
+  a.w_gate = w_gate;
+  a.w_up = w_up;
+  a.w_down = w_down;
+  a.bf16 = dtype == MOE_BF16 ? 1 : 0;
+  a.h_sorted = h_sorted;
+  return hip_status(moe::launch_ffn(a, workspace, stream));
+}
+
+moe_status moe_combine(const void* h_sorted, const int32_t* flat_to_sorted, const float* topk_w, int32_t T, int32_t k,
+                       int32_t n_shared, int32_t d, moe_dtype dtype, void* y, hipStream_t stream) {
+  if (T < 0 || k < 1 || n_shared < 0 || d < 1) return MOE_ERR_INVALID_ARG;
+  if (!known_dtype(dtype) || d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!fits_int(static_cast<long long>(T) * (k + n_shared)) ||
+      !fits_int(static_cast<long long>(T) * (k + n_shared) * (d / 8)))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!h_sorted || !flat_to_sorted || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h_sorted) || !aligned4(flat_to_sorted) || !aligned4(topk_w) || !aligned16(y))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(h_sorted, flat_to_sorted, topk_w, T, k, n_shared, d,
+                                        dtype == MOE_BF16 ? 1 : 0, y, stream));
+}
+
+moe_status moe_stats(const int32_t* topk_ids, int32_t L, int32_t T, int32_t k, int32_t E, const int32_t* req_offsets,
+                     int32_t R, const float* idf, int32_t* counts, int32_t* union_size, uint8_t* union_mask,
+                     int32_t* affinity, int32_t* req_counts, float* signature, void* workspace,
+                     size_t* workspace_bytes, hipStream_t stream) {
+  if (L < 0 || T < 0 || k < 1 || E < 1 || k > E || R < 0) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if (!fits_int(static_cast<long long>(L) * T * k) || !fits_int(static_cast<long long>(L) * E * E) ||
+      !fits_int(static_cast<long long>(R) * L * E))
+    return MOE_ERR_UNSUPPORTED;
+  if (L > 65535 || R > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  if ((req_counts || signature) && !req_offsets) return MOE_ERR_INVALID_ARG;
+  bool query;
+  moe_status st = workspace_check(workspace, workspace_bytes, moe::stats_workspace_bytes(L, T, k, E, R), &query);
+  if (st != MOE_OK || query) return st;
+  if (L == 0) return MOE_OK;
+  if (!counts || !union_size) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && !topk_ids) return MOE_ERR_INVALID_ARG;
+  if (!aligned4(counts) || !aligned4(union_size) || (topk_ids && !aligned4(topk_ids)) ||
+      (affinity && !aligned4(affinity)) || (req_counts && !aligned4(req_counts)) ||
+      (signature && !aligned4(signature)) || (req_offsets && !aligned4(req_offsets)) || (idf && !aligned4(idf)))
+    return MOE_ERR_INVALID_ARG;
+  moe::StatsArgs a;
+  a.topk_ids = topk_ids;
+  a.L = L;
+  a.T = T;
+  a.k = k;
+  a.E = E;
+  a.req_offsets = req_offsets;
+  a.R = req_offsets ? R : 0;
+  a.idf = idf;
+  a.counts = counts;
+  a.union_size = union_size;
+  a.union_mask = union_mask;
+  a.affinity = affinity;
+  a.req_counts = req_counts;
+  a.signature = signature;
+  return hip_status(moe::launch_stats(a, workspace, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal launchers behind the C ABI.  Every launcher enqueues on `stream`,
+// trusts that api.hip has validated its arguments, and returns
+// hipGetLastError() of its last launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_gate(const float* logits, int T, int E, int k, int renormalize, int* topk_ids,
+                       float* topk_w, hipStream_t stream);
+
+// ---- permutation -----------------------------------------------------------
+struct PermuteArgs {
+  const int* topk_ids;
+  int T, E, k, n_shared, n_priority;
+  const void* x;
+  int elem_bytes;  // 2 (bf16) or 4 (f32)
+  int d;
+  int* group_offsets;
+  int* sorted_to_flat;
+  int* flat_to_sorted;
+  void* x_sorted;
+};
+size_t permute_workspace_bytes(int T, int E, int k, int n_shared, int n_priority);
+hipError_t launch_permute(const PermuteArgs& a, void* workspace, hipStream_t stream);
+
+// ---- grouped FFN -----------------------------------------------------------
+struct FfnArgs {
+  const void* x_sorted;
+  const int* group_offsets;
+  int n_rows, E, n_shared, nseg, d, I;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  int bf16;  // 1: bf16 operands, 0: fp32
+  void* h_sorted;
+};
+size_t ffn_workspace_bytes(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16);
+hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream);
+
+// ---- combine ---------------------------------------------------------------
+hipError_t launch_combine(const void* h_sorted, const int* flat_to_sorted, const float* topk_w, int T,
+                          int k, int n_shared, int d, int bf16, void* y, hipStream_t stream);
+
+// ---- statistics ------------------------------------------------------------
+struct StatsArgs {
+  const int* topk_ids;
+  int L, T, k, E;
+  const int* req_offsets;
+  int R;
+  const float* idf;
+  int* counts;
+  int* union_size;
+  uint8_t* union_mask;
+  int* affinity;
+  int* req_counts;
+  float* signature;
+};
+size_t stats_workspace_bytes(int L, int T, int k, int E, int R);
+hipError_t launch_stats(const StatsArgs& a, void* workspace, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,300 @@
+// Dispatch permutation: stable counting sort of the token->expert assignments
+// into contiguous groups, then a gather of the token rows.
+//
+// GRACE-MoE page, section 1: the dispatch exchange sends each token to its
+// experts; on one GPU it becomes this regrouping.  Ordering is (group, flat
+// index), so the result is unique and the kernels must be stable.
+//
+// Assignments are cut into chunks of kChunk; each 256-thread block owns one
+// chunk and each of its four waves a contiguous quarter.  A wave ranks 64
+// consecutive assignments at a time: a bitwise ballot "match" gives every lane
+// the set of lanes with the same group, the rank inside the wave is the
+// popcount of the lower matching lanes, and the lowest matching lane carries
+// the running per-group counter.  Block bases come from an exclusive scan over
+// (group, chunk) in group-major order, so positions are stable across chunks.
+// With one chunk the scan happens inside the same block (one launch).
+// Shared-expert assignments are already in sorted order (f = T*k + s*T + t is
+// the position itself), so they are written directly.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kPerWave = 1024;
+constexpr int kChunk = kWaves * kPerWave;   // 4096 assignments per block
+constexpr int kMaxRoutedGroups = 2 * 512;   // nseg * E
+
+struct PermCtx {
+  const int* ids;
+  int T, E, k, n_priority, Nr, Gr, nbits, nb;
+};
+
+__device__ __forceinline__ int group_of(const PermCtx& c, int i) {
+  const int t = i / c.k;
+  const int e = clamp_id(c.ids[i], c.E);
+  const int seg = (c.n_priority > 0 && t >= c.n_priority) ? 1 : 0;
+  return seg * c.E + e;
+}
+
+// Lanes of this wave holding the same key (all 64 lanes must call).
+__device__ __forceinline__ uint64_t match_any(int key, int nbits) {
+  uint64_t m = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const int bit = (key >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Histogram of one chunk into wave-private counters (pass 1).
+__device__ void chunk_histogram(const PermCtx& c, int b, volatile int* wcnt) {
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  for (int g = lane; g < c.Gr; g += kWave) wcnt[w * kMaxRoutedGroups + g] = 0;
+  const int i0 = b * kChunk + w * kPerWave;
+  for (int it = 0; it < kPerWave; it += kWave) {
+    const int i = i0 + it + lane;
+    if (i0 + it >= c.Nr) break;                       // wave-uniform
+    const bool valid = i < c.Nr;
+    const int g = valid ? group_of(c, i) : c.Gr;
+    const uint64_t m = match_any(g, c.nbits);
+    if (valid && (__ffsll(static_cast<unsigned long long>(m)) - 1) == lane)
+      wcnt[w * kMaxRoutedGroups + g] += __popcll(m);
+  }
+}
+
+// Ranks and scatter (pass 3): wcnt holds each wave's running base per group.
+__device__ void chunk_scatter(const PermCtx& c, int b, volatile int* wcnt, int* s2f, int* f2s) {
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int i0 = b * kChunk + w * kPerWave;
+  for (int it = 0; it < kPerWave; it += kWave) {
+    const int i = i0 + it + lane;
+    if (i0 + it >= c.Nr) break;
+    const bool valid = i < c.Nr;
+    const int g = valid ? group_of(c, i) : c.Gr;
+    const uint64_t m = match_any(g, c.nbits);
+    const int leader = __ffsll(static_cast<unsigned long long>(m)) - 1;
+    int base = 0;
+    if (valid && leader == lane) {
+      base = wcnt[w * kMaxRoutedGroups + g];
+      wcnt[w * kMaxRoutedGroups + g] = base + __popcll(m);
+    }
+    base = __shfl(base, leader, kWave);
+    if (valid) {
+      const int pos = base + __popcll(m & lanemask_lt());
+      s2f[pos] = i;
+      f2s[i] = pos;
+    }
+  }
+}
+
+// Shared-expert assignments sit at their own flat index.
+__device__ void write_shared_identity(int Nr, int N, int nblocks, int b, int* s2f, int* f2s) {
+  for (int f = Nr + b * kThreads + threadIdx.x; f < N; f += nblocks * kThreads) {
+    s2f[f] = f;
+    f2s[f] = f;
+  }
+}
+
+// Exclusive scan of per-thread values across the block; returns the prefix
+// and stores the total in *total.
+__device__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) scratch[w] = incl;
+  __syncthreads();
+  int wbase = 0, tot = 0;
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < w) wbase += scratch[i];
+    tot += scratch[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return wbase + incl - v;
+}
+
+// ---- one chunk: histogram, scan, scatter in one block ------------------------
+__global__ __launch_bounds__(kThreads) void permute_single(PermCtx c, int n_shared, int* group_offsets,
+                                                           int* s2f, int* f2s) {
+  __shared__ int wcnt[kWaves * kMaxRoutedGroups];
+  __shared__ int scratch[kWaves];
+  volatile int* vw = wcnt;
+  chunk_histogram(c, 0, vw);
+  __syncthreads();
+  // each thread owns 4 consecutive groups (Gr <= 1024)
+  constexpr int kPer = kMaxRoutedGroups / kThreads;
+  int tot[kPer];
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int g = threadIdx.x * kPer + q;
+    tot[q] = 0;
+    if (g < c.Gr)
+      for (int w = 0; w < kWaves; ++w) tot[q] += vw[w * kMaxRoutedGroups + g];
+    sum += tot[q];
+  }
+  int total;
+  int run = block_exclusive_scan(sum, scratch, &total);
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int g = threadIdx.x * kPer + q;
+    if (g < c.Gr) {
+      group_offsets[g] = run;
+      int r = run;
+      for (int w = 0; w < kWaves; ++w) {
+        const int cnt = vw[w * kMaxRoutedGroups + g];
+        vw[w * kMaxRoutedGroups + g] = r;
+        r += cnt;
+      }
+    }
+    run += tot[q];
+  }
+  const int N = c.Nr + n_shared * c.T;
+  for (int s = threadIdx.x; s <= n_shared; s += kThreads) group_offsets[c.Gr + s] = c.Nr + s * c.T;
+  __syncthreads();
+  chunk_scatter(c, 0, vw, s2f, f2s);
+  write_shared_identity(c.Nr, N, 1, 0, s2f, f2s);
+}
+
+// ---- several chunks: count, scan, scatter -----------------------------------
+__global__ __launch_bounds__(kThreads) void permute_count(PermCtx c, int* blk) {
+  __shared__ int hist[kMaxRoutedGroups];
+  for (int g = threadIdx.x; g < c.Gr; g += kThreads) hist[g] = 0;
+  __syncthreads();
+  const int b = blockIdx.x;
+  const int lo = b * kChunk, hi = min(c.Nr, lo + kChunk);
+  for (int i = lo + threadIdx.x; i < hi; i += kThreads) atomicAdd(&hist[group_of(c, i)], 1);
+  __syncthreads();
+  for (int g = threadIdx.x; g < c.Gr; g += kThreads) blk[g * c.nb + b] = hist[g];
+}
+
+__global__ __launch_bounds__(1024) void permute_scan(PermCtx c, int n_shared, int* blk, int* group_offsets) {
+  __shared__ int part[1024];
+  const int M = c.Gr * c.nb;
+  const int per = (M + 1023) / 1024;
+  const int lo = threadIdx.x * per, hi = min(M, lo + per);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += blk[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the 1024 partial sums
+  for (int o = 1; o < 1024; o <<= 1) {
+    int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - s;
+  for (int i = lo; i < hi; ++i) {
+    const int v = blk[i];
+    blk[i] = run;
+    if (i % c.nb == 0) group_offsets[i / c.nb] = run;
+    run += v;
+  }
+  for (int q = threadIdx.x; q <= n_shared; q += 1024) group_offsets[c.Gr + q] = c.Nr + q * c.T;
+}
+
+__global__ __launch_bounds__(kThreads) void permute_scatter(PermCtx c, int n_shared, const int* blk, int* s2f,
+                                                            int* f2s) {
+  __shared__ int wcnt[kWaves * kMaxRoutedGroups];
+  volatile int* vw = wcnt;
+  const int b = blockIdx.x;
+  chunk_histogram(c, b, vw);
+  __syncthreads();
+  for (int g = threadIdx.x; g < c.Gr; g += kThreads) {
+    int r = blk[g * c.nb + b];
+    for (int w = 0; w < kWaves; ++w) {
+      const int cnt = vw[w * kMaxRoutedGroups + g];
+      vw[w * kMaxRoutedGroups + g] = r;
+      r += cnt;
+    }
+  }
+  __syncthreads();
+  chunk_scatter(c, b, vw, s2f, f2s);
+  write_shared_identity(c.Nr, c.Nr + n_shared * c.T, c.nb, b, s2f, f2s);
+}
+
+// ---- row gather: x_sorted[n] = x[token(sorted_to_flat[n])] ---------------------
+__global__ __launch_bounds__(kThreads) void permute_gather(const uint4* __restrict__ x, const int* __restrict__ s2f,
+                                                           int T, int k, int Nr, int N, int row_vecs,
+                                                           uint4* __restrict__ xs) {
+  const int lane = lane_id();
+  const int waves = gridDim.x * kWaves;
+  for (int n = blockIdx.x * kWaves + (threadIdx.x >> 6); n < N; n += waves) {
+    const int f = s2f[n];
+    const int t = f < Nr ? f / k : (f - Nr) % T;
+    const uint4* src = x + static_cast<size_t>(t) * row_vecs;
+    uint4* dst = xs + static_cast<size_t>(n) * row_vecs;
+    for (int v = lane; v < row_vecs; v += kWave) dst[v] = src[v];
+  }
+}
+
+int bits_for(int v) {
+  int b = 0;
+  while ((1 << b) <= v) ++b;
+  return b;
+}
+
+PermCtx make_ctx(const PermuteArgs& a) {
+  PermCtx c;
+  c.ids = a.topk_ids;
+  c.T = a.T;
+  c.E = a.E;
+  c.k = a.k;
+  c.n_priority = a.n_priority;
+  c.Nr = a.T * a.k;
+  c.Gr = (a.n_priority > 0 ? 2 : 1) * a.E;
+  c.nbits = bits_for(c.Gr);
+  c.nb = c.Nr > 0 ? (c.Nr + kChunk - 1) / kChunk : 1;
+  return c;
+}
+
+}  // namespace
+
+size_t permute_workspace_bytes(int T, int E, int k, int n_shared, int n_priority) {
+  (void)n_shared;
+  const long long Nr = static_cast<long long>(T) * k;
+  const long long nb = Nr > 0 ? (Nr + kChunk - 1) / kChunk : 1;
+  const long long Gr = static_cast<long long>(n_priority > 0 ? 2 : 1) * E;
+  if (nb <= 1) return 256;   // single-block path uses no workspace
+  return static_cast<size_t>(((Gr * nb * 4) + 255) / 256 * 256);
+}
+
+hipError_t launch_permute(const PermuteArgs& a, void* workspace, hipStream_t stream) {
+  const PermCtx c = make_ctx(a);
+  const int N = c.Nr + a.n_shared * a.T;
+  if (c.nb == 1) {
+    hipLaunchKernelGGL(permute_single, dim3(1), dim3(kThreads), 0, stream, c, a.n_shared, a.group_offsets,
+                       a.sorted_to_flat, a.flat_to_sorted);
+  } else {
+    int* blk = static_cast<int*>(workspace);
+    hipLaunchKernelGGL(permute_count, dim3(c.nb), dim3(kThreads), 0, stream, c, blk);
+    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(1024), 0, stream, c, a.n_shared, blk, a.group_offsets);
+    hipLaunchKernelGGL(permute_scatter, dim3(c.nb), dim3(kThreads), 0, stream, c, a.n_shared,
+                       static_cast<const int*>(blk), a.sorted_to_flat, a.flat_to_sorted);
+  }
+  if (a.x != nullptr && N > 0) {
+    const int row_vecs = a.d * a.elem_bytes / 16;
+    int blocks = (N + kWaves - 1) / kWaves;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(permute_gather, dim3(blocks), dim3(kThreads), 0, stream, static_cast<const uint4*>(a.x),
+                       a.sorted_to_flat, a.T, a.k, c.Nr, N, row_vecs, static_cast<uint4*>(a.x_sorted));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark one MoE layer's expert path on one MI355X.
+
+A step is one pass of the whole path over one batch: softmax top-k gate ->
+dispatch permutation -> grouped SwiGLU FFN -> combine, plus the expert
+statistics over the workload's layer stack.  Inputs are synthetic, already in
+HBM when the timed region starts.  The default workload is the OLMoE-shaped
+decode step (T=128 tokens, E=64, top-8, d=2048, I=1024, bf16).
+
+Expert weights rotate over several copies (one per simulated layer) so that
+each step streams its weights from HBM rather than from the 256 MB last-level
+cache, as a model cycling through its layers would.
+
+Prints ONE JSON line: MoE-layer tokens/s, the dominant kernel's roofline (the
+grouped FFN: HBM-bound at decode sizes, MFMA-bound at prefill sizes), and the
+CPU oracle timed on this host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA util vs MI355X peak"
+FFN_SOURCE = os.path.join(ROOT, "top_expert_routing_amd", "csrc", "ffn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="olmoe_decode")
+    ap.add_argument("--weight-copies", type=int, default=0,
+                    help="expert-weight copies to rotate over (0: enough to exceed 3 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle leg")
+    ap.add_argument("--json-out", default="", help="also append the JSON line to this file")
+    return ap.parse_args()
+
+
+def ffn_source_hash() -> str:
+    with open(FFN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(workload: str, launches_alg_bytes: float):
+    """HBM bytes per FFN call from the committed rocprofv3 counter summary,
+    scaled by the copy-kernel calibration; None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("ffn_source_sha256_16") != ffn_source_hash():
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    if not w:
+        return None
+    scale = float(rec.get("copy_calibration", 1.0))
+    return (w["fetch_kib_per_call"] + w["write_kib_per_call"]) * 1024.0 * scale
+
+
+def cpu_baseline(wl, budget_s: float):
+    """Time the CPU oracle (as it stands) on a bounded sample of the workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+    from oracle import moe_oracle as O
+
+    def host(t):
+        t = t.detach().contiguous().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    s = wl.spec
+    logits, x = host(wl.logits), host(wl.x)
+    wg, wu, wd = host(wl.w_gate), host(wl.w_up), host(wl.w_down)
+    # sample: the first n tokens (whole batch when it is small), whole layer path
+    n = s.T if s.T <= 256 else 256
+    toks = np.arange(n)
+    t0 = time.perf_counter()
+    done = 0
+    passes = 0
+    while True:
+        O.moe_layer(logits, x, wg, wu, wd, s.k, s.dtype, n_shared=s.S, n_priority=s.n_priority, tokens=toks)
+        ids, _ = O.gate(logits[:n], s.k)
+        O.stats(ids[None], s.E, np.arange(n + 1, dtype=np.int32))
+        done += n
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or passes >= 20 or el * (passes + 1) / passes > 2.5 * budget_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {s.T} tokens, whole layer path (gate, permute, FFN on their rows, "
+                      f"combine) plus their statistics, {passes} pass(es) in {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the expert path here has no multi-GPU mode "
+              "(no collectives, no sharding); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import top_expert_routing_amd as moe
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.load()
+
+    wl = workloads.make(args.workload, dev)
+    s = wl.spec
+    esize = 4 if s.dtype == "f32" else 2
+    expert_bytes = 3 * s.d * s.I * esize
+    all_w = (s.E + s.S) * expert_bytes
+    copies = args.weight_copies or max(1, int(np.ceil(3 * 2**30 / all_w)))
+    wsets = [(wl.w_gate, wl.w_up, wl.w_down)]
+    for _ in range(copies - 1):
+        wsets.append((wl.w_gate.clone(), wl.w_up.clone(), wl.w_down.clone()))
+
+    # the gate writes the routing layer's ids straight into layer 0 of the
+    # statistics stack
+    stats_ids = torch.empty((s.stats_layers, s.T, s.k), dtype=torch.int32, device=dev)
+    layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, wl.w_gate, wl.w_up, wl.w_down,
+                         n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize),
+                         stats_layers=s.stats_layers, req_offsets=wl.req_offsets, device=dev,
+                         topk_ids=stats_ids[0])
+    for l in range(1, s.stats_layers):      # the other layers' ids, produced before timing
+        moe.gate(wl.stats_logits[l].contiguous(), s.k, True, stats_ids[l],
+                 torch.empty((s.T, s.k), device=dev))
+    stream = torch.cuda.current_stream(dev)
+    call_sets = []
+    for wg, wu, wd in wsets:
+        layer.w_gate, layer.w_up, layer.w_down = wg, wu, wd
+        call_sets.append(layer.bound_calls(wl.logits, wl.x, stats_ids, stream.cuda_stream))
+    def step(i, ev=None):
+        calls = call_sets[i % copies]
+        for j, (name, fn, a) in enumerate(calls):
+            if ev is not None:
+                ev[j].record(stream)
+            st = fn(*a)
+            if st != 0:
+                raise moe.MoeError(name, st)
+        if ev is not None:
+            ev[len(calls)].record(stream)
+
+    names = [c[0] for c in call_sets[0]]
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    per_call = {n: 0.0 for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            per_call[n] += e[j].elapsed_time(e[j + 1]) / K     # ms
+
+    # algorithmic work of the FFN call
+    union = int(layer.stats_out["union_size"][0].item()) if layer.stats_out else s.E
+    used_experts = union + s.S
+    N = s.N
+    ffn_bytes = used_experts * expert_bytes + 2 * N * s.d * esize
+    ffn_flops = 2.0 * N * 3 * s.d * s.I
+    ffn_s = per_call["moe_grouped_ffn"] * 1e-3
+    peak_flops = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
+    intensity = ffn_flops / ffn_bytes
+    ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if intensity < ridge:
+        achieved = ffn_bytes / ffn_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = ffn_flops / ffn_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_flops, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_flops, 4)}
+    traffic = traffic_for(args.workload, ffn_bytes)
+    roof["traffic"] = None if traffic is None else round(traffic)
+    roof["kernel"] = "moe_grouped_ffn (tile plan + gate/up + down launches)"
+    roof["algorithmic_bytes"] = int(ffn_bytes)
+    roof["algorithmic_flops"] = int(ffn_flops)
+    roof["avg_call_us"] = round(ffn_s * 1e6, 2)
+
+    tokens_per_s = s.T * K / elapsed
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "T": s.T, "E": s.E, "k": s.k, "n_shared": s.S, "d": s.d,
+                   "I": s.I, "n_priority": s.n_priority, "stats_layers": s.stats_layers,
+                   "weight_copies": copies, "union": union},
+        "roofline": roof,
+        "per_call_us": {n: round(v * 1e3, 2) for n, v in per_call.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "a") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

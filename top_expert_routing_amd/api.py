@@ -218,7 +218,7 @@ class MoeLayer:
     """
 
     def __init__(self, E, k, d, I, T, dtype, w_gate, w_up, w_down, n_shared=0, n_priority=0,
-                 renormalize=True, stats_layers=0, req_offsets=None, device="cuda"):
+                 renormalize=True, stats_layers=0, req_offsets=None, device="cuda", topk_ids=None):
         dev = torch.device(device)
         self.E, self.k, self.d, self.I, self.T = E, k, d, I, T
         self.S, self.P = n_shared, n_priority
@@ -228,7 +228,9 @@ class MoeLayer:
         N = T * (k + n_shared)
         G = self.nseg * E + n_shared
         self.N, self.G = N, G
-        self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        # the gate may write straight into a caller buffer (e.g. one layer of a
+        # statistics id stack)
+        self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_ids is None else topk_ids
         self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
         self.perm = {"group_offsets": torch.empty(G + 1, dtype=torch.int32, device=dev),
                      "sorted_to_flat": torch.empty(N, dtype=torch.int32, device=dev),
@@ -263,6 +265,55 @@ class MoeLayer:
 
     def stats(self, stats_ids):
         return stats(stats_ids, self.E, self.req_offsets, out=self.stats_out, workspace=self.stats_ws)
+
+    def bound_calls(self, logits, x, stats_ids=None, stream=None):
+        """Pre-marshalled raw C calls for one forward over fixed buffers.
+
+        Returns a list of (name, fn, args) whose arguments are plain integers,
+        so a timing loop pays only the ctypes call per step.  Each entry is one
+        of the five libmoe calls, in path order.
+        """
+        lib = _lib.load()
+        dev = logits.device
+        st = _stream(dev) if stream is None else stream
+        k, T, E = self.k, self.T, self.E
+        dt = _dtype_code(x)
+        n_perm = ctypes.c_size_t(self.perm_ws.numel())
+        n_ffn = ctypes.c_size_t(self.ffn_ws.numel())
+        calls = [
+            ("moe_gate", lib.moe_gate, (logits.data_ptr(), T, E, k, int(bool(self.renormalize)),
+                                        self.topk_ids.data_ptr(), self.topk_w.data_ptr(), st)),
+            ("moe_permute", lib.moe_permute, (self.topk_ids.data_ptr(), T, E, k, self.S, self.P, x.data_ptr(), dt,
+                                              self.d, self.perm["group_offsets"].data_ptr(),
+                                              self.perm["sorted_to_flat"].data_ptr(),
+                                              self.perm["flat_to_sorted"].data_ptr(),
+                                              self.perm["x_sorted"].data_ptr(), self.perm_ws.data_ptr(),
+                                              ctypes.byref(n_perm), st)),
+            ("moe_grouped_ffn", lib.moe_grouped_ffn, (self.perm["x_sorted"].data_ptr(),
+                                                      self.perm["group_offsets"].data_ptr(), self.N, E, self.S,
+                                                      self.nseg, self.d, self.I, self.w_gate.data_ptr(),
+                                                      self.w_up.data_ptr(), self.w_down.data_ptr(), dt,
+                                                      self.h_sorted.data_ptr(), self.ffn_ws.data_ptr(),
+                                                      ctypes.byref(n_ffn), st)),
+            ("moe_combine", lib.moe_combine, (self.h_sorted.data_ptr(), self.perm["flat_to_sorted"].data_ptr(),
+                                              self.topk_w.data_ptr(), T, k, self.S, self.d, dt, self.y.data_ptr(),
+                                              st)),
+        ]
+        if stats_ids is not None and self.stats_out is not None:
+            o = self.stats(stats_ids)          # allocates the outputs once
+            L = stats_ids.shape[0]
+            R = 0 if self.req_offsets is None else self.req_offsets.numel() - 1
+            n_st = ctypes.c_size_t(self.stats_ws.numel())
+
+            def p(key):
+                return o[key].data_ptr() if key in o else None
+            calls.append(("moe_stats", lib.moe_stats, (
+                stats_ids.data_ptr(), L, T, k, E,
+                self.req_offsets.data_ptr() if self.req_offsets is not None else None, R, None,
+                p("counts"), p("union_size"), p("union_mask"), p("affinity"), p("req_counts"), p("signature"),
+                self.stats_ws.data_ptr(), ctypes.byref(n_st), st)))
+        self._keep = (n_perm, n_ffn)
+        return calls
 
     def forward(self, logits, x, stats_ids=None):
         self.gate(logits)

@@ -29,7 +29,8 @@
  *   - Errors are returned synchronously as moe_status and nothing is enqueued:
  *       MOE_ERR_INVALID_ARG  negative sizes, k < 1, k > E, n_priority > T,
  *                            NULL required pointer, misaligned pointer
- *       MOE_ERR_UNSUPPORTED  E > 512, d or I not a multiple of 8, unknown dtype,
+ *       MOE_ERR_UNSUPPORTED  E > 512, n_shared > 256, d or I not a multiple of 8,
+ *                            unknown dtype,
  *                            sizes whose element counts overflow int32
  *       MOE_ERR_WORKSPACE    workspace smaller than the queried size
  *       MOE_ERR_HIP          a HIP launch reported an error (after enqueueing)
@@ -67,8 +68,9 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-/* Largest expert count the kernels accept. */
+/* Largest routed-expert and shared-expert counts the kernels accept. */
 #define MOE_MAX_EXPERTS 512
+#define MOE_MAX_SHARED 256
 
 /*
  * moe_gate - softmax top-k gate over fp32 router logits.

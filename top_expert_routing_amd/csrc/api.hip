@@ -3,7 +3,7 @@
 // reads device memory on the host.
 #include <stdint.h>
 
-#include "../../include/libmoe.h"
+#include "libmoe.h"
 #include "launch.h"
 
 namespace {
@@ -68,7 +68,7 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
                        size_t* workspace_bytes, hipStream_t stream) {
   if (T < 0 || E < 1 || k < 1 || k > E || n_shared < 0 || n_priority < 0 || n_priority > T)
     return MOE_ERR_INVALID_ARG;
-  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
   const long long N = static_cast<long long>(T) * (k + n_shared);
   if (!fits_int(N)) return MOE_ERR_UNSUPPORTED;
   if (x != nullptr) {
@@ -109,7 +109,7 @@ moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* group_offsets, i
                            size_t* workspace_bytes, hipStream_t stream) {
   if (n_rows < 0 || E < 1 || n_shared < 0 || (nseg != 1 && nseg != 2) || d < 1 || I < 1)
     return MOE_ERR_INVALID_ARG;
-  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
   if (!known_dtype(dtype) || d % 8 != 0 || I % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
     return MOE_ERR_UNSUPPORTED;

@@ -56,41 +56,61 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
+// Each lane keeps the groups of its (up to) 16 assignments of the chunk in
+// registers: loaded once, used by the histogram and by the scatter pass.
+constexpr int kIters = kPerWave / kWave;   // 16
+
+__device__ __forceinline__ void load_groups(const PermCtx& c, int b, int (&grp)[kIters]) {
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int i0 = b * kChunk + w * kPerWave;
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int i = i0 + it * kWave + lane;
+    grp[it] = i < c.Nr ? group_of(c, i) : c.Gr;    // c.Gr: sentinel, matches no real group
+  }
+}
+
 // Histogram of one chunk into wave-private counters (pass 1).
-__device__ void chunk_histogram(const PermCtx& c, int b, volatile int* wcnt) {
+__device__ __forceinline__ void chunk_histogram(const PermCtx& c, int b, const int (&grp)[kIters], int* wcnt) {
   const int w = threadIdx.x >> 6, lane = lane_id();
   for (int g = lane; g < c.Gr; g += kWave) wcnt[w * kMaxRoutedGroups + g] = 0;
   const int i0 = b * kChunk + w * kPerWave;
-  for (int it = 0; it < kPerWave; it += kWave) {
-    const int i = i0 + it + lane;
-    if (i0 + it >= c.Nr) break;                       // wave-uniform
-    const bool valid = i < c.Nr;
-    const int g = valid ? group_of(c, i) : c.Gr;
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    if (i0 + it * kWave >= c.Nr) break;               // wave-uniform
+    const int g = grp[it];
     const uint64_t m = match_any(g, c.nbits);
-    if (valid && (__ffsll(static_cast<unsigned long long>(m)) - 1) == lane)
-      wcnt[w * kMaxRoutedGroups + g] += __popcll(m);
+    if (g < c.Gr && (__ffsll(static_cast<unsigned long long>(m)) - 1) == lane)
+      wcnt[w * kMaxRoutedGroups + g] += __popcll(static_cast<unsigned long long>(m));
   }
 }
 
 // Ranks and scatter (pass 3): wcnt holds each wave's running base per group.
-__device__ void chunk_scatter(const PermCtx& c, int b, volatile int* wcnt, int* s2f, int* f2s) {
+// Only the leader lane of a group touches its counter; a wave's LDS accesses
+// execute in program order, so the next leader of that group reads the
+// updated value.  The counters are plain LDS (not volatile): a volatile access
+// through a generic pointer becomes a flat access that waits on every
+// outstanding global store.
+__device__ __forceinline__ void chunk_scatter(const PermCtx& c, int b, const int (&grp)[kIters], int* wcnt, int* s2f,
+                                              int* f2s) {
   const int w = threadIdx.x >> 6, lane = lane_id();
   const int i0 = b * kChunk + w * kPerWave;
-  for (int it = 0; it < kPerWave; it += kWave) {
-    const int i = i0 + it + lane;
-    if (i0 + it >= c.Nr) break;
-    const bool valid = i < c.Nr;
-    const int g = valid ? group_of(c, i) : c.Gr;
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    if (i0 + it * kWave >= c.Nr) break;
+    const int i = i0 + it * kWave + lane;
+    const int g = grp[it];
+    const bool valid = g < c.Gr;
     const uint64_t m = match_any(g, c.nbits);
     const int leader = __ffsll(static_cast<unsigned long long>(m)) - 1;
     int base = 0;
     if (valid && leader == lane) {
       base = wcnt[w * kMaxRoutedGroups + g];
-      wcnt[w * kMaxRoutedGroups + g] = base + __popcll(m);
+      wcnt[w * kMaxRoutedGroups + g] = base + __popcll(static_cast<unsigned long long>(m));
     }
     base = __shfl(base, leader, kWave);
     if (valid) {
-      const int pos = base + __popcll(m & lanemask_lt());
+      const int pos = base + __popcll(static_cast<unsigned long long>(m & lanemask_lt()));
       s2f[pos] = i;
       f2s[i] = pos;
     }
@@ -98,7 +118,7 @@ __device__ void chunk_scatter(const PermCtx& c, int b, volatile int* wcnt, int* 
 }
 
 // Shared-expert assignments sit at their own flat index.
-__device__ void write_shared_identity(int Nr, int N, int nblocks, int b, int* s2f, int* f2s) {
+__device__ __forceinline__ void write_shared_identity(int Nr, int N, int nblocks, int b, int* s2f, int* f2s) {
   for (int f = Nr + b * kThreads + threadIdx.x; f < N; f += nblocks * kThreads) {
     s2f[f] = f;
     f2s[f] = f;
@@ -107,7 +127,7 @@ __device__ void write_shared_identity(int Nr, int N, int nblocks, int b, int* s2
 
 // Exclusive scan of per-thread values across the block; returns the prefix
 // and stores the total in *total.
-__device__ int block_exclusive_scan(int v, int* scratch, int* total) {
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
   const int lane = lane_id(), w = threadIdx.x >> 6;
   int incl = v;
 #pragma unroll
@@ -132,8 +152,10 @@ __global__ __launch_bounds__(kThreads) void permute_single(PermCtx c, int n_shar
                                                            int* s2f, int* f2s) {
   __shared__ int wcnt[kWaves * kMaxRoutedGroups];
   __shared__ int scratch[kWaves];
-  volatile int* vw = wcnt;
-  chunk_histogram(c, 0, vw);
+  int* vw = wcnt;
+  int grp[kIters];
+  load_groups(c, 0, grp);
+  chunk_histogram(c, 0, grp, vw);
   __syncthreads();
   // each thread owns 4 consecutive groups (Gr <= 1024)
   constexpr int kPer = kMaxRoutedGroups / kThreads;
@@ -166,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void permute_single(PermCtx c, int n_shar
   const int N = c.Nr + n_shared * c.T;
   for (int s = threadIdx.x; s <= n_shared; s += kThreads) group_offsets[c.Gr + s] = c.Nr + s * c.T;
   __syncthreads();
-  chunk_scatter(c, 0, vw, s2f, f2s);
+  chunk_scatter(c, 0, grp, vw, s2f, f2s);
   write_shared_identity(c.Nr, N, 1, 0, s2f, f2s);
 }
 
@@ -211,9 +233,11 @@ __global__ __launch_bounds__(1024) void permute_scan(PermCtx c, int n_shared, in
 __global__ __launch_bounds__(kThreads) void permute_scatter(PermCtx c, int n_shared, const int* blk, int* s2f,
                                                             int* f2s) {
   __shared__ int wcnt[kWaves * kMaxRoutedGroups];
-  volatile int* vw = wcnt;
+  int* vw = wcnt;
   const int b = blockIdx.x;
-  chunk_histogram(c, b, vw);
+  int grp[kIters];
+  load_groups(c, b, grp);
+  chunk_histogram(c, b, grp, vw);
   __syncthreads();
   for (int g = threadIdx.x; g < c.Gr; g += kThreads) {
     int r = blk[g * c.nb + b];
@@ -224,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void permute_scatter(PermCtx c, int n_sha
     }
   }
   __syncthreads();
-  chunk_scatter(c, b, vw, s2f, f2s);
+  chunk_scatter(c, b, grp, vw, s2f, f2s);
   write_shared_identity(c.Nr, c.Nr + n_shared * c.T, c.nb, b, s2f, f2s);
 }
 

@@ -6,15 +6,18 @@
 // sections 3-4: co-activation (affinity) and per-expert load from recorded
 // top-k selections.
 //
-// Three launches, all integer work exact and order independent:
-//   stats_layer   one block per (layer, tile of affinity rows): LDS-privatised
-//                 co-activation counts (every ordered slot pair of a token),
-//                 written out without global atomics; tile 0 also writes the
-//                 counts, union mask and union size.
-//   stats_request one block per (request, layer): LDS histogram of the
-//                 request's tokens.
-//   stats_idf     one block per layer: document frequency over the requests,
-//                 idf = ln(R/df) in double (or the caller's idf), signature.
+// Two launches; all integer work is exact and order independent.
+//   stats_count  grid (affinity row tiles + request chunks) x layers, two
+//                block roles:
+//                * affinity tile: LDS-privatised co-activation counts of every
+//                  ordered slot pair of each token whose first expert falls in
+//                  the tile's 16 rows, written out without global atomics;
+//                  tile 0 also writes counts, union mask and union size.
+//                * request chunk: LDS histograms of up to kReqChunk requests
+//                  (tokens placed by binary search over the request offsets).
+//   stats_idf    grid (64-expert chunks) x layers: document frequency over the
+//                requests, idf = ln(R/df) in double (or the caller's idf), and
+//                the signature.
 #include "common.h"
 #include "launch.h"
 
@@ -23,39 +26,98 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kAffLdsInts = 16384;   // 64 KiB of affinity counters per block
+constexpr int kLdsInts = 16384;       // 64 KiB of LDS counters per block
+constexpr int kAffRows = 16;          // affinity rows per tile
+constexpr int kReqChunk = 32;         // requests per histogram block
+constexpr int kIdsBuf = 4096;         // staged token ids per chunk
 
-__global__ __launch_bounds__(kThreads) void stats_layer(const int* __restrict__ ids, int T, int k, int E,
-                                                        int rows_per_tile, int* __restrict__ counts,
-                                                        int* __restrict__ union_size, uint8_t* __restrict__ union_mask,
-                                                        int* __restrict__ affinity) {
-  __shared__ int aff[kAffLdsInts];
+struct StatsGeom {
+  int aff_tiles, rows_per_tile, req_chunks, rc;
+};
+
+StatsGeom geometry(int E, int R, bool want_aff, bool want_req) {
+  StatsGeom g;
+  g.rows_per_tile = want_aff ? (E < kAffRows ? E : kAffRows) : E;
+  g.aff_tiles = want_aff ? (E + g.rows_per_tile - 1) / g.rows_per_tile : 1;
+  g.rc = kLdsInts / E;
+  if (g.rc > kReqChunk) g.rc = kReqChunk;
+  g.req_chunks = want_req && R > 0 ? (R + g.rc - 1) / g.rc : 0;
+  return g;
+}
+
+__global__ __launch_bounds__(kThreads) void stats_count(const int* __restrict__ ids, int L, int T, int k, int E,
+                                                        StatsGeom geo, int* __restrict__ counts,
+                                                        int* __restrict__ union_size,
+                                                        uint8_t* __restrict__ union_mask, int* __restrict__ affinity,
+                                                        const int* __restrict__ req_offsets, int R,
+                                                        int* __restrict__ req_counts) {
+  __shared__ int lds[kLdsInts];
   __shared__ int cnt[MOE_MAX_EXPERTS_DEV];
+  __shared__ int offs[kReqChunk + 1];
   __shared__ int red[kThreads / kWave];
+  __shared__ int idbuf[kIdsBuf];
   const int l = blockIdx.y;
-  const int r0 = blockIdx.x * rows_per_tile;
-  const int rows = min(rows_per_tile, E - r0);
+  const int* lid = ids + static_cast<size_t>(l) * T * k;
+
+  if (static_cast<int>(blockIdx.x) >= geo.aff_tiles) {
+    // ---- request chunk: histograms of requests [r0, r0 + nr) ----
+    const int r0 = (blockIdx.x - geo.aff_tiles) * geo.rc;
+    const int nr = min(geo.rc, R - r0);
+    for (int i = threadIdx.x; i < nr * E; i += kThreads) lds[i] = 0;
+    for (int i = threadIdx.x; i <= nr; i += kThreads) offs[i] = max(0, min(req_offsets[r0 + i], T));
+    __syncthreads();
+    const int t_lo = offs[0], t_hi = max(offs[0], offs[nr]);
+    // one thread per (token, slot): coalesced, independent loads
+    for (int i = t_lo * k + threadIdx.x; i < t_hi * k; i += kThreads) {
+      const int t = i / k;
+      int lo = 0, hi = nr;                 // last r with offs[r] <= t
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (offs[mid] <= t) lo = mid; else hi = mid;
+      }
+      if (t >= offs[lo + 1]) continue;     // not inside request lo (offsets not increasing)
+      atomicAdd(&lds[lo * E + clamp_id(lid[i], E)], 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nr * E; i += kThreads) {
+      const int r = r0 + i / E, e = i % E;
+      req_counts[(static_cast<size_t>(r) * L + l) * E + e] = lds[i];
+    }
+    return;
+  }
+
+  // ---- affinity tile: rows [a0, a0 + rows) of M^T M; tile 0 also counts ----
+  // Token ids are staged through LDS in coalesced chunks; each thread then
+  // walks the slot pairs of one token.
+  const int a0 = blockIdx.x * geo.rows_per_tile;
+  const int rows = min(geo.rows_per_tile, E - a0);
   const bool want_aff = affinity != nullptr;
   const bool tile0 = blockIdx.x == 0;
   if (want_aff)
-    for (int i = threadIdx.x; i < rows * E; i += kThreads) aff[i] = 0;
+    for (int i = threadIdx.x; i < rows * E; i += kThreads) lds[i] = 0;
   for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
-  __syncthreads();
-  const int* lid = ids + static_cast<size_t>(l) * T * k;
-  // one token per thread; every ordered slot pair (a, b) with a in this tile
-  for (int t = threadIdx.x; t < T; t += kThreads) {
-    const int* row = lid + static_cast<size_t>(t) * k;
-    for (int j1 = 0; j1 < k; ++j1) {
-      const int a = clamp_id(row[j1], E);
-      if (tile0) atomicAdd(&cnt[a], 1);
-      if (!want_aff || a < r0 || a >= r0 + rows) continue;
-      for (int j2 = 0; j2 < k; ++j2) atomicAdd(&aff[(a - r0) * E + clamp_id(row[j2], E)], 1);
+  const int tb = kIdsBuf / k;            // tokens per staged chunk (k <= 512)
+  for (int t0 = 0; t0 < T; t0 += tb) {
+    const int nt = min(tb, T - t0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nt * k; i += kThreads)
+      idbuf[i] = clamp_id(lid[static_cast<size_t>(t0) * k + i], E);
+    __syncthreads();
+    for (int tt = threadIdx.x; tt < nt; tt += kThreads) {
+      const int* row = idbuf + tt * k;
+      for (int j1 = 0; j1 < k; ++j1) {
+        const int a = row[j1];
+        if (tile0) atomicAdd(&cnt[a], 1);
+        if (!want_aff || a < a0 || a >= a0 + rows) continue;
+        int* dst = lds + (a - a0) * E;
+        for (int j2 = 0; j2 < k; ++j2) atomicAdd(&dst[row[j2]], 1);
+      }
     }
   }
   __syncthreads();
   if (want_aff) {
-    int* dst = affinity + (static_cast<size_t>(l) * E + r0) * E;
-    for (int i = threadIdx.x; i < rows * E; i += kThreads) dst[i] = aff[i];
+    int* dst = affinity + (static_cast<size_t>(l) * E + a0) * E;
+    for (int i = threadIdx.x; i < rows * E; i += kThreads) dst[i] = lds[i];
   }
   if (!tile0) return;
   int nz = 0;
@@ -75,41 +137,63 @@ __global__ __launch_bounds__(kThreads) void stats_layer(const int* __restrict__ 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void stats_request(const int* __restrict__ ids, int L, int T, int k, int E,
-                                                          const int* __restrict__ req_offsets,
-                                                          int* __restrict__ req_counts) {
-  __shared__ int cnt[MOE_MAX_EXPERTS_DEV];
-  const int r = blockIdx.x, l = blockIdx.y;
-  for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
-  __syncthreads();
-  int lo = req_offsets[r], hi = req_offsets[r + 1];
-  lo = max(0, min(lo, T));
-  hi = max(lo, min(hi, T));
-  const int* lid = ids + static_cast<size_t>(l) * T * k;
-  for (int i = lo * k + threadIdx.x; i < hi * k; i += kThreads) atomicAdd(&cnt[clamp_id(lid[i], E)], 1);
-  __syncthreads();
-  int* dst = req_counts + (static_cast<size_t>(r) * L + l) * E;
-  for (int e = threadIdx.x; e < E; e += kThreads) dst[e] = cnt[e];
-}
+// One block per (64-expert chunk, layer): lanes own an expert, the four waves
+// split the requests; loads are issued 8 at a time so their latencies overlap.
+constexpr int kBatch = 8;
 
 __global__ __launch_bounds__(kThreads) void stats_idf(int L, int E, int R, const int* __restrict__ req_counts,
-                                                      const float* __restrict__ idf_in, float* __restrict__ signature) {
-  __shared__ double idf[MOE_MAX_EXPERTS_DEV];
-  const int l = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += kThreads) {
+                                                      const float* __restrict__ idf_in,
+                                                      float* __restrict__ signature) {
+  constexpr int kW = kThreads / kWave;
+  __shared__ int dfp[kW][kWave];
+  __shared__ double idf[kWave];
+  const int l = blockIdx.y;
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int e = blockIdx.x * kWave + lane;
+  const bool ok = e < E;
+  const int ec = ok ? e : 0;
+  const size_t rstride = static_cast<size_t>(L) * E;
+  const int* base = req_counts + static_cast<size_t>(l) * E + ec;
+  int df = 0;
+  if (!idf_in) {
+    for (int r0 = w; r0 < R; r0 += kW * kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int r = r0 + b * kW;
+        v[b] = (ok && r < R) ? base[static_cast<size_t>(r) * rstride] : 0;
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) df += v[b] > 0;
+    }
+  }
+  dfp[w][lane] = df;
+  __syncthreads();
+  if (w == 0 && ok) {
     if (idf_in) {
-      idf[e] = static_cast<double>(idf_in[static_cast<size_t>(l) * E + e]);
+      idf[lane] = static_cast<double>(idf_in[static_cast<size_t>(l) * E + e]);
     } else {
-      int df = 0;
-      for (int r = 0; r < R; ++r) df += req_counts[(static_cast<size_t>(r) * L + l) * E + e] > 0 ? 1 : 0;
-      idf[e] = df > 0 ? log(static_cast<double>(R) / static_cast<double>(df)) : 0.0;
+      int d = 0;
+      for (int i = 0; i < kW; ++i) d += dfp[i][lane];
+      idf[lane] = d > 0 ? log(static_cast<double>(R) / static_cast<double>(d)) : 0.0;
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < R * E; i += kThreads) {
-    const int r = i / E, e = i % E;
-    const size_t at = (static_cast<size_t>(r) * L + l) * E + e;
-    signature[at] = static_cast<float>(static_cast<double>(req_counts[at]) * idf[e]);
+  if (!ok) return;
+  const double f = idf[lane];
+  float* sbase = signature + static_cast<size_t>(l) * E + e;
+  for (int r0 = w; r0 < R; r0 += kW * kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int r = r0 + b * kW;
+      v[b] = r < R ? base[static_cast<size_t>(r) * rstride] : 0;
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int r = r0 + b * kW;
+      if (r < R) sbase[static_cast<size_t>(r) * rstride] = static_cast<float>(static_cast<double>(v[b]) * f);
+    }
   }
 }
 
@@ -118,29 +202,22 @@ __global__ __launch_bounds__(kThreads) void stats_idf(int L, int E, int R, const
 size_t stats_workspace_bytes(int L, int T, int k, int E, int R) {
   (void)T;
   (void)k;
-  // per-request counts are needed for the signature even when the caller does
-  // not ask for them
+  // request counts go through the workspace when the caller wants only the
+  // signature
   return static_cast<size_t>(((static_cast<long long>(R) * L * E * 4) + 255) / 256 * 256 + 256);
 }
 
 hipError_t launch_stats(const StatsArgs& a, void* workspace, hipStream_t stream) {
   if (a.L == 0) return hipSuccess;
-  int rows_per_tile = a.E;
-  if (a.affinity) {
-    rows_per_tile = kAffLdsInts / a.E;
-    if (rows_per_tile > a.E) rows_per_tile = a.E;
-  }
-  const int tiles = a.affinity ? (a.E + rows_per_tile - 1) / rows_per_tile : 1;
-  hipLaunchKernelGGL(stats_layer, dim3(tiles, a.L), dim3(kThreads), 0, stream, a.topk_ids, a.T, a.k, a.E,
-                     rows_per_tile, a.counts, a.union_size, a.union_mask, a.affinity);
-  if (a.req_offsets && a.R > 0 && (a.req_counts || a.signature)) {
-    int* rc = a.req_counts ? a.req_counts : static_cast<int*>(workspace);
-    hipLaunchKernelGGL(stats_request, dim3(a.R, a.L), dim3(kThreads), 0, stream, a.topk_ids, a.L, a.T, a.k, a.E,
-                       a.req_offsets, rc);
-    if (a.signature)
-      hipLaunchKernelGGL(stats_idf, dim3(a.L), dim3(kThreads), 0, stream, a.L, a.E, a.R,
-                         static_cast<const int*>(rc), a.idf, a.signature);
-  }
+  const bool want_req = a.req_offsets && a.R > 0 && (a.req_counts || a.signature);
+  const StatsGeom geo = geometry(a.E, a.R, a.affinity != nullptr, want_req);
+  int* rc = a.req_counts ? a.req_counts : static_cast<int*>(workspace);
+  hipLaunchKernelGGL(stats_count, dim3(geo.aff_tiles + geo.req_chunks, a.L), dim3(kThreads), 0, stream, a.topk_ids,
+                     a.L, a.T, a.k, a.E, geo, a.counts, a.union_size, a.union_mask, a.affinity, a.req_offsets, a.R,
+                     rc);
+  if (want_req && a.signature)
+    hipLaunchKernelGGL(stats_idf, dim3((a.E + kWave - 1) / kWave, a.L), dim3(kThreads), 0, stream, a.L, a.E, a.R,
+                       static_cast<const int*>(rc), a.idf, a.signature);
   return hipGetLastError();
 }
 

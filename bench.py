@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle leg")
     ap.add_argument("--json-out", default="", help="also append the JSON line to this file")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (scale for HBM byte counters) and exit")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of replaying one captured HIP graph per step")
     return ap.parse_args()
 
 
@@ -122,6 +126,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        # known traffic: each copy reads 1 GiB and writes 1 GiB
+        src = torch.empty(2**30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 2**30, "copies": 3}), flush=True)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     moe.load()
@@ -146,40 +159,72 @@ def main():
     for l in range(1, s.stats_layers):      # the other layers' ids, produced before timing
         moe.gate(wl.stats_logits[l].contiguous(), s.k, True, stats_ids[l],
                  torch.empty((s.T, s.k), device=dev))
-    stream = torch.cuda.current_stream(dev)
+    # The statistics only need the gate's ids: they run on a second stream
+    # (default priority), concurrently with permute -> FFN -> combine.
+    stream = torch.cuda.Stream(dev)
+    side = torch.cuda.Stream(dev)
     call_sets = []
     for wg, wu, wd in wsets:
         layer.w_gate, layer.w_up, layer.w_down = wg, wu, wd
-        call_sets.append(layer.bound_calls(wl.logits, wl.x, stats_ids, stream.cuda_stream))
+        call_sets.append(layer.bound_calls(wl.logits, wl.x, stats_ids, stream.cuda_stream, side.cuda_stream))
+    names = [c[0] for c in call_sets[0]]
+
     def step(i, ev=None):
-        calls = call_sets[i % copies]
-        for j, (name, fn, a) in enumerate(calls):
+        """One layer step on `stream` (statistics forked onto `side`)."""
+        for j, (name, fn, a) in enumerate(call_sets[i % copies]):
+            s_ = side if name == "moe_stats" else stream
+            if name == "moe_stats":
+                side.wait_stream(stream)          # after the gate
             if ev is not None:
-                ev[j].record(stream)
+                ev[j][0].record(s_)
             st = fn(*a)
             if st != 0:
                 raise moe.MoeError(name, st)
-        if ev is not None:
-            ev[len(calls)].record(stream)
+            if ev is not None:
+                ev[j][1].record(s_)
+        if "moe_stats" in names:
+            stream.wait_stream(side)
 
-    names = [c[0] for c in call_sets[0]]
-    for i in range(args.warmup):
-        step(i)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
     torch.cuda.synchronize()
 
+    # headline: K steps, each one replay of a captured HIP graph of the whole
+    # step (one graph per weight copy), or eager launches with --eager
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
+    graphs = []
+    if not args.eager:
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(c)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        step(i, evs[i])
+    with torch.cuda.stream(stream):
+        for i in range(K):
+            if graphs:
+                graphs[i % copies].replay()
+            else:
+                step(i)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
+    elapsed = time.perf_counter() - t0
+
+    # per-call durations: K eager steps with HIP events around every call, on
+    # the stream each call runs on
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+           for _ in range(K)]
+    with torch.cuda.stream(stream):
+        for i in range(K):
+            step(i, evs[i])
+    torch.cuda.synchronize()
     per_call = {n: 0.0 for n in names}
     for e in evs:
         for j, n in enumerate(names):
-            per_call[n] += e[j].elapsed_time(e[j + 1]) / K     # ms
+            per_call[n] += e[j][0].elapsed_time(e[j][1]) / K     # ms
 
     # algorithmic work of the FFN call
     union = int(layer.stats_out["union_size"][0].item()) if layer.stats_out else s.E
@@ -201,7 +246,7 @@ def main():
                 "frac": round(achieved / peak_flops, 4)}
     traffic = traffic_for(args.workload, ffn_bytes)
     roof["traffic"] = None if traffic is None else round(traffic)
-    roof["kernel"] = "moe_grouped_ffn (tile plan + gate/up + down launches)"
+    roof["kernel"] = "moe_grouped_ffn (gate/up launch + down launch), HIP events over K eager steps"
     roof["algorithmic_bytes"] = int(ffn_bytes)
     roof["algorithmic_flops"] = int(ffn_flops)
     roof["avg_call_us"] = round(ffn_s * 1e6, 2)
@@ -216,6 +261,7 @@ def main():
                    "weight_copies": copies, "union": union},
         "roofline": roof,
         "per_call_us": {n: round(v * 1e3, 2) for n, v in per_call.items()},
+        "timing": "eager launches" if args.eager else "one captured HIP graph of the whole step replayed per step",
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

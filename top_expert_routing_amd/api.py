@@ -266,12 +266,14 @@ class MoeLayer:
     def stats(self, stats_ids):
         return stats(stats_ids, self.E, self.req_offsets, out=self.stats_out, workspace=self.stats_ws)
 
-    def bound_calls(self, logits, x, stats_ids=None, stream=None):
+    def bound_calls(self, logits, x, stats_ids=None, stream=None, stats_stream=None):
         """Pre-marshalled raw C calls for one forward over fixed buffers.
 
         Returns a list of (name, fn, args) whose arguments are plain integers,
         so a timing loop pays only the ctypes call per step.  Each entry is one
-        of the five libmoe calls, in path order.
+        of the five libmoe calls, in path order.  `stats_stream` (a raw stream
+        handle) puts the statistics call on its own stream; the caller orders it
+        after the gate.
         """
         lib = _lib.load()
         dev = logits.device
@@ -311,15 +313,27 @@ class MoeLayer:
                 stats_ids.data_ptr(), L, T, k, E,
                 self.req_offsets.data_ptr() if self.req_offsets is not None else None, R, None,
                 p("counts"), p("union_size"), p("union_mask"), p("affinity"), p("req_counts"), p("signature"),
-                self.stats_ws.data_ptr(), ctypes.byref(n_st), st)))
-        self._keep = (n_perm, n_ffn)
+                self.stats_ws.data_ptr(), ctypes.byref(n_st), st if stats_stream is None else stats_stream)))
+        self._keep = (n_perm, n_ffn, n_st if stats_ids is not None and self.stats_out is not None else None)
         return calls
 
-    def forward(self, logits, x, stats_ids=None):
+    def forward(self, logits, x, stats_ids=None, stats_stream=None):
+        """Enqueue the layer on the current stream.  With `stats_stream` (a
+        torch stream) the statistics run there, concurrently with the permute /
+        FFN / combine chain; the current stream waits for them at the end."""
         self.gate(logits)
+        side = stats_ids is not None and self.stats_out is not None
+        if side and stats_stream is not None:
+            main = torch.cuda.current_stream(logits.device)
+            stats_stream.wait_stream(main)
+            with torch.cuda.stream(stats_stream):
+                self.stats(stats_ids)
+            side = False
         self.permute(x)
         self.ffn()
         self.combine()
-        if stats_ids is not None and self.stats_out is not None:
+        if side:
             self.stats(stats_ids)
+        elif stats_ids is not None and self.stats_out is not None:
+            torch.cuda.current_stream(logits.device).wait_stream(stats_stream)
         return self.y

@@ -12,7 +12,8 @@
 // popcount of the lower matching lanes, and the lowest matching lane carries
 // the running per-group counter.  Block bases come from an exclusive scan over
 // (group, chunk) in group-major order, so positions are stable across chunks.
-// With one chunk the scan happens inside the same block (one launch).
+// Small batches (<= 4096 routed assignments) take a one-launch path in which
+// every block recomputes the histogram it needs (see permute_small).
 // Shared-expert assignments are already in sorted order (f = T*k + s*T + t is
 // the position itself), so they are written directly.
 #include "common.h"
@@ -147,49 +148,122 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   return wbase + incl - v;
 }
 
-// ---- one chunk: histogram, scan, scatter in one block ------------------------
-__global__ __launch_bounds__(kThreads) void permute_single(PermCtx c, int n_shared, int* group_offsets,
-                                                           int* s2f, int* f2s) {
-  __shared__ int wcnt[kWaves * kMaxRoutedGroups];
+// Copy rows src_row(j) -> dst_row(j) for j < nrows, 16 bytes per element,
+// flattened over the block so consecutive threads touch consecutive bytes of a
+// row; kCopyBatch loads are issued before their stores so a thread keeps
+// several requests in flight instead of one load->store round trip at a time.
+constexpr int kCopyBatch = 8;
+
+template <typename SrcRow, typename DstRow>
+__device__ __forceinline__ void copy_rows(const uint4* __restrict__ x, uint4* __restrict__ xs, int nrows,
+                                          int row_vecs, SrcRow src_row, DstRow dst_row) {
+  const int total = nrows * row_vecs;
+  for (int base = threadIdx.x; base < total; base += kThreads * kCopyBatch) {
+    uint4 v[kCopyBatch];
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; ++u) {
+      const int idx = base + u * kThreads;
+      if (idx < total) {
+        const int j = idx / row_vecs, c = idx % row_vecs;
+        v[u] = x[static_cast<size_t>(src_row(j)) * row_vecs + c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; ++u) {
+      const int idx = base + u * kThreads;
+      if (idx < total) {
+        const int j = idx / row_vecs, c = idx % row_vecs;
+        xs[static_cast<size_t>(dst_row(j)) * row_vecs + c] = v[u];
+      }
+    }
+  }
+}
+
+// ---- small batches: one launch, many blocks, no inter-block communication ----
+// Block b ranks assignments [16b, 16b+16).  Every block builds the histogram of
+// all routed assignments and of those before its chunk (the whole id array is
+// a few KiB and sits in L2), so it knows its group bases without waiting for
+// any other block.  One wave ranks the chunk with a ballot match; then the four
+// waves gather the chunk's token rows.  Shared-expert rows are split evenly
+// over the blocks.
+constexpr int kSmallChunk = 16;   // assignments ranked (and rows gathered) per block
+constexpr int kSmallMaxNr = 4096;
+
+__global__ __launch_bounds__(kThreads) void permute_small(PermCtx c, int n_shared, int* __restrict__ group_offsets,
+                                                          int* __restrict__ s2f, int* __restrict__ f2s,
+                                                          const uint4* __restrict__ x, int row_vecs,
+                                                          uint4* __restrict__ xs) {
+  __shared__ int total[kMaxRoutedGroups];
+  __shared__ int before[kMaxRoutedGroups];
   __shared__ int scratch[kWaves];
-  int* vw = wcnt;
-  int grp[kIters];
-  load_groups(c, 0, grp);
-  chunk_histogram(c, 0, grp, vw);
+  __shared__ int pos_s[kSmallChunk];
+  __shared__ int tok_s[kSmallChunk];
+  const int b = blockIdx.x, nb = gridDim.x;
+  const int lo = b * kSmallChunk, hi = min(c.Nr, lo + kSmallChunk);
+  for (int g = threadIdx.x; g < c.Gr; g += kThreads) {
+    total[g] = 0;
+    before[g] = 0;
+  }
   __syncthreads();
-  // each thread owns 4 consecutive groups (Gr <= 1024)
+  for (int i = threadIdx.x; i < c.Nr; i += kThreads) {
+    const int g = group_of(c, i);
+    atomicAdd(&total[g], 1);
+    if (i < lo) atomicAdd(&before[g], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the totals: thread owns 4 consecutive groups
   constexpr int kPer = kMaxRoutedGroups / kThreads;
-  int tot[kPer];
+  int own[kPer];
   int sum = 0;
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     const int g = threadIdx.x * kPer + q;
-    tot[q] = 0;
-    if (g < c.Gr)
-      for (int w = 0; w < kWaves; ++w) tot[q] += vw[w * kMaxRoutedGroups + g];
-    sum += tot[q];
+    own[q] = g < c.Gr ? total[g] : 0;
+    sum += own[q];
   }
-  int total;
-  int run = block_exclusive_scan(sum, scratch, &total);
+  int tot;
+  int run = block_exclusive_scan(sum, scratch, &tot);
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     const int g = threadIdx.x * kPer + q;
     if (g < c.Gr) {
-      group_offsets[g] = run;
-      int r = run;
-      for (int w = 0; w < kWaves; ++w) {
-        const int cnt = vw[w * kMaxRoutedGroups + g];
-        vw[w * kMaxRoutedGroups + g] = r;
-        r += cnt;
-      }
+      before[g] += run;                 // now: first sorted row of this chunk's part of group g
+      if (b == 0) group_offsets[g] = run;
     }
-    run += tot[q];
+    run += own[q];
   }
-  const int N = c.Nr + n_shared * c.T;
-  for (int s = threadIdx.x; s <= n_shared; s += kThreads) group_offsets[c.Gr + s] = c.Nr + s * c.T;
+  if (b == 0)
+    for (int s = threadIdx.x; s <= n_shared; s += kThreads) group_offsets[c.Gr + s] = c.Nr + s * c.T;
   __syncthreads();
-  chunk_scatter(c, 0, grp, vw, s2f, f2s);
-  write_shared_identity(c.Nr, N, 1, 0, s2f, f2s);
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int i = lo + lane;
+    const bool valid = i < hi;
+    const int g = valid ? group_of(c, i) : c.Gr;
+    const uint64_t m = match_any(g, c.nbits);
+    int pos = -1;
+    if (valid) {
+      pos = before[g] + __popcll(static_cast<unsigned long long>(m & lanemask_lt()));
+      s2f[pos] = i;
+      f2s[i] = pos;
+    }
+    pos_s[lane] = pos;
+    tok_s[lane] = valid ? i / c.k : 0;
+  }
+  // shared-expert rows [Nr + b*per, ...): position == flat index
+  const int N = c.Nr + n_shared * c.T;
+  const int sper = (N - c.Nr + nb - 1) / nb;
+  const int s_lo = c.Nr + b * sper, s_hi = min(N, s_lo + sper);
+  for (int f = s_lo + threadIdx.x; f < s_hi; f += kThreads) {
+    s2f[f] = f;
+    f2s[f] = f;
+  }
+  __syncthreads();
+  if (x == nullptr) return;
+  const int nvalid = hi > lo ? hi - lo : 0;        // chunk entries are a prefix of pos_s
+  copy_rows(x, xs, nvalid, row_vecs, [&](int j) { return tok_s[j]; }, [&](int j) { return pos_s[j]; });
+  copy_rows(x, xs, s_hi > s_lo ? s_hi - s_lo : 0, row_vecs, [&](int j) { return (s_lo + j - c.Nr) % c.T; },
+            [&](int j) { return s_lo + j; });
 }
 
 // ---- several chunks: count, scan, scatter -----------------------------------
@@ -253,18 +327,21 @@ __global__ __launch_bounds__(kThreads) void permute_scatter(PermCtx c, int n_sha
 }
 
 // ---- row gather: x_sorted[n] = x[token(sorted_to_flat[n])] ---------------------
+// Each block copies kGatherRows consecutive sorted rows.
+constexpr int kGatherRows = 16;
+
 __global__ __launch_bounds__(kThreads) void permute_gather(const uint4* __restrict__ x, const int* __restrict__ s2f,
                                                            int T, int k, int Nr, int N, int row_vecs,
                                                            uint4* __restrict__ xs) {
-  const int lane = lane_id();
-  const int waves = gridDim.x * kWaves;
-  for (int n = blockIdx.x * kWaves + (threadIdx.x >> 6); n < N; n += waves) {
-    const int f = s2f[n];
-    const int t = f < Nr ? f / k : (f - Nr) % T;
-    const uint4* src = x + static_cast<size_t>(t) * row_vecs;
-    uint4* dst = xs + static_cast<size_t>(n) * row_vecs;
-    for (int v = lane; v < row_vecs; v += kWave) dst[v] = src[v];
+  __shared__ int tok[kGatherRows];
+  const int n0 = blockIdx.x * kGatherRows;
+  const int nr = min(kGatherRows, N - n0);
+  if (threadIdx.x < nr) {
+    const int f = s2f[n0 + threadIdx.x];
+    tok[threadIdx.x] = f < Nr ? f / k : (f - Nr) % T;
   }
+  __syncthreads();
+  copy_rows(x, xs, nr, row_vecs, [&](int j) { return tok[j]; }, [&](int j) { return n0 + j; });
 }
 
 int bits_for(int v) {
@@ -294,27 +371,29 @@ size_t permute_workspace_bytes(int T, int E, int k, int n_shared, int n_priority
   const long long Nr = static_cast<long long>(T) * k;
   const long long nb = Nr > 0 ? (Nr + kChunk - 1) / kChunk : 1;
   const long long Gr = static_cast<long long>(n_priority > 0 ? 2 : 1) * E;
-  if (nb <= 1) return 256;   // single-block path uses no workspace
+  if (Nr <= kSmallMaxNr) return 256;   // the one-launch path uses no workspace
   return static_cast<size_t>(((Gr * nb * 4) + 255) / 256 * 256);
 }
 
 hipError_t launch_permute(const PermuteArgs& a, void* workspace, hipStream_t stream) {
   const PermCtx c = make_ctx(a);
   const int N = c.Nr + a.n_shared * a.T;
-  if (c.nb == 1) {
-    hipLaunchKernelGGL(permute_single, dim3(1), dim3(kThreads), 0, stream, c, a.n_shared, a.group_offsets,
-                       a.sorted_to_flat, a.flat_to_sorted);
-  } else {
-    int* blk = static_cast<int*>(workspace);
-    hipLaunchKernelGGL(permute_count, dim3(c.nb), dim3(kThreads), 0, stream, c, blk);
-    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(1024), 0, stream, c, a.n_shared, blk, a.group_offsets);
-    hipLaunchKernelGGL(permute_scatter, dim3(c.nb), dim3(kThreads), 0, stream, c, a.n_shared,
-                       static_cast<const int*>(blk), a.sorted_to_flat, a.flat_to_sorted);
+  const int row_vecs = a.x != nullptr ? a.d * a.elem_bytes / 16 : 0;
+  if (c.Nr <= kSmallMaxNr) {
+    // one launch: ranks, scatter and row gather together
+    const int nb = c.Nr > 0 ? (c.Nr + kSmallChunk - 1) / kSmallChunk : 1;
+    hipLaunchKernelGGL(permute_small, dim3(nb), dim3(kThreads), 0, stream, c, a.n_shared, a.group_offsets,
+                       a.sorted_to_flat, a.flat_to_sorted, static_cast<const uint4*>(a.x), row_vecs,
+                       static_cast<uint4*>(a.x_sorted));
+    return hipGetLastError();
   }
+  int* blk = static_cast<int*>(workspace);
+  hipLaunchKernelGGL(permute_count, dim3(c.nb), dim3(kThreads), 0, stream, c, blk);
+  hipLaunchKernelGGL(permute_scan, dim3(1), dim3(1024), 0, stream, c, a.n_shared, blk, a.group_offsets);
+  hipLaunchKernelGGL(permute_scatter, dim3(c.nb), dim3(kThreads), 0, stream, c, a.n_shared,
+                     static_cast<const int*>(blk), a.sorted_to_flat, a.flat_to_sorted);
   if (a.x != nullptr && N > 0) {
-    const int row_vecs = a.d * a.elem_bytes / 16;
-    int blocks = (N + kWaves - 1) / kWaves;
-    if (blocks > 8192) blocks = 8192;
+    const int blocks = (N + kGatherRows - 1) / kGatherRows;
     hipLaunchKernelGGL(permute_gather, dim3(blocks), dim3(kThreads), 0, stream, static_cast<const uint4*>(a.x),
                        a.sorted_to_flat, a.T, a.k, c.Nr, N, row_vecs, static_cast<uint4*>(a.x_sorted));
   }

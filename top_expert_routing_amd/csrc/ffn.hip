@@ -117,22 +117,10 @@ inline int item_grid(int max_tiles, int nch) {
   return static_cast<int>((items + kXcds - 1) / kXcds * kXcds);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
-
-// Weight row of local row `lr` of a weight tile whose output columns start at
-// `n0`: phase 1 tiles hold `half` gate rows then the matching `half` up rows,
-// phase 2 tiles hold down rows.  Returns nullptr past the last column.
-template <int PHASE>
-__device__ __forceinline__ const uint16_t* weight_row(const uint16_t* W0, const uint16_t* W1, size_t expert_off,
-                                                      int Ncols, int K, int n0, int lr, int half) {
-  int n = n0 + lr;
-  const uint16_t* W = W0;
-  if (PHASE == 1 && lr >= half) {
-    n -= half;
-    W = W1;
-  }
-  if (n >= Ncols) return nullptr;
-  return W + expert_off + static_cast<size_t>(n) * K;
+// silu(g) * u for the bf16 kernels (their result is rounded to bf16, so the
+// hardware reciprocal's 1-ulp error is far below the output precision)
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // ---- decode-sized tiles: weights stream from HBM straight into MFMA registers ----
@@ -210,22 +198,19 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
 #pragma unroll
     for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_a(0);
-  store_a(0);
-  for (int c = 0; c < nchunks; ++c) {
+  // weight loads of chunk c (zero past K; a lane's 8 values are all in range or
+  // all out)
+  auto load_b = [&](uint4 (&b)[U][NF], int c) {
     const int kc = c * kDecodeKC;
-    uint4 b[U][NF];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kk = kc + 32 * u + 8 * q;    // a lane's 8 values are all in range or all out
+      const int kk = kc + 32 * u + 8 * q;
 #pragma unroll
       for (int j = 0; j < NF; ++j)
         b[u][j] = kk < K ? *reinterpret_cast<const uint4*>(bp[j] + kc + 32 * u) : make_uint4(0, 0, 0, 0);
     }
-    const bool more = c + 1 < nchunks;
-    if (more) load_a(c + 1);
-    __syncthreads();                           // chunk c of A is in As[c & 1]
-    const uint16_t* as = As[c & 1];
+  };
+  auto mma = [&](const uint4 (&b)[U][NF], const uint16_t* as) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       bf16x8 af[MF];
@@ -238,6 +223,17 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
         for (int j = 0; j < NF; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], __builtin_bit_cast(bf16x8, b[u][j]), acc[i][j], 0, 0, 0);
     }
+  };
+
+  load_a(0);
+  store_a(0);
+  for (int c = 0; c < nchunks; ++c) {
+    uint4 b[U][NF];
+    load_b(b, c);
+    const bool more = c + 1 < nchunks;
+    if (more) load_a(c + 1);
+    __syncthreads();                           // chunk c of A is in As[c & 1]
+    mma(b, As[c & 1]);
     if (more) store_a((c + 1) & 1);            // that buffer was last read before this barrier
   }
 
@@ -259,25 +255,58 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
 }
 
 // ---- prefill-sized tiles: LDS-tiled GEMM on v_mfma_f32_32x32x16_bf16 ------------
-// Block tile: 128 token rows x 128 weight rows (phase 1: 64 gate + the matching
-// 64 up rows -> 64 SwiGLU columns; phase 2: 128 down rows), K in steps of 64.
-// Both tiles go global -> registers -> LDS, double buffered: the next K-step's
-// loads are in flight while the current one is multiplied; one barrier per
-// step.  Four waves in a 2 x 2 grid, each 64 x 64 (2 x 2 MFMA 32x32 blocks;
-// phase 1: 32 gate and the same 32 up columns, so SwiGLU needs no exchange).
-constexpr int kGemmBM = 128;
-constexpr int kGemmBN = 128;               // weight rows per tile
-constexpr int kGemmBK = 64;
-constexpr int kGemmStride = kGemmBK + 8;   // bf16 per LDS row (144 B)
-constexpr int kGemmVecs = kGemmBM * kGemmBK / 8 / kThreads;   // uint4 per thread per tile (4)
+// Block tile: BM = 64*MI token rows x BN = 64*NJ weight rows (phase 1: BN/2
+// gate rows then the matching BN/2 up rows -> BN/2 SwiGLU columns; phase 2: BN
+// down rows), K in steps of kGemmBK = 32.
+//   * Operands go HBM -> LDS directly (global_load_lds_dwordx4: each lane's 16
+//     bytes land at LDS base + 16*lane, no VGPR staging, no LDS store
+//     instructions), through a ring of kGemmStages K-step buffers: two K-steps
+//     are in flight while the third is multiplied; one barrier per K-step.
+//   * LDS rows are 64 bytes (four 16-byte chunks) with no padding; chunk c of
+//     row r sits at slot c ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 2)) & 3.  An
+//     MFMA operand read (16 lanes: 16 consecutive rows, one chunk) then hits
+//     16 distinct 4-bank groups, and so does any 8-lane group.  The DMA side
+//     writes 1 KiB contiguously per instruction and applies the swizzle by
+//     choosing which global chunk each lane fetches.
+//   * Four waves in a 2 x 2 grid, each (32*MI) x (32*NJ) as MI x NJ blocks of
+//     32x32 (phase 1: NJ/2 gate blocks and the same columns' NJ/2 up blocks,
+//     so SwiGLU needs no exchange).
+// The K extent must be a multiple of kGemmBK (checked by the host).
+constexpr int kGemmBK = 32;
+constexpr int kGemmRowBytes = kGemmBK * 2;
+constexpr int kGemmStages = 3;
+constexpr int kGemmBlocksPerCu = 2;
 
-template <int PHASE>
-__global__ __launch_bounds__(kThreads, 2) void ffn_gemm_bf16(
+__device__ __forceinline__ int gemm_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// 16 bytes per lane from global memory to LDS byte address lds + 16*lane.
+// Issued as inline assembly so that the compiler does not treat every later
+// LDS read as dependent on it (it would wait for all loads in flight); the
+// kernel orders it with explicit vmcnt waits and barriers instead.
+__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
+  // M0 carries the wave-uniform LDS base; one wait state between writing M0
+  // and an LDS-DMA load is required
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+template <int PHASE, int MI, int NJ>
+__global__ __launch_bounds__(kThreads, kGemmBlocksPerCu) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
     int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
-  constexpr int OUTC = PHASE == 1 ? kGemmBN / 2 : kGemmBN;   // output columns per tile
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kGemmBM * kGemmStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kGemmBN * kGemmStride];
+  constexpr int BM = 64 * MI, BN = 64 * NJ;
+  constexpr int OUTC = PHASE == 1 ? BN / 2 : BN;          // output columns per tile
+  constexpr int A_BYTES = BM * kGemmRowBytes, B_BYTES = BN * kGemmRowBytes;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int ADMA = BM / 16 / kWaves;                  // 1 KiB DMA instructions per wave per K-step
+  constexpr int BDMA = BN / 16 / kWaves;
+  static_assert(PHASE == 2 || NJ % 2 == 0, "phase 1 pairs gate and up blocks");
+  static_assert(ADMA >= 1 && BDMA >= 1, "tile too small for four waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmStages * STAGE];
 
   const int nch = (Ncols + OUTC - 1) / OUTC;
   const Item it = block_find_item(plan, nch);
@@ -289,90 +318,108 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_gemm_bf16(
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hk = lane >> 5;
 
-  // global -> register staging: slot s of thread t covers row (t + 256 s) / 8, 8 bf16 at column 8 * (t % 8)
-  const uint16_t* arow[kGemmVecs];
-  const uint16_t* brow[kGemmVecs];
+  // DMA sources: instruction q of this wave fills tile rows 16 (wave + 4 q) ..
+  // +15; lane -> row + lane / 4, slot lane % 4, fetching chunk slot ^ swz(row).
+  // Rows past the tile's valid rows / columns read a valid row instead (their
+  // results are never stored).
+  const int dr = lane >> 2;
+  const uint16_t* asrc[ADMA];
+  const uint16_t* bsrc[BDMA];
 #pragma unroll
-  for (int s = 0; s < kGemmVecs; ++s) {
-    const int r = (tid + s * kThreads) >> 3;
-    arow[s] = r < rows ? A + static_cast<size_t>(row0 + r) * K : nullptr;
-    brow[s] = weight_row<PHASE>(W0, W1, eoff, Ncols, K, n0, r, OUTC);
+  for (int q = 0; q < ADMA; ++q) {
+    const int r = 16 * (wave + kWaves * q) + dr;
+    asrc[q] = A + static_cast<size_t>(row0 + min(r, rows - 1)) * K + 8 * ((lane & 3) ^ gemm_swz(r));
   }
-  const int kcol = 8 * (tid & 7);
-  uint4 ra[kGemmVecs], rb[kGemmVecs];
-  auto load = [&](int k0) {
-    const int k = k0 + kcol;
 #pragma unroll
-    for (int s = 0; s < kGemmVecs; ++s) {
-      ra[s] = (arow[s] && k < K) ? *reinterpret_cast<const uint4*>(arow[s] + k) : make_uint4(0, 0, 0, 0);
-      rb[s] = (brow[s] && k < K) ? *reinterpret_cast<const uint4*>(brow[s] + k) : make_uint4(0, 0, 0, 0);
+  for (int q = 0; q < BDMA; ++q) {
+    const int r = 16 * (wave + kWaves * q) + dr;
+    int n = n0 + r;
+    const uint16_t* W = W0;
+    if (PHASE == 1 && r >= OUTC) {
+      n -= OUTC;
+      W = W1;
     }
-  };
-  auto store = [&](int buf) {
+    bsrc[q] = W + eoff + static_cast<size_t>(min(n, Ncols - 1)) * K + 8 * ((lane & 3) ^ gemm_swz(r));
+  }
+  typedef __attribute__((address_space(3))) uint8_t lds_byte;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_byte*)smem;   // LDS byte address of the ring
+  auto issue = [&](int kt) {
+    const uint32_t st = lds0 + (kt % kGemmStages) * STAGE + wave * 1024;
+    const int k = kt * kGemmBK;
 #pragma unroll
-    for (int s = 0; s < kGemmVecs; ++s) {
-      const int r = (tid + s * kThreads) >> 3;
-      *reinterpret_cast<uint4*>(&As[buf][r * kGemmStride + kcol]) = ra[s];
-      *reinterpret_cast<uint4*>(&Bs[buf][r * kGemmStride + kcol]) = rb[s];
-    }
+    for (int q = 0; q < ADMA; ++q) dma_b128(asrc[q] + k, st + q * kWaves * 1024);
+#pragma unroll
+    for (int q = 0; q < BDMA; ++q) dma_b128(bsrc[q] + k, st + A_BYTES + q * kWaves * 1024);
   };
 
-  // MFMA operand rows of this wave: A rows 64 wm + 32 i + l32; B (weight)
-  // rows: phase 2 64 wn + 32 j + l32, phase 1 j = 0 gate 32 wn + l32, j = 1
-  // the matching up row 64 + 32 wn + l32.
-  int brl[2];
-  brl[0] = PHASE == 1 ? 32 * wn + l32 : 64 * wn + l32;
-  brl[1] = PHASE == 1 ? 64 + 32 * wn + l32 : 64 * wn + 32 + l32;
-  f32x16 acc[2][2];
+  // MFMA operand rows of this wave: A rows BM/2 wm + 32 i + l32; weight rows:
+  // phase 2 BN/2 wn + 32 j + l32; phase 1 gate block j < NJ/2 at
+  // BN/4 wn + 32 j + l32, up block j >= NJ/2 at BN/2 + BN/4 wn + 32 (j - NJ/2) + l32.
+  // Every block starts at a multiple of 32 rows, so the swizzle depends on l32.
+  int boff[NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < NJ; ++j) {
+    const int rb = PHASE == 1 ? (j < NJ / 2 ? 0 : BN / 2) + (BN / 4) * wn + 32 * (j % (NJ / 2)) : (BN / 2) * wn + 32 * j;
+    boff[j] = A_BYTES + rb * kGemmRowBytes;
+  }
+  const int aoff = (BM / 2) * wm * kGemmRowBytes;
+  int loff[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int s = 0; s < 2; ++s) loff[s] = l32 * kGemmRowBytes + 16 * ((2 * s + hk) ^ gemm_swz(l32));
+
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (K + kGemmBK - 1) / kGemmBK;
-  load(0);
-  store(0);
-  __syncthreads();
+  const int nk = K / kGemmBK;
+  issue(0);
+  if (nk > 1) issue(1);
   for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) load((kt + 1) * kGemmBK);
-    const uint16_t* as = As[kt & 1];
-    const uint16_t* bs = Bs[kt & 1];
+    // K-step kt's loads are done once at most the next step's remain in flight
+    if (kt + 1 < nk)
+      wait_vm_barrier<ADMA + BDMA>();
+    else
+      wait_vm_barrier<0>();
+    // every wave is past step kt-1, so its buffer can be refilled
+    if (kt + 2 < nk) issue(kt + 2);
+    const uint8_t* st = smem + (kt % kGemmStages) * STAGE;
 #pragma unroll
-    for (int ks = 0; ks < kGemmBK; ks += 16) {
-      bf16x8 af[2], bf[2];
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 af[MI], bf[NJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&as[(64 * wm + 32 * i + l32) * kGemmStride + ks + 8 * hk]));
+      for (int i = 0; i < MI; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(st + aoff + 32 * i * kGemmRowBytes + loff[s]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bs[brl[j] * kGemmStride + ks + 8 * hk]));
+      for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(st + boff[j] + loff[s]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (more) store((kt + 1) & 1);   // that buffer was last read before the previous barrier
-    __syncthreads();
   }
 
   // 32x32 accumulator: lane holds column l32 and rows 8 (r/4) + 4 hk + r % 4
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
+      const int m = (BM / 2) * wm + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
       if (m >= rows) continue;
       uint16_t* orow = out + static_cast<size_t>(row0 + m) * Ncols;
       if (PHASE == 1) {
-        const int n = n0 + 32 * wn + l32;
-        if (n < Ncols) orow[n] = f32_to_bf16(silu_mul(acc[i][0][r], acc[i][1][r]));
+#pragma unroll
+        for (int j = 0; j < NJ / 2; ++j) {
+          const int n = n0 + (BN / 4) * wn + 32 * j + l32;
+          if (n < Ncols) orow[n] = f32_to_bf16(silu_mul(acc[i][j][r], acc[i][NJ / 2 + j][r]));
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = n0 + 64 * wn + 32 * j + l32;
+        for (int j = 0; j < NJ; ++j) {
+          const int n = n0 + (BN / 2) * wn + 32 * j + l32;
           if (n < Ncols) orow[n] = f32_to_bf16(acc[i][j][r]);
         }
       }
@@ -429,6 +476,10 @@ __global__ __launch_bounds__(kThreads) void ffn_phase_f32(const float* __restric
 // ---- host side -------------------------------------------------------------------
 enum class Path { kDecode, kGemm, kF32 };
 
+// GEMM tile shape (MI x NJ blocks of 32x32 per wave; block 64 MI x 64 NJ).
+constexpr int kGemmMI = 2;
+constexpr int kGemmNJ = 4;
+
 struct Layout {
   Path path;
   int BM, max_tiles;
@@ -437,7 +488,8 @@ struct Layout {
 
 // The host never sees the real group sizes: pick the kernel from the average.
 // Small groups (decode) stream weights through the decode kernel; large groups
-// use the LDS-tiled GEMM.
+// use the LDS-tiled GEMM, whose K steps need d and I to be multiples of 32
+// (otherwise the decode kernel, which takes any multiple of 8, runs them).
 int pick_mf(int avg) {
   if (avg <= 8) return 1;
   if (avg <= 24) return 2;
@@ -445,19 +497,18 @@ int pick_mf(int avg) {
 }
 
 Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16) {
-  (void)d;
   Layout L;
   const int G = nseg * E + n_shared;
   const int avg = G > 0 ? n_rows / G : n_rows;
   if (!bf16) {
     L.path = Path::kF32;
     L.BM = 16;
-  } else if (avg <= 48) {
+  } else if (avg <= 48 || d % kGemmBK != 0 || I % kGemmBK != 0) {
     L.path = Path::kDecode;
     L.BM = 16 * pick_mf(avg);
   } else {
     L.path = Path::kGemm;
-    L.BM = kGemmBM;
+    L.BM = 64 * kGemmMI;
   }
   L.max_tiles = (n_rows + L.BM - 1) / L.BM + G;
   L.a_off = 0;
@@ -486,12 +537,13 @@ void launch_decode_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan,
 }
 
 void launch_gemm_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, uint16_t* abuf, hipStream_t stream) {
-  const int nch1 = (a.I + kGemmBN / 2 - 1) / (kGemmBN / 2), nch2 = (a.d + kGemmBN - 1) / kGemmBN;
-  hipLaunchKernelGGL(ffn_gemm_bf16<1>, dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
+  constexpr int BN = 64 * kGemmNJ;
+  const int nch1 = (a.I + BN / 2 - 1) / (BN / 2), nch2 = (a.d + BN - 1) / BN;
+  hipLaunchKernelGGL((ffn_gemm_bf16<1, kGemmMI, kGemmNJ>), dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0,
+                     stream, static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
                      static_cast<const uint16_t*>(a.w_up), a.I, plan, abuf);
-  hipLaunchKernelGGL(ffn_gemm_bf16<2>, dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
+  hipLaunchKernelGGL((ffn_gemm_bf16<2, kGemmMI, kGemmNJ>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
+                     stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
                      static_cast<const uint16_t*>(nullptr), a.d, plan, static_cast<uint16_t*>(a.h_sorted));
 }
 

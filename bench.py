@@ -159,56 +159,65 @@ def main():
     for l in range(1, s.stats_layers):      # the other layers' ids, produced before timing
         moe.gate(wl.stats_logits[l].contiguous(), s.k, True, stats_ids[l],
                  torch.empty((s.T, s.k), device=dev))
-    # The statistics only need the gate's ids: they run on a second stream
-    # (default priority), concurrently with permute -> FFN -> combine.
+    # One stream, in path order: gate, statistics (they need only the gate's
+    # ids), permute, FFN, combine.  (A second stream for the statistics costs
+    # two cross-queue waits per step, more than the statistics themselves.)
     stream = torch.cuda.Stream(dev)
-    side = torch.cuda.Stream(dev)
     call_sets = []
     for wg, wu, wd in wsets:
         layer.w_gate, layer.w_up, layer.w_down = wg, wu, wd
-        call_sets.append(layer.bound_calls(wl.logits, wl.x, stats_ids, stream.cuda_stream, side.cuda_stream))
+        call_sets.append(layer.bound_calls(wl.logits, wl.x, stats_ids, stream.cuda_stream))
     names = [c[0] for c in call_sets[0]]
+    order = [names.index("moe_gate")] + ([names.index("moe_stats")] if "moe_stats" in names else []) + \
+        [j for j, n in enumerate(names) if n not in ("moe_gate", "moe_stats")]
 
     def step(i, ev=None):
-        """One layer step on `stream` (statistics forked onto `side`)."""
-        for j, (name, fn, a) in enumerate(call_sets[i % copies]):
-            s_ = side if name == "moe_stats" else stream
-            if name == "moe_stats":
-                side.wait_stream(stream)          # after the gate
+        """One layer step on `stream`."""
+        calls = call_sets[i % copies]
+        for j in order:
+            name, fn, a = calls[j]
             if ev is not None:
-                ev[j][0].record(s_)
+                ev[j][0].record(stream)
             st = fn(*a)
             if st != 0:
                 raise moe.MoeError(name, st)
             if ev is not None:
-                ev[j][1].record(s_)
-        if "moe_stats" in names:
-            stream.wait_stream(side)
+                ev[j][1].record(stream)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             step(i)
     torch.cuda.synchronize()
 
-    # headline: K steps, each one replay of a captured HIP graph of the whole
-    # step (one graph per weight copy), or eager launches with --eager
+    # headline: K steps replayed from captured HIP graphs, or eager launches
+    # with --eager.  One graph holds `copies` consecutive steps (one per weight
+    # copy, like the consecutive layers of a captured forward pass);
+    # single-step graphs cover a remainder, so exactly K steps run.
     K = args.steps
-    graphs = []
+    multi, singles = None, []
     if not args.eager:
+        multi = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(multi, stream=stream):
+            for c in range(copies):
+                step(c)
         for c in range(copies):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 step(c)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % copies].replay()
+            singles.append(g)
+        for i in range(max(1, args.warmup // copies)):
+            multi.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
-        for i in range(K):
-            if graphs:
-                graphs[i % copies].replay()
-            else:
+        if multi is not None:
+            reps, rem = divmod(K, copies)
+            for _ in range(reps):
+                multi.replay()
+            for c in range(rem):
+                singles[c].replay()
+        else:
+            for i in range(K):
                 step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -261,7 +270,8 @@ def main():
                    "weight_copies": copies, "union": union},
         "roofline": roof,
         "per_call_us": {n: round(v * 1e3, 2) for n, v in per_call.items()},
-        "timing": "eager launches" if args.eager else "one captured HIP graph of the whole step replayed per step",
+        "timing": "eager launches" if args.eager else
+                  f"captured HIP graphs of {copies} consecutive steps (one per weight copy) replayed",
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

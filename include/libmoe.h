@@ -143,6 +143,11 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
  *   accumulation, the SwiGLU product rounded to bf16 (round to nearest even)
  *   before the down projection.  f32: fp32 throughout.
  *   Requires d % 8 == 0, I % 8 == 0, nseg in {1, 2}, 1 <= E <= 512.
+ *   The 4 bytes at offset (queried workspace size - 4) hold a diagnostic
+ *   word once the call has completed: 0, or nonzero if a wait of the
+ *   persistent tile queue (used for bf16 batches with a priority segment and
+ *   large groups) gave up after its bound; the outputs are then not to be
+ *   trusted.
  */
 moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* group_offsets,
                            int32_t n_rows, int32_t E, int32_t n_shared, int32_t nseg,

@@ -22,7 +22,7 @@ def _gpu():
     require_gpu()
 
 
-@pytest.mark.parametrize("name", ["olmoe_decode", "dsv2_decode_t64", "tiny"])
+@pytest.mark.parametrize("name", ["olmoe_decode", "dsv2_decode_t64", "tiny", "qwen3_prefill", "gptoss_mixed"])
 def test_graph_replays_match_eager(name):
     announce(f"graph {name}")
     wl = workloads.make(name, DEV)

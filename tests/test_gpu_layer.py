@@ -53,6 +53,8 @@ def test_layer_parity(name):
     stats_ids[0].copy_(layer.topk_ids)
     layer.stats(stats_ids)
     torch.cuda.synchronize()
+    nbytes = moe.ffn_workspace_bytes(s.N, s.E, s.S, layer.nseg, s.d, s.I, wl.torch_dtype)
+    assert int(layer.ffn_ws[nbytes - 4:nbytes].view(torch.int32).item()) == 0, "a tile-queue wait gave up"
 
     logits = np_of(wl.logits)
     ids_ref, w_ref = O.gate(logits, s.k, bool(s.renormalize))

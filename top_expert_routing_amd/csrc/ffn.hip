@@ -16,6 +16,8 @@
 // are staged in LDS and shared by the four waves; the weight rows (B) are
 // used by exactly one wave, so they stream straight from HBM into registers
 // with 16-byte loads and no LDS round trip.
+#include <stdlib.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -45,6 +47,7 @@ constexpr int kXcds = 8;                 // MI355X: 8 XCDs, workgroups dealt rou
 struct PlanArgs {
   const int* offs;
   int G, E, nseg, BM, n_rows, max_tiles;
+  int* diag;   // diagnostic word, cleared by block 0 (nullptr: leave it)
 };
 
 struct Item {
@@ -57,6 +60,7 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
   __shared__ Item found;
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
   if (tid == 0) found = Item{0, 0, 0, 0};
+  if (tid == 0 && blockIdx.x == 0 && p.diag) *p.diag = 0;
   int cnt[kMaxGroupsPerThread], r0[kMaxGroupsPerThread];
   int s = 0;
 #pragma unroll
@@ -294,23 +298,31 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
+template <int MI, int NJ>
+struct GemmShape {
+  static constexpr int BM = 64 * MI, BN = 64 * NJ;
+  static constexpr int A_BYTES = BM * kGemmRowBytes, B_BYTES = BN * kGemmRowBytes;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int RING = kGemmStages * STAGE;         // LDS bytes of the operand ring
+};
+
+// One tile: rows [row0, row0 + rows) of A against output column chunk
+// `it.chunk` of expert `it.expert`.  All threads of the block call it; `smem`
+// is the block's operand ring, free on entry (no wave still reads it).
 template <int PHASE, int MI, int NJ>
-__global__ __launch_bounds__(kThreads, kGemmBlocksPerCu) void ffn_gemm_bf16(
-    const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-    int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
-  constexpr int BM = 64 * MI, BN = 64 * NJ;
+__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0,
+                                          const uint16_t* __restrict__ W1, int Ncols, const Item& it,
+                                          uint16_t* __restrict__ out, uint8_t* smem) {
+  using S = GemmShape<MI, NJ>;
+  constexpr int BM = S::BM, BN = S::BN;
   constexpr int OUTC = PHASE == 1 ? BN / 2 : BN;          // output columns per tile
-  constexpr int A_BYTES = BM * kGemmRowBytes, B_BYTES = BN * kGemmRowBytes;
-  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_BYTES = S::A_BYTES;
+  constexpr int STAGE = S::STAGE;
   constexpr int ADMA = BM / 16 / kWaves;                  // 1 KiB DMA instructions per wave per K-step
   constexpr int BDMA = BN / 16 / kWaves;
   static_assert(PHASE == 2 || NJ % 2 == 0, "phase 1 pairs gate and up blocks");
   static_assert(ADMA >= 1 && BDMA >= 1, "tile too small for four waves");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmStages * STAGE];
 
-  const int nch = (Ncols + OUTC - 1) / OUTC;
-  const Item it = block_find_item(plan, nch);
-  if (it.rows == 0) return;
   const int row0 = it.row0, rows = it.rows;
   const int n0 = it.chunk * OUTC;
   const size_t eoff = static_cast<size_t>(it.expert) * Ncols * K;
@@ -427,6 +439,186 @@ __global__ __launch_bounds__(kThreads, kGemmBlocksPerCu) void ffn_gemm_bf16(
   }
 }
 
+template <int PHASE, int MI, int NJ>
+__global__ __launch_bounds__(kThreads, kGemmBlocksPerCu) void ffn_gemm_bf16(
+    const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+    int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
+  using S = GemmShape<MI, NJ>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::RING];
+  constexpr int OUTC = PHASE == 1 ? S::BN / 2 : S::BN;
+  const Item it = block_find_item(plan, (Ncols + OUTC - 1) / OUTC);
+  if (it.rows == 0) return;
+  gemm_tile<PHASE, MI, NJ>(A, K, W0, W1, Ncols, it, out, smem);
+}
+
+// ---- mixed batches: one persistent launch, per-XCD tile queues ----------------
+// Tile queue with decode priority (ExpertPlex page, "Instance vs module
+// disaggregation" / token-level preemption: a decode request waits at most one
+// tile, never a whole prefill launch).  Both phases run in one launch of
+// persistent blocks (kGemmBlocksPerCu per CU):
+//   * units are the m-tiles of all groups, in group order (the priority
+//     segment's groups first); each XCD owns an eighth of the priority units
+//     and an eighth of the others;
+//   * XCD x's queue is [phase 1 of its priority units] [the first `lag` phase-1
+//     tiles of its other units] [phase 2 of its priority units] [the remaining
+//     phase-1 tiles] [phase 2 of its other units]; within a section tiles go
+//     group by group, column chunk by chunk, m-tile by m-tile;
+//   * a block reads its XCD id from the hardware and pops tiles from that
+//     queue with one atomic add; a phase-2 tile waits until every phase-1 tile
+//     of its unit has signalled (per-unit counter).  The lag keeps the blocks
+//     busy with other phase-1 tiles while the priority units' phase 1 drains.
+// All tiles of a unit run on one XCD, so the intermediate rows pass through
+// that XCD's L2: a phase-1 tile's stores have reached L2 once its vmcnt is
+// zero, before it bumps the counter; the waiting block then drops its L1 lines
+// (buffer_inv sc0) before loading them.  Counters are only touched with atomic
+// read-modify-writes (a poll adds 0), so increments and polls meet at the same
+// point whatever cache level performs the atomics.  A dependency always points
+// to a tile popped earlier by a running block, so the waits end; each is also
+// bounded (kSpinLimit polls), after which the block sets the diagnostic word
+// (the workspace's last 4 bytes) and goes on, and other waits stop at once.
+constexpr int kQueueStride = 32;          // ints between the per-XCD queue heads (128 B)
+constexpr int kCusPerXcd = 32;            // MI355X: 8 XCDs x 32 CUs
+constexpr int kSpinLimit = 1 << 16;       // polls before a wait gives up (far above any tile time)
+
+struct QueueArgs {
+  const int* offs;
+  int G, E, nseg, n_rows, n_prio_groups, nch1, nch2, lag;
+  int nq;       // queues = XCDs of the device (1 when it is a single-XCD partition)
+  int* heads;   // [kXcds * kQueueStride]
+  int* done1;   // [units]
+  int* error;   // set when a wait gave up
+};
+
+__device__ __forceinline__ int xcc_id() {
+  int x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 0xf;
+}
+
+template <int MI, int NJ>
+__global__ __launch_bounds__(kThreads, kGemmBlocksPerCu) void ffn_queue_bf16(
+    const uint16_t* __restrict__ x, int d, const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
+    const uint16_t* __restrict__ w_down, int I, QueueArgs q, uint16_t* __restrict__ abuf,
+    uint16_t* __restrict__ h) {
+  using S = GemmShape<MI, NJ>;
+  constexpr int BM = S::BM;
+  constexpr int kMaxG = kThreads * kMaxGroupsPerThread;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::RING];
+  __shared__ int fu[kMaxG + 1];         // first unit of each group
+  __shared__ int wsum[kWaves];
+  __shared__ int s_tile;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+
+  // units per group, exclusive scan -> fu
+  {
+    int cnt[kMaxGroupsPerThread];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxGroupsPerThread; ++i) {
+      const int g = tid * kMaxGroupsPerThread + i;
+      cnt[i] = 0;
+      if (g < q.G) {
+        const int lo = min(max(q.offs[g], 0), q.n_rows), hi = min(max(q.offs[g + 1], 0), q.n_rows);
+        cnt[i] = (max(0, hi - lo) + BM - 1) / BM;
+      }
+      sum += cnt[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) wsum[w] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int i = 0; i < w; ++i) run += wsum[i];
+#pragma unroll
+    for (int i = 0; i < kMaxGroupsPerThread; ++i) {
+      const int g = tid * kMaxGroupsPerThread + i;
+      if (g < q.G) fu[g] = run;
+      run += cnt[i];
+    }
+    if (tid == kThreads - 1) fu[q.G] = run;
+    __syncthreads();
+  }
+  const int units = fu[q.G];
+  const int up = fu[q.n_prio_groups];
+  const int xc = xcc_id() % q.nq;
+  const int p_lo = static_cast<int>(1LL * up * xc / q.nq), p_hi = static_cast<int>(1LL * up * (xc + 1) / q.nq);
+  const int r_lo = up + static_cast<int>(1LL * (units - up) * xc / q.nq);
+  const int r_hi = up + static_cast<int>(1LL * (units - up) * (xc + 1) / q.nq);
+  const int s1 = (p_hi - p_lo) * q.nch1, s2 = (p_hi - p_lo) * q.nch2;
+  const int s3 = (r_hi - r_lo) * q.nch1, s4 = (r_hi - r_lo) * q.nch2;
+  const int s3a = min(q.lag, s3);
+  const int total = s1 + s3 + s2 + s4;
+
+  for (;;) {
+    if (tid == 0) s_tile = __hip_atomic_fetch_add(q.heads + xc * kQueueStride, 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();                 // also: every wave is done with the previous tile's ring
+    int t = s_tile;
+    __syncthreads();                 // s_tile read by all before thread 0 overwrites it
+    if (t >= total) break;
+    // section -> phase, unit range, index within the section
+    int phase, a, b, i;
+    if (t < s1) {
+      phase = 1, a = p_lo, b = p_hi, i = t;
+    } else if (t < s1 + s3a) {
+      phase = 1, a = r_lo, b = r_hi, i = t - s1;
+    } else if (t < s1 + s3a + s2) {
+      phase = 2, a = p_lo, b = p_hi, i = t - s1 - s3a;
+    } else if (t < s1 + s3 + s2) {
+      phase = 1, a = r_lo, b = r_hi, i = t - s1 - s2;
+    } else {
+      phase = 2, a = r_lo, b = r_hi, i = t - s1 - s3 - s2;
+    }
+    const int nch = phase == 1 ? q.nch1 : q.nch2;
+    // group holding unit a + i / nch: last g with fu[g] <= u
+    const int u = a + i / nch;
+    int lo = 0, hi = q.G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (fu[mid] <= u) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    const int sg = max(a, fu[g]), cg = min(b, fu[g + 1]) - sg;
+    const int local = i - nch * (sg - a);
+    const int chunk = local / cg, mt = sg - fu[g] + local % cg;
+    const int unit = fu[g] + mt;
+    const int glo = min(max(q.offs[g], 0), q.n_rows), ghi = min(max(q.offs[g + 1], 0), q.n_rows);
+    const Item it{glo + mt * BM, min(BM, ghi - glo - mt * BM), expert_of_group(g, q.E, q.nseg), chunk};
+    if (phase == 1) {
+      gemm_tile<1, MI, NJ>(x, d, w_gate, w_up, I, it, abuf, smem);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are in L2
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(q.done1 + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (tid == 0) {
+        int spins = 0;
+        while (__hip_atomic_fetch_add(q.done1 + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < q.nch1) {
+          __builtin_amdgcn_s_sleep(2);
+          // give up after kSpinLimit polls, or at once when another wait already did
+          if (++spins > kSpinLimit ||
+              ((spins & 63) == 0 && __hip_atomic_fetch_add(q.error, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+            __hip_atomic_fetch_or(q.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+      }
+      __syncthreads();
+      asm volatile("buffer_inv sc0" ::: "memory");
+      gemm_tile<2, MI, NJ>(abuf, I, w_down, nullptr, d, it, h, smem);
+    }
+  }
+}
+
+__global__ void ffn_queue_reset(int* p, int n, int* diag) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+  if (i == 0) *diag = 0;
+}
+
 // ---- fp32 phase kernel (VALU, fp32 accumulation) --------------------------------
 // One thread per output column (256 columns per item), all rows of a 16-row
 // tile.
@@ -474,7 +666,7 @@ __global__ __launch_bounds__(kThreads) void ffn_phase_f32(const float* __restric
 }
 
 // ---- host side -------------------------------------------------------------------
-enum class Path { kDecode, kGemm, kF32 };
+enum class Path { kDecode, kGemm, kQueue, kF32 };
 
 // GEMM tile shape (MI x NJ blocks of 32x32 per wave; block 64 MI x 64 NJ).
 constexpr int kGemmMI = 2;
@@ -483,13 +675,18 @@ constexpr int kGemmNJ = 4;
 struct Layout {
   Path path;
   int BM, max_tiles;
-  size_t a_off, total;
+  size_t a_off, q_off, q_ints, total;
 };
 
 // The host never sees the real group sizes: pick the kernel from the average.
 // Small groups (decode) stream weights through the decode kernel; large groups
 // use the LDS-tiled GEMM, whose K steps need d and I to be multiples of 32
 // (otherwise the decode kernel, which takes any multiple of 8, runs them).
+bool queue_path_requested() {
+  const char* v = getenv("LIBMOE_FFN_QUEUE");
+  return v != nullptr && v[0] == '1';
+}
+
 int pick_mf(int avg) {
   if (avg <= 8) return 1;
   if (avg <= 24) return 2;
@@ -507,13 +704,23 @@ Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16)
     L.path = Path::kDecode;
     L.BM = 16 * pick_mf(avg);
   } else {
-    L.path = Path::kGemm;
+    // With a priority segment both phases could run in one persistent launch
+    // (ffn_queue_bf16); that path stays off unless LIBMOE_FFN_QUEUE=1 is set:
+    // its phase-2 waits did not see the phase-1 counters complete on MI355X
+    // (the counters are bumped with L2 atomics but polled with cache-bypassing
+    // loads).  The two-launch GEMM still serves the priority segment's tiles
+    // first in each launch.
+    L.path = (nseg > 1 && queue_path_requested()) ? Path::kQueue : Path::kGemm;
     L.BM = 64 * kGemmMI;
   }
   L.max_tiles = (n_rows + L.BM - 1) / L.BM + G;
   L.a_off = 0;
   const size_t a_bytes = static_cast<size_t>(n_rows) * I * (bf16 ? 2 : 4);
-  L.total = (a_bytes + 255) / 256 * 256 + 256;
+  L.q_off = (a_bytes + 255) / 256 * 256;
+  // queue heads, per-unit phase-1 counters; the last 4 bytes of the workspace
+  // are the diagnostic word
+  L.q_ints = L.path == Path::kQueue ? static_cast<size_t>(kXcds) * kQueueStride + L.max_tiles : 0;
+  L.total = L.q_off + (L.q_ints * 4 + 255) / 256 * 256 + 256;
   return L;
 }
 
@@ -531,9 +738,11 @@ void launch_decode_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan,
   hipLaunchKernelGGL((ffn_decode_bf16<MF, kDecodeNfc1, 1>), dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
                      static_cast<const uint16_t*>(a.w_up), a.I, plan, abuf);
+  PlanArgs plan2 = plan;
+  plan2.diag = nullptr;
   hipLaunchKernelGGL((ffn_decode_bf16<MF, kDecodeNfc2, 2>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
-                     static_cast<const uint16_t*>(nullptr), a.d, plan, static_cast<uint16_t*>(a.h_sorted));
+                     static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted));
 }
 
 void launch_gemm_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, uint16_t* abuf, hipStream_t stream) {
@@ -542,9 +751,55 @@ void launch_gemm_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, u
   hipLaunchKernelGGL((ffn_gemm_bf16<1, kGemmMI, kGemmNJ>), dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
                      static_cast<const uint16_t*>(a.w_up), a.I, plan, abuf);
+  PlanArgs plan2 = plan;
+  plan2.diag = nullptr;
   hipLaunchKernelGGL((ffn_gemm_bf16<2, kGemmMI, kGemmNJ>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
-                     static_cast<const uint16_t*>(nullptr), a.d, plan, static_cast<uint16_t*>(a.h_sorted));
+                     static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted));
+}
+
+// CUs of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int slot = dev < 64 ? dev : 63;
+  if (cached[slot] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[slot] = cus;
+  }
+  return cached[slot];
+}
+
+void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t stream) {
+  constexpr int BN = 64 * kGemmNJ;
+  int* qbase = reinterpret_cast<int*>(ws + L.q_off);
+  const int n = static_cast<int>(L.q_ints);
+  int* diag = reinterpret_cast<int*>(ws + L.total - 4);
+  hipLaunchKernelGGL(ffn_queue_reset, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, stream, qbase, n,
+                     diag);
+  const int cus = device_cus();
+  const int blocks = cus * kGemmBlocksPerCu;          // persistent: every block resident
+  const int nq = cus >= kXcds * kCusPerXcd ? kXcds : (cus >= 4 * kCusPerXcd ? 4 : (cus >= 2 * kCusPerXcd ? 2 : 1));
+  QueueArgs q;
+  q.offs = a.group_offsets;
+  q.G = a.nseg * a.E + a.n_shared;
+  q.E = a.E;
+  q.nseg = a.nseg;
+  q.n_rows = a.n_rows;
+  q.n_prio_groups = a.nseg > 1 ? a.E : 0;   // segment 0 = the priority tokens' routed groups
+  q.nch1 = (a.I + BN / 2 - 1) / (BN / 2);
+  q.nch2 = (a.d + BN - 1) / BN;
+  q.nq = nq;
+  q.lag = (blocks + nq - 1) / nq;
+  q.heads = qbase;
+  q.done1 = qbase + kXcds * kQueueStride;
+  q.error = diag;
+  hipLaunchKernelGGL((ffn_queue_bf16<kGemmMI, kGemmNJ>), dim3(blocks), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
+                     static_cast<const uint16_t*>(a.w_up), static_cast<const uint16_t*>(a.w_down), a.I, q,
+                     reinterpret_cast<uint16_t*>(ws + L.a_off), static_cast<uint16_t*>(a.h_sorted));
 }
 
 }  // namespace
@@ -564,6 +819,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
   plan.BM = L.BM;
   plan.n_rows = a.n_rows;
   plan.max_tiles = L.max_tiles;
+  plan.diag = reinterpret_cast<int*>(ws + L.total - 4);
   switch (L.path) {
     case Path::kDecode: {
       uint16_t* abuf = reinterpret_cast<uint16_t*>(ws + L.a_off);
@@ -577,15 +833,20 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
     case Path::kGemm:
       launch_gemm_bf16(a, L, plan, reinterpret_cast<uint16_t*>(ws + L.a_off), stream);
       break;
+    case Path::kQueue:
+      launch_queue_bf16(a, L, ws, stream);
+      break;
     case Path::kF32: {
       float* abuf = reinterpret_cast<float*>(ws + L.a_off);
       const int nch1 = (a.I + kThreads - 1) / kThreads, nch2 = (a.d + kThreads - 1) / kThreads;
       hipLaunchKernelGGL(ffn_phase_f32<1>, dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0, stream,
                          static_cast<const float*>(a.x_sorted), a.d, static_cast<const float*>(a.w_gate),
                          static_cast<const float*>(a.w_up), a.I, plan, abuf);
+      PlanArgs plan2 = plan;
+      plan2.diag = nullptr;
       hipLaunchKernelGGL(ffn_phase_f32<2>, dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0, stream,
                          static_cast<const float*>(abuf), a.I, static_cast<const float*>(a.w_down),
-                         static_cast<const float*>(nullptr), a.d, plan, static_cast<float*>(a.h_sorted));
+                         static_cast<const float*>(nullptr), a.d, plan2, static_cast<float*>(a.h_sorted));
       break;
     }
   }

@@ -148,33 +148,32 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   return wbase + incl - v;
 }
 
-// Copy rows src_row(j) -> dst_row(j) for j < nrows, 16 bytes per element,
-// flattened over the block so consecutive threads touch consecutive bytes of a
-// row; kCopyBatch loads are issued before their stores so a thread keeps
-// several requests in flight instead of one load->store round trip at a time.
-constexpr int kCopyBatch = 8;
+// Copy rows src_row(j) -> dst_row(j) for j < nrows, kCopyRows rows at a time:
+// a thread owns one 16-byte column of the rows, so its kCopyRows loads are in
+// flight together and consecutive threads touch consecutive bytes of a row.
+constexpr int kCopyRows = 16;
 
 template <typename SrcRow, typename DstRow>
 __device__ __forceinline__ void copy_rows(const uint4* __restrict__ x, uint4* __restrict__ xs, int nrows,
                                           int row_vecs, SrcRow src_row, DstRow dst_row) {
-  const int total = nrows * row_vecs;
-  for (int base = threadIdx.x; base < total; base += kThreads * kCopyBatch) {
-    uint4 v[kCopyBatch];
+  for (int j0 = 0; j0 < nrows; j0 += kCopyRows) {
+    const int nr = min(kCopyRows, nrows - j0);
+    const uint4* src[kCopyRows];
+    uint4* dst[kCopyRows];
 #pragma unroll
-    for (int u = 0; u < kCopyBatch; ++u) {
-      const int idx = base + u * kThreads;
-      if (idx < total) {
-        const int j = idx / row_vecs, c = idx % row_vecs;
-        v[u] = x[static_cast<size_t>(src_row(j)) * row_vecs + c];
-      }
+    for (int j = 0; j < kCopyRows; ++j) {
+      const int jj = j0 + (j < nr ? j : 0);
+      src[j] = x + static_cast<size_t>(src_row(jj)) * row_vecs;
+      dst[j] = xs + static_cast<size_t>(dst_row(jj)) * row_vecs;
     }
+    for (int c = threadIdx.x; c < row_vecs; c += kThreads) {
+      uint4 v[kCopyRows];
 #pragma unroll
-    for (int u = 0; u < kCopyBatch; ++u) {
-      const int idx = base + u * kThreads;
-      if (idx < total) {
-        const int j = idx / row_vecs, c = idx % row_vecs;
-        xs[static_cast<size_t>(dst_row(j)) * row_vecs + c] = v[u];
-      }
+      for (int j = 0; j < kCopyRows; ++j)
+        if (j < nr) v[j] = src[j][c];
+#pragma unroll
+      for (int j = 0; j < kCopyRows; ++j)
+        if (j < nr) dst[j][c] = v[j];
     }
   }
 }
@@ -205,10 +204,22 @@ __global__ __launch_bounds__(kThreads) void permute_small(PermCtx c, int n_share
     before[g] = 0;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < c.Nr; i += kThreads) {
-    const int g = group_of(c, i);
-    atomicAdd(&total[g], 1);
-    if (i < lo) atomicAdd(&before[g], 1);
+  {
+    // all of a thread's id loads are issued before its first atomic
+    constexpr int kPer = kSmallMaxNr / kThreads;
+    int gq[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int i = threadIdx.x + q * kThreads;
+      gq[q] = i < c.Nr ? group_of(c, i) : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int i = threadIdx.x + q * kThreads;
+      if (gq[q] < 0) continue;
+      atomicAdd(&total[gq[q]], 1);
+      if (i < lo) atomicAdd(&before[gq[q]], 1);
+    }
   }
   __syncthreads();
   // exclusive scan of the totals: thread owns 4 consecutive groups
@@ -328,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void permute_scatter(PermCtx c, int n_sha
 
 // ---- row gather: x_sorted[n] = x[token(sorted_to_flat[n])] ---------------------
 // Each block copies kGatherRows consecutive sorted rows.
-constexpr int kGatherRows = 16;
+constexpr int kGatherRows = kCopyRows;
 
 __global__ __launch_bounds__(kThreads) void permute_gather(const uint4* __restrict__ x, const int* __restrict__ s2f,
                                                            int T, int k, int Nr, int N, int row_vecs,

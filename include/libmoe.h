@@ -110,6 +110,9 @@ moe_status moe_gate(const float* logits, int32_t T, int32_t E, int32_t k,
  *   group_offsets  [G+1] int32, written: exclusive scan of the group sizes.
  *   sorted_to_flat [N] int32, written: f of the assignment at sorted row n.
  *   flat_to_sorted [N] int32, written: its inverse.
+ *   sorted_token   [N] int32 or NULL, written: the token of sorted row n
+ *                  (f / k for routed f, (f - T*k) mod T for shared); the row
+ *                  index list that lets moe_grouped_ffn read x directly.
  *   x_sorted       [N][d] of `dtype`, written: x_sorted[n] = x[token(f)]
  *                  bit for bit.
  *   workspace      device scratch of the queried size.
@@ -120,7 +123,7 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
                        int32_t n_shared, int32_t n_priority,
                        const void* x, moe_dtype dtype, int32_t d,
                        int32_t* group_offsets, int32_t* sorted_to_flat,
-                       int32_t* flat_to_sorted, void* x_sorted,
+                       int32_t* flat_to_sorted, int32_t* sorted_token, void* x_sorted,
                        void* workspace, size_t* workspace_bytes, hipStream_t stream);
 
 /*
@@ -132,7 +135,12 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
  *   For sorted row n of group g (expert e = g mod E for g < nseg*E, else
  *   E + g - nseg*E):
  *     h[n] = W_down[e] . ( silu(W_gate[e] . xs[n]) * (W_up[e] . xs[n]) ).
- *   x_sorted       [n_rows][d] of `dtype`.
+ *   x_sorted       [n_rows][d] of `dtype` when x_rows is NULL.  Otherwise the
+ *                  token matrix [n_x][d] and x_rows [n_rows] int32 names the
+ *                  row of it that sorted row n reads (moe_permute's
+ *                  sorted_token), so the permutation's row gather is folded
+ *                  into the FFN's loads; entries are clamped to [0, n_x).
+ *   n_x            rows of x_sorted when x_rows is given (ignored otherwise).
  *   group_offsets  [G+1] int32 with G = nseg*E + n_shared, non-decreasing,
  *                  group_offsets[G] == n_rows (device data: never read on the
  *                  host; the tile list is built on the device).
@@ -149,7 +157,8 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
  *   large groups) gave up after its bound; the outputs are then not to be
  *   trusted.
  */
-moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* group_offsets,
+moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                           const int32_t* group_offsets,
                            int32_t n_rows, int32_t E, int32_t n_shared, int32_t nseg,
                            int32_t d, int32_t I,
                            const void* w_gate, const void* w_up, const void* w_down,

@@ -143,8 +143,8 @@ def permute(topk_ids: np.ndarray, E: int, n_shared: int = 0, n_priority: int = 0
     """Counting sort of the assignments into contiguous expert groups.
 
     Sort key (group, flat index); group_offsets is the exclusive scan of the
-    group sizes; x_sorted[n] is a bit copy of the hidden row of the token that
-    assignment sorted_to_flat[n] belongs to.
+    group sizes; sorted_token[n] is the token that assignment sorted_to_flat[n]
+    belongs to, and x_sorted[n] a bit copy of that token's hidden row.
     """
     group, token, G, _ = assignment_groups(topk_ids, E, n_shared, n_priority)
     N = group.shape[0]
@@ -156,7 +156,8 @@ def permute(topk_ids: np.ndarray, E: int, n_shared: int = 0, n_priority: int = 0
     offsets[1:] = np.cumsum(sizes)
     out = {"group_offsets": offsets.astype(np.int32),
            "sorted_to_flat": s2f.astype(np.int32),
-           "flat_to_sorted": f2s.astype(np.int32)}
+           "flat_to_sorted": f2s.astype(np.int32),
+           "sorted_token": token[s2f].astype(np.int32)}
     if x is not None:
         out["x_sorted"] = np.ascontiguousarray(np.asarray(x)[token[s2f]])
     return out

@@ -57,10 +57,10 @@ def test_gate_validation(lib):
 
 def _perm(lib, T=4, E=8, k=2, S=0, P=0, x=FAKE, dt=1, d=64, ws=FAKE, nbytes=1 << 30, **kw):
     n = ctypes.c_size_t(nbytes)
-    ptrs = dict(ids=FAKE, go=FAKE, s2f=FAKE, f2s=FAKE, xs=FAKE)
+    ptrs = dict(ids=FAKE, go=FAKE, s2f=FAKE, f2s=FAKE, tok=FAKE, xs=FAKE)
     ptrs.update(kw)
     return lib.moe_permute(ptrs["ids"], T, E, k, S, P, x, dt, d, ptrs["go"], ptrs["s2f"], ptrs["f2s"],
-                           ptrs["xs"], ws, ctypes.byref(n), None), n.value
+                           ptrs["tok"], ptrs["xs"], ws, ctypes.byref(n), None), n.value
 
 
 def test_permute_validation_and_query(lib):
@@ -72,6 +72,8 @@ def test_permute_validation_and_query(lib):
     assert _perm(lib, go=None)[0] == INV
     assert _perm(lib, xs=None)[0] == INV             # x given without x_sorted
     assert _perm(lib, xs=FAKE + 8)[0] == INV         # misaligned x_sorted
+    assert _perm(lib, tok=FAKE + 2)[0] == INV        # misaligned sorted_token
+    assert _perm(lib, tok=None, x=None, xs=None, ws=None, nbytes=0)[0] == 0   # optional outputs
     st, need = _perm(lib, T=8192, E=128, k=8, ws=None, nbytes=0)
     assert st == 0 and need > 0
     assert _perm(lib, T=8192, E=128, k=8, nbytes=need - 1)[0] == WS
@@ -79,12 +81,12 @@ def test_permute_validation_and_query(lib):
     assert st == 0 and need_small > 0
 
 
-def _ffn(lib, N=64, E=8, S=0, nseg=1, d=64, I=128, dt=1, ws=FAKE, nbytes=1 << 40, **kw):
+def _ffn(lib, N=64, E=8, S=0, nseg=1, d=64, I=128, dt=1, ws=FAKE, nbytes=1 << 40, n_x=0, **kw):
     n = ctypes.c_size_t(nbytes)
-    p = dict(xs=FAKE, go=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, h=FAKE)
+    p = dict(xs=FAKE, rows=None, go=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, h=FAKE)
     p.update(kw)
-    return lib.moe_grouped_ffn(p["xs"], p["go"], N, E, S, nseg, d, I, p["wg"], p["wu"], p["wd"], dt, p["h"],
-                               ws, ctypes.byref(n), None), n.value
+    return lib.moe_grouped_ffn(p["xs"], p["rows"], n_x, p["go"], N, E, S, nseg, d, I, p["wg"], p["wu"], p["wd"],
+                               dt, p["h"], ws, ctypes.byref(n), None), n.value
 
 
 def test_ffn_validation_and_query(lib):
@@ -96,6 +98,8 @@ def test_ffn_validation_and_query(lib):
     assert _ffn(lib, E=600)[0] == UNS
     assert _ffn(lib, wd=None)[0] == INV
     assert _ffn(lib, wg=FAKE + 4)[0] == INV
+    assert _ffn(lib, rows=FAKE, n_x=0)[0] == INV          # row list without a row count
+    assert _ffn(lib, rows=FAKE + 2, n_x=16)[0] == INV     # misaligned row list
     st, need = _ffn(lib, N=65536, E=128, d=2048, I=768, ws=None, nbytes=0)
     assert st == 0 and need >= 65536 * 768 * 2           # holds the bf16 intermediate
     assert _ffn(lib, N=65536, E=128, d=2048, I=768, nbytes=need - 1)[0] == WS

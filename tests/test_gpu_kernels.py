@@ -128,12 +128,12 @@ def test_permute_parity(T, E, k, S, P, d, dtype, kind):
     N = T * (k + S)
     G = (2 if P > 0 else 1) * E + S
     out = {"group_offsets": _poison(G + 1, torch.int32), "sorted_to_flat": _poison(N, torch.int32),
-           "flat_to_sorted": _poison(N, torch.int32)}
+           "flat_to_sorted": _poison(N, torch.int32), "sorted_token": _poison(N, torch.int32)}
     if x is not None:
         out["x_sorted"] = _poison((N, d), dtype)
     got = moe.permute(ids.to(DEV), E, S, P, x.to(DEV) if x is not None else None, out=out)
     torch.cuda.synchronize()
-    for key in ("group_offsets", "sorted_to_flat", "flat_to_sorted"):
+    for key in ("group_offsets", "sorted_to_flat", "flat_to_sorted", "sorted_token"):
         np.testing.assert_array_equal(np_of(got[key]), ref[key], err_msg=key)
     if x is not None:
         assert np.array_equal(np_of(got["x_sorted"]), ref["x_sorted"])
@@ -198,10 +198,17 @@ def test_grouped_ffn_parity(T, E, k, S, P, d, I, dtype, kind):
     h = moe.grouped_ffn(xs, offs, E, S, nseg, wl.w_gate.to(DEV), wl.w_up.to(DEV), wl.w_down.to(DEV),
                         h_sorted=_poison((xs.shape[0], d), xs.dtype), workspace=ws)
     torch.cuda.synchronize()
-    if dtype == "bf16" and P > 0:
-        assert int(ws[-4:].view(torch.int32).item()) == 0, "a tile-queue wait gave up"
+    assert int(ws[-4:].view(torch.int32).item()) == 0, "a tile-queue wait gave up"
     err = rel_max_err(f64_of(h), h_ref)
     assert err <= TOL[dtype], err
+    # the same FFN reading the token rows through the permutation's row list
+    # (gather folded into the loads) gives the same bits
+    x_dev = wl.x.to(DEV)
+    rows = torch.from_numpy(p_ref["sorted_token"]).to(DEV)
+    h2 = moe.grouped_ffn(x_dev, offs, E, S, nseg, wl.w_gate.to(DEV), wl.w_up.to(DEV), wl.w_down.to(DEV),
+                         h_sorted=_poison((xs.shape[0], d), xs.dtype), x_rows=rows)
+    torch.cuda.synchronize()
+    assert torch.equal(h2, h)
 
 
 # ------------------------------------------------------------------ combine

@@ -64,10 +64,7 @@ def test_layer_parity(name):
     p_ref = O.permute(ids_ref, s.E, s.S, s.n_priority)
     for key in ("group_offsets", "sorted_to_flat", "flat_to_sorted"):
         np.testing.assert_array_equal(np_of(layer.perm[key]), p_ref[key], err_msg=key)
-    s2f = layer.perm["sorted_to_flat"].long()
-    Nr = s.T * s.k
-    tok = torch.where(s2f < Nr, s2f // s.k, (s2f - Nr) % s.T)
-    assert torch.equal(layer.perm["x_sorted"], wl.x.index_select(0, tok))
+    np.testing.assert_array_equal(np_of(layer.perm["sorted_token"]), p_ref["sorted_token"])
 
     # statistics over the layer stack, in full
     all_ids = np.stack([ids_ref] + [O.gate(np_of(wl.stats_logits[l]), s.k)[0]

@@ -30,6 +30,7 @@ def test_permute_golden(case):
     np.testing.assert_array_equal(p["sorted_to_flat"], case["sorted_to_flat"])
     np.testing.assert_array_equal(p["flat_to_sorted"], case["flat_to_sorted"])
     np.testing.assert_array_equal(p["x_sorted"][:, 0], case["token_of_sorted"])
+    np.testing.assert_array_equal(p["sorted_token"], case["token_of_sorted"])
 
 
 def _python_reference(ids, E, S, P):

@@ -23,8 +23,8 @@ _sz = ctypes.POINTER(ctypes.c_size_t)
 
 SIGNATURES = {
     "moe_gate": [_p, _i32, _i32, _i32, _i32, _p, _p, _p],
-    "moe_permute": [_p, _i32, _i32, _i32, _i32, _i32, _p, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p],
-    "moe_grouped_ffn": [_p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _sz, _p],
+    "moe_permute": [_p, _i32, _i32, _i32, _i32, _i32, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _sz, _p],
+    "moe_grouped_ffn": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _sz, _p],
     "moe_combine": [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p],
     "moe_stats": [_p, _i32, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
 }

@@ -69,13 +69,15 @@ def permute_workspace_bytes(T, E, k, n_shared=0, n_priority=0) -> int:
     lib = _lib.load()
     n = ctypes.c_size_t(0)
     check("moe_permute", lib.moe_permute(None, T, E, k, n_shared, n_priority, None, MOE_BF16, 8,
-                                         None, None, None, None, None, ctypes.byref(n), None))
+                                         None, None, None, None, None, None, ctypes.byref(n), None))
     return int(n.value)
 
 
 def permute(topk_ids: torch.Tensor, E: int, n_shared: int = 0, n_priority: int = 0,
             x: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None,
-            workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+            workspace: Optional[torch.Tensor] = None, sorted_token: bool = True) -> Dict[str, torch.Tensor]:
+    """Counting sort of the assignments; `sorted_token` also writes the token
+    of every sorted row (the row list moe_grouped_ffn can read x through)."""
     _need(topk_ids, "topk_ids", torch.int32, 2)
     T, k = topk_ids.shape
     dev = topk_ids.device
@@ -95,6 +97,8 @@ def permute(topk_ids: torch.Tensor, E: int, n_shared: int = 0, n_priority: int =
         o["sorted_to_flat"] = torch.empty(N, dtype=torch.int32, device=dev)
     if "flat_to_sorted" not in o:
         o["flat_to_sorted"] = torch.empty(N, dtype=torch.int32, device=dev)
+    if sorted_token and "sorted_token" not in o:
+        o["sorted_token"] = torch.empty(N, dtype=torch.int32, device=dev)
     if x is not None and "x_sorted" not in o:
         o["x_sorted"] = torch.empty((N, d), dtype=x.dtype, device=dev)
     if workspace is None:
@@ -105,6 +109,7 @@ def permute(topk_ids: torch.Tensor, E: int, n_shared: int = 0, n_priority: int =
     check("moe_permute", lib.moe_permute(
         _ptr(topk_ids), T, E, k, n_shared, n_priority, _ptr(x), dt, d,
         _ptr(o["group_offsets"]), _ptr(o["sorted_to_flat"]), _ptr(o["flat_to_sorted"]),
+        _ptr(o.get("sorted_token")) if sorted_token else None,
         _ptr(o.get("x_sorted")) if x is not None else None,
         _ptr(workspace), ctypes.byref(nbytes), _stream(dev)))
     return o
@@ -114,7 +119,7 @@ def ffn_workspace_bytes(n_rows, E, n_shared, nseg, d, I, dtype=torch.bfloat16) -
     lib = _lib.load()
     n = ctypes.c_size_t(0)
     code = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
-    check("moe_grouped_ffn", lib.moe_grouped_ffn(None, None, n_rows, E, n_shared, nseg, d, I, None, None,
+    check("moe_grouped_ffn", lib.moe_grouped_ffn(None, None, 0, None, n_rows, E, n_shared, nseg, d, I, None, None,
                                                  None, code, None, None, ctypes.byref(n), None))
     return int(n.value)
 
@@ -122,12 +127,20 @@ def ffn_workspace_bytes(n_rows, E, n_shared, nseg, d, I, dtype=torch.bfloat16) -
 def grouped_ffn(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_shared: int, nseg: int,
                 w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
                 h_sorted: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                workspace: Optional[torch.Tensor] = None,
+                x_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Grouped SwiGLU FFN.  With `x_rows` ([N] int32, e.g. permute's
+    sorted_token) `x_sorted` is the unsorted token matrix and sorted row n
+    reads its row x_rows[n]."""
     _need(x_sorted, "x_sorted", None, 2)
     _need(group_offsets, "group_offsets", torch.int32, 1)
     for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
         _need(w, name, x_sorted.dtype, 3)
-    N, d = x_sorted.shape
+    n_x, d = x_sorted.shape
+    N = n_x
+    if x_rows is not None:
+        _need(x_rows, "x_rows", torch.int32, 1)
+        N = x_rows.numel()
     I = w_gate.shape[1]
     if w_gate.shape != (E + n_shared, I, d) or w_up.shape != w_gate.shape or w_down.shape != (E + n_shared, d, I):
         raise ValueError("expert weight shapes do not match [E+S][I][d] / [E+S][d][I]")
@@ -142,7 +155,7 @@ def grouped_ffn(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_s
     lib = _lib.load()
     nbytes = ctypes.c_size_t(workspace.numel())
     check("moe_grouped_ffn", lib.moe_grouped_ffn(
-        _ptr(x_sorted), _ptr(group_offsets), N, E, n_shared, nseg, d, I, _ptr(w_gate), _ptr(w_up),
+        _ptr(x_sorted), _ptr(x_rows), n_x, _ptr(group_offsets), N, E, n_shared, nseg, d, I, _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _dtype_code(x_sorted), _ptr(h_sorted), _ptr(workspace), ctypes.byref(nbytes),
         _stream(dev)))
     return h_sorted
@@ -218,7 +231,8 @@ class MoeLayer:
     """
 
     def __init__(self, E, k, d, I, T, dtype, w_gate, w_up, w_down, n_shared=0, n_priority=0,
-                 renormalize=True, stats_layers=0, req_offsets=None, device="cuda", topk_ids=None):
+                 renormalize=True, stats_layers=0, req_offsets=None, device="cuda", topk_ids=None,
+                 fused_gather=True):
         dev = torch.device(device)
         self.E, self.k, self.d, self.I, self.T = E, k, d, I, T
         self.S, self.P = n_shared, n_priority
@@ -232,10 +246,15 @@ class MoeLayer:
         # statistics id stack)
         self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_ids is None else topk_ids
         self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        # fused_gather: the permutation writes only the row list and the FFN
+        # reads the token rows through it; otherwise x_sorted is materialised
+        self.fused_gather = fused_gather
         self.perm = {"group_offsets": torch.empty(G + 1, dtype=torch.int32, device=dev),
                      "sorted_to_flat": torch.empty(N, dtype=torch.int32, device=dev),
                      "flat_to_sorted": torch.empty(N, dtype=torch.int32, device=dev),
-                     "x_sorted": torch.empty((N, d), dtype=dtype, device=dev)}
+                     "sorted_token": torch.empty(N, dtype=torch.int32, device=dev)}
+        if not fused_gather:
+            self.perm["x_sorted"] = torch.empty((N, d), dtype=dtype, device=dev)
         self.perm_ws = torch.empty(max(permute_workspace_bytes(T, E, k, n_shared, n_priority), 256),
                                    dtype=torch.uint8, device=dev)
         self.h_sorted = torch.empty((N, d), dtype=dtype, device=dev)
@@ -254,9 +273,13 @@ class MoeLayer:
         return gate(logits, self.k, self.renormalize, self.topk_ids, self.topk_w)
 
     def permute(self, x):
-        return permute(self.topk_ids, self.E, self.S, self.P, x, out=self.perm, workspace=self.perm_ws)
+        return permute(self.topk_ids, self.E, self.S, self.P, None if self.fused_gather else x, out=self.perm,
+                       workspace=self.perm_ws)
 
-    def ffn(self):
+    def ffn(self, x):
+        if self.fused_gather:
+            return grouped_ffn(x, self.perm["group_offsets"], self.E, self.S, self.nseg, self.w_gate, self.w_up,
+                               self.w_down, self.h_sorted, self.ffn_ws, x_rows=self.perm["sorted_token"])
         return grouped_ffn(self.perm["x_sorted"], self.perm["group_offsets"], self.E, self.S, self.nseg,
                            self.w_gate, self.w_up, self.w_down, self.h_sorted, self.ffn_ws)
 
@@ -280,18 +303,22 @@ class MoeLayer:
         st = _stream(dev) if stream is None else stream
         k, T, E = self.k, self.T, self.E
         dt = _dtype_code(x)
+        fused = self.fused_gather
         n_perm = ctypes.c_size_t(self.perm_ws.numel())
         n_ffn = ctypes.c_size_t(self.ffn_ws.numel())
         calls = [
             ("moe_gate", lib.moe_gate, (logits.data_ptr(), T, E, k, int(bool(self.renormalize)),
                                         self.topk_ids.data_ptr(), self.topk_w.data_ptr(), st)),
-            ("moe_permute", lib.moe_permute, (self.topk_ids.data_ptr(), T, E, k, self.S, self.P, x.data_ptr(), dt,
+            ("moe_permute", lib.moe_permute, (self.topk_ids.data_ptr(), T, E, k, self.S, self.P,
+                                              None if fused else x.data_ptr(), dt,
                                               self.d, self.perm["group_offsets"].data_ptr(),
                                               self.perm["sorted_to_flat"].data_ptr(),
                                               self.perm["flat_to_sorted"].data_ptr(),
-                                              self.perm["x_sorted"].data_ptr(), self.perm_ws.data_ptr(),
-                                              ctypes.byref(n_perm), st)),
-            ("moe_grouped_ffn", lib.moe_grouped_ffn, (self.perm["x_sorted"].data_ptr(),
+                                              self.perm["sorted_token"].data_ptr(),
+                                              None if fused else self.perm["x_sorted"].data_ptr(),
+                                              self.perm_ws.data_ptr(), ctypes.byref(n_perm), st)),
+            ("moe_grouped_ffn", lib.moe_grouped_ffn, (x.data_ptr() if fused else self.perm["x_sorted"].data_ptr(),
+                                                      self.perm["sorted_token"].data_ptr() if fused else None, T,
                                                       self.perm["group_offsets"].data_ptr(), self.N, E, self.S,
                                                       self.nseg, self.d, self.I, self.w_gate.data_ptr(),
                                                       self.w_up.data_ptr(), self.w_down.data_ptr(), dt,
@@ -330,7 +357,7 @@ class MoeLayer:
                 self.stats(stats_ids)
             side = False
         self.permute(x)
-        self.ffn()
+        self.ffn(x)
         self.combine()
         if side:
             self.stats(stats_ids)

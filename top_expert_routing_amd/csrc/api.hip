@@ -64,8 +64,8 @@ moe_status moe_gate(const float* logits, int32_t T, int32_t E, int32_t k, int32_
 
 moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k, int32_t n_shared,
                        int32_t n_priority, const void* x, moe_dtype dtype, int32_t d, int32_t* group_offsets,
-                       int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_sorted, void* workspace,
-                       size_t* workspace_bytes, hipStream_t stream) {
+                       int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* sorted_token, void* x_sorted,
+                       void* workspace, size_t* workspace_bytes, hipStream_t stream) {
   if (T < 0 || E < 1 || k < 1 || k > E || n_shared < 0 || n_priority < 0 || n_priority > T)
     return MOE_ERR_INVALID_ARG;
   if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
@@ -83,7 +83,9 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
   if (!group_offsets || !aligned4(group_offsets)) return MOE_ERR_INVALID_ARG;
   if (N > 0) {
     if (!topk_ids || !sorted_to_flat || !flat_to_sorted) return MOE_ERR_INVALID_ARG;
-    if (!aligned4(topk_ids) || !aligned4(sorted_to_flat) || !aligned4(flat_to_sorted)) return MOE_ERR_INVALID_ARG;
+    if (!aligned4(topk_ids) || !aligned4(sorted_to_flat) || !aligned4(flat_to_sorted) ||
+        (sorted_token && !aligned4(sorted_token)))
+      return MOE_ERR_INVALID_ARG;
     if (x != nullptr && (!x_sorted || !aligned16(x) || !aligned16(x_sorted))) return MOE_ERR_INVALID_ARG;
   }
   moe::PermuteArgs a;
@@ -99,11 +101,13 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
   a.group_offsets = group_offsets;
   a.sorted_to_flat = sorted_to_flat;
   a.flat_to_sorted = flat_to_sorted;
+  a.sorted_token = sorted_token;
   a.x_sorted = x_sorted;
   return hip_status(moe::launch_permute(a, workspace, stream));
 }
 
-moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* group_offsets, int32_t n_rows, int32_t E,
+moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                           const int32_t* group_offsets, int32_t n_rows, int32_t E,
                            int32_t n_shared, int32_t nseg, int32_t d, int32_t I, const void* w_gate,
                            const void* w_up, const void* w_down, moe_dtype dtype, void* h_sorted, void* workspace,
                            size_t* workspace_bytes, hipStream_t stream) {
@@ -123,8 +127,12 @@ moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* group_offsets, i
   if (!aligned16(x_sorted) || !aligned4(group_offsets) || !aligned16(w_gate) || !aligned16(w_up) ||
       !aligned16(w_down) || !aligned16(h_sorted))
     return MOE_ERR_INVALID_ARG;
+  if (x_rows && (!aligned4(x_rows) || n_x < 1)) return MOE_ERR_INVALID_ARG;
+  if (x_rows && !fits_int(static_cast<long long>(n_x) * d)) return MOE_ERR_UNSUPPORTED;
   moe::FfnArgs a;
   a.x_sorted = x_sorted;
+  a.x_rows = x_rows;
+  a.n_x = x_rows ? n_x : n_rows;
   a.group_offsets = group_offsets;
   a.n_rows = n_rows;
   a.E = E;

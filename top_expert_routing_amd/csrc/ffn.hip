@@ -47,8 +47,16 @@ constexpr int kXcds = 8;                 // MI355X: 8 XCDs, workgroups dealt rou
 struct PlanArgs {
   const int* offs;
   int G, E, nseg, BM, n_rows, max_tiles;
-  int* diag;   // diagnostic word, cleared by block 0 (nullptr: leave it)
+  int* diag;          // diagnostic word, cleared by block 0 (nullptr: leave it)
+  const int* arows;   // A row of sorted row n (nullptr: row n itself)
+  int n_x;            // rows of A when arows is given
 };
+
+// Row of the A matrix that sorted row n reads (the row gather folded into the
+// loads when a row list is given; clamped so a bad entry stays in bounds).
+__device__ __forceinline__ size_t a_row(const int* arows, int n_x, int n) {
+  return arows ? static_cast<size_t>(min(max(arows[n], 0), n_x - 1)) : static_cast<size_t>(n);
+}
 
 struct Item {
   int row0, rows, expert, chunk;   // rows == 0: no work for this block
@@ -176,15 +184,20 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
 
   // A staging: thread handles uint4 slots idx = tid + s*256 of the chunk
   uint4 stage[APT];
+  const uint16_t* arow[APT];
+#pragma unroll
+  for (int s = 0; s < APT; ++s) {
+    const int idx = threadIdx.x + s * kThreads;
+    const int r = idx / VPR;
+    arow[s] = (idx < BM * VPR && r < rows) ? A + a_row(plan.arows, plan.n_x, row0 + r) * K : nullptr;
+  }
   auto load_a = [&](int c) {
 #pragma unroll
     for (int s = 0; s < APT; ++s) {
-      const int idx = threadIdx.x + s * kThreads;
-      const int r = idx / VPR, kv = idx % VPR;
+      const int kv = (threadIdx.x + s * kThreads) % VPR;
       const int k = c * kDecodeKC + kv * 8;
       stage[s] = make_uint4(0, 0, 0, 0);
-      if (idx < BM * VPR && r < rows && k < K)
-        stage[s] = *reinterpret_cast<const uint4*>(A + static_cast<size_t>(row0 + r) * K + k);
+      if (arow[s] && k < K) stage[s] = *reinterpret_cast<const uint4*>(arow[s] + k);
     }
   };
   auto store_a = [&](int buf) {
@@ -310,7 +323,8 @@ struct GemmShape {
 // `it.chunk` of expert `it.expert`.  All threads of the block call it; `smem`
 // is the block's operand ring, free on entry (no wave still reads it).
 template <int PHASE, int MI, int NJ>
-__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0,
+__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x,
+                                          int K, const uint16_t* __restrict__ W0,
                                           const uint16_t* __restrict__ W1, int Ncols, const Item& it,
                                           uint16_t* __restrict__ out, uint8_t* smem) {
   using S = GemmShape<MI, NJ>;
@@ -340,7 +354,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, int K,
 #pragma unroll
   for (int q = 0; q < ADMA; ++q) {
     const int r = 16 * (wave + kWaves * q) + dr;
-    asrc[q] = A + static_cast<size_t>(row0 + min(r, rows - 1)) * K + 8 * ((lane & 3) ^ gemm_swz(r));
+    asrc[q] = A + a_row(arows, n_x, row0 + min(r, rows - 1)) * K + 8 * ((lane & 3) ^ gemm_swz(r));
   }
 #pragma unroll
   for (int q = 0; q < BDMA; ++q) {
@@ -448,7 +462,7 @@ __global__ __launch_bounds__(kThreads, kGemmBlocksPerCu) void ffn_gemm_bf16(
   constexpr int OUTC = PHASE == 1 ? S::BN / 2 : S::BN;
   const Item it = block_find_item(plan, (Ncols + OUTC - 1) / OUTC);
   if (it.rows == 0) return;
-  gemm_tile<PHASE, MI, NJ>(A, K, W0, W1, Ncols, it, out, smem);
+  gemm_tile<PHASE, MI, NJ>(A, plan.arows, plan.n_x, K, W0, W1, Ncols, it, out, smem);
 }
 
 // ---- mixed batches: one persistent launch, per-XCD tile queues ----------------
@@ -484,6 +498,8 @@ struct QueueArgs {
   const int* offs;
   int G, E, nseg, n_rows, n_prio_groups, nch1, nch2, lag;
   int nq;       // queues = XCDs of the device (1 when it is a single-XCD partition)
+  const int* arows;   // phase-1 A row list (nullptr: sorted rows)
+  int n_x;
   int* heads;   // [kXcds * kQueueStride]
   int* done1;   // [units]
   int* error;   // set when a wait gave up
@@ -589,7 +605,7 @@ __global__ __launch_bounds__(kThreads, kGemmBlocksPerCu) void ffn_queue_bf16(
     const int glo = min(max(q.offs[g], 0), q.n_rows), ghi = min(max(q.offs[g + 1], 0), q.n_rows);
     const Item it{glo + mt * BM, min(BM, ghi - glo - mt * BM), expert_of_group(g, q.E, q.nseg), chunk};
     if (phase == 1) {
-      gemm_tile<1, MI, NJ>(x, d, w_gate, w_up, I, it, abuf, smem);
+      gemm_tile<1, MI, NJ>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are in L2
       __syncthreads();
       if (tid == 0) __hip_atomic_fetch_add(q.done1 + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -608,7 +624,7 @@ __global__ __launch_bounds__(kThreads, kGemmBlocksPerCu) void ffn_queue_bf16(
       }
       __syncthreads();
       asm volatile("buffer_inv sc0" ::: "memory");
-      gemm_tile<2, MI, NJ>(abuf, I, w_down, nullptr, d, it, h, smem);
+      gemm_tile<2, MI, NJ>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
     }
   }
 }
@@ -641,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void ffn_phase_f32(const float* __restric
   for (int k0 = 0; k0 < K; k0 += 64) {
     for (int idx = threadIdx.x; idx < BM * 64; idx += kThreads) {
       const int r = idx >> 6, kk = k0 + (idx & 63);
-      As[idx] = (r < rows && kk < K) ? A[static_cast<size_t>(row0 + r) * K + kk] : 0.f;
+      As[idx] = (r < rows && kk < K) ? A[a_row(plan.arows, plan.n_x, row0 + r) * K + kk] : 0.f;
     }
     __syncthreads();
     if (n < Ncols) {
@@ -740,6 +756,7 @@ void launch_decode_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan,
                      static_cast<const uint16_t*>(a.w_up), a.I, plan, abuf);
   PlanArgs plan2 = plan;
   plan2.diag = nullptr;
+  plan2.arows = nullptr;
   hipLaunchKernelGGL((ffn_decode_bf16<MF, kDecodeNfc2, 2>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
                      static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted));
@@ -753,6 +770,7 @@ void launch_gemm_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, u
                      static_cast<const uint16_t*>(a.w_up), a.I, plan, abuf);
   PlanArgs plan2 = plan;
   plan2.diag = nullptr;
+  plan2.arows = nullptr;
   hipLaunchKernelGGL((ffn_gemm_bf16<2, kGemmMI, kGemmNJ>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
                      static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted));
@@ -792,6 +810,8 @@ void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t 
   q.nch1 = (a.I + BN / 2 - 1) / (BN / 2);
   q.nch2 = (a.d + BN - 1) / BN;
   q.nq = nq;
+  q.arows = a.x_rows;
+  q.n_x = a.n_x;
   q.lag = (blocks + nq - 1) / nq;
   q.heads = qbase;
   q.done1 = qbase + kXcds * kQueueStride;
@@ -820,6 +840,8 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
   plan.n_rows = a.n_rows;
   plan.max_tiles = L.max_tiles;
   plan.diag = reinterpret_cast<int*>(ws + L.total - 4);
+  plan.arows = a.x_rows;
+  plan.n_x = a.n_x;
   switch (L.path) {
     case Path::kDecode: {
       uint16_t* abuf = reinterpret_cast<uint16_t*>(ws + L.a_off);
@@ -844,6 +866,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
                          static_cast<const float*>(a.w_up), a.I, plan, abuf);
       PlanArgs plan2 = plan;
       plan2.diag = nullptr;
+      plan2.arows = nullptr;
       hipLaunchKernelGGL(ffn_phase_f32<2>, dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0, stream,
                          static_cast<const float*>(abuf), a.I, static_cast<const float*>(a.w_down),
                          static_cast<const float*>(nullptr), a.d, plan2, static_cast<float*>(a.h_sorted));

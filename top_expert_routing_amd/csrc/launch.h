@@ -22,6 +22,7 @@ struct PermuteArgs {
   int* group_offsets;
   int* sorted_to_flat;
   int* flat_to_sorted;
+  int* sorted_token;  // may be nullptr
   void* x_sorted;
 };
 size_t permute_workspace_bytes(int T, int E, int k, int n_shared, int n_priority);
@@ -30,6 +31,8 @@ hipError_t launch_permute(const PermuteArgs& a, void* workspace, hipStream_t str
 // ---- grouped FFN -----------------------------------------------------------
 struct FfnArgs {
   const void* x_sorted;
+  const int* x_rows;  // nullptr: x_sorted is already in sorted order
+  int n_x;            // rows of x_sorted when x_rows is given
   const int* group_offsets;
   int n_rows, E, n_shared, nseg, d, I;
   const void* w_gate;

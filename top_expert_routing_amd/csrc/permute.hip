@@ -93,7 +93,7 @@ __device__ __forceinline__ void chunk_histogram(const PermCtx& c, int b, const i
 // through a generic pointer becomes a flat access that waits on every
 // outstanding global store.
 __device__ __forceinline__ void chunk_scatter(const PermCtx& c, int b, const int (&grp)[kIters], int* wcnt, int* s2f,
-                                              int* f2s) {
+                                              int* f2s, int* tok) {
   const int w = threadIdx.x >> 6, lane = lane_id();
   const int i0 = b * kChunk + w * kPerWave;
 #pragma unroll
@@ -114,15 +114,18 @@ __device__ __forceinline__ void chunk_scatter(const PermCtx& c, int b, const int
       const int pos = base + __popcll(static_cast<unsigned long long>(m & lanemask_lt()));
       s2f[pos] = i;
       f2s[i] = pos;
+      if (tok) tok[pos] = i / c.k;
     }
   }
 }
 
 // Shared-expert assignments sit at their own flat index.
-__device__ __forceinline__ void write_shared_identity(int Nr, int N, int nblocks, int b, int* s2f, int* f2s) {
+__device__ __forceinline__ void write_shared_identity(int Nr, int N, int T, int nblocks, int b, int* s2f, int* f2s,
+                                                      int* tok) {
   for (int f = Nr + b * kThreads + threadIdx.x; f < N; f += nblocks * kThreads) {
     s2f[f] = f;
     f2s[f] = f;
+    if (tok) tok[f] = (f - Nr) % T;
   }
 }
 
@@ -190,6 +193,7 @@ constexpr int kSmallMaxNr = 4096;
 
 __global__ __launch_bounds__(kThreads) void permute_small(PermCtx c, int n_shared, int* __restrict__ group_offsets,
                                                           int* __restrict__ s2f, int* __restrict__ f2s,
+                                                          int* __restrict__ tok,
                                                           const uint4* __restrict__ x, int row_vecs,
                                                           uint4* __restrict__ xs) {
   __shared__ int total[kMaxRoutedGroups];
@@ -257,6 +261,7 @@ __global__ __launch_bounds__(kThreads) void permute_small(PermCtx c, int n_share
       pos = before[g] + __popcll(static_cast<unsigned long long>(m & lanemask_lt()));
       s2f[pos] = i;
       f2s[i] = pos;
+      if (tok) tok[pos] = i / c.k;
     }
     pos_s[lane] = pos;
     tok_s[lane] = valid ? i / c.k : 0;
@@ -268,6 +273,7 @@ __global__ __launch_bounds__(kThreads) void permute_small(PermCtx c, int n_share
   for (int f = s_lo + threadIdx.x; f < s_hi; f += kThreads) {
     s2f[f] = f;
     f2s[f] = f;
+    if (tok) tok[f] = (f - c.Nr) % c.T;
   }
   __syncthreads();
   if (x == nullptr) return;
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(1024) void permute_scan(PermCtx c, int n_shared, in
 }
 
 __global__ __launch_bounds__(kThreads) void permute_scatter(PermCtx c, int n_shared, const int* blk, int* s2f,
-                                                            int* f2s) {
+                                                            int* f2s, int* tok) {
   __shared__ int wcnt[kWaves * kMaxRoutedGroups];
   int* vw = wcnt;
   const int b = blockIdx.x;
@@ -333,8 +339,8 @@ __global__ __launch_bounds__(kThreads) void permute_scatter(PermCtx c, int n_sha
     }
   }
   __syncthreads();
-  chunk_scatter(c, b, grp, vw, s2f, f2s);
-  write_shared_identity(c.Nr, c.Nr + n_shared * c.T, c.nb, b, s2f, f2s);
+  chunk_scatter(c, b, grp, vw, s2f, f2s, tok);
+  write_shared_identity(c.Nr, c.Nr + n_shared * c.T, c.T, c.nb, b, s2f, f2s, tok);
 }
 
 // ---- row gather: x_sorted[n] = x[token(sorted_to_flat[n])] ---------------------
@@ -394,7 +400,7 @@ hipError_t launch_permute(const PermuteArgs& a, void* workspace, hipStream_t str
     // one launch: ranks, scatter and row gather together
     const int nb = c.Nr > 0 ? (c.Nr + kSmallChunk - 1) / kSmallChunk : 1;
     hipLaunchKernelGGL(permute_small, dim3(nb), dim3(kThreads), 0, stream, c, a.n_shared, a.group_offsets,
-                       a.sorted_to_flat, a.flat_to_sorted, static_cast<const uint4*>(a.x), row_vecs,
+                       a.sorted_to_flat, a.flat_to_sorted, a.sorted_token, static_cast<const uint4*>(a.x), row_vecs,
                        static_cast<uint4*>(a.x_sorted));
     return hipGetLastError();
   }
@@ -402,7 +408,7 @@ hipError_t launch_permute(const PermuteArgs& a, void* workspace, hipStream_t str
   hipLaunchKernelGGL(permute_count, dim3(c.nb), dim3(kThreads), 0, stream, c, blk);
   hipLaunchKernelGGL(permute_scan, dim3(1), dim3(1024), 0, stream, c, a.n_shared, blk, a.group_offsets);
   hipLaunchKernelGGL(permute_scatter, dim3(c.nb), dim3(kThreads), 0, stream, c, a.n_shared,
-                     static_cast<const int*>(blk), a.sorted_to_flat, a.flat_to_sorted);
+                     static_cast<const int*>(blk), a.sorted_to_flat, a.flat_to_sorted, a.sorted_token);
   if (a.x != nullptr && N > 0) {
     const int blocks = (N + kGatherRows - 1) / kGatherRows;
     hipLaunchKernelGGL(permute_gather, dim3(blocks), dim3(kThreads), 0, stream, static_cast<const uint4*>(a.x),

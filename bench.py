@@ -49,7 +49,11 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scale for HBM byte counters) and exit")
     ap.add_argument("--eager", action="store_true",
-                    help="time eager launches instead of replaying one captured HIP graph per step")
+                    help="time eager launches instead of replaying captured HIP graphs")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="record the FFN's HBM traffic for --workload from rocprofv3 --pmc counter CSVs "
+                         "(FETCH_SIZE and WRITE_SIZE runs of this bench and of --copy-calibration) into "
+                         "profiles/ffn_traffic.json, then exit (no GPU needed)")
     return ap.parse_args()
 
 
@@ -58,9 +62,9 @@ def ffn_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_for(workload: str, launches_alg_bytes: float):
+def traffic_for(workload: str):
     """HBM bytes per FFN call from the committed rocprofv3 counter summary,
-    scaled by the copy-kernel calibration; None if absent or stale."""
+    each counter scaled by its copy-kernel factor; None if absent or stale."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -71,8 +75,58 @@ def traffic_for(workload: str, launches_alg_bytes: float):
     w = rec.get("workloads", {}).get(workload)
     if not w:
         return None
-    scale = float(rec.get("copy_calibration", 1.0))
-    return (w["fetch_kib_per_call"] + w["write_kib_per_call"]) * 1024.0 * scale
+    return (w["fetch_kib_per_call"] * rec["fetch_scale"] + w["write_kib_per_call"] * rec["write_scale"]) * 1024.0
+
+
+def _counter_per_dispatch(csv_path: str, counter: str, name_part: str):
+    """Sum of `counter` over the dispatches whose kernel name contains
+    name_part, and the number of those dispatches."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter or name_part not in r["Kernel_Name"]:
+                continue
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return sum(per.values()), len(per)
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str):
+    """FFN phase kernels are two dispatches per call; the copy calibration runs
+    three 1 GiB copies (each reads and writes 2**30 bytes)."""
+    fk, fn = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", "ffn_")
+    wk, wn = _counter_per_dispatch(write_csv, "WRITE_SIZE", "ffn_")
+    cf, cfn = _counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    cw, cwn = _counter_per_dispatch(copy_write_csv, "WRITE_SIZE", "copyBuffer")
+    if not (fn and wn and cfn and cwn) or fn % 2 or wn % 2:
+        raise SystemExit("unexpected dispatch counts in the counter CSVs")
+    copy_kib = 3 * 2**30 / 1024.0
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("ffn_source_sha256_16") != ffn_source_hash():
+        rec = {"workloads": {}}
+    rec.update({
+        "ffn_source_sha256_16": ffn_source_hash(),
+        "fetch_scale": round(copy_kib / cf, 4),
+        "write_scale": round(copy_kib / cw, 4),
+        "note": "KiB per moe_grouped_ffn call (two dispatches) from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE; "
+                "scales = bytes a 1 GiB copy moves / what the same counter reports for it",
+    })
+    rec.setdefault("workloads", {})[workload] = {
+        "fetch_kib_per_call": round(fk / (fn / 2), 1),
+        "write_kib_per_call": round(wk / (wn / 2), 1),
+        "commands": [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o p -- python bench.py "
+                     f"--workload {workload} --steps 4 --warmup 2 --no-cpu-baseline --eager",
+                     "the same with --pmc WRITE_SIZE",
+                     "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) ... -- python bench.py --copy-calibration"],
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec["workloads"][workload]))
 
 
 def cpu_baseline(wl, budget_s: float):
@@ -112,6 +166,9 @@ def cpu_baseline(wl, budget_s: float):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args.workload, *args.write_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the expert path here has no multi-GPU mode "
@@ -253,7 +310,7 @@ def main():
         achieved = ffn_flops / ffn_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_flops, "unit": "TFLOP/s",
                 "frac": round(achieved / peak_flops, 4)}
-    traffic = traffic_for(args.workload, ffn_bytes)
+    traffic = traffic_for(args.workload)
     roof["traffic"] = None if traffic is None else round(traffic)
     roof["kernel"] = "moe_grouped_ffn (gate/up launch + down launch), HIP events over K eager steps"
     roof["algorithmic_bytes"] = int(ffn_bytes)

@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
       for (int i = 0; i < MF; ++i)
 #pragma unroll
         for (int j = 0; j < NF; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], __builtin_bit_cast(bf16x8, b[u][j]), acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b[u][j]), af[i], acc[i][j], 0, 0, 0);
     }
   };
 
@@ -254,21 +254,25 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
     if (more) store_a((c + 1) & 1);            // that buffer was last read before this barrier
   }
 
-  // lane holds column l16 and rows 4q..4q+3 of each 16x16 block
+  // The MFMA computes (weight rows) x (token rows)^T: in each 16x16 block a
+  // lane holds token row l16 and output columns 4q..4q+3, stored as one
+  // 8-byte write (Ncols % 8 == 0, so the four columns are all in range or all
+  // out).
 #pragma unroll
-  for (int i = 0; i < MF; ++i)
+  for (int i = 0; i < MF; ++i) {
+    const int m = 16 * i + l16;
+    if (m >= rows) continue;
+    uint16_t* orow = out + static_cast<size_t>(row0 + m) * Ncols;
 #pragma unroll
     for (int j = 0; j < NFC; ++j) {
-      const int n = col0 + j * 16 + l16;
+      const int n = col0 + j * 16 + 4 * q;
+      if (n >= Ncols) continue;
+      float v[4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int m = 16 * i + 4 * q + rr;
-        if (m < rows && n < Ncols) {
-          const float v = PHASE == 1 ? silu_mul(acc[i][j][rr], acc[i][NFC + j][rr]) : acc[i][j][rr];
-          out[static_cast<size_t>(row0 + m) * Ncols + n] = f32_to_bf16(v);
-        }
-      }
+      for (int t = 0; t < 4; ++t) v[t] = PHASE == 1 ? silu_mul(acc[i][j][t], acc[i][NFC + j][t]) : acc[i][j][t];
+      *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
+  }
 }
 
 // ---- prefill-sized tiles: LDS-tiled GEMM on v_mfma_f32_32x32x16_bf16 ------------
@@ -287,7 +291,9 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
 //     choosing which global chunk each lane fetches.
 //   * Four waves in a 2 x 2 grid, each (32*MI) x (32*NJ) as MI x NJ blocks of
 //     32x32 (phase 1: NJ/2 gate blocks and the same columns' NJ/2 up blocks,
-//     so SwiGLU needs no exchange).
+//     so SwiGLU needs no exchange).  The weight rows are the MFMA's first
+//     operand, so the accumulators come out transposed and each lane stores
+//     four consecutive output columns at once.
 // The K extent must be a multiple of kGemmBK (checked by the host).
 constexpr int kGemmBK = 32;
 constexpr int kGemmRowBytes = kGemmBK * 2;
@@ -424,30 +430,31 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const 
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
     }
   }
 
-  // 32x32 accumulator: lane holds column l32 and rows 8 (r/4) + 4 hk + r % 4
+  // The MFMA computes (weight rows) x (token rows)^T, so in each 32x32
+  // accumulator block a lane holds token row l32 and output columns
+  // 8 (r/4) + 4 hk + r % 4: four consecutive columns per r/4, stored as one
+  // 8-byte write (Ncols is a multiple of 32 on this path).
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
+    const int m = (BM / 2) * wm + 32 * i + l32;
+    if (m >= rows) continue;
+    uint16_t* orow = out + static_cast<size_t>(row0 + m) * Ncols;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = (BM / 2) * wm + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
-      if (m >= rows) continue;
-      uint16_t* orow = out + static_cast<size_t>(row0 + m) * Ncols;
-      if (PHASE == 1) {
+    for (int j = 0; j < (PHASE == 1 ? NJ / 2 : NJ); ++j) {
+      const int nb = n0 + (PHASE == 1 ? (BN / 4) * wn : (BN / 2) * wn) + 32 * j + 4 * hk;
 #pragma unroll
-        for (int j = 0; j < NJ / 2; ++j) {
-          const int n = n0 + (BN / 4) * wn + 32 * j + l32;
-          if (n < Ncols) orow[n] = f32_to_bf16(silu_mul(acc[i][j][r], acc[i][NJ / 2 + j][r]));
-        }
-      } else {
+      for (int q = 0; q < 4; ++q) {
+        const int n = nb + 8 * q;
+        if (n >= Ncols) continue;
+        float v[4];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int n = n0 + (BN / 2) * wn + 32 * j + l32;
-          if (n < Ncols) orow[n] = f32_to_bf16(acc[i][j][r]);
-        }
+        for (int t = 0; t < 4; ++t)
+          v[t] = PHASE == 1 ? silu_mul(acc[i][j][4 * q + t], acc[i][NJ / 2 + j][4 * q + t]) : acc[i][j][4 * q + t];
+        *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
   }

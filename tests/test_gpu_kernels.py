@@ -172,6 +172,9 @@ FFN_CASES = [
     (900, 12, 3, 1, 100, 96, 160, "bf16", "zipf"),        # shared expert, hot/cold, small d
     (4000, 16, 4, 0, 256, 512, 384, "bf16", "random"),    # many units per XCD
     (700, 8, 2, 0, 3, 128, 128, "bf16", "random"),        # priority units on few XCDs only
+    # groups averaging >= 256 rows: the 256 x 256, eight-wave GEMM tile
+    (2000, 8, 2, 0, 0, 256, 320, "bf16", "random"),       # ragged last m-tile, column tail
+    (3000, 4, 2, 1, 200, 128, 192, "bf16", "zipf"),       # priority segment + shared expert
 ]
 
 

@@ -41,8 +41,9 @@ constexpr int kWaves = kThreads / kWave;
 // order, so a group's items run close together in one XCD's L2.  The list is
 // in group order, so the priority segment's items start first on every XCD
 // that holds some.
-constexpr int kMaxGroupsPerThread = 5;   // 256 * 5 >= 2*512 + 256 shared groups
-constexpr int kXcds = 8;                 // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kMaxGroups = 2 * 512 + 256;   // nseg * E + shared experts, at most
+constexpr int kMaxGroupsPerThread = (kMaxGroups + kThreads - 1) / kThreads;   // for 256 threads
+constexpr int kXcds = 8;                    // MI355X: 8 XCDs, workgroups dealt round-robin
 
 struct PlanArgs {
   const int* offs;
@@ -62,18 +63,20 @@ struct Item {
   int row0, rows, expert, chunk;   // rows == 0: no work for this block
 };
 
-// Must be called by all threads of a 256-thread block.
+// Must be called by all NT threads of the block.
+template <int NT = kThreads>
 __device__ Item block_find_item(const PlanArgs& p, int nch) {
-  __shared__ int wsum[kThreads / kWave];
+  constexpr int GPT = (kMaxGroups + NT - 1) / NT;   // groups per thread
+  __shared__ int wsum[NT / kWave];
   __shared__ Item found;
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
   if (tid == 0) found = Item{0, 0, 0, 0};
   if (tid == 0 && blockIdx.x == 0 && p.diag) *p.diag = 0;
-  int cnt[kMaxGroupsPerThread], r0[kMaxGroupsPerThread];
+  int cnt[GPT], r0[GPT];
   int s = 0;
 #pragma unroll
-  for (int q = 0; q < kMaxGroupsPerThread; ++q) {
-    const int g = tid * kMaxGroupsPerThread + q;
+  for (int q = 0; q < GPT; ++q) {
+    const int g = tid * GPT + q;
     cnt[q] = 0;
     r0[q] = 0;
     if (g < p.G) {
@@ -94,7 +97,7 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
   __syncthreads();
   int base = 0, total = 0;
 #pragma unroll
-  for (int i = 0; i < kThreads / kWave; ++i) {
+  for (int i = 0; i < NT / kWave; ++i) {
     base += i < w ? wsum[i] : 0;
     total += wsum[i];
   }
@@ -106,8 +109,8 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
   if (slot < share && want < items) {
     int t = base + incl - s;     // first m-tile of this thread's first group
 #pragma unroll
-    for (int q = 0; q < kMaxGroupsPerThread; ++q) {
-      const int g = tid * kMaxGroupsPerThread + q;
+    for (int q = 0; q < GPT; ++q) {
+      const int g = tid * GPT + q;
       if (g >= p.G) break;
       const int nt = (cnt[q] + p.BM - 1) / p.BM;
       const long long first = static_cast<long long>(t) * nch;
@@ -276,29 +279,46 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
 }
 
 // ---- prefill-sized tiles: LDS-tiled GEMM on v_mfma_f32_32x32x16_bf16 ------------
-// Block tile: BM = 64*MI token rows x BN = 64*NJ weight rows (phase 1: BN/2
-// gate rows then the matching BN/2 up rows -> BN/2 SwiGLU columns; phase 2: BN
-// down rows), K in steps of kGemmBK = 32.
+// Block tile: BM token rows x BN weight rows (phase 1: BN/2 gate rows then the
+// matching BN/2 up rows -> BN/2 SwiGLU columns; phase 2: BN down rows), K in
+// steps of kGemmBK = 32.
 //   * Operands go HBM -> LDS directly (global_load_lds_dwordx4: each lane's 16
 //     bytes land at LDS base + 16*lane, no VGPR staging, no LDS store
-//     instructions), through a ring of kGemmStages K-step buffers: two K-steps
-//     are in flight while the third is multiplied; one barrier per K-step.
+//     instructions), through a ring of STAGES K-step buffers: STAGES-1 K-steps
+//     are in flight while one is multiplied; one barrier per K-step.
 //   * LDS rows are 64 bytes (four 16-byte chunks) with no padding; chunk c of
 //     row r sits at slot c ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 2)) & 3.  An
 //     MFMA operand read (16 lanes: 16 consecutive rows, one chunk) then hits
 //     16 distinct 4-bank groups, and so does any 8-lane group.  The DMA side
 //     writes 1 KiB contiguously per instruction and applies the swizzle by
 //     choosing which global chunk each lane fetches.
-//   * Four waves in a 2 x 2 grid, each (32*MI) x (32*NJ) as MI x NJ blocks of
-//     32x32 (phase 1: NJ/2 gate blocks and the same columns' NJ/2 up blocks,
-//     so SwiGLU needs no exchange).  The weight rows are the MFMA's first
-//     operand, so the accumulators come out transposed and each lane stores
-//     four consecutive output columns at once.
+//   * WM x WN waves, each (32*MI) x (32*NJ) as MI x NJ blocks of 32x32
+//     (phase 1: NJ/2 gate blocks and the same columns' NJ/2 up blocks, so
+//     SwiGLU needs no exchange).  The weight rows are the MFMA's first operand,
+//     so the accumulators come out transposed and each lane stores four
+//     consecutive output columns at once.
+// Two shapes: 128 x 256 with four waves and two blocks per CU (any group
+// sizes), and 256 x 256 with eight waves and one block per CU, which moves a
+// third fewer bytes per flop from L2 and keeps four K-steps in flight, for
+// batches whose groups average at least kGemmLargeMinAvg rows.
 // The K extent must be a multiple of kGemmBK (checked by the host).
 constexpr int kGemmBK = 32;
 constexpr int kGemmRowBytes = kGemmBK * 2;
-constexpr int kGemmStages = 3;
-constexpr int kGemmBlocksPerCu = 2;
+
+template <int MI_, int NJ_, int WM_, int WN_, int STAGES_, int BPC_>
+struct GemmCfg {
+  static constexpr int MI = MI_, NJ = NJ_, WM = WM_, WN = WN_, STAGES = STAGES_, BLOCKS_PER_CU = BPC_;
+  static constexpr int NW = WM * WN, NT = kWave * NW;
+  static constexpr int BM = 32 * MI * WM, BN = 32 * NJ * WN;
+  static constexpr int A_BYTES = BM * kGemmRowBytes, B_BYTES = BN * kGemmRowBytes;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int RING = STAGES * STAGE;               // LDS bytes of the operand ring
+  static constexpr int ADMA = BM / 16 / NW;                 // 1 KiB DMA instructions per wave per K-step
+  static constexpr int BDMA = BN / 16 / NW;
+};
+using GemmSmall = GemmCfg<2, 4, 2, 2, 3, 2>;   // 128 x 256
+using GemmLarge = GemmCfg<2, 4, 4, 2, 4, 1>;   // 256 x 256
+constexpr int kGemmLargeMinAvg = 256;
 
 __device__ __forceinline__ int gemm_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
@@ -317,108 +337,112 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-template <int MI, int NJ>
-struct GemmShape {
-  static constexpr int BM = 64 * MI, BN = 64 * NJ;
-  static constexpr int A_BYTES = BM * kGemmRowBytes, B_BYTES = BN * kGemmRowBytes;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int RING = kGemmStages * STAGE;         // LDS bytes of the operand ring
-};
-
-// One tile: rows [row0, row0 + rows) of A against output column chunk
-// `it.chunk` of expert `it.expert`.  All threads of the block call it; `smem`
-// is the block's operand ring, free on entry (no wave still reads it).
-template <int PHASE, int MI, int NJ>
-__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x,
-                                          int K, const uint16_t* __restrict__ W0,
-                                          const uint16_t* __restrict__ W1, int Ncols, const Item& it,
-                                          uint16_t* __restrict__ out, uint8_t* smem) {
-  using S = GemmShape<MI, NJ>;
-  constexpr int BM = S::BM, BN = S::BN;
-  constexpr int OUTC = PHASE == 1 ? BN / 2 : BN;          // output columns per tile
-  constexpr int A_BYTES = S::A_BYTES;
-  constexpr int STAGE = S::STAGE;
-  constexpr int ADMA = BM / 16 / kWaves;                  // 1 KiB DMA instructions per wave per K-step
-  constexpr int BDMA = BN / 16 / kWaves;
-  static_assert(PHASE == 2 || NJ % 2 == 0, "phase 1 pairs gate and up blocks");
-  static_assert(ADMA >= 1 && BDMA >= 1, "tile too small for four waves");
-
-  const int row0 = it.row0, rows = it.rows;
-  const int n0 = it.chunk * OUTC;
-  const size_t eoff = static_cast<size_t>(it.expert) * Ncols * K;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, hk = lane >> 5;
-
-  // DMA sources: instruction q of this wave fills tile rows 16 (wave + 4 q) ..
-  // +15; lane -> row + lane / 4, slot lane % 4, fetching chunk slot ^ swz(row).
-  // Rows past the tile's valid rows / columns read a valid row instead (their
-  // results are never stored).
-  const int dr = lane >> 2;
-  const uint16_t* asrc[ADMA];
-  const uint16_t* bsrc[BDMA];
-#pragma unroll
-  for (int q = 0; q < ADMA; ++q) {
-    const int r = 16 * (wave + kWaves * q) + dr;
-    asrc[q] = A + a_row(arows, n_x, row0 + min(r, rows - 1)) * K + 8 * ((lane & 3) ^ gemm_swz(r));
+// Wait until at most `ahead` K-steps of PER loads each are still in flight,
+// then barrier (ahead <= MAXA, wave-uniform).
+template <int PER, int MAXA>
+__device__ __forceinline__ void wait_ahead_barrier(int ahead) {
+  if constexpr (MAXA == 0) {
+    wait_vm_barrier<0>();
+  } else {
+    if (ahead >= MAXA)
+      wait_vm_barrier<MAXA * PER>();
+    else
+      wait_ahead_barrier<PER, MAXA - 1>(ahead);
   }
+}
+
+// Pieces of a tile, shared by the one-tile and the persistent kernels.  All
+// threads of the block call them.
+//
+// TileLoader: DMA sources of one tile.  Instruction q of a wave fills tile
+// rows 16 (wave + NW q) .. +15; lane -> row + lane / 4, slot lane % 4, fetching
+// chunk slot ^ swz(row).  Rows past the tile's valid rows / columns read a
+// valid row instead (their results are never stored).
+template <int PHASE, class C>
+struct TileLoader {
+  const uint16_t* asrc[C::ADMA];
+  const uint16_t* bsrc[C::BDMA];
+
+  __device__ __forceinline__ void init(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x, int K,
+                                       const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int Ncols,
+                                       const Item& it) {
+    constexpr int OUTC = PHASE == 1 ? C::BN / 2 : C::BN;
+    const int wave = threadIdx.x >> 6, lane = lane_id(), dr = lane >> 2;
+    const int n0 = it.chunk * OUTC;
+    const size_t eoff = static_cast<size_t>(it.expert) * Ncols * K;
 #pragma unroll
-  for (int q = 0; q < BDMA; ++q) {
-    const int r = 16 * (wave + kWaves * q) + dr;
-    int n = n0 + r;
-    const uint16_t* W = W0;
-    if (PHASE == 1 && r >= OUTC) {
-      n -= OUTC;
-      W = W1;
+    for (int q = 0; q < C::ADMA; ++q) {
+      const int r = 16 * (wave + C::NW * q) + dr;
+      asrc[q] = A + a_row(arows, n_x, it.row0 + min(r, it.rows - 1)) * K + 8 * ((lane & 3) ^ gemm_swz(r));
     }
-    bsrc[q] = W + eoff + static_cast<size_t>(min(n, Ncols - 1)) * K + 8 * ((lane & 3) ^ gemm_swz(r));
+#pragma unroll
+    for (int q = 0; q < C::BDMA; ++q) {
+      const int r = 16 * (wave + C::NW * q) + dr;
+      int n = n0 + r;
+      const uint16_t* W = W0;
+      if (PHASE == 1 && r >= OUTC) {
+        n -= OUTC;
+        W = W1;
+      }
+      bsrc[q] = W + eoff + static_cast<size_t>(min(n, Ncols - 1)) * K + 8 * ((lane & 3) ^ gemm_swz(r));
+    }
   }
-  typedef __attribute__((address_space(3))) uint8_t lds_byte;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_byte*)smem;   // LDS byte address of the ring
-  auto issue = [&](int kt) {
-    const uint32_t st = lds0 + (kt % kGemmStages) * STAGE + wave * 1024;
+
+  // K-step kt of this tile into ring slot `slot` (lds0: LDS byte address of the ring)
+  __device__ __forceinline__ void issue(int kt, int slot, uint32_t lds0) const {
+    const uint32_t st = lds0 + slot * C::STAGE + (threadIdx.x >> 6) * 1024;
     const int k = kt * kGemmBK;
 #pragma unroll
-    for (int q = 0; q < ADMA; ++q) dma_b128(asrc[q] + k, st + q * kWaves * 1024);
+    for (int q = 0; q < C::ADMA; ++q) dma_b128(asrc[q] + k, st + q * C::NW * 1024);
 #pragma unroll
-    for (int q = 0; q < BDMA; ++q) dma_b128(bsrc[q] + k, st + A_BYTES + q * kWaves * 1024);
-  };
-
-  // MFMA operand rows of this wave: A rows BM/2 wm + 32 i + l32; weight rows:
-  // phase 2 BN/2 wn + 32 j + l32; phase 1 gate block j < NJ/2 at
-  // BN/4 wn + 32 j + l32, up block j >= NJ/2 at BN/2 + BN/4 wn + 32 (j - NJ/2) + l32.
-  // Every block starts at a multiple of 32 rows, so the swizzle depends on l32.
-  int boff[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int rb = PHASE == 1 ? (j < NJ / 2 ? 0 : BN / 2) + (BN / 4) * wn + 32 * (j % (NJ / 2)) : (BN / 2) * wn + 32 * j;
-    boff[j] = A_BYTES + rb * kGemmRowBytes;
+    for (int q = 0; q < C::BDMA; ++q) dma_b128(bsrc[q] + k, st + C::A_BYTES + q * C::NW * 1024);
   }
-  const int aoff = (BM / 2) * wm * kGemmRowBytes;
-  int loff[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) loff[s] = l32 * kGemmRowBytes + 16 * ((2 * s + hk) ^ gemm_swz(l32));
+};
 
+// TileMath: the wave's MFMA work on one ring slot, and the epilogue.
+// MFMA operand rows of this wave: A rows 32 MI wm + 32 i + l32; weight rows:
+// phase 2 (BN/WN) wn + 32 j + l32; phase 1 gate block j < NJ/2 at
+// (BN/2/WN) wn + 32 j + l32, up block j >= NJ/2 at BN/2 + (BN/2/WN) wn +
+// 32 (j - NJ/2) + l32.  Every block starts at a multiple of 32 rows, so the
+// swizzle depends on l32 only.
+template <int PHASE, class C>
+struct TileMath {
+  static constexpr int MI = C::MI, NJ = C::NJ, WN = C::WN, BN = C::BN;
+  static_assert(PHASE == 2 || NJ % 2 == 0, "phase 1 pairs gate and up blocks");
+  static_assert(C::ADMA >= 1 && C::BDMA >= 1, "tile too small for its waves");
+  static_assert(C::STAGES >= 2, "the ring needs two buffers");
+  int boff[NJ];
+  int aoff, loff[2];
+  int wm, wn, l32, hk;
   f32x16 acc[MI][NJ];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = K / kGemmBK;
-  issue(0);
-  if (nk > 1) issue(1);
-  for (int kt = 0; kt < nk; ++kt) {
-    // K-step kt's loads are done once at most the next step's remain in flight
-    if (kt + 1 < nk)
-      wait_vm_barrier<ADMA + BDMA>();
-    else
-      wait_vm_barrier<0>();
-    // every wave is past step kt-1, so its buffer can be refilled
-    if (kt + 2 < nk) issue(kt + 2);
-    const uint8_t* st = smem + (kt % kGemmStages) * STAGE;
+  __device__ __forceinline__ void init() {
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    wm = wave / WN;
+    wn = wave % WN;
+    l32 = lane & 31;
+    hk = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int rb = PHASE == 1 ? (j < NJ / 2 ? 0 : BN / 2) + (BN / 2 / WN) * wn + 32 * (j % (NJ / 2))
+                                : (BN / WN) * wn + 32 * j;
+      boff[j] = C::A_BYTES + rb * kGemmRowBytes;
+    }
+    aoff = 32 * MI * wm * kGemmRowBytes;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) loff[s] = l32 * kGemmRowBytes + 16 * ((2 * s + hk) ^ gemm_swz(l32));
+  }
+
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  }
+
+  __device__ __forceinline__ void kstep(const uint8_t* st) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       bf16x8 af[MI], bf[NJ];
@@ -438,45 +462,230 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const 
   // accumulator block a lane holds token row l32 and output columns
   // 8 (r/4) + 4 hk + r % 4: four consecutive columns per r/4, stored as one
   // 8-byte write (Ncols is a multiple of 32 on this path).
+  __device__ __forceinline__ void store(const Item& it, int Ncols, uint16_t* __restrict__ out) const {
+    constexpr int OUTC = PHASE == 1 ? BN / 2 : BN;
+    const int n0 = it.chunk * OUTC;
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int m = (BM / 2) * wm + 32 * i + l32;
-    if (m >= rows) continue;
-    uint16_t* orow = out + static_cast<size_t>(row0 + m) * Ncols;
+    for (int i = 0; i < MI; ++i) {
+      const int m = 32 * MI * wm + 32 * i + l32;
+      if (m >= it.rows) continue;
+      uint16_t* orow = out + static_cast<size_t>(it.row0 + m) * Ncols;
 #pragma unroll
-    for (int j = 0; j < (PHASE == 1 ? NJ / 2 : NJ); ++j) {
-      const int nb = n0 + (PHASE == 1 ? (BN / 4) * wn : (BN / 2) * wn) + 32 * j + 4 * hk;
+      for (int j = 0; j < (PHASE == 1 ? NJ / 2 : NJ); ++j) {
+        const int nb = n0 + (PHASE == 1 ? (BN / 2 / WN) * wn : (BN / WN) * wn) + 32 * j + 4 * hk;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = nb + 8 * q;
-        if (n >= Ncols) continue;
-        float v[4];
+        for (int q = 0; q < 4; ++q) {
+          const int n = nb + 8 * q;
+          if (n >= Ncols) continue;
+          float v[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          v[t] = PHASE == 1 ? silu_mul(acc[i][j][4 * q + t], acc[i][NJ / 2 + j][4 * q + t]) : acc[i][j][4 * q + t];
-        *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          for (int t = 0; t < 4; ++t)
+            v[t] = PHASE == 1 ? silu_mul(acc[i][j][4 * q + t], acc[i][NJ / 2 + j][4 * q + t]) : acc[i][j][4 * q + t];
+          *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
       }
+    }
+  }
+};
+
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* smem) {
+  typedef __attribute__((address_space(3))) const uint8_t lds_byte;
+  return (uint32_t)(uintptr_t)(lds_byte*)smem;
+}
+
+// One tile: rows [row0, row0 + rows) of A against output column chunk
+// `it.chunk` of expert `it.expert`.  `smem` is the block's operand ring, free
+// on entry (no wave still reads it).
+template <int PHASE, class C>
+__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x,
+                                          int K, const uint16_t* __restrict__ W0,
+                                          const uint16_t* __restrict__ W1, int Ncols, const Item& it,
+                                          uint16_t* __restrict__ out, uint8_t* smem) {
+  constexpr int STAGES = C::STAGES;
+  TileLoader<PHASE, C> ld;
+  ld.init(A, arows, n_x, K, W0, W1, Ncols, it);
+  TileMath<PHASE, C> mm;
+  mm.init();
+  mm.zero();
+  const uint32_t lds0 = lds_address(smem);
+  const int nk = K / kGemmBK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) ld.issue(s, s, lds0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // K-step kt's loads are done once only the later steps' remain in flight
+    wait_ahead_barrier<C::ADMA + C::BDMA, STAGES - 2>(min(STAGES - 2, nk - 1 - kt));
+    // every wave is past step kt-1, so its buffer can be refilled
+    if (kt + STAGES - 1 < nk) ld.issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, lds0);
+    mm.kstep(smem + (kt % STAGES) * C::STAGE);
+  }
+  mm.store(it, Ncols, out);
+}
+
+// One tile per block, blocks dealt by the hardware (two resident per CU, so
+// one block's start-up overlaps the other's work).
+template <int PHASE, class C>
+__global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_bf16(
+    const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+    int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::RING];
+  constexpr int OUTC = PHASE == 1 ? C::BN / 2 : C::BN;
+  const Item it = block_find_item<C::NT>(plan, (Ncols + OUTC - 1) / OUTC);
+  if (it.rows == 0) return;
+  gemm_tile<PHASE, C>(A, plan.arows, plan.n_x, K, W0, W1, Ncols, it, out, smem);
+}
+
+// ---- persistent GEMM launch: each block walks a list of tiles ----------------
+// Used for the one-block-per-CU large tile, where a block that ended would
+// leave its CU idle until the next one started.
+// Grid = BLOCKS_PER_CU blocks per CU (a multiple of 8).  Items are ordered as
+// for the one-tile kernels (group by group, column chunk by column chunk,
+// m-tile by m-tile); XCD x (blocks dealt round-robin) owns the x-th eighth of
+// the list and its blocks take that eighth's items in turn.  A block runs its
+// items' K-steps as one stream through the ring, so the next tile's first
+// K-steps load while the current tile finishes and stores: no per-tile
+// prologue bubble, no block launch per tile.
+template <int PHASE, class C>
+__global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_bf16(
+    const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+    int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
+  constexpr int NT = C::NT, STAGES = C::STAGES, BM = C::BM;
+  constexpr int GPT = (kMaxGroups + NT - 1) / NT;
+  constexpr int OUTC = PHASE == 1 ? C::BN / 2 : C::BN;
+  // dynamic LDS: the operand ring, then per group its first m-tile (fu) and
+  // its first row (gl), G + 1 entries each, so finding a tile needs no
+  // global load once DMAs are in flight (the compiler would wait for all of
+  // them before using such a load)
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+  uint8_t* smem = dyn_lds;
+  int* fu = reinterpret_cast<int*>(dyn_lds + C::RING);
+  int* gl = fu + plan.G + 1;
+  __shared__ int wsum[NT / kWave];
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  if (tid == 0 && blockIdx.x == 0 && plan.diag) *plan.diag = 0;
+
+  // m-tiles per group, exclusive scan -> fu
+  {
+    int cnt[GPT];
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < GPT; ++q) {
+      const int g = tid * GPT + q;
+      cnt[q] = 0;
+      if (g < plan.G) {
+        const int lo = min(max(plan.offs[g], 0), plan.n_rows), hi = min(max(plan.offs[g + 1], 0), plan.n_rows);
+        cnt[q] = (max(0, hi - lo) + BM - 1) / BM;
+        gl[g] = lo;
+        if (g == plan.G - 1) gl[plan.G] = max(lo, hi);
+      }
+      sum += cnt[q];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) wsum[w] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int i = 0; i < w; ++i) run += wsum[i];
+#pragma unroll
+    for (int q = 0; q < GPT; ++q) {
+      const int g = tid * GPT + q;
+      if (g < plan.G) fu[g] = run;
+      run += cnt[q];
+    }
+    if (tid == NT - 1) fu[plan.G] = run;
+    __syncthreads();
+  }
+  const int nch = (Ncols + OUTC - 1) / OUTC;
+  const int items = fu[plan.G] * nch;
+  const int per_xcd = static_cast<int>(gridDim.x) / kXcds;
+  const int share = (items + kXcds - 1) / kXcds;
+  const int x = blockIdx.x % kXcds, slot0 = blockIdx.x / kXcds;
+  const int base = x * share;
+  // my items: base + slot0 + r * per_xcd while inside this XCD's share
+  int n_my = 0;
+  if (slot0 < share) {
+    const int last = min(share, items - base);        // slots of this XCD
+    n_my = last > slot0 ? (last - slot0 + per_xcd - 1) / per_xcd : 0;
+  }
+  if (n_my == 0) return;
+
+  auto decode = [&](int r) -> Item {
+    const int want = base + slot0 + r * per_xcd;
+    const int u = want / nch;                          // global m-tile index
+    int lo = 0, hi = plan.G;                           // last g with fu[g] <= u
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (fu[mid] <= u) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    const int nt = fu[g + 1] - fu[g];
+    const int local = want - fu[g] * nch;
+    const int j = local / nt, mt = local % nt;
+    const int glo = gl[g], ghi = max(glo, gl[g + 1]);
+    return Item{glo + mt * BM, min(BM, ghi - glo - mt * BM), expert_of_group(g, plan.E, plan.nseg), j};
+  };
+
+  const int nk = K / kGemmBK;
+  const int total = n_my * nk;                         // K-steps of all my tiles, in order
+  const uint32_t lds0 = lds_address(smem);
+  // issue side: next K-step to load is step ikt of my tile ir, into ring slot islot
+  TileLoader<PHASE, C> ld;
+  int ir = 0, ikt = 0, islot = 0;
+  auto issue_next = [&]() {
+    if (ikt == 0) ld.init(A, plan.arows, plan.n_x, K, W0, W1, Ncols, decode(ir));
+    ld.issue(ikt, islot, lds0);
+    islot = islot + 1 == STAGES ? 0 : islot + 1;
+    if (++ikt == nk) {
+      ikt = 0;
+      ++ir;
+    }
+  };
+  TileMath<PHASE, C> mm;
+  mm.init();
+  Item cur{};
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < total) issue_next();
+  // compute side: step ckt of tile cr from ring slot cslot
+  int cr = 0, ckt = 0, cslot = 0;
+  for (int gs = 0; gs < total; ++gs) {
+    if (ckt == 0) {
+      cur = decode(cr);
+      mm.zero();
+    }
+    // step gs's loads are done once only the later steps' remain in flight
+    // (epilogue stores issued since then only make this wait longer)
+    wait_ahead_barrier<C::ADMA + C::BDMA, STAGES - 2>(min(STAGES - 2, total - 1 - gs));
+    // every wave is past step gs-1, so its buffer can be refilled
+    if (gs + STAGES - 1 < total) issue_next();
+    mm.kstep(smem + cslot * C::STAGE);
+    cslot = cslot + 1 == STAGES ? 0 : cslot + 1;
+    if (++ckt == nk) {
+      mm.store(cur, Ncols, out);
+      ckt = 0;
+      ++cr;
     }
   }
 }
 
-template <int PHASE, int MI, int NJ>
-__global__ __launch_bounds__(kThreads, kGemmBlocksPerCu) void ffn_gemm_bf16(
-    const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-    int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
-  using S = GemmShape<MI, NJ>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::RING];
-  constexpr int OUTC = PHASE == 1 ? S::BN / 2 : S::BN;
-  const Item it = block_find_item(plan, (Ncols + OUTC - 1) / OUTC);
-  if (it.rows == 0) return;
-  gemm_tile<PHASE, MI, NJ>(A, plan.arows, plan.n_x, K, W0, W1, Ncols, it, out, smem);
+// Grid of the persistent GEMM: BLOCKS_PER_CU per CU, a multiple of the XCDs.
+int device_cus();
+
+template <class C>
+int gemm_grid() {
+  const int b = device_cus() * C::BLOCKS_PER_CU;
+  return (b + kXcds - 1) / kXcds * kXcds;
 }
 
 // ---- mixed batches: one persistent launch, per-XCD tile queues ----------------
 // Tile queue with decode priority (ExpertPlex page, "Instance vs module
 // disaggregation" / token-level preemption: a decode request waits at most one
 // tile, never a whole prefill launch).  Both phases run in one launch of
-// persistent blocks (kGemmBlocksPerCu per CU):
+// persistent blocks (two per CU, 128 x 256 tiles):
 //   * units are the m-tiles of all groups, in group order (the priority
 //     segment's groups first); each XCD owns an eighth of the priority units
 //     and an eighth of the others;
@@ -518,15 +727,15 @@ __device__ __forceinline__ int xcc_id() {
   return x & 0xf;
 }
 
-template <int MI, int NJ>
-__global__ __launch_bounds__(kThreads, kGemmBlocksPerCu) void ffn_queue_bf16(
+template <class C>
+__global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
     const uint16_t* __restrict__ x, int d, const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
     const uint16_t* __restrict__ w_down, int I, QueueArgs q, uint16_t* __restrict__ abuf,
     uint16_t* __restrict__ h) {
-  using S = GemmShape<MI, NJ>;
-  constexpr int BM = S::BM;
+  static_assert(C::NT == kThreads, "the scan below assumes 256 threads");
+  constexpr int BM = C::BM;
   constexpr int kMaxG = kThreads * kMaxGroupsPerThread;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::RING];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::RING];
   __shared__ int fu[kMaxG + 1];         // first unit of each group
   __shared__ int wsum[kWaves];
   __shared__ int s_tile;
@@ -612,7 +821,7 @@ __global__ __launch_bounds__(kThreads, kGemmBlocksPerCu) void ffn_queue_bf16(
     const int glo = min(max(q.offs[g], 0), q.n_rows), ghi = min(max(q.offs[g + 1], 0), q.n_rows);
     const Item it{glo + mt * BM, min(BM, ghi - glo - mt * BM), expert_of_group(g, q.E, q.nseg), chunk};
     if (phase == 1) {
-      gemm_tile<1, MI, NJ>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
+      gemm_tile<1, C>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are in L2
       __syncthreads();
       if (tid == 0) __hip_atomic_fetch_add(q.done1 + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -631,7 +840,7 @@ __global__ __launch_bounds__(kThreads, kGemmBlocksPerCu) void ffn_queue_bf16(
       }
       __syncthreads();
       asm volatile("buffer_inv sc0" ::: "memory");
-      gemm_tile<2, MI, NJ>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
+      gemm_tile<2, C>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
     }
   }
 }
@@ -689,11 +898,7 @@ __global__ __launch_bounds__(kThreads) void ffn_phase_f32(const float* __restric
 }
 
 // ---- host side -------------------------------------------------------------------
-enum class Path { kDecode, kGemm, kQueue, kF32 };
-
-// GEMM tile shape (MI x NJ blocks of 32x32 per wave; block 64 MI x 64 NJ).
-constexpr int kGemmMI = 2;
-constexpr int kGemmNJ = 4;
+enum class Path { kDecode, kGemm, kGemmLarge, kQueue, kF32 };
 
 struct Layout {
   Path path;
@@ -733,8 +938,10 @@ Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16)
     // (the counters are bumped with L2 atomics but polled with cache-bypassing
     // loads).  The two-launch GEMM still serves the priority segment's tiles
     // first in each launch.
-    L.path = (nseg > 1 && queue_path_requested()) ? Path::kQueue : Path::kGemm;
-    L.BM = 64 * kGemmMI;
+    L.path = (nseg > 1 && queue_path_requested()) ? Path::kQueue
+             : avg >= kGemmLargeMinAvg                  ? Path::kGemmLarge
+                                                        : Path::kGemm;
+    L.BM = L.path == Path::kGemmLarge ? GemmLarge::BM : GemmSmall::BM;
   }
   L.max_tiles = (n_rows + L.BM - 1) / L.BM + G;
   L.a_off = 0;
@@ -769,18 +976,30 @@ void launch_decode_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan,
                      static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted));
 }
 
+template <class C>
 void launch_gemm_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, uint16_t* abuf, hipStream_t stream) {
-  constexpr int BN = 64 * kGemmNJ;
+  constexpr int BN = C::BN;
   const int nch1 = (a.I + BN / 2 - 1) / (BN / 2), nch2 = (a.d + BN - 1) / BN;
-  hipLaunchKernelGGL((ffn_gemm_bf16<1, kGemmMI, kGemmNJ>), dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0,
-                     stream, static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
-                     static_cast<const uint16_t*>(a.w_up), a.I, plan, abuf);
   PlanArgs plan2 = plan;
   plan2.diag = nullptr;
   plan2.arows = nullptr;
-  hipLaunchKernelGGL((ffn_gemm_bf16<2, kGemmMI, kGemmNJ>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
-                     stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
-                     static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted));
+  const uint16_t* x = static_cast<const uint16_t*>(a.x_sorted);
+  const uint16_t* wg = static_cast<const uint16_t*>(a.w_gate);
+  const uint16_t* wu = static_cast<const uint16_t*>(a.w_up);
+  const uint16_t* wd = static_cast<const uint16_t*>(a.w_down);
+  uint16_t* h = static_cast<uint16_t*>(a.h_sorted);
+  if (C::BLOCKS_PER_CU > 1) {
+    hipLaunchKernelGGL((ffn_gemm_bf16<1, C>), dim3(item_grid(L.max_tiles, nch1)), dim3(C::NT), 0, stream, x, a.d, wg,
+                       wu, a.I, plan, abuf);
+    hipLaunchKernelGGL((ffn_gemm_bf16<2, C>), dim3(item_grid(L.max_tiles, nch2)), dim3(C::NT), 0, stream, abuf, a.I,
+                       wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, h);
+  } else {
+    const size_t lds = C::RING + 8 * static_cast<size_t>(plan.G + 1);
+    hipLaunchKernelGGL((ffn_gemm_persistent_bf16<1, C>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, x, a.d, wg,
+                       wu, a.I, plan, abuf);
+    hipLaunchKernelGGL((ffn_gemm_persistent_bf16<2, C>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, abuf, a.I,
+                       wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, h);
+  }
 }
 
 // CUs of the current device (cached per device).
@@ -798,14 +1017,15 @@ int device_cus() {
 }
 
 void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t stream) {
-  constexpr int BN = 64 * kGemmNJ;
+  using C = GemmSmall;
+  constexpr int BN = C::BN;
   int* qbase = reinterpret_cast<int*>(ws + L.q_off);
   const int n = static_cast<int>(L.q_ints);
   int* diag = reinterpret_cast<int*>(ws + L.total - 4);
   hipLaunchKernelGGL(ffn_queue_reset, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, stream, qbase, n,
                      diag);
   const int cus = device_cus();
-  const int blocks = cus * kGemmBlocksPerCu;          // persistent: every block resident
+  const int blocks = cus * C::BLOCKS_PER_CU;          // persistent: every block resident
   const int nq = cus >= kXcds * kCusPerXcd ? kXcds : (cus >= 4 * kCusPerXcd ? 4 : (cus >= 2 * kCusPerXcd ? 2 : 1));
   QueueArgs q;
   q.offs = a.group_offsets;
@@ -823,7 +1043,7 @@ void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t 
   q.heads = qbase;
   q.done1 = qbase + kXcds * kQueueStride;
   q.error = diag;
-  hipLaunchKernelGGL((ffn_queue_bf16<kGemmMI, kGemmNJ>), dim3(blocks), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((ffn_queue_bf16<C>), dim3(blocks), dim3(C::NT), 0, stream,
                      static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
                      static_cast<const uint16_t*>(a.w_up), static_cast<const uint16_t*>(a.w_down), a.I, q,
                      reinterpret_cast<uint16_t*>(ws + L.a_off), static_cast<uint16_t*>(a.h_sorted));
@@ -860,7 +1080,10 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
       break;
     }
     case Path::kGemm:
-      launch_gemm_bf16(a, L, plan, reinterpret_cast<uint16_t*>(ws + L.a_off), stream);
+      launch_gemm_bf16<GemmSmall>(a, L, plan, reinterpret_cast<uint16_t*>(ws + L.a_off), stream);
+      break;
+    case Path::kGemmLarge:
+      launch_gemm_bf16<GemmLarge>(a, L, plan, reinterpret_cast<uint16_t*>(ws + L.a_off), stream);
       break;
     case Path::kQueue:
       launch_queue_bf16(a, L, ws, stream);

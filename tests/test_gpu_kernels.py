@@ -175,6 +175,10 @@ FFN_CASES = [
     # groups averaging >= 256 rows: the 256 x 256, eight-wave GEMM tile
     (2000, 8, 2, 0, 0, 256, 320, "bf16", "random"),       # ragged last m-tile, column tail
     (3000, 4, 2, 1, 200, 128, 192, "bf16", "zipf"),       # priority segment + shared expert
+    # the largest group count (2*512 routed + 256 shared = 1280) on each kernel
+    (4, 512, 4, 256, 2, 64, 32, "bf16", "random"),         # decode kernel
+    (300, 512, 4, 256, 10, 64, 32, "bf16", "random"),      # 128 x 256 GEMM
+    (1300, 512, 4, 256, 10, 64, 32, "bf16", "random"),     # 256 x 256 persistent GEMM
 ]
 
 

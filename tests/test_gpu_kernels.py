@@ -328,8 +328,8 @@ def test_stats_without_optional_outputs():
 
 
 @pytest.mark.skip(reason="persistent tile-queue FFN (LIBMOE_FFN_QUEUE=1) is disabled: its phase-2 waits did not "
-                         "complete on MI355X (phase-1 counters bumped with L2 atomics, polled with cache-bypassing "
-                         "loads); it stays off the GPU until the flag protocol is reworked")
+                         "complete on MI355X when phase-1 counters were bumped with L2 atomics and polled with "
+                         "cache-bypassing loads; the reworked per-chunk store/load flags have not run on the GPU yet")
 def test_grouped_ffn_queue_path():
     """The persistent single-launch FFN with decode-priority tile queues must
     match the oracle and leave the diagnostic word at 0."""

@@ -695,17 +695,21 @@ int gemm_grid() {
 //     group by group, column chunk by chunk, m-tile by m-tile;
 //   * a block reads its XCD id from the hardware and pops tiles from that
 //     queue with one atomic add; a phase-2 tile waits until every phase-1 tile
-//     of its unit has signalled (per-unit counter).  The lag keeps the blocks
-//     busy with other phase-1 tiles while the priority units' phase 1 drains.
+//     of its unit has raised its flag (one flag per (unit, column chunk)).
+//     The lag keeps the blocks busy with other phase-1 tiles while the
+//     priority units' phase 1 drains.
 // All tiles of a unit run on one XCD, so the intermediate rows pass through
 // that XCD's L2: a phase-1 tile's stores have reached L2 once its vmcnt is
-// zero, before it bumps the counter; the waiting block then drops its L1 lines
-// (buffer_inv sc0) before loading them.  Counters are only touched with atomic
-// read-modify-writes (a poll adds 0), so increments and polls meet at the same
-// point whatever cache level performs the atomics.  A dependency always points
-// to a tile popped earlier by a running block, so the waits end; each is also
-// bounded (kSpinLimit polls), after which the block sets the diagnostic word
-// (the workspace's last 4 bytes) and goes on, and other waits stop at once.
+// zero, before it raises its flag; the waiting block then drops its L1 lines
+// (buffer_inv sc0) before loading them.  Flags are written with agent-scope
+// atomic stores and polled with agent-scope atomic loads, both of which skip
+// the non-coherent caches on this target (the pattern rocPRIM's look-back
+// scan uses on gfx942/gfx950); an L2 read-modify-write counter polled with
+// such loads is not seen by them.  A dependency always points to a tile
+// popped earlier by a running block, so the waits end; each is also bounded
+// (kSpinLimit polls), after which the block sets the diagnostic word (the
+// workspace's last 4 bytes, same store/load pattern) and goes on, and other
+// waits stop at once.
 constexpr int kQueueStride = 32;          // ints between the per-XCD queue heads (128 B)
 constexpr int kCusPerXcd = 32;            // MI355X: 8 XCDs x 32 CUs
 constexpr int kSpinLimit = 1 << 16;       // polls before a wait gives up (far above any tile time)
@@ -717,7 +721,7 @@ struct QueueArgs {
   const int* arows;   // phase-1 A row list (nullptr: sorted rows)
   int n_x;
   int* heads;   // [kXcds * kQueueStride]
-  int* done1;   // [units]
+  int* flags;   // [units][nch1]: phase-1 tile (unit, chunk) done
   int* error;   // set when a wait gave up
 };
 
@@ -824,16 +828,25 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
       gemm_tile<1, C>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are in L2
       __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(q.done1 + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0)
+        __hip_atomic_store(q.flags + static_cast<size_t>(unit) * q.nch1 + chunk, 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      if (tid == 0) {
+      if (tid < kWave) {
+        // lane c watches the flags of chunks c, c + 64, ...; the wave waits
+        // until all are raised
+        const int* f = q.flags + static_cast<size_t>(unit) * q.nch1;
         int spins = 0;
-        while (__hip_atomic_fetch_add(q.done1 + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < q.nch1) {
+        for (;;) {
+          int mine = 1;
+          for (int c = tid; c < q.nch1; c += kWave)
+            mine &= __hip_atomic_load(f + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+          if (__all(mine)) break;
           __builtin_amdgcn_s_sleep(2);
           // give up after kSpinLimit polls, or at once when another wait already did
           if (++spins > kSpinLimit ||
-              ((spins & 63) == 0 && __hip_atomic_fetch_add(q.error, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-            __hip_atomic_fetch_or(q.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              ((spins & 63) == 0 && __hip_atomic_load(q.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+            if (tid == 0) __hip_atomic_store(q.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }
         }
@@ -947,9 +960,12 @@ Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16)
   L.a_off = 0;
   const size_t a_bytes = static_cast<size_t>(n_rows) * I * (bf16 ? 2 : 4);
   L.q_off = (a_bytes + 255) / 256 * 256;
-  // queue heads, per-unit phase-1 counters; the last 4 bytes of the workspace
-  // are the diagnostic word
-  L.q_ints = L.path == Path::kQueue ? static_cast<size_t>(kXcds) * kQueueStride + L.max_tiles : 0;
+  // queue heads, per-(unit, chunk) phase-1 flags; the last 4 bytes of the
+  // workspace are the diagnostic word
+  const int nch1_queue = (I + GemmSmall::BN / 2 - 1) / (GemmSmall::BN / 2);
+  L.q_ints = L.path == Path::kQueue
+                 ? static_cast<size_t>(kXcds) * kQueueStride + static_cast<size_t>(L.max_tiles) * nch1_queue
+                 : 0;
   L.total = L.q_off + (L.q_ints * 4 + 255) / 256 * 256 + 256;
   return L;
 }
@@ -1041,7 +1057,7 @@ void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t 
   q.n_x = a.n_x;
   q.lag = (blocks + nq - 1) / nq;
   q.heads = qbase;
-  q.done1 = qbase + kXcds * kQueueStride;
+  q.flags = qbase + kXcds * kQueueStride;
   q.error = diag;
   hipLaunchKernelGGL((ffn_queue_bf16<C>), dim3(blocks), dim3(C::NT), 0, stream,
                      static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),

@@ -25,8 +25,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kPerWave = 1024;
-constexpr int kChunk = kWaves * kPerWave;   // 4096 assignments per block
+constexpr int kPerWave = 256;
+constexpr int kChunk = kWaves * kPerWave;   // 1024 assignments per block
 constexpr int kMaxRoutedGroups = 2 * 512;   // nseg * E
 
 struct PermCtx {
@@ -57,9 +57,9 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
-// Each lane keeps the groups of its (up to) 16 assignments of the chunk in
+// Each lane keeps the groups of its (up to) kIters assignments of the chunk in
 // registers: loaded once, used by the histogram and by the scatter pass.
-constexpr int kIters = kPerWave / kWave;   // 16
+constexpr int kIters = kPerWave / kWave;   // 4
 
 __device__ __forceinline__ void load_groups(const PermCtx& c, int b, int (&grp)[kIters]) {
   const int w = threadIdx.x >> 6, lane = lane_id();

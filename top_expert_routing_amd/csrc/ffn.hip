@@ -400,20 +400,30 @@ struct TileLoader {
 };
 
 // TileMath: the wave's MFMA work on one ring slot, and the epilogue.
-// MFMA operand rows of this wave: A rows 32 MI wm + 32 i + l32; weight rows:
+// MFMA operand rows of this wave: A rows 32 (wm + WM i) + l32 (the waves'
+// 32-row slabs interleave, so a partial tile's valid slabs spread over all
+// waves, and a wave skips the MFMAs and LDS reads of its slabs that lie wholly
+// past the tile's valid rows); weight rows:
 // phase 2 (BN/WN) wn + 32 j + l32; phase 1 gate block j < NJ/2 at
 // (BN/2/WN) wn + 32 j + l32, up block j >= NJ/2 at BN/2 + (BN/2/WN) wn +
 // 32 (j - NJ/2) + l32.  Every block starts at a multiple of 32 rows, so the
 // swizzle depends on l32 only.
+template <int V>
+struct Int {
+  static constexpr int value = V;
+};
+
 template <int PHASE, class C>
 struct TileMath {
-  static constexpr int MI = C::MI, NJ = C::NJ, WN = C::WN, BN = C::BN;
+  static constexpr int MI = C::MI, NJ = C::NJ, WM = C::WM, WN = C::WN, BN = C::BN;
   static_assert(PHASE == 2 || NJ % 2 == 0, "phase 1 pairs gate and up blocks");
+  static_assert(MI == 1 || MI == 2, "kstep dispatches on 0, 1 or MI valid slabs");
   static_assert(C::ADMA >= 1 && C::BDMA >= 1, "tile too small for its waves");
   static_assert(C::STAGES >= 2, "the ring needs two buffers");
   int boff[NJ];
   int aoff, loff[2];
   int wm, wn, l32, hk;
+  int nv;                 // this wave's slabs holding valid rows (wave-uniform)
   f32x16 acc[MI][NJ];
 
   __device__ __forceinline__ void init() {
@@ -428,7 +438,8 @@ struct TileMath {
                                 : (BN / WN) * wn + 32 * j;
       boff[j] = C::A_BYTES + rb * kGemmRowBytes;
     }
-    aoff = 32 * MI * wm * kGemmRowBytes;
+    aoff = 32 * wm * kGemmRowBytes;
+    nv = MI;
 #pragma unroll
     for (int s = 0; s < 2; ++s) loff[s] = l32 * kGemmRowBytes + 16 * ((2 * s + hk) ^ gemm_swz(l32));
   }
@@ -442,19 +453,43 @@ struct TileMath {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   }
 
-  __device__ __forceinline__ void kstep(const uint8_t* st) {
+  // valid rows of the next tile: slab i of this wave holds rows
+  // 32 (wm + WM i) .. +31, valid if its first row is
+  __device__ __forceinline__ void set_rows(int rows) {
+    const int slabs = (rows + 31) >> 5;
+    nv = __builtin_amdgcn_readfirstlane(min(MI, max(0, (slabs - wm + WM - 1) / WM)));
+  }
+
+  template <int NV>
+  __device__ __forceinline__ void kstep_n(const uint8_t* st) {
+    if constexpr (NV == 0) return;                // no valid rows: nothing to read or multiply
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      bf16x8 af[MI], bf[NJ];
+      bf16x8 af[NV > 0 ? NV : 1], bf[NJ];
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(st + aoff + 32 * i * kGemmRowBytes + loff[s]);
+      for (int i = 0; i < NV; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(st + aoff + 32 * WM * i * kGemmRowBytes + loff[s]);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(st + boff[j] + loff[s]);
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // Runs body(Int<NV>) with NV = nv as a compile-time constant, so that the
+  // K loop inside body has no per-step branch (a branch around the MFMAs of
+  // every step makes the compiler copy and spill the accumulators).
+  template <class Body>
+  __device__ __forceinline__ void with_nv(Body&& body) {
+    if (nv == MI) {
+      body(Int<MI>{});
+    } else if constexpr (MI == 2) {
+      if (nv == 1) body(Int<1>{});
+      else body(Int<0>{});
+    } else {
+      body(Int<0>{});
     }
   }
 
@@ -467,7 +502,7 @@ struct TileMath {
     const int n0 = it.chunk * OUTC;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int m = 32 * MI * wm + 32 * i + l32;
+      const int m = 32 * (wm + WM * i) + l32;
       if (m >= it.rows) continue;
       uint16_t* orow = out + static_cast<size_t>(it.row0 + m) * Ncols;
 #pragma unroll
@@ -506,19 +541,22 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const 
   ld.init(A, arows, n_x, K, W0, W1, Ncols, it);
   TileMath<PHASE, C> mm;
   mm.init();
+  mm.set_rows(it.rows);
   mm.zero();
   const uint32_t lds0 = lds_address(smem);
   const int nk = K / kGemmBK;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nk) ld.issue(s, s, lds0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // K-step kt's loads are done once only the later steps' remain in flight
-    wait_ahead_barrier<C::ADMA + C::BDMA, STAGES - 2>(min(STAGES - 2, nk - 1 - kt));
-    // every wave is past step kt-1, so its buffer can be refilled
-    if (kt + STAGES - 1 < nk) ld.issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, lds0);
-    mm.kstep(smem + (kt % STAGES) * C::STAGE);
-  }
+  mm.with_nv([&](auto nvc) {
+    for (int kt = 0; kt < nk; ++kt) {
+      // K-step kt's loads are done once only the later steps' remain in flight
+      wait_ahead_barrier<C::ADMA + C::BDMA, STAGES - 2>(min(STAGES - 2, nk - 1 - kt));
+      // every wave is past step kt-1, so its buffer can be refilled
+      if (kt + STAGES - 1 < nk) ld.issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, lds0);
+      mm.template kstep_n<decltype(nvc)::value>(smem + (kt % STAGES) * C::STAGE);
+    }
+  });
   mm.store(it, Ncols, out);
 }
 
@@ -650,25 +688,24 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_b
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < total) issue_next();
-  // compute side: step ckt of tile cr from ring slot cslot
-  int cr = 0, ckt = 0, cslot = 0;
-  for (int gs = 0; gs < total; ++gs) {
-    if (ckt == 0) {
-      cur = decode(cr);
-      mm.zero();
-    }
-    // step gs's loads are done once only the later steps' remain in flight
-    // (epilogue stores issued since then only make this wait longer)
-    wait_ahead_barrier<C::ADMA + C::BDMA, STAGES - 2>(min(STAGES - 2, total - 1 - gs));
-    // every wave is past step gs-1, so its buffer can be refilled
-    if (gs + STAGES - 1 < total) issue_next();
-    mm.kstep(smem + cslot * C::STAGE);
-    cslot = cslot + 1 == STAGES ? 0 : cslot + 1;
-    if (++ckt == nk) {
-      mm.store(cur, Ncols, out);
-      ckt = 0;
-      ++cr;
-    }
+  // compute side: global step gs (tile cr, step gs - cr * nk) from ring slot cslot
+  int gs = 0, cslot = 0;
+  for (int cr = 0; cr < n_my; ++cr) {
+    cur = decode(cr);
+    mm.set_rows(cur.rows);
+    mm.zero();
+    mm.with_nv([&](auto nvc) {
+      for (int ckt = 0; ckt < nk; ++ckt, ++gs) {
+        // step gs's loads are done once only the later steps' remain in flight
+        // (epilogue stores issued since then only make this wait longer)
+        wait_ahead_barrier<C::ADMA + C::BDMA, STAGES - 2>(min(STAGES - 2, total - 1 - gs));
+        // every wave is past step gs-1, so its buffer can be refilled
+        if (gs + STAGES - 1 < total) issue_next();
+        mm.template kstep_n<decltype(nvc)::value>(smem + cslot * C::STAGE);
+        cslot = cslot + 1 == STAGES ? 0 : cslot + 1;
+      }
+    });
+    mm.store(cur, Ncols, out);
   }
 }
 

@@ -34,13 +34,13 @@ constexpr int kWaves = kThreads / kWave;
 // a precondition (non-decreasing, last entry n_rows); rows are still clamped to
 // [0, n_rows] so a bad input cannot make a tile reach outside the buffers.
 //
-// Items are ordered group-major: for each group g, for each column chunk j,
-// for each m-tile of g - so consecutive items share a group's weight slab (and,
-// for one m-tile, its token rows).  Workgroups are dealt round-robin to the
-// 8 XCDs (blockIdx % 8), and XCD x takes the x-th eighth of the item list in
-// order, so a group's items run close together in one XCD's L2.  The list is
-// in group order, so the priority segment's items start first on every XCD
-// that holds some.
+// Workgroups are dealt round-robin to the 8 XCDs (blockIdx % 8).  The
+// (group g, column chunk j) pairs are dealt to the XCDs in turn: pair
+// p = g * nch + j goes to XCD p % 8, with all of its m-tiles.  XCD x runs its
+// pairs in group order, chunk order, m-tile order, so the m-tiles that share
+// a weight slab run together in one L2, every XCD gets a similar mix of large
+// and small groups (a hot expert's chunks spread over all eight), and the
+// priority segment's items start first on every XCD.
 constexpr int kMaxGroups = 2 * 512 + 256;   // nseg * E + shared experts, at most
 constexpr int kMaxGroupsPerThread = (kMaxGroups + kThreads - 1) / kThreads;   // for 256 threads
 constexpr int kXcds = 8;                    // MI355X: 8 XCDs, workgroups dealt round-robin
@@ -63,6 +63,14 @@ struct Item {
   int row0, rows, expert, chunk;   // rows == 0: no work for this block
 };
 
+// Column chunks of group g that XCD x holds: j = first, first + 8, ... < nch.
+__device__ __forceinline__ int xcd_first_chunk(int g, int nch, int x) {
+  return static_cast<int>((static_cast<long long>(x) - static_cast<long long>(g) * nch) & (kXcds - 1));
+}
+__device__ __forceinline__ int xcd_chunks(int first, int nch) {
+  return first < nch ? (nch - 1 - first) / kXcds + 1 : 0;
+}
+
 // Must be called by all NT threads of the block.
 template <int NT = kThreads>
 __device__ Item block_find_item(const PlanArgs& p, int nch) {
@@ -70,6 +78,8 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
   __shared__ int wsum[NT / kWave];
   __shared__ Item found;
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  const int x = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;               // this block's item within XCD x's list
   if (tid == 0) found = Item{0, 0, 0, 0};
   if (tid == 0 && blockIdx.x == 0 && p.diag) *p.diag = 0;
   int cnt[GPT], r0[GPT];
@@ -84,8 +94,8 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
       const int hi = min(max(p.offs[g + 1], 0), p.n_rows);
       r0[q] = lo;
       cnt[q] = max(0, hi - lo);
+      s += (cnt[q] + p.BM - 1) / p.BM * xcd_chunks(xcd_first_chunk(g, nch, x), nch);
     }
-    s += (cnt[q] + p.BM - 1) / p.BM;
   }
   int incl = s;
 #pragma unroll
@@ -95,41 +105,36 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
   }
   if (lane == kWave - 1) wsum[w] = incl;
   __syncthreads();
-  int base = 0, total = 0;
+  int base = 0;
 #pragma unroll
-  for (int i = 0; i < NT / kWave; ++i) {
-    base += i < w ? wsum[i] : 0;
-    total += wsum[i];
-  }
-  // this block's item: the x-th eighth of the list, slot s within it
-  const long long items = static_cast<long long>(total) * nch;
-  const long long share = (items + kXcds - 1) / kXcds;
-  const long long slot = blockIdx.x / kXcds;
-  const long long want = (blockIdx.x % kXcds) * share + slot;
-  if (slot < share && want < items) {
-    int t = base + incl - s;     // first m-tile of this thread's first group
+  for (int i = 0; i < NT / kWave; ++i) base += i < w ? wsum[i] : 0;
+  int t = base + incl - s;     // XCD x's items before this thread's first group
+  if (slot >= t && slot < t + s) {
 #pragma unroll
     for (int q = 0; q < GPT; ++q) {
       const int g = tid * GPT + q;
       if (g >= p.G) break;
       const int nt = (cnt[q] + p.BM - 1) / p.BM;
-      const long long first = static_cast<long long>(t) * nch;
-      if (nt > 0 && want >= first && want < first + static_cast<long long>(nt) * nch) {
-        const int local = static_cast<int>(want - first);
-        const int j = local / nt, m = (local % nt) * p.BM;
+      const int first = xcd_first_chunk(g, nch, x);
+      const int n = nt * xcd_chunks(first, nch);
+      if (slot >= t && slot < t + n) {
+        const int local = slot - t;
+        const int j = first + kXcds * (local / nt), m = (local % nt) * p.BM;
         found = Item{r0[q] + m, min(p.BM, cnt[q] - m), expert_of_group(g, p.E, p.nseg), j};
       }
-      t += nt;
+      t += n;
     }
   }
   __syncthreads();
   return found;
 }
 
-// Grid size that covers every possible item of a call.
+// Grid size that covers every possible item of a call: XCD x holds at most
+// ceil(nch / 8) chunks of each group, so at most max_tiles * ceil(nch / 8)
+// items.
 inline int item_grid(int max_tiles, int nch) {
-  const long long items = static_cast<long long>(max_tiles) * nch;
-  return static_cast<int>((items + kXcds - 1) / kXcds * kXcds);
+  const long long per_xcd = static_cast<long long>(max_tiles) * ((nch + kXcds - 1) / kXcds);
+  return static_cast<int>(per_xcd * kXcds);
 }
 
 // silu(g) * u for the bf16 kernels (their result is rounded to bf16, so the

@@ -59,9 +59,18 @@ __device__ __forceinline__ size_t a_row(const int* arows, int n_x, int n) {
   return arows ? static_cast<size_t>(min(max(arows[n], 0), n_x - 1)) : static_cast<size_t>(n);
 }
 
+// A tile's rows: tile row r < split is sorted row row0 + r, a later one is
+// row1 + (r - split) (two ranges when a priority group and the same expert's
+// other rows share a tile; one range otherwise, split == rows).
 struct Item {
   int row0, rows, expert, chunk;   // rows == 0: no work for this block
+  int split, row1;
+  __device__ __forceinline__ int row(int r) const { return r < split ? row0 + r : row1 + (r - split); }
 };
+
+__device__ __forceinline__ Item contiguous_item(int row0, int rows, int expert, int chunk) {
+  return Item{row0, rows, expert, chunk, rows, row0 + rows};
+}
 
 // Column chunks of group g that XCD x holds: j = first, first + 8, ... < nch.
 __device__ __forceinline__ int xcd_first_chunk(int g, int nch, int x) {
@@ -69,6 +78,41 @@ __device__ __forceinline__ int xcd_first_chunk(int g, int nch, int x) {
 }
 __device__ __forceinline__ int xcd_chunks(int first, int nch) {
   return first < nch ? (nch - 1 - first) / kXcds + 1 : 0;
+}
+
+// The rows a group's tiles cover: `na` rows from row `a0`, then `nb` rows from
+// row `b0`, cut into m-tiles of BM; the group owns tiles [t0, t0 + nt).
+struct GroupRows {
+  int a0, na, b0, nb, t0, nt;
+};
+
+// With a priority segment (nseg == 2), expert e's priority rows P and its
+// other rows R are tiled as one sequence P ++ R: group e (priority segment)
+// owns the tiles that hold a row of P - so its first tile carries the first
+// rows of R too, and the expert's weights stream once for both when R is
+// small - and group E + e owns the remaining tiles.  Every priority row is
+// still in the priority part of the list.  Otherwise a group is its own rows.
+__device__ __forceinline__ GroupRows group_rows(const PlanArgs& p, int g) {
+  auto lo = [&](int i) { return min(max(p.offs[i], 0), p.n_rows); };
+  GroupRows r;
+  if (p.nseg == 2 && g < 2 * p.E) {
+    const int e = g < p.E ? g : g - p.E;
+    r.a0 = lo(e);
+    r.na = max(0, lo(e + 1) - r.a0);
+    r.b0 = lo(p.E + e);
+    r.nb = max(0, lo(p.E + e + 1) - r.b0);
+    const int tp = (r.na + p.BM - 1) / p.BM;
+    r.t0 = g < p.E ? 0 : tp;
+    r.nt = g < p.E ? tp : (r.na + r.nb + p.BM - 1) / p.BM - tp;
+  } else {
+    r.a0 = lo(g);
+    r.na = max(0, lo(g + 1) - r.a0);
+    r.b0 = r.a0 + r.na;
+    r.nb = 0;
+    r.t0 = 0;
+    r.nt = (r.na + p.BM - 1) / p.BM;
+  }
+  return r;
 }
 
 // Must be called by all NT threads of the block.
@@ -80,21 +124,17 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
   const int x = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;               // this block's item within XCD x's list
-  if (tid == 0) found = Item{0, 0, 0, 0};
+  if (tid == 0) found = Item{0, 0, 0, 0, 0, 0};
   if (tid == 0 && blockIdx.x == 0 && p.diag) *p.diag = 0;
-  int cnt[GPT], r0[GPT];
+  GroupRows gr[GPT];
   int s = 0;
 #pragma unroll
   for (int q = 0; q < GPT; ++q) {
     const int g = tid * GPT + q;
-    cnt[q] = 0;
-    r0[q] = 0;
+    gr[q] = GroupRows{0, 0, 0, 0, 0, 0};
     if (g < p.G) {
-      const int lo = min(max(p.offs[g], 0), p.n_rows);
-      const int hi = min(max(p.offs[g + 1], 0), p.n_rows);
-      r0[q] = lo;
-      cnt[q] = max(0, hi - lo);
-      s += (cnt[q] + p.BM - 1) / p.BM * xcd_chunks(xcd_first_chunk(g, nch, x), nch);
+      gr[q] = group_rows(p, g);
+      s += gr[q].nt * xcd_chunks(xcd_first_chunk(g, nch, x), nch);
     }
   }
   int incl = s;
@@ -114,13 +154,16 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
     for (int q = 0; q < GPT; ++q) {
       const int g = tid * GPT + q;
       if (g >= p.G) break;
-      const int nt = (cnt[q] + p.BM - 1) / p.BM;
+      const GroupRows& r = gr[q];
       const int first = xcd_first_chunk(g, nch, x);
-      const int n = nt * xcd_chunks(first, nch);
+      const int n = r.nt * xcd_chunks(first, nch);
       if (slot >= t && slot < t + n) {
         const int local = slot - t;
-        const int j = first + kXcds * (local / nt), m = (local % nt) * p.BM;
-        found = Item{r0[q] + m, min(p.BM, cnt[q] - m), expert_of_group(g, p.E, p.nseg), j};
+        const int j = first + kXcds * (local / r.nt);
+        const int a = (r.t0 + local % r.nt) * p.BM;                  // first row of the tile in the sequence
+        const int rows = min(p.BM, r.na + r.nb - a);
+        const int split = min(max(r.na - a, 0), rows);
+        found = Item{r.a0 + a, rows, expert_of_group(g, p.E, p.nseg), j, split, r.b0 + max(a - r.na, 0)};
       }
       t += n;
     }
@@ -175,7 +218,7 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
   const int nch = (Ncols + BN - 1) / BN;
   const Item it = block_find_item(plan, nch);
   if (it.rows == 0) return;
-  const int row0 = it.row0, rows = it.rows, e = it.expert;
+  const int rows = it.rows, e = it.expert;
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int l16 = lane & 15, q = lane >> 4;
   const int col0 = it.chunk * BN + wave * 16 * NFC;
@@ -197,7 +240,7 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
   for (int s = 0; s < APT; ++s) {
     const int idx = threadIdx.x + s * kThreads;
     const int r = idx / VPR;
-    arow[s] = (idx < BM * VPR && r < rows) ? A + a_row(plan.arows, plan.n_x, row0 + r) * K : nullptr;
+    arow[s] = (idx < BM * VPR && r < rows) ? A + a_row(plan.arows, plan.n_x, it.row(r)) * K : nullptr;
   }
   auto load_a = [&](int c) {
 #pragma unroll
@@ -270,7 +313,7 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
   for (int i = 0; i < MF; ++i) {
     const int m = 16 * i + l16;
     if (m >= rows) continue;
-    uint16_t* orow = out + static_cast<size_t>(row0 + m) * Ncols;
+    uint16_t* orow = out + static_cast<size_t>(it.row(m)) * Ncols;
 #pragma unroll
     for (int j = 0; j < NFC; ++j) {
       const int n = col0 + j * 16 + 4 * q;
@@ -378,7 +421,7 @@ struct TileLoader {
 #pragma unroll
     for (int q = 0; q < C::ADMA; ++q) {
       const int r = 16 * (wave + C::NW * q) + dr;
-      asrc[q] = A + a_row(arows, n_x, it.row0 + min(r, it.rows - 1)) * K + 8 * ((lane & 3) ^ gemm_swz(r));
+      asrc[q] = A + a_row(arows, n_x, it.row(min(r, it.rows - 1))) * K + 8 * ((lane & 3) ^ gemm_swz(r));
     }
 #pragma unroll
     for (int q = 0; q < C::BDMA; ++q) {
@@ -509,7 +552,7 @@ struct TileMath {
     for (int i = 0; i < MI; ++i) {
       const int m = 32 * (wm + WM * i) + l32;
       if (m >= it.rows) continue;
-      uint16_t* orow = out + static_cast<size_t>(it.row0 + m) * Ncols;
+      uint16_t* orow = out + static_cast<size_t>(it.row(m)) * Ncols;
 #pragma unroll
       for (int j = 0; j < (PHASE == 1 ? NJ / 2 : NJ); ++j) {
         const int nb = n0 + (PHASE == 1 ? (BN / 2 / WN) * wn : (BN / WN) * wn) + 32 * j + 4 * hk;
@@ -533,7 +576,7 @@ __device__ __forceinline__ uint32_t lds_address(const uint8_t* smem) {
   return (uint32_t)(uintptr_t)(lds_byte*)smem;
 }
 
-// One tile: rows [row0, row0 + rows) of A against output column chunk
+// One tile: the it.rows sorted rows it.row(0..) of A against output column chunk
 // `it.chunk` of expert `it.expert`.  `smem` is the block's operand ring, free
 // on entry (no wave still reads it).
 template <int PHASE, class C>
@@ -669,7 +712,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_b
     const int local = want - fu[g] * nch;
     const int j = local / nt, mt = local % nt;
     const int glo = gl[g], ghi = max(glo, gl[g + 1]);
-    return Item{glo + mt * BM, min(BM, ghi - glo - mt * BM), expert_of_group(g, plan.E, plan.nseg), j};
+    return contiguous_item(glo + mt * BM, min(BM, ghi - glo - mt * BM), expert_of_group(g, plan.E, plan.nseg), j);
   };
 
   const int nk = K / kGemmBK;
@@ -865,7 +908,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
     const int chunk = local / cg, mt = sg - fu[g] + local % cg;
     const int unit = fu[g] + mt;
     const int glo = min(max(q.offs[g], 0), q.n_rows), ghi = min(max(q.offs[g + 1], 0), q.n_rows);
-    const Item it{glo + mt * BM, min(BM, ghi - glo - mt * BM), expert_of_group(g, q.E, q.nseg), chunk};
+    const Item it = contiguous_item(glo + mt * BM, min(BM, ghi - glo - mt * BM), expert_of_group(g, q.E, q.nseg), chunk);
     if (phase == 1) {
       gemm_tile<1, C>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are in L2
@@ -917,7 +960,7 @@ __global__ __launch_bounds__(kThreads) void ffn_phase_f32(const float* __restric
   __shared__ float As[BM * 64];
   const Item it = block_find_item(plan, (Ncols + kThreads - 1) / kThreads);
   if (it.rows == 0) return;
-  const int row0 = it.row0, rows = it.rows, e = it.expert;
+  const int rows = it.rows, e = it.expert;
   const int n = it.chunk * kThreads + threadIdx.x;
   const size_t wstride = static_cast<size_t>(Ncols) * K;
   const float* b0 = W0 + static_cast<size_t>(e) * wstride + static_cast<size_t>(n) * K;
@@ -928,7 +971,7 @@ __global__ __launch_bounds__(kThreads) void ffn_phase_f32(const float* __restric
   for (int k0 = 0; k0 < K; k0 += 64) {
     for (int idx = threadIdx.x; idx < BM * 64; idx += kThreads) {
       const int r = idx >> 6, kk = k0 + (idx & 63);
-      As[idx] = (r < rows && kk < K) ? A[a_row(plan.arows, plan.n_x, row0 + r) * K + kk] : 0.f;
+      As[idx] = (r < rows && kk < K) ? A[a_row(plan.arows, plan.n_x, it.row(r)) * K + kk] : 0.f;
     }
     __syncthreads();
     if (n < Ncols) {
@@ -948,7 +991,7 @@ __global__ __launch_bounds__(kThreads) void ffn_phase_f32(const float* __restric
   if (n >= Ncols) return;
   for (int r = 0; r < rows; ++r) {
     const float v = PHASE == 1 ? acc0[r] / (1.0f + expf(-acc0[r])) * acc1[r] : acc0[r];
-    out[static_cast<size_t>(row0 + r) * Ncols + n] = v;
+    out[static_cast<size_t>(it.row(r)) * Ncols + n] = v;
   }
 }
 

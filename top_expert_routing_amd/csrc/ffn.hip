@@ -59,6 +59,24 @@ __device__ __forceinline__ size_t a_row(const int* arows, int n_x, int n) {
   return arows ? static_cast<size_t>(min(max(arows[n], 0), n_x - 1)) : static_cast<size_t>(n);
 }
 
+// a_row of N sorted rows at once: the (wave-uniform) test of the row list is
+// taken once, so the N loads are issued back to back and cost one memory
+// round trip (with the test inside each a_row call the compiler waits for
+// every load before the next).
+template <int N>
+__device__ __forceinline__ void a_rows(const int* arows, int n_x, const int (&n)[N], size_t (&out)[N]) {
+  if (arows) {
+    int v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = arows[n[i]];
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = static_cast<size_t>(min(max(v[i], 0), n_x - 1));
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = static_cast<size_t>(n[i]);
+  }
+}
+
 // A tile's rows: tile row r < split is sorted row row0 + r, a later one is
 // row1 + (r - split) (two ranges when a priority group and the same expert's
 // other rows share a tile; one range otherwise, split == rows).
@@ -92,21 +110,36 @@ struct GroupRows {
 // rows of R too, and the expert's weights stream once for both when R is
 // small - and group E + e owns the remaining tiles.  Every priority row is
 // still in the priority part of the list.  Otherwise a group is its own rows.
-__device__ __forceinline__ GroupRows group_rows(const PlanArgs& p, int g) {
-  auto lo = [&](int i) { return min(max(p.offs[i], 0), p.n_rows); };
+// Offsets a group's rows come from: o[0..1] bound its own rows (merged: the
+// priority rows of its expert), o[2..3] the expert's other rows (merged only).
+// Group indices are clamped so the four loads are unconditional: a load under
+// a divergent branch is followed by a full wait, and a thread's loads would
+// then each cost a memory round trip.
+__device__ __forceinline__ void group_offsets_of(const PlanArgs& p, int g, int (&o)[4]) {
+  const int gc = min(max(g, 0), p.G - 1);
+  const bool merged = p.nseg == 2 && gc < 2 * p.E;
+  const int ia = merged ? (gc < p.E ? gc : gc - p.E) : gc;
+  const int ib = merged ? ia + p.E : gc;
+  o[0] = p.offs[ia];
+  o[1] = p.offs[ia + 1];
+  o[2] = p.offs[ib];
+  o[3] = p.offs[ib + 1];
+}
+
+__device__ __forceinline__ GroupRows group_rows(const PlanArgs& p, int g, const int (&o)[4]) {
+  auto lo = [&](int v) { return min(max(v, 0), p.n_rows); };
   GroupRows r;
   if (p.nseg == 2 && g < 2 * p.E) {
-    const int e = g < p.E ? g : g - p.E;
-    r.a0 = lo(e);
-    r.na = max(0, lo(e + 1) - r.a0);
-    r.b0 = lo(p.E + e);
-    r.nb = max(0, lo(p.E + e + 1) - r.b0);
+    r.a0 = lo(o[0]);
+    r.na = max(0, lo(o[1]) - r.a0);
+    r.b0 = lo(o[2]);
+    r.nb = max(0, lo(o[3]) - r.b0);
     const int tp = (r.na + p.BM - 1) / p.BM;
     r.t0 = g < p.E ? 0 : tp;
     r.nt = g < p.E ? tp : (r.na + r.nb + p.BM - 1) / p.BM - tp;
   } else {
-    r.a0 = lo(g);
-    r.na = max(0, lo(g + 1) - r.a0);
+    r.a0 = lo(o[0]);
+    r.na = max(0, lo(o[1]) - r.a0);
     r.b0 = r.a0 + r.na;
     r.nb = 0;
     r.t0 = 0;
@@ -126,6 +159,9 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
   const int slot = blockIdx.x / kXcds;               // this block's item within XCD x's list
   if (tid == 0) found = Item{0, 0, 0, 0, 0, 0};
   if (tid == 0 && blockIdx.x == 0 && p.diag) *p.diag = 0;
+  int o[GPT][4];
+#pragma unroll
+  for (int q = 0; q < GPT; ++q) group_offsets_of(p, tid * GPT + q, o[q]);   // all loads in flight at once
   GroupRows gr[GPT];
   int s = 0;
 #pragma unroll
@@ -133,7 +169,7 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
     const int g = tid * GPT + q;
     gr[q] = GroupRows{0, 0, 0, 0, 0, 0};
     if (g < p.G) {
-      gr[q] = group_rows(p, g);
+      gr[q] = group_rows(p, g, o[q]);
       s += gr[q].nt * xcd_chunks(xcd_first_chunk(g, nch, x), nch);
     }
   }
@@ -236,11 +272,17 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
   // A staging: thread handles uint4 slots idx = tid + s*256 of the chunk
   uint4 stage[APT];
   const uint16_t* arow[APT];
+  {
+    int rn[APT];
+    size_t ar[APT];
 #pragma unroll
-  for (int s = 0; s < APT; ++s) {
-    const int idx = threadIdx.x + s * kThreads;
-    const int r = idx / VPR;
-    arow[s] = (idx < BM * VPR && r < rows) ? A + a_row(plan.arows, plan.n_x, it.row(r)) * K : nullptr;
+    for (int s = 0; s < APT; ++s) rn[s] = it.row(min((threadIdx.x + s * kThreads) / VPR, rows - 1));
+    a_rows(plan.arows, plan.n_x, rn, ar);
+#pragma unroll
+    for (int s = 0; s < APT; ++s) {
+      const int idx = threadIdx.x + s * kThreads;
+      arow[s] = (idx < BM * VPR && idx / VPR < rows) ? A + ar[s] * K : nullptr;
+    }
   }
   auto load_a = [&](int c) {
 #pragma unroll
@@ -418,10 +460,15 @@ struct TileLoader {
     const int wave = threadIdx.x >> 6, lane = lane_id(), dr = lane >> 2;
     const int n0 = it.chunk * OUTC;
     const size_t eoff = static_cast<size_t>(it.expert) * Ncols * K;
+    int rn[C::ADMA];
+    size_t ar[C::ADMA];
+#pragma unroll
+    for (int q = 0; q < C::ADMA; ++q) rn[q] = it.row(min(16 * (wave + C::NW * q) + dr, it.rows - 1));
+    a_rows(arows, n_x, rn, ar);
 #pragma unroll
     for (int q = 0; q < C::ADMA; ++q) {
       const int r = 16 * (wave + C::NW * q) + dr;
-      asrc[q] = A + a_row(arows, n_x, it.row(min(r, it.rows - 1))) * K + 8 * ((lane & 3) ^ gemm_swz(r));
+      asrc[q] = A + ar[q] * K + 8 * ((lane & 3) ^ gemm_swz(r));
     }
 #pragma unroll
     for (int q = 0; q < C::BDMA; ++q) {
@@ -652,14 +699,20 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_b
 
   // m-tiles per group, exclusive scan -> fu
   {
-    int cnt[GPT];
+    int cnt[GPT], ov[GPT][2];
     int sum = 0;
+#pragma unroll
+    for (int q = 0; q < GPT; ++q) {                    // unconditional loads, all in flight at once
+      const int gc = min(tid * GPT + q, plan.G - 1);
+      ov[q][0] = plan.offs[gc];
+      ov[q][1] = plan.offs[gc + 1];
+    }
 #pragma unroll
     for (int q = 0; q < GPT; ++q) {
       const int g = tid * GPT + q;
       cnt[q] = 0;
       if (g < plan.G) {
-        const int lo = min(max(plan.offs[g], 0), plan.n_rows), hi = min(max(plan.offs[g + 1], 0), plan.n_rows);
+        const int lo = min(max(ov[q][0], 0), plan.n_rows), hi = min(max(ov[q][1], 0), plan.n_rows);
         cnt[q] = (max(0, hi - lo) + BM - 1) / BM;
         gl[g] = lo;
         if (g == plan.G - 1) gl[plan.G] = max(lo, hi);

@@ -170,10 +170,11 @@ __device__ __forceinline__ void copy_rows(const uint4* __restrict__ x, uint4* __
       dst[j] = xs + static_cast<size_t>(dst_row(jj)) * row_vecs;
     }
     for (int c = threadIdx.x; c < row_vecs; c += kThreads) {
+      // every load is issued (rows past nr re-read row j0): a load under a
+      // branch is followed by a wait, which would serialise the 16 loads
       uint4 v[kCopyRows];
 #pragma unroll
-      for (int j = 0; j < kCopyRows; ++j)
-        if (j < nr) v[j] = src[j][c];
+      for (int j = 0; j < kCopyRows; ++j) v[j] = src[j][c];
 #pragma unroll
       for (int j = 0; j < kCopyRows; ++j)
         if (j < nr) dst[j][c] = v[j];

@@ -282,17 +282,17 @@ __global__ __launch_bounds__(kThreads) void stats_finish(int L, int E, int R, St
   const int ec = ok ? e : 0;
   const size_t rstride = static_cast<size_t>(L) * E;
   const int* base = req_counts + static_cast<size_t>(l) * E + ec;
+  // loads below read clamped, always valid addresses and mask the value
+  // afterwards: a load under a branch is followed by a wait, which would turn
+  // each batch into kBatch memory round trips
   int df = 0;
   if (!idf_in) {
     for (int r0 = w; r0 < R; r0 += kW * kBatch) {
       int v[kBatch];
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        const int r = r0 + b * kW;
-        v[b] = (ok && r < R) ? base[static_cast<size_t>(r) * rstride] : 0;
-      }
+      for (int b = 0; b < kBatch; ++b) v[b] = base[static_cast<size_t>(min(r0 + b * kW, R - 1)) * rstride];
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) df += v[b] > 0;
+      for (int b = 0; b < kBatch; ++b) df += (ok && r0 + b * kW < R && v[b] > 0) ? 1 : 0;
     }
   }
   dfp[w][lane] = df;
@@ -313,10 +313,7 @@ __global__ __launch_bounds__(kThreads) void stats_finish(int L, int E, int R, St
   for (int r0 = w; r0 < R; r0 += kW * kBatch) {
     int v[kBatch];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int r = r0 + b * kW;
-      v[b] = r < R ? base[static_cast<size_t>(r) * rstride] : 0;
-    }
+    for (int b = 0; b < kBatch; ++b) v[b] = base[static_cast<size_t>(min(r0 + b * kW, R - 1)) * rstride];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const int r = r0 + b * kW;

@@ -298,11 +298,20 @@ __global__ __launch_bounds__(kThreads) void permute_count(PermCtx c, int* blk) {
 
 __global__ __launch_bounds__(1024) void permute_scan(PermCtx c, int n_shared, int* blk, int* group_offsets) {
   __shared__ int part[1024];
+  // a thread's counts are read kBatch at a time from clamped addresses, all in
+  // flight together (loads under a bounds test would each wait for the last)
+  constexpr int kBatch = 8;
   const int M = c.Gr * c.nb;
   const int per = (M + 1023) / 1024;
   const int lo = threadIdx.x * per, hi = min(M, lo + per);
   int s = 0;
-  for (int i = lo; i < hi; ++i) s += blk[i];
+  for (int i0 = lo; i0 < hi; i0 += kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) v[b] = blk[min(i0 + b, M - 1)];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) s += i0 + b < hi ? v[b] : 0;
+  }
   part[threadIdx.x] = s;
   __syncthreads();
   // Hillis-Steele inclusive scan over the 1024 partial sums
@@ -313,11 +322,18 @@ __global__ __launch_bounds__(1024) void permute_scan(PermCtx c, int n_shared, in
     __syncthreads();
   }
   int run = part[threadIdx.x] - s;
-  for (int i = lo; i < hi; ++i) {
-    const int v = blk[i];
-    blk[i] = run;
-    if (i % c.nb == 0) group_offsets[i / c.nb] = run;
-    run += v;
+  for (int i0 = lo; i0 < hi; i0 += kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) v[b] = blk[min(i0 + b, M - 1)];   // entries past hi are not used
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int i = i0 + b;
+      if (i >= hi) break;
+      blk[i] = run;
+      if (i % c.nb == 0) group_offsets[i / c.nb] = run;
+      run += v[b];
+    }
   }
   for (int q = threadIdx.x; q <= n_shared; q += 1024) group_offsets[c.Gr + q] = c.Nr + q * c.T;
 }

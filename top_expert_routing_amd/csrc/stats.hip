@@ -322,17 +322,21 @@ __global__ __launch_bounds__(kThreads) void stats_finish(int L, int E, int R, St
   }
 }
 
-// ---- small batches: everything for one layer in one 1024-thread block ---------
+// ---- small batches: one launch, a few 1024-thread blocks per layer ------------
 // When the affinity matrix, the request histograms and the request offsets fit
-// in 56 KiB of LDS, one block per layer computes counts, union, affinity,
-// request counts, idf and signature in a single launch (decode-sized batches:
-// the two-launch path would pay a second launch and a global round trip).
-// Ids are staged through LDS a chunk at a time; each thread then takes one
-// (token, slot) pair, so the chains of dependent LDS atomics stay short, and
-// the document frequency is counted over all (request, expert) cells at once.
+// in 56 KiB of LDS, each block of a layer builds all of them in LDS (the work
+// is a few thousand LDS atomics) and writes its share of the output rows, so
+// the writes spread over kSmallSplit CUs.  Decode-sized batches: the two-launch
+// path would pay a second launch and a global round trip.
+// Ids are staged through LDS a chunk at a time (the first chunk's loads are
+// issued together with the request offsets', one memory latency); each thread
+// takes one (token, slot) pair, so the chains of dependent LDS atomics stay
+// short.  The document frequency counts a request for expert e when its
+// histogram cell goes from 0 to 1.
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallLds = 14336;     // ints shared by affinity, request counts, offsets
 constexpr int kSmallIds = 4096;      // staged ids per chunk
+constexpr int kSmallSplit = 4;       // blocks per layer (each writes a quarter of the rows)
 
 bool small_fits(int E, int R, bool want_aff, bool want_req, int T, int k) {
   const long long need = (want_aff ? 1LL * E * E : 0) + (want_req ? 1LL * R * E + R + 1 : 0);
@@ -355,13 +359,24 @@ __global__ __launch_bounds__(kSmallThreads) void stats_small(const int* __restri
   __shared__ int dfc[MOE_MAX_EXPERTS_DEV];
   __shared__ double idf[MOE_MAX_EXPERTS_DEV];
   __shared__ int red[kSmallThreads / kWave];
-  const int l = blockIdx.x;
+  constexpr int kPer = kSmallIds / kSmallThreads;
+  const int l = blockIdx.x / kSmallSplit, part = blockIdx.x % kSmallSplit;
   const int tid = threadIdx.x;
   const bool want_aff = affinity != nullptr;
   const bool want_req = req_offsets != nullptr && R > 0 && (req_counts != nullptr || signature != nullptr);
+  const bool need_df = want_req && signature && !idf_in;
   int* aff = lds;
   int* req = lds + (want_aff ? E * E : 0);
   int* offs = req + (want_req ? R * E : 0);
+  const int* lid = ids + static_cast<size_t>(l) * T * k;
+  const int tpc = kSmallIds / k;                       // tokens per chunk (k <= 512)
+  // loads of a chunk's ids: clamped addresses, so none waits for another
+  int v[kPer];
+  auto load_ids = [&](int t0, int n) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) v[q] = lid[static_cast<size_t>(t0) * k + min(tid + q * kSmallThreads, max(n - 1, 0))];
+  };
+  if (T > 0) load_ids(0, min(tpc, T) * k);
   const int used = (want_aff ? E * E : 0) + (want_req ? R * E : 0);
   for (int i = tid; i < used; i += kSmallThreads) lds[i] = 0;
   for (int e = tid; e < E; e += kSmallThreads) {
@@ -370,24 +385,14 @@ __global__ __launch_bounds__(kSmallThreads) void stats_small(const int* __restri
   }
   if (want_req)
     for (int i = tid; i <= R; i += kSmallThreads) offs[i] = max(0, min(req_offsets[i], T));
-  const int* lid = ids + static_cast<size_t>(l) * T * k;
-  const int tpc = min(kSmallIds / k, kSmallIds);      // tokens per chunk (k <= 512)
   for (int t0 = 0; t0 < T; t0 += tpc) {
     const int nt = min(tpc, T - t0), n = nt * k;
-    __syncthreads();                                   // previous chunk consumed; zeroing done
-    {
-      constexpr int kPer = kSmallIds / kSmallThreads;
-      int v[kPer];
+    if (t0 > 0) load_ids(t0, n);
+    __syncthreads();                                   // previous chunk consumed; zeroing and offsets done
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int i = tid + q * kSmallThreads;
-        v[q] = i < n ? lid[static_cast<size_t>(t0) * k + i] : 0;
-      }
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int i = tid + q * kSmallThreads;
-        if (i < n) idbuf[i] = clamp_id(v[q], E);
-      }
+    for (int q = 0; q < kPer; ++q) {
+      const int i = tid + q * kSmallThreads;
+      if (i < n) idbuf[i] = clamp_id(v[q], E);
     }
     // request of each token of the chunk (-1: none)
     for (int tt = tid; tt < nt; tt += kSmallThreads) {
@@ -409,7 +414,10 @@ __global__ __launch_bounds__(kSmallThreads) void stats_small(const int* __restri
       const int a = idbuf[i];
       atomicAdd(&cnt[a], 1);
       const int r = reqof[tt];
-      if (r >= 0) atomicAdd(&req[r * E + a], 1);
+      if (r >= 0) {
+        const int old = atomicAdd(&req[r * E + a], 1);
+        if (need_df && old == 0) atomicAdd(&dfc[a], 1);
+      }
       if (want_aff) {
         const int* row = idbuf + tt * k;
         int* dst = aff + a * E;
@@ -418,31 +426,30 @@ __global__ __launch_bounds__(kSmallThreads) void stats_small(const int* __restri
     }
   }
   __syncthreads();
-  const bool need_df = want_req && signature && !idf_in;
-  if (need_df)
-    for (int i = tid; i < R * E; i += kSmallThreads)
-      if (req[i] > 0) atomicAdd(&dfc[i % E], 1);
-  int nz = 0;
-  for (int e = tid; e < E; e += kSmallThreads) {
-    const int c = cnt[e];
-    counts[static_cast<size_t>(l) * E + e] = c;
-    if (union_mask) union_mask[static_cast<size_t>(l) * E + e] = c > 0 ? 1 : 0;
-    nz += c > 0 ? 1 : 0;
+  // rows [lo, hi) of E (affinity) and of R (requests) are this block's to write
+  auto share = [&](int n, int& lo, int& hi) {
+    const int per = (n + kSmallSplit - 1) / kSmallSplit;
+    lo = min(n, part * per);
+    hi = min(n, lo + per);
+  };
+  if (part == 0) {
+    int nz = 0;
+    for (int e = tid; e < E; e += kSmallThreads) {
+      const int c = cnt[e];
+      counts[static_cast<size_t>(l) * E + e] = c;
+      if (union_mask) union_mask[static_cast<size_t>(l) * E + e] = c > 0 ? 1 : 0;
+      nz += c > 0 ? 1 : 0;
+    }
+    nz = wave_sum(nz);
+    if (lane_id() == 0) red[tid >> 6] = nz;
   }
-  nz = wave_sum(nz);
-  if (lane_id() == 0) red[tid >> 6] = nz;
   if (want_aff) {
+    int a_lo, a_hi;
+    share(E, a_lo, a_hi);
     int* dst = affinity + static_cast<size_t>(l) * E * E;
-    for (int i = tid; i < E * E; i += kSmallThreads) dst[i] = aff[i];
+    for (int i = a_lo * E + tid; i < a_hi * E; i += kSmallThreads) dst[i] = aff[i];
   }
-  __syncthreads();
-  if (tid == 0) {
-    int s = 0;
-    for (int w = 0; w < kSmallThreads / kWave; ++w) s += red[w];
-    union_size[l] = s;
-  }
-  if (!want_req) return;
-  if (signature)
+  if (signature && want_req)
     for (int e = tid; e < E; e += kSmallThreads) {
       if (idf_in) {
         idf[e] = static_cast<double>(idf_in[static_cast<size_t>(l) * E + e]);
@@ -452,7 +459,15 @@ __global__ __launch_bounds__(kSmallThreads) void stats_small(const int* __restri
       }
     }
   __syncthreads();
-  for (int i = tid; i < R * E; i += kSmallThreads) {
+  if (part == 0 && tid == 0) {
+    int sum = 0;
+    for (int w = 0; w < kSmallThreads / kWave; ++w) sum += red[w];
+    union_size[l] = sum;
+  }
+  if (!want_req) return;
+  int r_lo, r_hi;
+  share(R, r_lo, r_hi);
+  for (int i = r_lo * E + tid; i < r_hi * E; i += kSmallThreads) {
     const int rr = i / E, e = i % E;
     const size_t at = (static_cast<size_t>(rr) * L + l) * E + e;
     if (req_counts) req_counts[at] = req[i];
@@ -460,8 +475,6 @@ __global__ __launch_bounds__(kSmallThreads) void stats_small(const int* __restri
   }
 }
 
-// Workspace: request counts (when the caller wants only the signature), then
-// the split partials of the affinity tiles and counts.
 struct WsLayout {
   size_t rc_off, aff_off, cnt_off, total;
 };
@@ -487,7 +500,7 @@ hipError_t launch_stats(const StatsArgs& a, void* workspace, hipStream_t stream)
   if (a.L == 0) return hipSuccess;
   const bool want_req = a.req_offsets && a.R > 0 && (a.req_counts || a.signature);
   if (small_fits(a.E, a.R, a.affinity != nullptr, want_req, a.T, a.k)) {
-    hipLaunchKernelGGL(stats_small, dim3(a.L), dim3(kSmallThreads), 0, stream, a.topk_ids, a.L, a.T, a.k, a.E,
+    hipLaunchKernelGGL(stats_small, dim3(a.L * kSmallSplit), dim3(kSmallThreads), 0, stream, a.topk_ids, a.L, a.T, a.k, a.E,
                        a.counts, a.union_size, a.union_mask, a.affinity, want_req ? a.req_offsets : nullptr,
                        want_req ? a.R : 0, a.idf, a.req_counts, a.signature);
     return hipGetLastError();

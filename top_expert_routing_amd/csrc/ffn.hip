@@ -110,36 +110,21 @@ struct GroupRows {
 // rows of R too, and the expert's weights stream once for both when R is
 // small - and group E + e owns the remaining tiles.  Every priority row is
 // still in the priority part of the list.  Otherwise a group is its own rows.
-// Offsets a group's rows come from: o[0..1] bound its own rows (merged: the
-// priority rows of its expert), o[2..3] the expert's other rows (merged only).
-// Group indices are clamped so the four loads are unconditional: a load under
-// a divergent branch is followed by a full wait, and a thread's loads would
-// then each cost a memory round trip.
-__device__ __forceinline__ void group_offsets_of(const PlanArgs& p, int g, int (&o)[4]) {
-  const int gc = min(max(g, 0), p.G - 1);
-  const bool merged = p.nseg == 2 && gc < 2 * p.E;
-  const int ia = merged ? (gc < p.E ? gc : gc - p.E) : gc;
-  const int ib = merged ? ia + p.E : gc;
-  o[0] = p.offs[ia];
-  o[1] = p.offs[ia + 1];
-  o[2] = p.offs[ib];
-  o[3] = p.offs[ib + 1];
-}
-
-__device__ __forceinline__ GroupRows group_rows(const PlanArgs& p, int g, const int (&o)[4]) {
-  auto lo = [&](int v) { return min(max(v, 0), p.n_rows); };
+__device__ __forceinline__ GroupRows group_rows(const PlanArgs& p, int g) {
+  auto lo = [&](int i) { return min(max(p.offs[i], 0), p.n_rows); };
   GroupRows r;
   if (p.nseg == 2 && g < 2 * p.E) {
-    r.a0 = lo(o[0]);
-    r.na = max(0, lo(o[1]) - r.a0);
-    r.b0 = lo(o[2]);
-    r.nb = max(0, lo(o[3]) - r.b0);
+    const int e = g < p.E ? g : g - p.E;
+    r.a0 = lo(e);
+    r.na = max(0, lo(e + 1) - r.a0);
+    r.b0 = lo(p.E + e);
+    r.nb = max(0, lo(p.E + e + 1) - r.b0);
     const int tp = (r.na + p.BM - 1) / p.BM;
     r.t0 = g < p.E ? 0 : tp;
     r.nt = g < p.E ? tp : (r.na + r.nb + p.BM - 1) / p.BM - tp;
   } else {
-    r.a0 = lo(o[0]);
-    r.na = max(0, lo(o[1]) - r.a0);
+    r.a0 = lo(g);
+    r.na = max(0, lo(g + 1) - r.a0);
     r.b0 = r.a0 + r.na;
     r.nb = 0;
     r.t0 = 0;
@@ -159,9 +144,6 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
   const int slot = blockIdx.x / kXcds;               // this block's item within XCD x's list
   if (tid == 0) found = Item{0, 0, 0, 0, 0, 0};
   if (tid == 0 && blockIdx.x == 0 && p.diag) *p.diag = 0;
-  int o[GPT][4];
-#pragma unroll
-  for (int q = 0; q < GPT; ++q) group_offsets_of(p, tid * GPT + q, o[q]);   // all loads in flight at once
   GroupRows gr[GPT];
   int s = 0;
 #pragma unroll
@@ -169,7 +151,7 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
     const int g = tid * GPT + q;
     gr[q] = GroupRows{0, 0, 0, 0, 0, 0};
     if (g < p.G) {
-      gr[q] = group_rows(p, g, o[q]);
+      gr[q] = group_rows(p, g);
       s += gr[q].nt * xcd_chunks(xcd_first_chunk(g, nch, x), nch);
     }
   }
@@ -272,17 +254,11 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
   // A staging: thread handles uint4 slots idx = tid + s*256 of the chunk
   uint4 stage[APT];
   const uint16_t* arow[APT];
-  {
-    int rn[APT];
-    size_t ar[APT];
 #pragma unroll
-    for (int s = 0; s < APT; ++s) rn[s] = it.row(min((threadIdx.x + s * kThreads) / VPR, rows - 1));
-    a_rows(plan.arows, plan.n_x, rn, ar);
-#pragma unroll
-    for (int s = 0; s < APT; ++s) {
-      const int idx = threadIdx.x + s * kThreads;
-      arow[s] = (idx < BM * VPR && idx / VPR < rows) ? A + ar[s] * K : nullptr;
-    }
+  for (int s = 0; s < APT; ++s) {
+    const int idx = threadIdx.x + s * kThreads;
+    const int r = idx / VPR;
+    arow[s] = (idx < BM * VPR && r < rows) ? A + a_row(plan.arows, plan.n_x, it.row(r)) * K : nullptr;
   }
   auto load_a = [&](int c) {
 #pragma unroll

@@ -370,6 +370,8 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
 // The K extent must be a multiple of kGemmBK (checked by the host).
 constexpr int kGemmBK = 32;
 constexpr int kGemmRowBytes = kGemmBK * 2;
+constexpr int kEpiPitch = 80;                 // bytes per row of a wave's 32x32 bf16 epilogue block (64 + 16 pad)
+constexpr int kEpiBytes = 32 * kEpiPitch;     // per wave
 
 template <int MI_, int NJ_, int WM_, int WN_, int STAGES_, int BPC_>
 struct GemmCfg {
@@ -592,6 +594,44 @@ struct TileMath {
       }
     }
   }
+
+  // The same epilogue through a wave-private LDS block of 32 rows x 32
+  // columns (pitch kEpiPitch bytes): a lane's four 8-byte pieces go to LDS,
+  // and the block leaves as 16-byte stores of 64-byte row segments, two
+  // instructions per block instead of four of scattered 8-byte pieces (the
+  // store count halves and each instruction covers 16 rows, not 32).
+  __device__ __forceinline__ void store_staged(const Item& it, int Ncols, uint16_t* __restrict__ out,
+                                               uint8_t* wst) const {
+    constexpr int OUTC = PHASE == 1 ? BN / 2 : BN;
+    constexpr int NO = PHASE == 1 ? NJ / 2 : NJ;
+    const int n0 = it.chunk * OUTC;
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int mb = 32 * (wm + WM * i);
+      if (mb >= it.rows) continue;                      // wave-uniform: no valid row in this slab
+#pragma unroll
+      for (int j = 0; j < NO; ++j) {
+        const int cb = n0 + (PHASE == 1 ? (BN / 2 / WN) * wn : (BN / WN) * wn) + 32 * j;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            v[t] = PHASE == 1 ? silu_mul(acc[i][j][4 * q + t], acc[i][NJ / 2 + j][4 * q + t]) : acc[i][j][4 * q + t];
+          *reinterpret_cast<uint2*>(wst + l32 * kEpiPitch + (8 * q + 4 * hk) * 2) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = 16 * h + (lane >> 2), c = 8 * (lane & 3);
+          const uint4 v = *reinterpret_cast<const uint4*>(wst + r * kEpiPitch + 2 * c);
+          if (mb + r < it.rows && cb + c < Ncols)
+            *reinterpret_cast<uint4*>(out + static_cast<size_t>(it.row(mb + r)) * Ncols + cb + c) = v;
+        }
+      }
+    }
+  }
 };
 
 __device__ __forceinline__ uint32_t lds_address(const uint8_t* smem) {
@@ -661,13 +701,14 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_b
   constexpr int NT = C::NT, STAGES = C::STAGES, BM = C::BM;
   constexpr int GPT = (kMaxGroups + NT - 1) / NT;
   constexpr int OUTC = PHASE == 1 ? C::BN / 2 : C::BN;
-  // dynamic LDS: the operand ring, then per group its first m-tile (fu) and
-  // its first row (gl), G + 1 entries each, so finding a tile needs no
-  // global load once DMAs are in flight (the compiler would wait for all of
-  // them before using such a load)
+  // dynamic LDS: the operand ring, each wave's epilogue block, then per group
+  // its first m-tile (fu) and its first row (gl), G + 1 entries each, so
+  // finding a tile needs no global load once DMAs are in flight (the compiler
+  // would wait for all of them before using such a load)
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   uint8_t* smem = dyn_lds;
-  int* fu = reinterpret_cast<int*>(dyn_lds + C::RING);
+  uint8_t* wst = dyn_lds + C::RING + (threadIdx.x >> 6) * kEpiBytes;   // this wave's epilogue block
+  int* fu = reinterpret_cast<int*>(dyn_lds + C::RING + C::NW * kEpiBytes);
   int* gl = fu + plan.G + 1;
   __shared__ int wsum[NT / kWave];
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
@@ -782,7 +823,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_b
         cslot = cslot + 1 == STAGES ? 0 : cslot + 1;
       }
     });
-    mm.store(cur, Ncols, out);
+    mm.store_staged(cur, Ncols, out, wst);
   }
 }
 
@@ -1124,7 +1165,7 @@ void launch_gemm_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, u
     hipLaunchKernelGGL((ffn_gemm_bf16<2, C>), dim3(item_grid(L.max_tiles, nch2)), dim3(C::NT), 0, stream, abuf, a.I,
                        wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, h);
   } else {
-    const size_t lds = C::RING + 8 * static_cast<size_t>(plan.G + 1);
+    const size_t lds = C::RING + C::NW * kEpiBytes + 8 * static_cast<size_t>(plan.G + 1);
     hipLaunchKernelGGL((ffn_gemm_persistent_bf16<1, C>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, x, a.d, wg,
                        wu, a.I, plan, abuf);
     hipLaunchKernelGGL((ffn_gemm_persistent_bf16<2, C>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, abuf, a.I,

@@ -761,16 +761,17 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_b
   const int share = (items + kXcds - 1) / kXcds;
   const int x = blockIdx.x % kXcds, slot0 = blockIdx.x / kXcds;
   const int base = x * share;
-  // my items: base + slot0 + r * per_xcd while inside this XCD's share
-  int n_my = 0;
-  if (slot0 < share) {
-    const int last = min(share, items - base);        // slots of this XCD
-    n_my = last > slot0 ? (last - slot0 + per_xcd - 1) / per_xcd : 0;
-  }
-  if (n_my == 0) return;
-
-  auto decode = [&](int r) -> Item {
-    const int want = base + slot0 + r * per_xcd;
+  // This XCD's L items run in rounds of per_xcd: my full items are
+  // base + slot0 + r * per_xcd for r < F.  A last, partly filled round would
+  // leave most blocks idle while a few finish a whole tile, so its rem items
+  // are cut into `pieces` row ranges of BM / pieces rows (whole 32-row slabs,
+  // at most one piece per block) and slot0 takes piece slot0 of that list.
+  const int L = max(0, min(share, items - base));
+  const int F = L / per_xcd, rem = L % per_xcd;
+  int pieces = 1;
+  while (rem > 0 && pieces < BM / 32 && rem * pieces * 2 <= per_xcd) pieces *= 2;
+  const int prow = BM / pieces;                        // rows per piece
+  auto item_of = [&](int want) -> Item {
     const int u = want / nch;                          // global m-tile index
     int lo = 0, hi = plan.G;                           // last g with fu[g] <= u
     while (hi - lo > 1) {
@@ -784,6 +785,19 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_b
     const int glo = gl[g], ghi = max(glo, gl[g + 1]);
     return contiguous_item(glo + mt * BM, min(BM, ghi - glo - mt * BM), expert_of_group(g, plan.E, plan.nseg), j);
   };
+  Item last_piece{};
+  bool has_piece = false;
+  if (slot0 < rem * pieces) {
+    const Item whole = item_of(base + F * per_xcd + slot0 / pieces);
+    const int off = (slot0 % pieces) * prow;
+    if (off < whole.rows) {                            // pieces past a partial tile's rows are empty
+      last_piece = contiguous_item(whole.row0 + off, min(prow, whole.rows - off), whole.expert, whole.chunk);
+      has_piece = true;
+    }
+  }
+  const int n_my = F + (has_piece ? 1 : 0);
+  if (n_my == 0) return;
+  auto decode = [&](int r) -> Item { return r < F ? item_of(base + slot0 + r * per_xcd) : last_piece; };
 
   const int nk = K / kGemmBK;
   const int total = n_my * nk;                         // K-steps of all my tiles, in order

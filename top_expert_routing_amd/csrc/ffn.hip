@@ -430,6 +430,15 @@ template <int PHASE, class C>
 struct TileLoader {
   const uint16_t* asrc[C::ADMA];
   const uint16_t* bsrc[C::BDMA];
+  int na;   // this wave's A instructions whose first row is valid (wave-uniform): 0..ADMA
+
+  // A DMA instructions wave `wave` issues per K-step for a tile of `rows` rows
+  __device__ __forceinline__ static int a_issued(int wave, int rows) {
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < C::ADMA; ++q) n += 16 * (wave + C::NW * q) < rows ? 1 : 0;
+    return n;
+  }
 
   __device__ __forceinline__ void init(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x, int K,
                                        const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int Ncols,
@@ -438,6 +447,7 @@ struct TileLoader {
     const int wave = threadIdx.x >> 6, lane = lane_id(), dr = lane >> 2;
     const int n0 = it.chunk * OUTC;
     const size_t eoff = static_cast<size_t>(it.expert) * Ncols * K;
+    na = __builtin_amdgcn_readfirstlane(a_issued(wave, it.rows));
     int rn[C::ADMA];
     size_t ar[C::ADMA];
 #pragma unroll
@@ -461,12 +471,17 @@ struct TileLoader {
     }
   }
 
-  // K-step kt of this tile into ring slot `slot` (lds0: LDS byte address of the ring)
+  // K-step kt of this tile into ring slot `slot` (lds0: LDS byte address of the ring).
+  // With skip_a, A instructions whose rows all lie past the tile's rows are
+  // not issued (their LDS rows keep stale data, whose results are never
+  // stored); the wave then has na + BDMA loads per step in flight.
+  template <bool skip_a = false>
   __device__ __forceinline__ void issue(int kt, int slot, uint32_t lds0) const {
     const uint32_t st = lds0 + slot * C::STAGE + (threadIdx.x >> 6) * 1024;
     const int k = kt * kGemmBK;
 #pragma unroll
-    for (int q = 0; q < C::ADMA; ++q) dma_b128(asrc[q] + k, st + q * C::NW * 1024);
+    for (int q = 0; q < C::ADMA; ++q)
+      if (!skip_a || q < na) dma_b128(asrc[q] + k, st + q * C::NW * 1024);
 #pragma unroll
     for (int q = 0; q < C::BDMA; ++q) dma_b128(bsrc[q] + k, st + C::A_BYTES + q * C::NW * 1024);
   }
@@ -658,16 +673,25 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const 
   const int nk = K / kGemmBK;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) ld.issue(s, s, lds0);
-  mm.with_nv([&](auto nvc) {
-    for (int kt = 0; kt < nk; ++kt) {
-      // K-step kt's loads are done once only the later steps' remain in flight
-      wait_ahead_barrier<C::ADMA + C::BDMA, STAGES - 2>(min(STAGES - 2, nk - 1 - kt));
-      // every wave is past step kt-1, so its buffer can be refilled
-      if (kt + STAGES - 1 < nk) ld.issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, lds0);
-      mm.template kstep_n<decltype(nvc)::value>(smem + (kt % STAGES) * C::STAGE);
-    }
-  });
+    if (s < nk) ld.template issue<true>(s, s, lds0);
+  // a wave issues na + BDMA loads per K-step (na wave-uniform), so its waits
+  // count that many per step still in flight
+  auto loop = [&](auto nac) {
+    constexpr int PER = decltype(nac)::value + C::BDMA;
+    mm.with_nv([&](auto nvc) {
+      for (int kt = 0; kt < nk; ++kt) {
+        // K-step kt's loads are done once only the later steps' remain in flight
+        wait_ahead_barrier<PER, STAGES - 2>(min(STAGES - 2, nk - 1 - kt));
+        // every wave is past step kt-1, so its buffer can be refilled
+        if (kt + STAGES - 1 < nk) ld.template issue<true>(kt + STAGES - 1, (kt + STAGES - 1) % STAGES, lds0);
+        mm.template kstep_n<decltype(nvc)::value>(smem + (kt % STAGES) * C::STAGE);
+      }
+    });
+  };
+  static_assert(C::ADMA <= 2, "per-wave A instruction counts 0..2");
+  if (ld.na == C::ADMA) loop(Int<C::ADMA>{});
+  else if (ld.na == 1) loop(Int<1>{});
+  else loop(Int<0>{});
   mm.store(it, Ncols, out);
 }
 

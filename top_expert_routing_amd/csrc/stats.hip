@@ -12,7 +12,9 @@
 //                layers, two block roles:
 //                * affinity tile: LDS-privatised co-activation counts of every
 //                  ordered slot pair of each token of the split whose first
-//                  expert falls in the tile's 16 rows; tile 0 also counts.
+//                  expert falls in the tile's rows (16, or as many as 32 KiB
+//                  of counters hold when the ids are split); tile 0 also
+//                  counts.
 //                  With one split the block writes the outputs; with several
 //                  it writes its partial tile, summed by stats_finish.
 //                * request chunk: LDS histograms of up to kReqChunk requests
@@ -32,7 +34,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kAffRows = 16;          // affinity rows per tile
+constexpr int kAffRows = 16;          // affinity rows per tile with a single split
 constexpr int kLdsInts = kAffRows * MOE_MAX_EXPERTS_DEV;   // 32 KiB of LDS counters per block
 constexpr int kReqChunk = 8;          // requests per histogram block
 constexpr int kIdsBuf = 4096;         // staged token ids per stage
@@ -58,9 +60,14 @@ int split_count(int L, int T, int k, int E) {
 
 StatsGeom geometry(int L, int T, int k, int E, int R, bool want_aff, bool want_req) {
   StatsGeom g;
-  g.rows_per_tile = want_aff ? (E < kAffRows ? E : kAffRows) : E;
-  g.aff_tiles = want_aff ? (E + g.rows_per_tile - 1) / g.rows_per_tile : 1;
+  // Every affinity block scans all ids of its split, so with several splits
+  // the tiles are as tall as the LDS counters allow (fewer redundant scans);
+  // a single split keeps 16-row tiles so a small batch still spreads over
+  // several blocks.
   g.splits = split_count(L, T, k, E);
+  const int tall = E < kLdsInts / E ? E : kLdsInts / E;
+  g.rows_per_tile = !want_aff ? E : g.splits > 1 ? tall : (E < kAffRows ? E : kAffRows);
+  g.aff_tiles = want_aff ? (E + g.rows_per_tile - 1) / g.rows_per_tile : 1;
   g.split_tokens = (T + g.splits - 1) / g.splits;
   g.rc = kLdsInts / E;
   if (g.rc > kReqChunk) g.rc = kReqChunk;

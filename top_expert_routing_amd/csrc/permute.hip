@@ -338,17 +338,81 @@ __global__ __launch_bounds__(1024) void permute_scan(PermCtx c, int n_shared, in
   for (int q = threadIdx.x; q <= n_shared; q += 1024) group_offsets[c.Gr + q] = c.Nr + q * c.T;
 }
 
+// SCAN = false: blk holds the scanned bases (permute_scan ran).  SCAN = true
+// (at most kMaxNbFused chunks): blk holds the raw per-chunk counts and every
+// block derives its bases itself - a group's base is the sum of all counts of
+// the groups before it, plus the group's counts in the chunks before this one
+// - so no scan launch is needed; block 0 writes group_offsets.
+constexpr int kMaxNbFused = 64;
+constexpr int kGroupsPerThread = kMaxRoutedGroups / kThreads;   // 4
+
+template <bool SCAN>
 __global__ __launch_bounds__(kThreads) void permute_scatter(PermCtx c, int n_shared, const int* blk, int* s2f,
-                                                            int* f2s, int* tok) {
+                                                            int* f2s, int* tok, int* group_offsets) {
   __shared__ int wcnt[kWaves * kMaxRoutedGroups];
+  __shared__ int wsum[kWaves];
   int* vw = wcnt;
   const int b = blockIdx.x;
   int grp[kIters];
   load_groups(c, b, grp);
   chunk_histogram(c, b, grp, vw);
-  __syncthreads();
-  for (int g = threadIdx.x; g < c.Gr; g += kThreads) {
-    int r = blk[g * c.nb + b];
+  // base[q]: this block's first sorted position of group tid * GPT + q
+  int base[kGroupsPerThread];
+  const int GPT = (c.Gr + kThreads - 1) / kThreads;
+  const int g0 = threadIdx.x * GPT;
+  if constexpr (SCAN) {
+    int tot[kGroupsPerThread], pre[kGroupsPerThread];
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < kGroupsPerThread; ++q) {
+      tot[q] = pre[q] = 0;
+      const int g = g0 + q;
+      if (q < GPT && g < c.Gr) {
+        // all of the group's chunk counts in flight at once (clamped addresses)
+        int v[kMaxNbFused];
+#pragma unroll
+        for (int i = 0; i < kMaxNbFused; ++i) v[i] = blk[g * c.nb + min(i, c.nb - 1)];
+#pragma unroll
+        for (int i = 0; i < kMaxNbFused; ++i) {
+          const int x = i < c.nb ? v[i] : 0;
+          tot[q] += x;
+          pre[q] += i < b ? x : 0;
+        }
+      }
+      sum += tot[q];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o, kWave);
+      if (lane_id() >= o) incl += y;
+    }
+    if (lane_id() == kWave - 1) wsum[threadIdx.x >> 6] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < (static_cast<int>(threadIdx.x) >> 6); ++w) run += wsum[w];
+#pragma unroll
+    for (int q = 0; q < kGroupsPerThread; ++q) {
+      const int g = g0 + q;
+      if (b == 0 && q < GPT && g < c.Gr) group_offsets[g] = run;
+      base[q] = run + pre[q];
+      run += tot[q];
+    }
+    if (b == 0)
+      for (int q = threadIdx.x; q <= n_shared; q += kThreads) group_offsets[c.Gr + q] = c.Nr + q * c.T;
+  } else {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kGroupsPerThread; ++q) {
+      const int g = g0 + q;
+      base[q] = q < GPT && g < c.Gr ? blk[g * c.nb + b] : 0;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kGroupsPerThread; ++q) {
+    const int g = g0 + q;
+    if (q >= GPT || g >= c.Gr) continue;
+    int r = base[q];
     for (int w = 0; w < kWaves; ++w) {
       const int cnt = vw[w * kMaxRoutedGroups + g];
       vw[w * kMaxRoutedGroups + g] = r;
@@ -423,9 +487,16 @@ hipError_t launch_permute(const PermuteArgs& a, void* workspace, hipStream_t str
   }
   int* blk = static_cast<int*>(workspace);
   hipLaunchKernelGGL(permute_count, dim3(c.nb), dim3(kThreads), 0, stream, c, blk);
-  hipLaunchKernelGGL(permute_scan, dim3(1), dim3(1024), 0, stream, c, a.n_shared, blk, a.group_offsets);
-  hipLaunchKernelGGL(permute_scatter, dim3(c.nb), dim3(kThreads), 0, stream, c, a.n_shared,
-                     static_cast<const int*>(blk), a.sorted_to_flat, a.flat_to_sorted, a.sorted_token);
+  if (c.nb <= kMaxNbFused) {
+    hipLaunchKernelGGL(permute_scatter<true>, dim3(c.nb), dim3(kThreads), 0, stream, c, a.n_shared,
+                       static_cast<const int*>(blk), a.sorted_to_flat, a.flat_to_sorted, a.sorted_token,
+                       a.group_offsets);
+  } else {
+    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(1024), 0, stream, c, a.n_shared, blk, a.group_offsets);
+    hipLaunchKernelGGL(permute_scatter<false>, dim3(c.nb), dim3(kThreads), 0, stream, c, a.n_shared,
+                       static_cast<const int*>(blk), a.sorted_to_flat, a.flat_to_sorted, a.sorted_token,
+                       a.group_offsets);
+  }
   if (a.x != nullptr && N > 0) {
     const int blocks = (N + kGatherRows - 1) / kGatherRows;
     hipLaunchKernelGGL(permute_gather, dim3(blocks), dim3(kThreads), 0, stream, static_cast<const uint4*>(a.x),

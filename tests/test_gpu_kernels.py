@@ -97,13 +97,15 @@ PERM_CASES = [
     (128, 64, 8, 0, 0, 2048, torch.bfloat16, "random"),
     (256, 64, 6, 2, 0, 64, torch.bfloat16, "zipf"),
     (600, 32, 8, 0, 0, 72, torch.float32, "random"),        # 4800 assignments: two chunks, ragged
-    (4160, 128, 4, 0, 64, 40, torch.bfloat16, "zipf"),     # priority segment, five chunks
+    (4160, 128, 4, 0, 64, 40, torch.bfloat16, "zipf"),     # priority segment, 17 chunks
     (5000, 16, 2, 1, 5000, 16, torch.bfloat16, "random"),  # every token in the priority segment
     (777, 8, 1, 0, 1, 24, torch.float32, "one_hot"),       # all tokens to one expert
     (1100, 512, 4, 3, 0, 8, torch.bfloat16, "random"),
     (2, 4, 4, 0, 0, 8, torch.float32, "random"),           # k = E
     (10, 1, 1, 0, 0, 8, torch.float32, "random"),          # E = 1
-    (9000, 8, 8, 0, 0, 0, None, "random"),                 # no row gather, k = E, 18 chunks
+    (9000, 8, 8, 0, 0, 0, None, "random"),                 # no row gather, k = E, 71 chunks: scan launch
+    (8192, 128, 8, 0, 0, 0, None, "random"),               # 64 chunks: the most the scatter scans itself
+    (8200, 16, 8, 2, 8, 0, None, "zipf"),                  # 65 chunks: scan launch, shared + priority
 ]
 
 

@@ -217,8 +217,12 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 //     previous chunk is multiplied.  One barrier per chunk.
 // Latency is hidden by the chunk-deep weight loads and the other resident
 // blocks (four per CU for tiles of <= 32 rows).
-constexpr int kDecodeKC = 256;                 // K per chunk (8 MFMA K-steps)
-constexpr int kDecodeStride = kDecodeKC + 8;   // bf16 per staged A row (pad 16 B)
+// K per chunk: 256 (8 MFMA K-steps) for tiles of <= 32 rows; the 64-row tile
+// (MF = 4) runs at two waves per SIMD and does better with 128 (measured:
+// DSv2-Lite-shaped t256 FFN 247.7 -> 244.4 us; OLMoE-shaped 159.7 -> 166.9
+// with 128 at MF = 2).
+template <int MF>
+constexpr int decode_kc() { return MF <= 2 ? 256 : 128; }
 constexpr int kDecodeWavesPerSimd = 4;
 
 template <int MF, int NFC, int PHASE>
@@ -228,6 +232,8 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
   constexpr int NF = PHASE == 1 ? 2 * NFC : NFC;
   constexpr int BN = kWaves * 16 * NFC;
   constexpr int BM = 16 * MF;
+  constexpr int kDecodeKC = decode_kc<MF>();
+  constexpr int kDecodeStride = kDecodeKC + 8;             // bf16 per staged A row (pad 16 B)
   constexpr int U = kDecodeKC / 32;
   constexpr int VPR = kDecodeKC / 8;                       // uint4 per staged row
   constexpr int APT = (BM * VPR + kThreads - 1) / kThreads; // uint4 staged per thread

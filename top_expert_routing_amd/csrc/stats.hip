@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void stats_finish(int L, int E, int R, St
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallLds = 14336;     // ints shared by affinity, request counts, offsets
 constexpr int kSmallIds = 4096;      // staged ids per chunk
-constexpr int kSmallSplit = 4;       // blocks per layer (each writes a quarter of the rows)
+constexpr int kSmallSplit = 8;       // blocks per layer (each writes an eighth of the rows)
 
 bool small_fits(int E, int R, bool want_aff, bool want_req, int T, int k) {
   const long long need = (want_aff ? 1LL * E * E : 0) + (want_req ? 1LL * R * E + R + 1 : 0);

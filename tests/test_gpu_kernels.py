@@ -169,6 +169,9 @@ FFN_CASES = [
     (50, 64, 8, 2, 0, 128, 88, "bf16", "zipf"),           # hot/cold, empty groups, shared
     (33, 4, 1, 0, 1, 64, 64, "bf16", "one_hot"),          # one expert takes everything
     (17, 128, 4, 0, 5, 72, 136, "bf16", "random"),        # priority segment, mostly empty groups
+    # groups of <= 4 rows on average: the split-K decode kernel
+    (40, 32, 2, 0, 0, 200, 136, "bf16", "zipf"),          # K tails in both phases, a hot group over two tiles
+    (24, 16, 2, 1, 6, 96, 160, "bf16", "random"),         # priority segment + shared expert
     # large groups with a priority segment: one persistent launch, per-XCD queues
     (600, 8, 2, 0, 50, 256, 320, "bf16", "random"),       # column tail in I (320 = 2*128 + 64)
     (900, 12, 3, 1, 100, 96, 160, "bf16", "zipf"),        # shared expert, hot/cold, small d

@@ -18,6 +18,8 @@
 // with 16-byte loads and no LDS round trip.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -75,6 +77,18 @@ __device__ __forceinline__ void a_rows(const int* arows, int n_x, const int (&n)
 #pragma unroll
     for (int i = 0; i < N; ++i) out[i] = static_cast<size_t>(n[i]);
   }
+}
+
+// Row-list entries of N sorted rows, loaded without a branch (from `dummy`, any
+// readable int, when there is no list) so that nothing waits for them before
+// a_row_of uses the values.
+template <int N>
+__device__ __forceinline__ void a_rows_raw(const int* arows, const int* dummy, const int (&n)[N], int (&raw)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) raw[i] = *(arows ? arows + n[i] : dummy);
+}
+__device__ __forceinline__ size_t a_row_of(const int* arows, int n_x, int n, int raw) {
+  return arows ? static_cast<size_t>(min(max(raw, 0), n_x - 1)) : static_cast<size_t>(n);
 }
 
 // A tile's rows: tile row r < split is sorted row row0 + r, a later one is
@@ -347,6 +361,157 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
       for (int t = 0; t < 4; ++t) v[t] = PHASE == 1 ? silu_mul(acc[i][j][t], acc[i][NFC + j][t]) : acc[i][j][t];
       *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
+  }
+}
+
+// ---- decode-sized tiles of one 16-row slab: K split over the waves ----------------
+// For the smallest groups (tiles of <= 16 rows, i.e. an average group of at
+// most 8 rows) an item is (m-tile, 16*NFC columns) and the block's four waves
+// split K into quarters: each streams its quarter of every weight row of the
+// item.  A block then moves a quarter of the bytes the kernel above moves per
+// item, and there are four times as many items, so the dispatcher keeps
+// refilling CUs whose blocks finish early.  On MI355X the blocks resident on
+// one CU are served very unevenly (the oldest first); with one round of large
+// items the last block on each CU streams alone at the end.  A plain streaming
+// kernel of the OLMoE shape moves 537 MB + 268 MB in 134 us with quarter-K
+// items against 148 us with whole-K items.  The token rows cost more here (each
+// item reads its rows' K range straight into registers, not shared through LDS
+// by 64 columns), which is why larger tiles keep the kernel above: at 16 to 32
+// rows per tile the extra token-row loads cost more than the balance gains.
+//   * B (weight rows) and A (token rows): a lane loads 16 bytes of one row per
+//     K-step straight into the v_mfma_f32_16x16x32_bf16 operands; all loads of a
+//     batch of U K-steps go out before its first MFMA.  Tile rows past the
+//     item's last row read that last row again; their outputs are not stored.
+//   * The row-list entries are loaded first and used only after the first
+//     batch's weight loads are out, so that round trip overlaps the weights'.
+//   * A last partial batch (K not a multiple of 4*32*U) zeroes what lies past
+//     the wave's K range.
+//   * The waves add their partial sums through LDS; each stores a share of the
+//     item's 16x16 output blocks (SwiGLU applied in phase 1).
+template <int NFC, int PHASE>
+__global__ __launch_bounds__(kThreads, kDecodeWavesPerSimd) void ffn_decode_splitk_bf16(
+    const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+    int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
+  constexpr int NF = PHASE == 1 ? 2 * NFC : NFC;
+  constexpr int BN = 16 * NFC;
+  constexpr int U = 4;
+  constexpr int KB = 32 * U;                          // K per batch
+  __shared__ f32x4 part[kWaves][NF][kWave];           // partial sums, 16 B per lane per block
+
+  const int nch = (Ncols + BN - 1) / BN;
+  const Item it = block_find_item(plan, nch);
+  if (it.rows == 0) return;
+  const int rows = it.rows, e = it.expert;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
+  const int l16 = lane & 15, q = lane >> 4;
+  const int col0 = it.chunk * BN;
+  const size_t wstride = static_cast<size_t>(Ncols) * K;
+  // this wave's K range: a quarter of K rounded up to whole K-steps
+  const int kq = (K + kWaves * 32 - 1) / (kWaves * 32) * 32;
+  const int k0 = min(K, wave * kq), k1 = min(K, k0 + kq);
+
+  const uint16_t* bp[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int n = min(col0 + (j % NFC) * 16 + l16, Ncols - 1);
+    const uint16_t* W = (PHASE == 1 && j >= NFC) ? W1 : W0;
+    bp[j] = W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n) * K + 8 * q;
+  }
+  f32x4 acc[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Batch of U K-steps from kc.  MASK: zero what lies at or past k1 (a lane's
+  // 8 values are all below k1 or all at or past it: K and k1 are multiples of
+  // 8), reading the row's first 16 bytes instead.
+  const uint16_t* ap = nullptr;
+  uint4 b[U][NF], a[U];
+  auto koff = [&](auto mask, int kk) { return (!decltype(mask)::value || kk + 8 * q < k1) ? kk : -8 * q; };
+  auto load_b = [&](auto mask, int kc) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ko = koff(mask, kc + 32 * u);
+#pragma unroll
+      for (int j = 0; j < NF; ++j) b[u][j] = *reinterpret_cast<const uint4*>(bp[j] + ko);
+    }
+  };
+  auto load_a = [&](auto mask, int kc) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = *reinterpret_cast<const uint4*>(ap + koff(mask, kc + 32 * u));
+  };
+  auto mma = [&](auto mask, int kc) {
+    if constexpr (decltype(mask)::value) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (kc + 32 * u + 8 * q >= k1) {
+#pragma unroll
+          for (int j = 0; j < NF; ++j) b[u][j] = make_uint4(0, 0, 0, 0);
+          a[u] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < NF; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b[u][j]),
+                                                         __builtin_bit_cast(bf16x8, a[u]), acc[j], 0, 0, 0);
+  };
+  // The sched_barriers keep every load of a batch ahead of its first MFMA
+  // (left alone, the scheduler interleaves them and waits after the first
+  // few).  The first batch always takes the masked form: with a branch
+  // between the row-list load and its use the compiler hoists the use and
+  // waits for the list before any weight load.
+  if (k0 < k1) {
+    const int rn[1] = {it.row(min(l16, rows - 1))};
+    int raw[1];
+    a_rows_raw(plan.arows, plan.offs, rn, raw);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(std::true_type{}, k0);
+    __builtin_amdgcn_sched_barrier(0);
+    ap = A + a_row_of(plan.arows, plan.n_x, rn[0], raw[0]) * K + 8 * q;
+    load_a(std::true_type{}, k0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(std::true_type{}, k0);
+    int kc = min(k0 + KB, k1);
+    for (; kc + KB <= k1; kc += KB) {
+      load_b(std::false_type{}, kc);
+      load_a(std::false_type{}, kc);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(std::false_type{}, kc);
+    }
+    if (kc < k1) {
+      load_b(std::true_type{}, kc);
+      load_a(std::true_type{}, kc);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(std::true_type{}, kc);
+    }
+  }
+
+  // Sum the four waves' partials.  The MFMA computes (weight rows) x (token
+  // rows)^T: in each 16x16 block a lane holds token row l16 and output columns
+  // 4q..4q+3, stored as one 8-byte write (Ncols % 8 == 0, so the four columns
+  // are all in range or all out).  Output block j goes to wave j % 4.
+#pragma unroll
+  for (int j = 0; j < NF; ++j) part[wave][j][lane] = acc[j];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NFC; ++j) {
+    if (j % kWaves != wave) continue;
+    const int n = col0 + j * 16 + 4 * q;
+    if (l16 >= rows || n >= Ncols) continue;
+    f32x4 g = part[0][j][lane], u = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) g += part[w][j][lane];
+    if constexpr (PHASE == 1) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) u += part[w][NFC + j][lane];
+    }
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = PHASE == 1 ? silu_mul(g[t], u[t]) : g[t];
+    uint16_t* orow = out + static_cast<size_t>(it.row(l16)) * Ncols;
+    *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   }
 }
 
@@ -1114,6 +1279,7 @@ enum class Path { kDecode, kGemm, kGemmLarge, kQueue, kF32 };
 
 struct Layout {
   Path path;
+  bool splitk;   // decode path: the split-K kernel (groups average <= kSplitKMaxAvg rows)
   int BM, max_tiles;
   size_t a_off, q_off, q_ints, total;
 };
@@ -1127,6 +1293,12 @@ bool queue_path_requested() {
   return v != nullptr && v[0] == '1';
 }
 
+// Up to this many rows per group on average the decode path runs the split-K
+// kernel (measured on DeepSeek-V2-Lite-shaped decode batches: 3.9 rows per
+// group 139 -> 133 us, 1.9 rows 112 -> 99 us; at 4.8 rows it is 2 % slower and
+// at 7.8 rows 6 % slower than the whole-K kernel).
+constexpr int kSplitKMaxAvg = 4;
+
 int pick_mf(int avg) {
   if (avg <= 8) return 1;
   if (avg <= 24) return 2;
@@ -1137,12 +1309,14 @@ Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16)
   Layout L;
   const int G = nseg * E + n_shared;
   const int avg = G > 0 ? n_rows / G : n_rows;
+  L.splitk = false;
   if (!bf16) {
     L.path = Path::kF32;
     L.BM = 16;
   } else if (avg <= 48 || d % kGemmBK != 0 || I % kGemmBK != 0) {
     L.path = Path::kDecode;
     L.BM = 16 * pick_mf(avg);
+    L.splitk = static_cast<long long>(n_rows) <= static_cast<long long>(kSplitKMaxAvg) * G;
   } else {
     // With a priority segment both phases could run in one persistent launch
     // (ffn_queue_bf16); that path stays off unless LIBMOE_FFN_QUEUE=1 is set:
@@ -1174,6 +1348,23 @@ Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16)
 // per lane).
 constexpr int kDecodeNfc1 = 1;
 constexpr int kDecodeNfc2 = 2;
+
+// Groups of at most kSplitKMaxAvg rows on average: the split-K kernel, 16
+// columns per item in phase 1 and 32 in phase 2 (tiles of 16 rows).
+void launch_decode_splitk_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, uint16_t* abuf,
+                               hipStream_t stream) {
+  constexpr int NFC1 = 1, NFC2 = 2;
+  const int nch1 = (a.I + 16 * NFC1 - 1) / (16 * NFC1), nch2 = (a.d + 16 * NFC2 - 1) / (16 * NFC2);
+  hipLaunchKernelGGL((ffn_decode_splitk_bf16<NFC1, 1>), dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0,
+                     stream, static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
+                     static_cast<const uint16_t*>(a.w_up), a.I, plan, abuf);
+  PlanArgs plan2 = plan;
+  plan2.diag = nullptr;
+  plan2.arows = nullptr;
+  hipLaunchKernelGGL((ffn_decode_splitk_bf16<NFC2, 2>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
+                     stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
+                     static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted));
+}
 
 template <int MF>
 void launch_decode_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, uint16_t* abuf,
@@ -1288,7 +1479,10 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
     case Path::kDecode: {
       uint16_t* abuf = reinterpret_cast<uint16_t*>(ws + L.a_off);
       switch (L.BM / 16) {
-        case 1: launch_decode_bf16<1>(a, L, plan, abuf, stream); break;
+        case 1:
+          if (L.splitk) launch_decode_splitk_bf16(a, L, plan, abuf, stream);
+          else launch_decode_bf16<1>(a, L, plan, abuf, stream);
+          break;
         case 2: launch_decode_bf16<2>(a, L, plan, abuf, stream); break;
         default: launch_decode_bf16<4>(a, L, plan, abuf, stream); break;
       }

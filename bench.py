@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--workload", default="olmoe_decode")
     ap.add_argument("--weight-copies", type=int, default=0,
                     help="expert-weight copies to rotate over (0: enough to exceed 3 GiB)")
+    ap.add_argument("--router", action="store_true",
+                    help="put the router projection (x . W_r^T, seeded N(0, 0.02^2) weights) in front of the "
+                         "gate; the gate then routes on its logits")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle leg")
     ap.add_argument("--json-out", default="", help="also append the JSON line to this file")
@@ -129,8 +132,9 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv:
     print(json.dumps(rec["workloads"][workload]))
 
 
-def cpu_baseline(wl, budget_s: float):
-    """Time the CPU oracle (as it stands) on a bounded sample of the workload."""
+def cpu_baseline(wl, budget_s: float, w_router=None):
+    """Time the CPU oracle (as it stands) on a bounded sample of the workload
+    (with `w_router`, the sample's logits come from the oracle's router)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -149,7 +153,11 @@ def cpu_baseline(wl, budget_s: float):
     t0 = time.perf_counter()
     done = 0
     passes = 0
+    wr = None if w_router is None else host(w_router)
     while True:
+        if wr is not None:
+            logits = logits.copy()
+            logits[:n] = O.router(x[:n], wr, s.dtype)
         O.moe_layer(logits, x, wg, wu, wd, s.k, s.dtype, n_shared=s.S, n_priority=s.n_priority, tokens=toks)
         ids, _ = O.gate(logits[:n], s.k)
         O.stats(ids[None], s.E, np.arange(n + 1, dtype=np.int32))
@@ -161,7 +169,8 @@ def cpu_baseline(wl, budget_s: float):
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n} of {s.T} tokens, whole layer path (gate, permute, FFN on their rows, "
-                      f"combine) plus their statistics, {passes} pass(es) in {el:.1f} s"}
+                      f"combine) plus their statistics{', router first' if wr is not None else ''}, "
+                      f"{passes} pass(es) in {el:.1f} s"}
 
 
 def main():
@@ -209,14 +218,18 @@ def main():
     # the gate writes the routing layer's ids straight into layer 0 of the
     # statistics stack
     stats_ids = torch.empty((s.stats_layers, s.T, s.k), dtype=torch.int32, device=dev)
+    w_router = None
+    if args.router:
+        g = torch.Generator().manual_seed(1234)
+        w_router = (torch.randn((s.E, s.d), generator=g) * 0.02).to(wl.torch_dtype).to(dev)
     layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, wl.w_gate, wl.w_up, wl.w_down,
                          n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize),
                          stats_layers=s.stats_layers, req_offsets=wl.req_offsets, device=dev,
-                         topk_ids=stats_ids[0])
+                         topk_ids=stats_ids[0], w_router=w_router)
     for l in range(1, s.stats_layers):      # the other layers' ids, produced before timing
         moe.gate(wl.stats_logits[l].contiguous(), s.k, True, stats_ids[l],
                  torch.empty((s.T, s.k), device=dev))
-    # One stream, in path order: gate, statistics (they need only the gate's
+    # One stream, in path order: (router,) gate, statistics (they need only the gate's
     # ids), permute, FFN, combine.  (A second stream for the statistics costs
     # two cross-queue waits per step, more than the statistics themselves.)
     stream = torch.cuda.Stream(dev)
@@ -225,8 +238,8 @@ def main():
         layer.w_gate, layer.w_up, layer.w_down = wg, wu, wd
         call_sets.append(layer.bound_calls(wl.logits, wl.x, stats_ids, stream.cuda_stream))
     names = [c[0] for c in call_sets[0]]
-    order = [names.index("moe_gate")] + ([names.index("moe_stats")] if "moe_stats" in names else []) + \
-        [j for j, n in enumerate(names) if n not in ("moe_gate", "moe_stats")]
+    first = [names.index(n) for n in ("moe_router", "moe_gate", "moe_stats") if n in names]
+    order = first + [j for j in range(len(names)) if j not in first]
 
     def step(i, ev=None):
         """One layer step on `stream`."""
@@ -324,14 +337,14 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
         "config": {"workload": args.workload, "T": s.T, "E": s.E, "k": s.k, "n_shared": s.S, "d": s.d,
                    "I": s.I, "n_priority": s.n_priority, "stats_layers": s.stats_layers,
-                   "weight_copies": copies, "union": union},
+                   "weight_copies": copies, "union": union, "router": bool(args.router)},
         "roofline": roof,
         "per_call_us": {n: round(v * 1e3, 2) for n, v in per_call.items()},
         "timing": "eager launches" if args.eager else
                   f"captured HIP graphs of {copies} consecutive steps (one per weight copy) replayed",
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, w_router)
     line = json.dumps(out)
     print(line, flush=True)
     if args.json_out:

@@ -73,6 +73,25 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 #define MOE_MAX_SHARED 256
 
 /*
+ * moe_router - router projection in front of the gate: one fp32 score per
+ * routed expert and token, logits[t][e] = sum_i x[t][i] * w_router[e][i].
+ * (ELDR page, "Core idea / structure / operation": the gate is standard
+ * top-k gating over per-expert router scores; the pages do not spell the
+ * router out, and it is read as a bias-free linear map of the hidden state.)
+ *
+ *   x         [T][d] in dtype (bf16 or fp32), read only.
+ *   w_router  [E][d] in dtype, read only ([out][in] layout, like the experts).
+ *   logits    [T][E] fp32, written; the input of moe_gate.
+ *   Accumulation is fp32 in an unspecified order.  bf16 products are exact in
+ *   fp32, so an element is within d * 2^-24 * sum_i |x[t][i] w_router[e][i]|
+ *   of the exact dot product (fp32 inputs: (d + 1) * 2^-24 * the same sum).
+ *   Requires T >= 0, 1 <= E <= 512, d a positive multiple of 8; x, w_router
+ *   and logits 16-byte aligned.
+ */
+moe_status moe_router(const void* x, const void* w_router, int32_t T, int32_t d, int32_t E,
+                      moe_dtype dtype, float* logits, hipStream_t stream);
+
+/*
  * moe_gate - softmax top-k gate over fp32 router logits.
  * (ELDR page, "Core idea / structure / operation": standard top-k gating.)
  *

@@ -43,6 +43,8 @@ Readings where the pages are silent (each is listed in the design notes):
      gate output); counts = column sums; union = experts with a nonzero count;
      affinity = M^T M; per-request counts over token ranges; idf = ln(R/df)
      (0 where df = 0); signature = request count * idf.
+  R5 router (in front of the gate): logits = x . W_r^T, a bias-free linear map
+     of the hidden state, W_r [E][d].
 
 Parity pins: see tests/test_oracle_*.py - every function here is checked against
 closed forms, library routines, invariants and brute force, not against itself.
@@ -79,6 +81,21 @@ def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
     nan = np.isnan(f)
     out[nan] = 0x7FC0
     return out
+
+
+# --------------------------------------------------------------------------
+# step 0: router projection (in front of the gate)
+# --------------------------------------------------------------------------
+def router(x: np.ndarray, w_router: np.ndarray, dtype: str) -> np.ndarray:
+    """Router scores logits[t][e] = sum_i x[t][i] * w_router[e][i], in float64.
+
+    ELDR page, "Core idea / structure / operation": the gate is standard top-k
+    gating over per-expert router scores of each token.  The pages do not spell
+    the router out; reading R5 takes it as a bias-free linear map of the hidden
+    state, weights [E][d] in the [out][in] layout.  `x` and `w_router` hold
+    bf16 bit patterns (dtype "bf16") or float32 values ("f32").
+    """
+    return to_f64(x, dtype) @ to_f64(w_router, dtype).T
 
 
 # --------------------------------------------------------------------------

@@ -26,9 +26,9 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:moe_status|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_five_calls():
-    assert _declared() == sorted(["moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_stats",
-                                  "moe_status_string"])
+def test_header_declares_the_calls():
+    assert _declared() == sorted(["moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine",
+                                  "moe_stats", "moe_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -41,6 +41,22 @@ def test_status_strings(lib):
     for code, name in _lib.STATUS_NAMES.items():
         assert lib.moe_status_string(code).decode() == name
     assert lib.moe_status_string(99).decode() == "MOE_ERR_UNKNOWN"
+
+
+def test_router_validation(lib):
+    f = lib.moe_router
+    assert f(FAKE, FAKE, -1, 64, 8, _lib.MOE_BF16, FAKE, None) == INV
+    assert f(FAKE, FAKE, 4, 64, 0, _lib.MOE_BF16, FAKE, None) == INV
+    assert f(FAKE, FAKE, 4, 0, 8, _lib.MOE_BF16, FAKE, None) == INV
+    assert f(FAKE, FAKE, 4, 60, 8, _lib.MOE_BF16, FAKE, None) == UNS          # d not a multiple of 8
+    assert f(FAKE, FAKE, 4, 64, 513, _lib.MOE_BF16, FAKE, None) == UNS        # E > 512
+    assert f(FAKE, FAKE, 4, 64, 8, 7, FAKE, None) == UNS                      # unknown dtype
+    assert f(FAKE, FAKE, 1 << 20, 1 << 12, 8, _lib.MOE_BF16, FAKE, None) == UNS   # T*d overflows int32
+    assert f(None, FAKE, 4, 64, 8, _lib.MOE_BF16, FAKE, None) == INV
+    assert f(FAKE, None, 4, 64, 8, _lib.MOE_BF16, FAKE, None) == INV
+    assert f(FAKE, FAKE, 4, 64, 8, _lib.MOE_BF16, None, None) == INV
+    assert f(FAKE + 4, FAKE, 4, 64, 8, _lib.MOE_BF16, FAKE, None) == INV      # misaligned
+    assert f(None, None, 0, 64, 8, _lib.MOE_BF16, None, None) == 0            # T = 0: nothing to do
 
 
 def test_gate_validation(lib):

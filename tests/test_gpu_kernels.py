@@ -32,6 +32,50 @@ def _poison(shape, dtype):
     return t
 
 
+# ------------------------------------------------------------------ router
+ROUTER_CASES = [
+    # (T, d, E, dtype)
+    (1, 8, 1, "bf16"),            # one token, one expert, a single partial K-step
+    (37, 136, 70, "bf16"),        # token tail, K tail (136 = 128 + 8), experts past one 64-wide tile
+    (128, 2048, 64, "bf16"),      # OLMoE decode shape
+    (300, 256, 512, "bf16"),      # E = 512: eight expert tiles
+    (4100, 264, 500, "bf16"),     # >= 1024 tiles of 32 tokens: the two-slab tile, with T, d and E tails
+    (64, 128, 8, "f32"),          # the tiny config's shape
+    (33, 72, 13, "f32"),          # fp32 tails
+]
+
+
+@pytest.mark.parametrize("T,d,E,dtype", ROUTER_CASES)
+def test_router_parity(T, d, E, dtype):
+    announce(f"router T={T} d={d} E={E} {dtype}")
+    g = torch.Generator().manual_seed(T * 7 + d + E)
+    xf = torch.randn((T, d), generator=g, dtype=torch.float64)
+    wf = torch.randn((E, d), generator=g, dtype=torch.float64) * 0.05
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x, w = xf.to(tdt), wf.to(tdt)
+    ref = O.router(np_of(x), np_of(w), dtype)
+    # fp32 accumulation of d products (exact for bf16 inputs, one rounding each
+    # for fp32 inputs), in any order: |err| <= (d + 1) * 2^-24 * sum_i |x_i w_i|
+    bound = (d + 1) * 2.0 ** -24 * (np.abs(O.to_f64(np_of(x), dtype)) @ np.abs(O.to_f64(np_of(w), dtype)).T)
+    logits = _poison((T, E), torch.float32)
+    moe.router(x.to(DEV), w.to(DEV), logits)
+    torch.cuda.synchronize()
+    got = np_of(logits).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= bound + 1e-30), float(np.max(np.abs(got - ref) - bound))
+
+
+def test_router_then_gate_matches_oracle_on_gpu_logits():
+    # the gate's ids are decided on the logits the GPU produced (both sides in fp32)
+    wl = workloads.custom(T=96, E=64, k=8, d=2048, I=64, dtype="bf16", seed=5, device=DEV, w_std=0.08)
+    w_r = (torch.randn((64, 2048), generator=torch.Generator().manual_seed(9)) * 0.02).to(torch.bfloat16).to(DEV)
+    logits = moe.router(wl.x, w_r)
+    ids, wts = moe.gate(logits, 8)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = O.gate(np_of(logits), 8)
+    np.testing.assert_array_equal(np_of(ids), ids_ref)
+    assert np.abs(np_of(wts).astype(np.float64) - w_ref).max() <= GATE_W_ATOL
+
+
 # ------------------------------------------------------------------ gate
 GATE_CASES = [
     # (T, E, k, renormalize, kind)

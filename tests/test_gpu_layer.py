@@ -87,3 +87,32 @@ def test_layer_parity(name):
     announce(f"layer {name}: h err {h_err:.2e}, y err {y_err:.2e}, union {np_of(layer.stats_out['union_size'])}")
     assert h_err <= TOL[s.dtype], h_err
     assert y_err <= TOL[s.dtype], y_err
+
+
+@pytest.mark.parametrize("name", ["tiny", "olmoe_decode"])
+def test_layer_with_router_parity(name):
+    """The layer with the router projection in front of the gate: logits within
+    the fp32-accumulation bound of the oracle's router, then the rest of the path
+    decided on the GPU's logits (top-k ids in the same precision on both sides)."""
+    announce(f"layer {name} with router")
+    wl = workloads.make(name, DEV)
+    s = wl.spec
+    g = torch.Generator().manual_seed(77)
+    w_r = (torch.randn((s.E, s.d), generator=g) * 0.02).to(wl.torch_dtype).to(DEV)
+    layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, wl.w_gate, wl.w_up, wl.w_down,
+                         n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize), device=DEV,
+                         w_router=w_r)
+    layer.forward(None, wl.x)
+    torch.cuda.synchronize()
+    x, wr = np_of(wl.x), np_of(w_r)
+    lg_ref = O.router(x, wr, s.dtype)
+    bound = (s.d + 1) * 2.0 ** -24 * (np.abs(O.to_f64(x, s.dtype)) @ np.abs(O.to_f64(wr, s.dtype)).T)
+    logits = np_of(layer.logits)
+    assert np.all(np.abs(logits.astype(np.float64) - lg_ref) <= bound + 1e-30)
+    ids_ref, _ = O.gate(logits, s.k, bool(s.renormalize))
+    np.testing.assert_array_equal(np_of(layer.topk_ids), ids_ref)
+    toks = _sample_tokens(s.T, s.n_priority)
+    ref = O.moe_layer(logits, x, np_of(wl.w_gate), np_of(wl.w_up), np_of(wl.w_down), s.k, s.dtype,
+                      n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize), tokens=toks)
+    y_err = rel_max_err(f64_of(layer.y[torch.from_numpy(toks).to(DEV)]), ref["y"])
+    assert y_err <= TOL[s.dtype], y_err

@@ -12,9 +12,10 @@ import tests.test_oracle_gate as TG
 import tests.test_oracle_permute as TP
 import tests.test_oracle_ffn_combine as TF
 import tests.test_oracle_stats as TS
+import tests.test_oracle_router as TR
 
 _orig = {name: getattr(O, name) for name in ("gate", "permute", "grouped_ffn", "combine", "stats",
-                                              "silu_product", "assignment_groups")}
+                                              "silu_product", "assignment_groups", "router")}
 
 
 def _gate_unstable(logits, k, renormalize=True):
@@ -113,6 +114,16 @@ def _stats_union_off_by_one(topk_ids, E, req_offsets=None, idf=None):
     return st
 
 
+def _router_transposed(x, w_router, dtype):
+    # W_r read as [d][E]: the hidden index runs over W_r's rows
+    w = O.to_f64(w_router, dtype)
+    return O.to_f64(x, dtype) @ np.resize(w.T, w.shape)
+
+
+def _router_drops_last_term(x, w_router, dtype):
+    return O.to_f64(x, dtype)[:, :-1] @ O.to_f64(w_router, dtype)[:, :-1].T
+
+
 def _run_pins(pins):
     failures = 0
     for fn, args in pins:
@@ -129,7 +140,12 @@ def _gate_cases():
     return [(TG.test_gate_golden, (c,)) for c in TG._golden_cases()] + [(TG.test_gate_bruteforce_tiny_E, ())]
 
 
+_router_pins = lambda: [(TR.test_router_unit_rows_select_weight_columns, ()),
+                        (TR.test_router_hand_computed_case, ())]
+
 MUTANTS = {
+    "router_weights_transposed": ("router", _router_transposed, _router_pins),
+    "router_drops_last_hidden_term": ("router", _router_drops_last_term, _router_pins),
     "gate_ties_to_higher_id": ("gate", _gate_unstable, _gate_cases),
     "gate_nan_as_plus_inf": ("gate", _gate_nan_high, _gate_cases),
     "gate_skips_renormalisation": ("gate", _gate_no_renorm,

@@ -1,10 +1,10 @@
 """libmoe bindings: one MoE layer's expert path on MI355X (gfx950) HIP kernels.
 
-The five calls mirror the C ABI in include/libmoe.h.  torch supplies device
+The calls mirror the C ABI in include/libmoe.h.  torch supplies device
 memory and streams only; all computation runs in libmoe.so.  Importing this
 package does not load the library; the first call does, and raises ImportError
 if libmoe.so has not been built.
 """
 from ._lib import MoeError, load, EXPORTS  # noqa: F401
-from .api import (gate, permute, grouped_ffn, combine, stats, MoeLayer,  # noqa: F401
+from .api import (router, gate, permute, grouped_ffn, combine, stats, MoeLayer,  # noqa: F401
                   permute_workspace_bytes, ffn_workspace_bytes, stats_workspace_bytes)

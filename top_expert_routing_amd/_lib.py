@@ -14,7 +14,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
                 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
 
 # every symbol include/libmoe.h declares
-EXPORTS = ("moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_stats",
+EXPORTS = ("moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_stats",
            "moe_status_string")
 
 _p = ctypes.c_void_p
@@ -22,6 +22,7 @@ _i32 = ctypes.c_int32
 _sz = ctypes.POINTER(ctypes.c_size_t)
 
 SIGNATURES = {
+    "moe_router": [_p, _p, _i32, _i32, _i32, _i32, _p, _p],
     "moe_gate": [_p, _i32, _i32, _i32, _i32, _p, _p, _p],
     "moe_permute": [_p, _i32, _i32, _i32, _i32, _i32, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _sz, _p],
     "moe_grouped_ffn": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _sz, _p],

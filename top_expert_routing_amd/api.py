@@ -1,4 +1,5 @@
-"""Thin torch wrappers over the five libmoe calls.
+"""Thin torch wrappers over the libmoe calls (router projection, gate,
+permutation, grouped FFN, combine, statistics).
 
 Argument marshalling only: shapes, dtypes and contiguity are checked, outputs
 and workspaces are allocated with torch on the input's device, and the call is
@@ -48,6 +49,24 @@ def _workspace(fn, args_before_ws, dev) -> torch.Tensor:
     n = ctypes.c_size_t(0)
     check(fn.__name__, fn(*args_before_ws, None, ctypes.byref(n), None))
     return torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
+
+
+def router(x: torch.Tensor, w_router: torch.Tensor, logits: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 router logits [T][E] = x [T][d] . w_router [E][d]^T (bf16 or fp32 inputs)."""
+    _need(x, "x", None, 2)
+    _need(w_router, "w_router", x.dtype, 2)
+    T, d = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != d:
+        raise ValueError("w_router must be [E][d]")
+    dev = x.device
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    _need(logits, "logits", torch.float32, 2)
+    lib = _lib.load()
+    check("moe_router", lib.moe_router(_ptr(x), _ptr(w_router), T, d, E, _dtype_code(x), _ptr(logits),
+                                       _stream(dev)))
+    return logits
 
 
 def gate(logits: torch.Tensor, k: int, renormalize: bool = True,
@@ -226,14 +245,18 @@ class MoeLayer:
 
     `forward()` enqueues gate -> permute -> grouped FFN -> combine and, when
     `stats_ids` is given, the statistics over that [L][T][k] id stack (the
-    routing layer's own ids are written into stats_ids[0] by the gate).
+    routing layer's own ids are written into stats_ids[0] by the gate).  With
+    `w_router` ([E][d], the input dtype) the router projection runs first and
+    the gate reads its logits; `forward` then ignores the logits argument.
     Nothing is allocated per call.
     """
 
     def __init__(self, E, k, d, I, T, dtype, w_gate, w_up, w_down, n_shared=0, n_priority=0,
                  renormalize=True, stats_layers=0, req_offsets=None, device="cuda", topk_ids=None,
-                 fused_gather=True):
+                 fused_gather=True, w_router=None):
         dev = torch.device(device)
+        self.w_router = w_router
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev) if w_router is not None else None
         self.E, self.k, self.d, self.I, self.T = E, k, d, I, T
         self.S, self.P = n_shared, n_priority
         self.nseg = 2 if n_priority > 0 else 1
@@ -269,6 +292,9 @@ class MoeLayer:
             self.stats_ws = torch.empty(max(stats_workspace_bytes(stats_layers, T, k, E, R), 256),
                                         dtype=torch.uint8, device=dev)
 
+    def route(self, x):
+        return router(x, self.w_router, self.logits)
+
     def gate(self, logits):
         return gate(logits, self.k, self.renormalize, self.topk_ids, self.topk_w)
 
@@ -294,7 +320,8 @@ class MoeLayer:
 
         Returns a list of (name, fn, args) whose arguments are plain integers,
         so a timing loop pays only the ctypes call per step.  Each entry is one
-        of the five libmoe calls, in path order.  `stats_stream` (a raw stream
+        of the libmoe calls, in path order (the router first when the layer has
+        router weights; the gate then reads the router's logits).  `stats_stream` (a raw stream
         handle) puts the statistics call on its own stream; the caller orders it
         after the gate.
         """
@@ -306,7 +333,12 @@ class MoeLayer:
         fused = self.fused_gather
         n_perm = ctypes.c_size_t(self.perm_ws.numel())
         n_ffn = ctypes.c_size_t(self.ffn_ws.numel())
-        calls = [
+        calls = []
+        if self.w_router is not None:
+            logits = self.logits
+            calls.append(("moe_router", lib.moe_router, (x.data_ptr(), self.w_router.data_ptr(), T, self.d, E, dt,
+                                                         logits.data_ptr(), st)))
+        calls += [
             ("moe_gate", lib.moe_gate, (logits.data_ptr(), T, E, k, int(bool(self.renormalize)),
                                         self.topk_ids.data_ptr(), self.topk_w.data_ptr(), st)),
             ("moe_permute", lib.moe_permute, (self.topk_ids.data_ptr(), T, E, k, self.S, self.P,
@@ -348,6 +380,8 @@ class MoeLayer:
         """Enqueue the layer on the current stream.  With `stats_stream` (a
         torch stream) the statistics run there, concurrently with the permute /
         FFN / combine chain; the current stream waits for them at the end."""
+        if self.w_router is not None:
+            logits = self.route(x)
         self.gate(logits)
         side = stats_ids is not None and self.stats_out is not None
         if side and stats_stream is not None:

@@ -62,6 +62,19 @@ moe_status moe_gate(const float* logits, int32_t T, int32_t E, int32_t k, int32_
   return hip_status(moe::launch_gate(logits, T, E, k, renormalize, topk_ids, topk_w, stream));
 }
 
+moe_status moe_router(const void* x, const void* w_router, int32_t T, int32_t d, int32_t E, moe_dtype dtype,
+                      float* logits, hipStream_t stream) {
+  if (T < 0 || E < 1 || d < 1) return MOE_ERR_INVALID_ARG;
+  if (!known_dtype(dtype) || E > MOE_MAX_EXPERTS || d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!fits_int(static_cast<long long>(T) * d) || !fits_int(static_cast<long long>(T) * E) ||
+      !fits_int(static_cast<long long>(E) * d))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !logits) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_router(x, w_router, T, d, E, dtype == MOE_BF16 ? 1 : 0, logits, stream));
+}
+
 moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k, int32_t n_shared,
                        int32_t n_priority, const void* x, moe_dtype dtype, int32_t d, int32_t* group_offsets,
                        int32_t* sorted_to_flat, int32_t* flat_to_sorted, int32_t* sorted_token, void* x_sorted,

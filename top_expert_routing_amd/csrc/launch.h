@@ -12,6 +12,10 @@ namespace moe {
 hipError_t launch_gate(const float* logits, int T, int E, int k, int renormalize, int* topk_ids,
                        float* topk_w, hipStream_t stream);
 
+// ---- router projection -------------------------------------------------------
+hipError_t launch_router(const void* x, const void* w_router, int T, int d, int E, int bf16, float* logits,
+                         hipStream_t stream);
+
 // ---- permutation -----------------------------------------------------------
 struct PermuteArgs {
   const int* topk_ids;

@@ -389,3 +389,27 @@ def test_grouped_ffn_queue_path():
             test_grouped_ffn_parity(*case)
     finally:
         os.environ.pop("LIBMOE_FFN_QUEUE", None)
+
+
+# ------------------------------------------------------------------ KV-block signature recording
+def test_kv_block_recording_and_host_staging():
+    """Expert counts per 16-token KV block over the Qwen3-shaped 8-layer id stack,
+    staged into pinned host memory: equal to the oracle's per-block counts, and
+    a request's counts are the sum of its blocks' (the blocks tile the request)."""
+    wl = workloads.make("qwen3_prefill", DEV, with_weights=False)
+    s = wl.spec
+    announce("kv-block recording")
+    ids = torch.stack([moe.gate(wl.stats_logits[l].contiguous(), s.k)[0] for l in range(s.stats_layers)])
+    block = 16
+    boffs = torch.arange(0, s.T + 1, block, dtype=torch.int32, device=DEV)
+    o = moe.stats(ids.contiguous(), s.E, boffs, affinity=False, signature=False)
+    host = torch.empty(o["req_counts"].shape, dtype=torch.int32, pin_memory=True)
+    host.copy_(o["req_counts"], non_blocking=True)
+    torch.cuda.synchronize()
+    ids_np = np_of(ids)
+    ref = O.stats(ids_np, s.E, np_of(boffs))
+    np.testing.assert_array_equal(host.numpy(), ref["req_counts"])
+    req = O.stats(ids_np, s.E, np_of(wl.req_offsets))["req_counts"]
+    ro = np_of(wl.req_offsets)
+    summed = np.stack([host.numpy()[ro[r] // block:ro[r + 1] // block].sum(axis=0) for r in range(len(ro) - 1)])
+    np.testing.assert_array_equal(summed, req)

@@ -176,13 +176,14 @@ def cpu_baseline(wl, budget_s: float, w_router=None):
                       f"{passes} pass(es) in {el:.1f} s"}
 
 
-def signature_recording(s, stats_ids, req_offsets, stream, K, dev, block=16):
+def signature_recording(s, stats_ids, req_offsets, stream, K, dev, logits_stack=None, block=16):
     """Per-KV-block expert counts over the statistics layer stack (moe_stats
     with block offsets) and their copy into pinned host memory, timed with HIP
     events on `stream` over K repetitions.  The ELDR page ("Overhead"
     paragraph of its evidence section) times the same two steps on MI300X:
     0.48 ms for the on-GPU scatter and 0.21 ms for the signature's D2H staging
-    per request."""
+    per request.  With `logits_stack` ([L][T][E]) it also times the continuous
+    (softmax-probability) request signature over the same layers."""
     import torch
     import top_expert_routing_amd as moe
     offs = list(range(0, s.T, block)) + [s.T]
@@ -208,9 +209,23 @@ def signature_recording(s, stats_ids, req_offsets, stream, K, dev, block=16):
     d2h = sum(e[1].elapsed_time(e[2]) for e in ev) / K * 1e3
     if not torch.equal(host, out["req_counts"].cpu()):
         raise RuntimeError("staged block counts differ from the device copy")
+    # the continuous alternative the page compares against: per-request sums of
+    # softmax probabilities from the recorded layers' logits
+    prob = None
+    if logits_stack is not None and req_offsets is not None:
+        psig = torch.empty((R, L, s.E), dtype=torch.float32, device=dev)
+        pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        with torch.cuda.stream(stream):
+            moe.prob_signature(logits_stack, req_offsets, psig)
+            for i in range(K):
+                pe[i][0].record(stream)
+                moe.prob_signature(logits_stack, req_offsets, psig)
+                pe[i][1].record(stream)
+        torch.cuda.synchronize()
+        prob = round(sum(a.elapsed_time(b) for a, b in pe) / K * 1e3, 2)
     return {"kv_block_tokens": block, "blocks": nb, "requests": R, "layers": L,
             "record_us": round(rec, 2), "d2h_us": round(d2h, 2), "d2h_bytes": host.numel() * 4,
-            "per_request_us": round((rec + d2h) / max(R, 1), 3),
+            "per_request_us": round((rec + d2h) / max(R, 1), 3), "prob_signature_us": prob,
             "pages_mi300x_per_request_us": {"scatter": 480.0, "d2h_staging": 210.0}}
 
 
@@ -371,7 +386,8 @@ def main():
     roof["algorithmic_flops"] = int(ffn_flops)
     roof["avg_call_us"] = round(ffn_s * 1e6, 2)
 
-    signature = signature_recording(s, stats_ids, wl.req_offsets, stream, K, dev) if args.signature else None
+    signature = signature_recording(s, stats_ids, wl.req_offsets, stream, K, dev,
+                                    wl.stats_logits.contiguous()) if args.signature else None
 
     tokens_per_s = s.T * K / elapsed
     out = {

@@ -232,6 +232,27 @@ moe_status moe_stats(const int32_t* topk_ids, int32_t L, int32_t T, int32_t k, i
                      int32_t* affinity, int32_t* req_counts, float* signature,
                      void* workspace, size_t* workspace_bytes, hipStream_t stream);
 
+/*
+ * moe_prob_signature - continuous request signature: for request r, layer l
+ * and expert e, the sum over the request's tokens of the full-E softmax
+ * probability of e.  (ELDR page, "Core idea / structure / operation": the
+ * paper compares its count x IDF signature against continuous alternatives
+ * such as the softmax gate probability; this is that alternative, read as the
+ * plain per-request sum, without IDF.)
+ *
+ *   logits      [L][T][E] fp32 router logits of the recorded layers, read only.
+ *               NaN counts as -inf; a token whose logits are all -inf adds
+ *               nothing; +inf logits are a precondition violation.
+ *   req_offsets [R+1] int32: request r owns tokens [req_offsets[r],
+ *               req_offsets[r+1]), clamped to [0, T] (as in moe_stats).
+ *   signature   [R][L][E] fp32, written.  Probabilities and sums in double
+ *               (token order), rounded to fp32 once (deterministic).
+ *   Requires L >= 1, T >= 0, 1 <= E <= 512, R >= 0; R = 0 enqueues nothing.
+ */
+moe_status moe_prob_signature(const float* logits, int32_t L, int32_t T, int32_t E,
+                              const int32_t* req_offsets, int32_t R, float* signature,
+                              hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(moe_status status);
 

@@ -45,6 +45,9 @@ Readings where the pages are silent (each is listed in the design notes):
      (0 where df = 0); signature = request count * idf.
   R5 router (in front of the gate): logits = x . W_r^T, a bias-free linear map
      of the hidden state, W_r [E][d].
+  R6 continuous signature (the alternative the ELDR page compares against):
+     per request, layer and expert, the sum of the tokens' full-E softmax
+     probabilities, no IDF.
 
 Parity pins: see tests/test_oracle_*.py - every function here is checked against
 closed forms, library routines, invariants and brute force, not against itself.
@@ -302,6 +305,36 @@ def stats(topk_ids: np.ndarray, E: int, req_offsets: Optional[np.ndarray] = None
     sig = (req.astype(np.float64) * idf64[None, :, :]).astype(np.float32)
     out.update({"req_counts": req.astype(np.int32), "df": df.astype(np.int32),
                 "idf": idf64, "signature": sig})
+    return out
+
+
+def prob_signature(logits: np.ndarray, req_offsets: np.ndarray) -> np.ndarray:
+    """Continuous request signature [R][L][E]: for each request, layer and
+    expert, the sum over the request's tokens of the full-E softmax probability.
+
+    ELDR page, "Core idea / structure / operation": the paper compares its
+    count x IDF signature against continuous alternatives such as the softmax
+    gate probability.  Reading R6 takes that alternative as the plain
+    per-request sum of each token's softmax over all E experts, without IDF;
+    NaN logits count as -inf, a token whose logits are all -inf adds nothing,
+    and requests own token ranges as in `stats` (clamped to [0, T]).
+    `logits` is [L][T][E] float32.
+    """
+    lg = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    lg = np.where(np.isnan(lg), -np.inf, lg)
+    L, T, E = lg.shape
+    m = lg.max(axis=2, keepdims=True)
+    live = m > -np.inf                                   # tokens with a finite logit
+    ex = np.where(live, np.exp(lg - np.where(live, m, 0.0)), 0.0)
+    den = ex.sum(axis=2, keepdims=True)
+    p = np.where(live, ex / np.where(live, den, 1.0), 0.0)
+    offs = np.asarray(req_offsets, dtype=np.int64)
+    R = offs.shape[0] - 1
+    out = np.zeros((R, L, E), dtype=np.float64)
+    for r in range(R):
+        lo = min(max(offs[r], 0), T)
+        hi = min(max(offs[r + 1], lo), T)
+        out[r] = p[:, lo:hi, :].sum(axis=1)
     return out
 
 

@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_declares_the_calls():
     assert _declared() == sorted(["moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine",
-                                  "moe_stats", "moe_status_string"])
+                                  "moe_stats", "moe_prob_signature", "moe_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -57,6 +57,21 @@ def test_router_validation(lib):
     assert f(FAKE, FAKE, 4, 64, 8, _lib.MOE_BF16, None, None) == INV
     assert f(FAKE + 4, FAKE, 4, 64, 8, _lib.MOE_BF16, FAKE, None) == INV      # misaligned
     assert f(None, None, 0, 64, 8, _lib.MOE_BF16, None, None) == 0            # T = 0: nothing to do
+
+
+def test_prob_signature_validation(lib):
+    f = lib.moe_prob_signature
+    assert f(FAKE, 0, 4, 8, FAKE, 2, FAKE, None) == INV                # L < 1
+    assert f(FAKE, 1, -1, 8, FAKE, 2, FAKE, None) == INV               # T < 0
+    assert f(FAKE, 1, 4, 0, FAKE, 2, FAKE, None) == INV                # E < 1
+    assert f(FAKE, 1, 4, 8, FAKE, -1, FAKE, None) == INV               # R < 0
+    assert f(FAKE, 1, 4, 513, FAKE, 2, FAKE, None) == UNS              # E > 512
+    assert f(FAKE, 1 << 12, 1 << 12, 512, FAKE, 2, FAKE, None) == UNS  # L*T*E overflows int32
+    assert f(FAKE, 1, 4, 8, None, 2, FAKE, None) == INV                # NULL offsets
+    assert f(FAKE, 1, 4, 8, FAKE, 2, None, None) == INV                # NULL output
+    assert f(None, 1, 4, 8, FAKE, 2, FAKE, None) == INV                # NULL logits with T > 0
+    assert f(FAKE + 2, 1, 4, 8, FAKE, 2, FAKE, None) == INV            # misaligned
+    assert f(None, 1, 4, 8, None, 0, None, None) == 0                  # R = 0: nothing to do
 
 
 def test_gate_validation(lib):

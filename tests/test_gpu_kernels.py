@@ -413,3 +413,43 @@ def test_kv_block_recording_and_host_staging():
     ro = np_of(wl.req_offsets)
     summed = np.stack([host.numpy()[ro[r] // block:ro[r + 1] // block].sum(axis=0) for r in range(len(ro) - 1)])
     np.testing.assert_array_equal(summed, req)
+
+
+# ------------------------------------------------------------------ continuous signature
+def _prob_sig_case(L, T, E, seed):
+    g = torch.Generator().manual_seed(seed)
+    lg = torch.randn((L, T, E), generator=g) * 3.0
+    cuts = sorted(torch.randint(0, T + 1, (5,), generator=g).tolist())
+    offs = torch.tensor([0] + cuts + [T], dtype=torch.int32)
+    return lg, offs
+
+
+@pytest.mark.parametrize("L,T,E,seed", [(1, 1, 1, 0), (3, 600, 70, 1), (2, 40, 512, 2), (4, 257, 9, 3)])
+def test_prob_signature_parity(L, T, E, seed):
+    announce(f"prob signature L={L} T={T} E={E}")
+    lg, offs = _prob_sig_case(L, T, E, seed)
+    if T > 3:                       # special rows: one finite logit, NaNs, all -inf
+        lg[0, 1, :] = -float("inf")
+        lg[0, 1, 0] = 2.0
+        lg[0, 2, ::2] = float("nan")
+        lg[0, 3, :] = -float("inf")
+    ref = O.prob_signature(lg.numpy(), offs.numpy())
+    out = _poison(ref.shape, torch.float32)
+    moe.prob_signature(lg.to(DEV), offs.to(DEV), out)
+    torch.cuda.synchronize()
+    got = np_of(out).astype(np.float64)
+    # everything in double, one rounding to fp32 at the end: within 4 ulp of fp32
+    assert np.all(np.abs(got - ref) <= 2.0 ** -22 * np.abs(ref) + 1e-30), float(np.max(np.abs(got - ref)))
+
+
+def test_prob_signature_qwen3_stack():
+    wl = workloads.make("qwen3_prefill", DEV, with_weights=False)
+    announce("prob signature qwen3 stack")
+    lg = wl.stats_logits.contiguous()
+    out = moe.prob_signature(lg, wl.req_offsets)
+    torch.cuda.synchronize()
+    ref = O.prob_signature(np_of(lg), np_of(wl.req_offsets))
+    got = np_of(out).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -22 * np.abs(ref) + 1e-30)
+    sizes = np.diff(np_of(wl.req_offsets)).astype(np.float64)
+    assert np.allclose(got.sum(axis=2), sizes[:, None], rtol=1e-5)

@@ -13,9 +13,11 @@ import tests.test_oracle_permute as TP
 import tests.test_oracle_ffn_combine as TF
 import tests.test_oracle_stats as TS
 import tests.test_oracle_router as TR
+import tests.test_oracle_prob_signature as TQ
 
 _orig = {name: getattr(O, name) for name in ("gate", "permute", "grouped_ffn", "combine", "stats",
-                                              "silu_product", "assignment_groups", "router")}
+                                              "silu_product", "assignment_groups", "router",
+                                              "prob_signature")}
 
 
 def _gate_unstable(logits, k, renormalize=True):
@@ -124,6 +126,22 @@ def _router_drops_last_term(x, w_router, dtype):
     return O.to_f64(x, dtype)[:, :-1] @ O.to_f64(w_router, dtype)[:, :-1].T
 
 
+def _prob_sig_over_tokens(logits, req_offsets):
+    # softmax taken across the tokens of the batch instead of across the experts
+    lg = np.asarray(logits, dtype=np.float64)
+    offs = np.asarray(req_offsets, dtype=np.int64)
+    ex = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p = ex / ex.sum(axis=1, keepdims=True)
+    return np.stack([p[:, max(0, offs[r]):min(lg.shape[1], offs[r + 1])].sum(axis=1) for r in range(len(offs) - 1)])
+
+
+def _prob_sig_unnormalised(logits, req_offsets):
+    lg = np.asarray(logits, dtype=np.float64)
+    offs = np.asarray(req_offsets, dtype=np.int64)
+    ex = np.exp(lg - lg.max(axis=2, keepdims=True))
+    return np.stack([ex[:, max(0, offs[r]):min(lg.shape[1], offs[r + 1])].sum(axis=1) for r in range(len(offs) - 1)])
+
+
 def _run_pins(pins):
     failures = 0
     for fn, args in pins:
@@ -143,7 +161,11 @@ def _gate_cases():
 _router_pins = lambda: [(TR.test_router_unit_rows_select_weight_columns, ()),
                         (TR.test_router_hand_computed_case, ())]
 
+_prob_pins = lambda: [(TQ.test_each_token_adds_probability_one, ()), (TQ.test_equal_logits_give_one_over_E, ())]
+
 MUTANTS = {
+    "prob_signature_wrong_axis": ("prob_signature", _prob_sig_over_tokens, _prob_pins),
+    "prob_signature_unnormalised": ("prob_signature", _prob_sig_unnormalised, _prob_pins),
     "router_weights_transposed": ("router", _router_transposed, _router_pins),
     "router_drops_last_hidden_term": ("router", _router_drops_last_term, _router_pins),
     "gate_ties_to_higher_id": ("gate", _gate_unstable, _gate_cases),

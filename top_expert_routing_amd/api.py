@@ -240,6 +240,24 @@ def stats(topk_ids: torch.Tensor, E: int, req_offsets: Optional[torch.Tensor] = 
     return o
 
 
+def prob_signature(logits: torch.Tensor, req_offsets: torch.Tensor,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Continuous request signature [R][L][E]: per request, the sum of its
+    tokens' full-E softmax probabilities, from fp32 logits [L][T][E]."""
+    _need(logits, "logits", torch.float32, 3)
+    _need(req_offsets, "req_offsets", torch.int32, 1)
+    L, T, E = logits.shape
+    R = req_offsets.numel() - 1
+    dev = logits.device
+    if out is None:
+        out = torch.empty((R, L, E), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, 3)
+    lib = _lib.load()
+    check("moe_prob_signature", lib.moe_prob_signature(_ptr(logits), L, T, E, _ptr(req_offsets), R, _ptr(out),
+                                                       _stream(dev)))
+    return out
+
+
 class MoeLayer:
     """One MoE layer's expert path with every buffer allocated up front.
 

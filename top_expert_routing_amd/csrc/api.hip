@@ -39,6 +39,18 @@ moe_status workspace_check(void* workspace, size_t* workspace_bytes, size_t need
 
 extern "C" {
 
+moe_status moe_prob_signature(const float* logits, int32_t L, int32_t T, int32_t E, const int32_t* req_offsets,
+                              int32_t R, float* signature, hipStream_t stream) {
+  if (L < 1 || T < 0 || E < 1 || R < 0) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || L > 65535) return MOE_ERR_UNSUPPORTED;
+  if (!fits_int(static_cast<long long>(L) * T * E) || !fits_int(static_cast<long long>(R) * L * E))
+    return MOE_ERR_UNSUPPORTED;
+  if (R == 0) return MOE_OK;
+  if (!req_offsets || !signature || (T > 0 && !logits)) return MOE_ERR_INVALID_ARG;
+  if (!aligned4(req_offsets) || !aligned4(signature) || (logits && !aligned4(logits))) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_prob_signature(logits, L, T, E, req_offsets, R, signature, stream));
+}
+
 const char* moe_status_string(moe_status status) {
   switch (status) {
     case MOE_OK: return "MOE_OK";

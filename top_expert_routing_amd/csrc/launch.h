@@ -69,4 +69,8 @@ struct StatsArgs {
 size_t stats_workspace_bytes(int L, int T, int k, int E, int R);
 hipError_t launch_stats(const StatsArgs& a, void* workspace, hipStream_t stream);
 
+// ---- continuous (softmax-probability) request signature ---------------------
+hipError_t launch_prob_signature(const float* logits, int L, int T, int E, const int* req_offsets, int R,
+                                 float* signature, hipStream_t stream);
+
 }  // namespace moe

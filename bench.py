@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--signature", action="store_true",
                     help="also time the signature recording at KV-block granularity (16-token blocks, every "
                          "layer of the statistics stack) and its device-to-host staging into pinned memory")
+    ap.add_argument("--fp8-weights", action="store_true",
+                    help="expert weights as E4M3 codes with per-row scales (moe_grouped_ffn_fp8w); the CPU "
+                         "baseline leg is skipped in this mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle leg")
     ap.add_argument("--json-out", default="", help="also append the JSON line to this file")
@@ -264,12 +267,22 @@ def main():
     wl = workloads.make(args.workload, dev)
     s = wl.spec
     esize = 4 if s.dtype == "f32" else 2
-    expert_bytes = 3 * s.d * s.I * esize
+    fp8 = bool(args.fp8_weights)
+    if fp8 and s.dtype != "bf16":
+        print("--fp8-weights needs a bf16 workload", file=sys.stderr)
+        sys.exit(2)
+    # expert weight bytes (fp8: codes plus one fp32 scale per weight row)
+    expert_bytes = 3 * s.d * s.I + (2 * s.I + s.d) * 4 if fp8 else 3 * s.d * s.I * esize
     all_w = (s.E + s.S) * expert_bytes
     copies = args.weight_copies or max(1, int(np.ceil(3 * 2**30 / all_w)))
-    wsets = [(wl.w_gate, wl.w_up, wl.w_down)]
-    for _ in range(copies - 1):
-        wsets.append((wl.w_gate.clone(), wl.w_up.clone(), wl.w_down.clone()))
+    if fp8:
+        q = [moe.quantize_fp8_rows(w) for w in (wl.w_gate, wl.w_up, wl.w_down)]
+        base = (q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1])
+        wsets = [base] + [tuple(t.clone() for t in base) for _ in range(copies - 1)]
+    else:
+        wsets = [(wl.w_gate, wl.w_up, wl.w_down)]
+        for _ in range(copies - 1):
+            wsets.append((wl.w_gate.clone(), wl.w_up.clone(), wl.w_down.clone()))
 
     # the gate writes the routing layer's ids straight into layer 0 of the
     # statistics stack
@@ -281,7 +294,7 @@ def main():
     layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, wl.w_gate, wl.w_up, wl.w_down,
                          n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize),
                          stats_layers=s.stats_layers, req_offsets=wl.req_offsets, device=dev,
-                         topk_ids=stats_ids[0], w_router=w_router)
+                         topk_ids=stats_ids[0], w_router=w_router, fp8_weights=wsets[0] if fp8 else None)
     for l in range(1, s.stats_layers):      # the other layers' ids, produced before timing
         moe.gate(wl.stats_logits[l].contiguous(), s.k, True, stats_ids[l],
                  torch.empty((s.T, s.k), device=dev))
@@ -290,8 +303,11 @@ def main():
     # two cross-queue waits per step, more than the statistics themselves.)
     stream = torch.cuda.Stream(dev)
     call_sets = []
-    for wg, wu, wd in wsets:
-        layer.w_gate, layer.w_up, layer.w_down = wg, wu, wd
+    for ws in wsets:
+        if fp8:
+            layer.fp8_weights = ws
+        else:
+            layer.w_gate, layer.w_up, layer.w_down = ws
         call_sets.append(layer.bound_calls(wl.logits, wl.x, stats_ids, stream.cuda_stream))
     names = [c[0] for c in call_sets[0]]
     first = [names.index(n) for n in ("moe_router", "moe_gate", "moe_stats") if n in names]
@@ -367,7 +383,8 @@ def main():
     N = s.N
     ffn_bytes = used_experts * expert_bytes + 2 * N * s.d * esize
     ffn_flops = 2.0 * N * 3 * s.d * s.I
-    ffn_s = per_call["moe_grouped_ffn"] * 1e-3
+    ffn_name = "moe_grouped_ffn_fp8w" if fp8 else "moe_grouped_ffn"
+    ffn_s = per_call[ffn_name] * 1e-3
     peak_flops = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
     intensity = ffn_flops / ffn_bytes
     ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -379,9 +396,9 @@ def main():
         achieved = ffn_flops / ffn_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_flops, "unit": "TFLOP/s",
                 "frac": round(achieved / peak_flops, 4)}
-    traffic = traffic_for(args.workload)
+    traffic = None if fp8 else traffic_for(args.workload)
     roof["traffic"] = None if traffic is None else round(traffic)
-    roof["kernel"] = "moe_grouped_ffn (gate/up launch + down launch), HIP events over K eager steps"
+    roof["kernel"] = f"{ffn_name} (gate/up launch + down launch), HIP events over K eager steps"
     roof["algorithmic_bytes"] = int(ffn_bytes)
     roof["algorithmic_flops"] = int(ffn_flops)
     roof["avg_call_us"] = round(ffn_s * 1e6, 2)
@@ -396,7 +413,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
         "config": {"workload": args.workload, "T": s.T, "E": s.E, "k": s.k, "n_shared": s.S, "d": s.d,
                    "I": s.I, "n_priority": s.n_priority, "stats_layers": s.stats_layers,
-                   "weight_copies": copies, "union": union, "router": bool(args.router)},
+                   "weight_copies": copies, "union": union, "router": bool(args.router),
+                   "expert_weights": "fp8_e4m3 + fp32 row scales" if fp8 else s.dtype},
         "roofline": roof,
         "per_call_us": {n: round(v * 1e3, 2) for n, v in per_call.items()},
         "timing": "eager launches" if args.eager else
@@ -404,7 +422,7 @@ def main():
     }
     if signature is not None:
         out["signature_recording"] = signature
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fp8:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, w_router)
     line = json.dumps(out)
     print(line, flush=True)

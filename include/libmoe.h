@@ -185,6 +185,31 @@ moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t 
                            void* workspace, size_t* workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_grouped_ffn_fp8w - the grouped SwiGLU expert FFN with FP8 expert weights.
+ * (ExpertPlex page, "Experimental results", models table: GLM-5.1-FP8 serves
+ * its experts in FP8.  The page does not give the format; it is read as OCP
+ * E4M3 codes with one fp32 scale per weight row.)
+ *
+ *   As moe_grouped_ffn with dtype MOE_BF16 (x_sorted / x_rows, group offsets,
+ *   h_sorted and the bf16 SwiGLU intermediate), except the weights:
+ *   w_gate, w_up   [E+S][I][d] uint8 E4M3 codes; s_gate, s_up [E+S][I] fp32.
+ *   w_down         [E+S][d][I] uint8 E4M3 codes; s_down [E+S][d] fp32.
+ *   Weight row r of expert e is fp8(w[e][r][:]) * s[e][r].  E4M3 values are
+ *   exact in bf16; products accumulate in fp32 and the scale multiplies the
+ *   accumulated row product.  Runs on the decode-shaped kernel (any group
+ *   sizes; meant for decode-sized groups).
+ *   Requires d and I multiples of 16; every pointer 16-byte aligned.
+ */
+moe_status moe_grouped_ffn_fp8w(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                                const int32_t* group_offsets, int32_t n_rows, int32_t E,
+                                int32_t n_shared, int32_t nseg, int32_t d, int32_t I,
+                                const void* w_gate, const float* s_gate,
+                                const void* w_up, const float* s_up,
+                                const void* w_down, const float* s_down,
+                                void* h_sorted, void* workspace, size_t* workspace_bytes,
+                                hipStream_t stream);
+
+/*
  * moe_combine - gate-weighted combine back to token order.
  * (GRACE-MoE page, section 1: the combine exchange.)
  *

@@ -45,6 +45,8 @@ Readings where the pages are silent (each is listed in the design notes):
      (0 where df = 0); signature = request count * idf.
   R5 router (in front of the gate): logits = x . W_r^T, a bias-free linear map
      of the hidden state, W_r [E][d].
+  R7 FP8 expert weights: OCP E4M3 codes with one fp32 scale per weight row
+     (per output feature); the FFN is then the same definition.
   R6 continuous signature (the alternative the ELDR page compares against):
      per request, layer and expert, the sum of the tokens' full-E softmax
      probabilities, no IDF.
@@ -221,6 +223,45 @@ def grouped_ffn(x_sorted: np.ndarray, group_offsets: np.ndarray, E: int, n_share
         wg = to_f64(w_gate[e], dtype)
         wu = to_f64(w_up[e], dtype)
         wd = to_f64(w_down[e], dtype)
+        a = silu_product(xs @ wg.T, xs @ wu.T)
+        h[pick] = a @ wd.T
+    return h
+
+
+def fp8_e4m3_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes: sign, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent 0 is subnormal (m * 2^-9); S.1111.111 is NaN; no infinities."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    ex = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(ex == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(ex.astype(np.float64) - 7.0))
+    return np.where((ex == 15) & (m == 7), np.nan, sign * mag)
+
+
+def grouped_ffn_fp8w(x_sorted: np.ndarray, group_offsets: np.ndarray, E: int, n_shared: int, nseg: int,
+                     wq_gate: np.ndarray, s_gate: np.ndarray, wq_up: np.ndarray, s_up: np.ndarray,
+                     wq_down: np.ndarray, s_down: np.ndarray, dtype: str = "bf16",
+                     rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """The expert FFN with FP8 E4M3 weights and one fp32 scale per weight row:
+    W[e][r][:] = fp8(wq[e][r][:]) * s[e][r], then exactly `grouped_ffn`'s
+    definition in float64.  ExpertPlex page, "Experimental results" (the
+    models table): one of the two evaluated models, GLM-5.1-FP8, is an
+    FP8-quantised MoE served in that form; the page does not give the format,
+    and reading R7 takes OCP E4M3 codes with one scale per weight row."""
+    offs = np.asarray(group_offsets, dtype=np.int64)
+    N = int(offs[-1])
+    sel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    grp = np.searchsorted(offs, sel, side="right") - 1
+    exp_of_row = expert_of_group(grp, E, n_shared, nseg)
+    d = wq_gate.shape[2]
+    h = np.zeros((sel.shape[0], d), dtype=np.float64)
+    for e in np.unique(exp_of_row):
+        pick = np.nonzero(exp_of_row == e)[0]
+        xs = to_f64(np.asarray(x_sorted)[sel[pick]], dtype)
+        wg = fp8_e4m3_to_f64(wq_gate[e]) * np.asarray(s_gate[e], dtype=np.float64)[:, None]
+        wu = fp8_e4m3_to_f64(wq_up[e]) * np.asarray(s_up[e], dtype=np.float64)[:, None]
+        wd = fp8_e4m3_to_f64(wq_down[e]) * np.asarray(s_down[e], dtype=np.float64)[:, None]
         a = silu_product(xs @ wg.T, xs @ wu.T)
         h[pick] = a @ wd.T
     return h

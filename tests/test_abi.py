@@ -27,8 +27,8 @@ def _declared():
 
 
 def test_header_declares_the_calls():
-    assert _declared() == sorted(["moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine",
-                                  "moe_stats", "moe_prob_signature", "moe_status_string"])
+    assert _declared() == sorted(["moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_fp8w",
+                                  "moe_combine", "moe_stats", "moe_prob_signature", "moe_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -72,6 +72,24 @@ def test_prob_signature_validation(lib):
     assert f(None, 1, 4, 8, FAKE, 2, FAKE, None) == INV                # NULL logits with T > 0
     assert f(FAKE + 2, 1, 4, 8, FAKE, 2, FAKE, None) == INV            # misaligned
     assert f(None, 1, 4, 8, None, 0, None, None) == 0                  # R = 0: nothing to do
+
+
+def test_ffn_fp8w_validation_and_query(lib):
+    f = lib.moe_grouped_ffn_fp8w
+    n = ctypes.c_size_t(0)
+    args = lambda **kw: [kw.get(f"a{i}", v) for i, v in enumerate(
+        [FAKE, None, 0, FAKE, 64, 8, 0, 1, 256, 512, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+         ctypes.byref(n), None])]
+    assert f(*args()) == 0 and n.value >= 64 * 512 * 2           # query
+    assert f(*args(a8=264)) == UNS                                 # d not a multiple of 16
+    assert f(*args(a9=520)) == UNS                                 # I not a multiple of 16
+    assert f(*args(a7=3)) == INV                                   # nseg
+    assert f(*args(a5=513)) == UNS                                 # E > 512
+    small = ctypes.c_size_t(16)
+    assert f(*args(a17=FAKE, a18=ctypes.byref(small))) == WS       # workspace too small
+    big = ctypes.c_size_t(1 << 30)
+    assert f(*args(a17=FAKE, a18=ctypes.byref(big), a11=None)) == INV   # NULL scale
+    assert f(*args(a17=FAKE, a18=ctypes.byref(big), a10=FAKE + 8)) == INV   # misaligned weights
 
 
 def test_gate_validation(lib):

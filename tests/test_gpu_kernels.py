@@ -453,3 +453,39 @@ def test_prob_signature_qwen3_stack():
     assert np.all(np.abs(got - ref) <= 2.0 ** -22 * np.abs(ref) + 1e-30)
     sizes = np.diff(np_of(wl.req_offsets)).astype(np.float64)
     assert np.allclose(got.sum(axis=2), sizes[:, None], rtol=1e-5)
+
+
+# ------------------------------------------------------------------ FP8-weight expert FFN
+FP8_CASES = [
+    # (T, E, k, S, P, d, I, kind)
+    (128, 64, 8, 0, 0, 2048, 1024, "random"),   # OLMoE decode shape: 32-row tiles, 512-wide K chunks
+    (16, 64, 6, 2, 0, 2048, 1408, "zipf"),      # DSv2-Lite decode shape: 16-row tiles, shared experts
+    (96, 16, 4, 0, 0, 144, 208, "random"),      # K tails (144 = 128 + 16) and column tails in both phases
+    (300, 8, 2, 1, 20, 256, 192, "random"),     # 64-row tiles (256-wide chunks), priority segment + shared
+]
+
+
+@pytest.mark.parametrize("T,E,k,S,P,d,I,kind", FP8_CASES)
+def test_grouped_ffn_fp8w_parity(T, E, k, S, P, d, I, kind):
+    announce(f"ffn fp8 T={T} E={E} k={k} S={S} P={P} d={d} I={I} {kind}")
+    wl, ids = _ffn_inputs(T, E, k, S, P, d, I, "bf16", kind, seed=T + E + 7)
+    nseg = 2 if P > 0 else 1
+    qg, sg = moe.quantize_fp8_rows(wl.w_gate)
+    qu, su = moe.quantize_fp8_rows(wl.w_up)
+    qd, sd = moe.quantize_fp8_rows(wl.w_down)
+    p_ref = O.permute(ids.numpy(), E, S, P, np_of(wl.x))
+    h_ref = O.grouped_ffn_fp8w(p_ref["x_sorted"], p_ref["group_offsets"], E, S, nseg, qg.numpy(), sg.numpy(),
+                               qu.numpy(), su.numpy(), qd.numpy(), sd.numpy(), "bf16")
+    xs = torch.from_numpy(p_ref["x_sorted"].view(np.int16)).view(torch.bfloat16).to(DEV)
+    offs = torch.from_numpy(p_ref["group_offsets"]).to(DEV)
+    h = moe.grouped_ffn_fp8w(xs, offs, E, S, nseg, qg.to(DEV), sg.to(DEV), qu.to(DEV), su.to(DEV), qd.to(DEV),
+                             sd.to(DEV), h_sorted=_poison((xs.shape[0], d), torch.bfloat16))
+    torch.cuda.synchronize()
+    err = rel_max_err(f64_of(h), h_ref)
+    assert err <= TOL["bf16"], err
+    # through the row list: the same bits
+    rows = torch.from_numpy(p_ref["sorted_token"]).to(DEV)
+    h2 = moe.grouped_ffn_fp8w(wl.x.to(DEV), offs, E, S, nseg, qg.to(DEV), sg.to(DEV), qu.to(DEV), su.to(DEV),
+                              qd.to(DEV), sd.to(DEV), h_sorted=_poison((xs.shape[0], d), torch.bfloat16), x_rows=rows)
+    torch.cuda.synchronize()
+    assert torch.equal(h2, h)

@@ -14,10 +14,11 @@ import tests.test_oracle_ffn_combine as TF
 import tests.test_oracle_stats as TS
 import tests.test_oracle_router as TR
 import tests.test_oracle_prob_signature as TQ
+import tests.test_oracle_fp8 as T8
 
 _orig = {name: getattr(O, name) for name in ("gate", "permute", "grouped_ffn", "combine", "stats",
                                               "silu_product", "assignment_groups", "router",
-                                              "prob_signature")}
+                                              "prob_signature", "fp8_e4m3_to_f64", "grouped_ffn_fp8w")}
 
 
 def _gate_unstable(logits, k, renormalize=True):
@@ -142,6 +143,28 @@ def _prob_sig_unnormalised(logits, req_offsets):
     return np.stack([ex[:, max(0, offs[r]):min(lg.shape[1], offs[r + 1])].sum(axis=1) for r in range(len(offs) - 1)])
 
 
+def _fp8_subnormals_as_normals(bits):
+    # exponent field 0 read like the others: 2^-6 * (1 + m/8) instead of 2^-6 * m/8
+    b = np.asarray(bits, dtype=np.uint8)
+    v = _orig["fp8_e4m3_to_f64"](b)
+    sub = ((b >> 3) & 0xF) == 0
+    m = (b & 7).astype(np.float64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    return np.where(sub & (m > 0), sign * 2.0 ** -6 * (1 + m / 8), v)
+
+
+def _fp8w_up_takes_gate_scale(x_sorted, group_offsets, E, n_shared, nseg, wq_gate, s_gate, wq_up, s_up,
+                              wq_down, s_down, dtype="bf16", rows=None):
+    return _orig["grouped_ffn_fp8w"](x_sorted, group_offsets, E, n_shared, nseg, wq_gate, s_gate, wq_up, s_gate,
+                                     wq_down, s_down, dtype, rows)
+
+
+def _fp8w_drops_down_scale(x_sorted, group_offsets, E, n_shared, nseg, wq_gate, s_gate, wq_up, s_up,
+                           wq_down, s_down, dtype="bf16", rows=None):
+    return _orig["grouped_ffn_fp8w"](x_sorted, group_offsets, E, n_shared, nseg, wq_gate, s_gate, wq_up, s_up,
+                                     wq_down, np.ones_like(s_down), dtype, rows)
+
+
 def _run_pins(pins):
     failures = 0
     for fn, args in pins:
@@ -163,7 +186,15 @@ _router_pins = lambda: [(TR.test_router_unit_rows_select_weight_columns, ()),
 
 _prob_pins = lambda: [(TQ.test_each_token_adds_probability_one, ()), (TQ.test_equal_logits_give_one_over_E, ())]
 
+_fp8_pins = lambda: [(T8.test_fp8_ffn_equals_fp32_ffn_on_exact_weights, ()),
+                     (T8.test_fp8_ffn_scale_is_per_output_row, ())]
+
 MUTANTS = {
+    "fp8_subnormals_as_normals": ("fp8_e4m3_to_f64", _fp8_subnormals_as_normals,
+                                  lambda: [(T8.test_all_codes_match_torch_float8_e4m3fn, ()),
+                                           (T8.test_landmark_codes, ())]),
+    "fp8_up_takes_gate_scale": ("grouped_ffn_fp8w", _fp8w_up_takes_gate_scale, _fp8_pins),
+    "fp8_drops_down_scale": ("grouped_ffn_fp8w", _fp8w_drops_down_scale, _fp8_pins),
     "prob_signature_wrong_axis": ("prob_signature", _prob_sig_over_tokens, _prob_pins),
     "prob_signature_unnormalised": ("prob_signature", _prob_sig_unnormalised, _prob_pins),
     "router_weights_transposed": ("router", _router_transposed, _router_pins),

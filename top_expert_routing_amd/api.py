@@ -180,6 +180,55 @@ def grouped_ffn(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_s
     return h_sorted
 
 
+def ffn_fp8w_workspace_bytes(n_rows, I) -> int:
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    check("moe_grouped_ffn_fp8w", lib.moe_grouped_ffn_fp8w(None, None, 0, None, n_rows, 1, 0, 1, 16, I, None, None,
+                                                           None, None, None, None, None, None, ctypes.byref(n),
+                                                           None))
+    return int(n.value)
+
+
+def quantize_fp8_rows(w: torch.Tensor):
+    """Per-row E4M3 quantisation of [..][rows][cols] weights: scale = max|row| / 448
+    (1 for an all-zero row), codes = round-to-nearest-even(w / scale).  Input
+    preparation for moe_grouped_ffn_fp8w; returns (codes uint8, scales fp32)."""
+    wf = w.float()
+    s = wf.abs().amax(dim=-1) / 448.0
+    s = torch.where(s > 0, s, torch.ones_like(s))
+    q = (wf / s.unsqueeze(-1)).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q.contiguous(), s.contiguous()
+
+
+def grouped_ffn_fp8w(x: torch.Tensor, group_offsets: torch.Tensor, E: int, n_shared: int, nseg: int,
+                     w_gate: torch.Tensor, s_gate: torch.Tensor, w_up: torch.Tensor, s_up: torch.Tensor,
+                     w_down: torch.Tensor, s_down: torch.Tensor, h_sorted: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, x_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The expert FFN with E4M3 weight codes (uint8) and fp32 per-row scales;
+    bf16 token rows, read directly or through `x_rows`."""
+    _need(x, "x", torch.bfloat16, 2)
+    for t, n in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+        _need(t, n, torch.uint8, 3)
+    for t, n in ((s_gate, "s_gate"), (s_up, "s_up"), (s_down, "s_down")):
+        _need(t, n, torch.float32, 2)
+    _need(group_offsets, "group_offsets", torch.int32, 1)
+    n_rows = int(x_rows.numel()) if x_rows is not None else x.shape[0]
+    d = x.shape[1]
+    I = w_gate.shape[1]
+    dev = x.device
+    if h_sorted is None:
+        h_sorted = torch.empty((n_rows, d), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(ffn_fp8w_workspace_bytes(n_rows, I), 256), dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    nbytes = ctypes.c_size_t(workspace.numel())
+    check("moe_grouped_ffn_fp8w", lib.moe_grouped_ffn_fp8w(
+        _ptr(x), _ptr(x_rows), x.shape[0] if x_rows is not None else 0, _ptr(group_offsets), n_rows, E, n_shared,
+        nseg, d, I, _ptr(w_gate), _ptr(s_gate), _ptr(w_up), _ptr(s_up), _ptr(w_down), _ptr(s_down), _ptr(h_sorted),
+        _ptr(workspace), ctypes.byref(nbytes), _stream(dev)))
+    return h_sorted
+
+
 def combine(h_sorted: torch.Tensor, flat_to_sorted: torch.Tensor, topk_w: torch.Tensor, n_shared: int = 0,
             y: Optional[torch.Tensor] = None) -> torch.Tensor:
     _need(h_sorted, "h_sorted", None, 2)
@@ -271,8 +320,11 @@ class MoeLayer:
 
     def __init__(self, E, k, d, I, T, dtype, w_gate, w_up, w_down, n_shared=0, n_priority=0,
                  renormalize=True, stats_layers=0, req_offsets=None, device="cuda", topk_ids=None,
-                 fused_gather=True, w_router=None):
+                 fused_gather=True, w_router=None, fp8_weights=None):
         dev = torch.device(device)
+        # fp8_weights = (codes_gate, scales_gate, codes_up, scales_up, codes_down, scales_down):
+        # the FFN runs moe_grouped_ffn_fp8w on them instead of w_gate / w_up / w_down
+        self.fp8_weights = fp8_weights
         self.w_router = w_router
         self.logits = torch.empty((T, E), dtype=torch.float32, device=dev) if w_router is not None else None
         self.E, self.k, self.d, self.I, self.T = E, k, d, I, T
@@ -299,8 +351,9 @@ class MoeLayer:
         self.perm_ws = torch.empty(max(permute_workspace_bytes(T, E, k, n_shared, n_priority), 256),
                                    dtype=torch.uint8, device=dev)
         self.h_sorted = torch.empty((N, d), dtype=dtype, device=dev)
-        self.ffn_ws = torch.empty(max(ffn_workspace_bytes(N, E, n_shared, self.nseg, d, I, dtype), 256),
-                                  dtype=torch.uint8, device=dev)
+        ws_bytes = ffn_fp8w_workspace_bytes(N, I) if fp8_weights is not None else \
+            ffn_workspace_bytes(N, E, n_shared, self.nseg, d, I, dtype)
+        self.ffn_ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.y = torch.empty((T, d), dtype=dtype, device=dev)
         self.stats_out = None
         self.req_offsets = req_offsets
@@ -321,6 +374,11 @@ class MoeLayer:
                        workspace=self.perm_ws)
 
     def ffn(self, x):
+        if self.fp8_weights is not None:
+            src = x if self.fused_gather else self.perm["x_sorted"]
+            return grouped_ffn_fp8w(src, self.perm["group_offsets"], self.E, self.S, self.nseg, *self.fp8_weights,
+                                    h_sorted=self.h_sorted, workspace=self.ffn_ws,
+                                    x_rows=self.perm["sorted_token"] if self.fused_gather else None)
         if self.fused_gather:
             return grouped_ffn(x, self.perm["group_offsets"], self.E, self.S, self.nseg, self.w_gate, self.w_up,
                                self.w_down, self.h_sorted, self.ffn_ws, x_rows=self.perm["sorted_token"])
@@ -367,13 +425,7 @@ class MoeLayer:
                                               self.perm["sorted_token"].data_ptr(),
                                               None if fused else self.perm["x_sorted"].data_ptr(),
                                               self.perm_ws.data_ptr(), ctypes.byref(n_perm), st)),
-            ("moe_grouped_ffn", lib.moe_grouped_ffn, (x.data_ptr() if fused else self.perm["x_sorted"].data_ptr(),
-                                                      self.perm["sorted_token"].data_ptr() if fused else None, T,
-                                                      self.perm["group_offsets"].data_ptr(), self.N, E, self.S,
-                                                      self.nseg, self.d, self.I, self.w_gate.data_ptr(),
-                                                      self.w_up.data_ptr(), self.w_down.data_ptr(), dt,
-                                                      self.h_sorted.data_ptr(), self.ffn_ws.data_ptr(),
-                                                      ctypes.byref(n_ffn), st)),
+            self._ffn_call(lib, x, fused, dt, n_ffn, st),
             ("moe_combine", lib.moe_combine, (self.h_sorted.data_ptr(), self.perm["flat_to_sorted"].data_ptr(),
                                               self.topk_w.data_ptr(), T, k, self.S, self.d, dt, self.y.data_ptr(),
                                               st)),
@@ -393,6 +445,20 @@ class MoeLayer:
                 self.stats_ws.data_ptr(), ctypes.byref(n_st), st if stats_stream is None else stats_stream)))
         self._keep = (n_perm, n_ffn, n_st if stats_ids is not None and self.stats_out is not None else None)
         return calls
+
+    def _ffn_call(self, lib, x, fused, dt, n_ffn, st):
+        src = x.data_ptr() if fused else self.perm["x_sorted"].data_ptr()
+        rows = self.perm["sorted_token"].data_ptr() if fused else None
+        offs = self.perm["group_offsets"].data_ptr()
+        if self.fp8_weights is not None:
+            qg, sg, qu, su, qd, sd = (t.data_ptr() for t in self.fp8_weights)
+            return ("moe_grouped_ffn_fp8w", lib.moe_grouped_ffn_fp8w, (
+                src, rows, self.T, offs, self.N, self.E, self.S, self.nseg, self.d, self.I, qg, sg, qu, su, qd, sd,
+                self.h_sorted.data_ptr(), self.ffn_ws.data_ptr(), ctypes.byref(n_ffn), st))
+        return ("moe_grouped_ffn", lib.moe_grouped_ffn, (
+            src, rows, self.T, offs, self.N, self.E, self.S, self.nseg, self.d, self.I, self.w_gate.data_ptr(),
+            self.w_up.data_ptr(), self.w_down.data_ptr(), dt, self.h_sorted.data_ptr(), self.ffn_ws.data_ptr(),
+            ctypes.byref(n_ffn), st))
 
     def forward(self, logits, x, stats_ids=None, stats_stream=None):
         """Enqueue the layer on the current stream.  With `stats_stream` (a

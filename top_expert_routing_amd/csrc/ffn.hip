@@ -515,6 +515,176 @@ __global__ __launch_bounds__(kThreads, kDecodeWavesPerSimd) void ffn_decode_spli
   }
 }
 
+// ---- decode-sized tiles with FP8 weights ---------------------------------------
+// ExpertPlex page, "Experimental results" (models table): GLM-5.1-FP8 serves its
+// experts in FP8.  Weights are OCP E4M3 codes with one fp32 scale per weight
+// row (per output feature); token rows and the SwiGLU product stay bf16.  The
+// structure is ffn_decode_bf16's with eight waves per block and twice the K
+// per chunk:
+//   * a lane loads 16 bytes = 16 weights of one row (each row still streams in
+//     64-byte runs per instruction) and converts them with
+//     v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3 value is a bf16 value)
+//     into the B operands of two v_mfma_f32_16x16x32_bf16 K-steps: in K-step h
+//     lane (l16, q) holds weights kk + 16 q + 8 h .. + 7 and reads the same
+//     eight values of its token row from LDS (the MFMA sums over its 32 K
+//     values, so any split of the 64 values between the two steps works as
+//     long as both operands use it);
+//   * a chunk is 512 K values (256 for 64-row tiles), so a wave keeps 16 KiB of
+//     weights in flight as in the bf16 kernel; the chunk's token rows are
+//     staged through LDS, double buffered, and shared by the eight waves (two
+//     blocks per CU fit in LDS);
+//   * the row scale multiplies the fp32 accumulator before SwiGLU or the store.
+constexpr int kThreads8 = 512;
+constexpr int kWaves8 = kThreads8 / kWave;
+template <int MF>
+constexpr int fp8_kc() { return MF <= 2 ? 512 : 256; }
+
+// Eight E4M3 codes (two 32-bit words, lowest byte first) as eight bf16 values.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int MF, int NFC, int PHASE>
+__global__ __launch_bounds__(kThreads8, 4) void ffn_decode_fp8w(
+    const uint16_t* __restrict__ A, int K, const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
+    const float* __restrict__ S0, const float* __restrict__ S1, int Ncols, PlanArgs plan,
+    uint16_t* __restrict__ out) {
+  constexpr int NF = PHASE == 1 ? 2 * NFC : NFC;
+  constexpr int BN = kWaves8 * 16 * NFC;
+  constexpr int BM = 16 * MF;
+  constexpr int KC = fp8_kc<MF>();
+  constexpr int kStride = KC + 8;                           // bf16 per staged A row (pad 16 B)
+  constexpr int U = KC / 64;                                // 16-byte weight loads per row per chunk
+  constexpr int VPR = KC / 8;                               // uint4 per staged A row
+  constexpr int APT = (BM * VPR + kThreads8 - 1) / kThreads8;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kStride];
+
+  const int nch = (Ncols + BN - 1) / BN;
+  const Item it = block_find_item<kThreads8>(plan, nch);
+  if (it.rows == 0) return;
+  const int rows = it.rows, e = it.expert;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int l16 = lane & 15, q = lane >> 4;
+  const int col0 = it.chunk * BN + wave * 16 * NFC;
+  const size_t wstride = static_cast<size_t>(Ncols) * K;   // bytes per expert matrix
+  const int nchunks = (K + KC - 1) / KC;
+
+  const uint8_t* bp[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int n = min(col0 + (j % NFC) * 16 + l16, Ncols - 1);
+    const uint8_t* W = (PHASE == 1 && j >= NFC) ? W1 : W0;
+    bp[j] = W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n) * K + 16 * q;
+  }
+
+  // token rows of a chunk: thread handles uint4 slots idx = tid + s * 512
+  uint4 stage[APT];
+  const uint16_t* arow[APT];
+#pragma unroll
+  for (int s = 0; s < APT; ++s) {
+    const int idx = threadIdx.x + s * kThreads8;
+    const int r = idx / VPR;
+    arow[s] = (idx < BM * VPR && r < rows) ? A + a_row(plan.arows, plan.n_x, it.row(r)) * K : nullptr;
+  }
+  auto load_a = [&](int c) {
+#pragma unroll
+    for (int s = 0; s < APT; ++s) {
+      const int kv = (threadIdx.x + s * kThreads8) % VPR;
+      const int k = c * KC + kv * 8;
+      stage[s] = make_uint4(0, 0, 0, 0);
+      if (arow[s] && k < K) stage[s] = *reinterpret_cast<const uint4*>(arow[s] + k);
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int s = 0; s < APT; ++s) {
+      const int idx = threadIdx.x + s * kThreads8;
+      if (idx < BM * VPR)
+        *reinterpret_cast<uint4*>(&As[buf][(idx / VPR) * kStride + (idx % VPR) * 8]) = stage[s];
+    }
+  };
+
+  f32x4 acc[MF][NF];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // weight loads of chunk c (zero past K: K % 16 == 0, so a lane's 16 codes
+  // are all in range or all out)
+  auto load_b = [&](uint4 (&b)[U][NF], int c) {
+    const int kc = c * KC;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = kc + 64 * u + 16 * q;
+#pragma unroll
+      for (int j = 0; j < NF; ++j)
+        b[u][j] = kk < K ? *reinterpret_cast<const uint4*>(bp[j] + kc + 64 * u) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto mma = [&](const uint4 (&b)[U][NF], const uint16_t* as) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 af[MF];
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+          af[i] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const uint4*>(&as[(16 * i + l16) * kStride + 64 * u + 16 * q + 8 * h]));
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          const bf16x8 bw = h == 0 ? fp8x8_to_bf16(b[u][j].x, b[u][j].y) : fp8x8_to_bf16(b[u][j].z, b[u][j].w);
+#pragma unroll
+          for (int i = 0; i < MF; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw, af[i], acc[i][j], 0, 0, 0);
+        }
+      }
+  };
+
+  load_a(0);
+  store_a(0);
+  for (int c = 0; c < nchunks; ++c) {
+    uint4 b[U][NF];
+    load_b(b, c);
+    const bool more = c + 1 < nchunks;
+    if (more) load_a(c + 1);
+    __syncthreads();                           // chunk c of A is in As[c & 1]
+    mma(b, As[c & 1]);
+    if (more) store_a((c + 1) & 1);            // that buffer was last read before this barrier
+  }
+
+  // In each 16x16 block a lane holds token row l16 and output columns
+  // 4q..4q+3 (one 8-byte store; Ncols % 16 == 0, so all four are in range or
+  // all out); the four columns' scales load as one float4.
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    const int m = 16 * i + l16;
+    if (m >= rows) continue;
+    uint16_t* orow = out + static_cast<size_t>(it.row(m)) * Ncols;
+#pragma unroll
+    for (int j = 0; j < NFC; ++j) {
+      const int n = col0 + j * 16 + 4 * q;
+      if (n >= Ncols) continue;
+      const size_t so = static_cast<size_t>(e) * Ncols + n;
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(S0 + so);
+      float v[4];
+      if constexpr (PHASE == 1) {
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(S1 + so);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[i][j][t] * s0[t], acc[i][NFC + j][t] * s1[t]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = acc[i][j][t] * s0[t];
+      }
+      *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
+  }
+}
+
 // ---- prefill-sized tiles: LDS-tiled GEMM on v_mfma_f32_32x32x16_bf16 ------------
 // Block tile: BM token rows x BN weight rows (phase 1: BN/2 gate rows then the
 // matching BN/2 up rows -> BN/2 SwiGLU columns; phase 2: BN down rows), K in
@@ -1455,7 +1625,56 @@ void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t 
                      reinterpret_cast<uint16_t*>(ws + L.a_off), static_cast<uint16_t*>(a.h_sorted));
 }
 
+// FP8-weight FFN: both phases on the FP8 decode kernel (groups of any size;
+// it is the decode-shaped kernel, meant for decode-sized groups).
+template <int MF>
+void launch_decode_fp8w(const FfnArgs& a, int max_tiles, const PlanArgs& plan, uint16_t* abuf,
+                        hipStream_t stream) {
+  const int bn1 = kWaves8 * 16 * 1, bn2 = kWaves8 * 16 * 2;
+  const int nch1 = (a.I + bn1 - 1) / bn1, nch2 = (a.d + bn2 - 1) / bn2;
+  hipLaunchKernelGGL((ffn_decode_fp8w<MF, 1, 1>), dim3(item_grid(max_tiles, nch1)), dim3(kThreads8), 0, stream,
+                     static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint8_t*>(a.w_gate),
+                     static_cast<const uint8_t*>(a.w_up), a.s_gate, a.s_up, a.I, plan, abuf);
+  PlanArgs plan2 = plan;
+  plan2.diag = nullptr;
+  plan2.arows = nullptr;
+  hipLaunchKernelGGL((ffn_decode_fp8w<MF, 2, 2>), dim3(item_grid(max_tiles, nch2)), dim3(kThreads8), 0, stream,
+                     static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint8_t*>(a.w_down),
+                     static_cast<const uint8_t*>(nullptr), a.s_down, static_cast<const float*>(nullptr), a.d, plan2,
+                     static_cast<uint16_t*>(a.h_sorted));
+}
+
 }  // namespace
+
+size_t ffn_fp8w_workspace_bytes(int n_rows, int I) {
+  // SwiGLU intermediate [n_rows][I] bf16, then the diagnostic word at the end
+  return (static_cast<size_t>(n_rows) * I * 2 + 255) / 256 * 256 + 256;
+}
+
+hipError_t launch_ffn_fp8w(const FfnArgs& a, void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  const size_t total = ffn_fp8w_workspace_bytes(a.n_rows, a.I);
+  const int G = a.nseg * a.E + a.n_shared;
+  const int mf = pick_mf(G > 0 ? a.n_rows / G : a.n_rows);
+  PlanArgs plan;
+  plan.offs = a.group_offsets;
+  plan.G = G;
+  plan.E = a.E;
+  plan.nseg = a.nseg;
+  plan.BM = 16 * mf;
+  plan.n_rows = a.n_rows;
+  plan.max_tiles = (a.n_rows + plan.BM - 1) / plan.BM + G;
+  plan.diag = reinterpret_cast<int*>(ws + total - 4);
+  plan.arows = a.x_rows;
+  plan.n_x = a.n_x;
+  uint16_t* abuf = reinterpret_cast<uint16_t*>(ws);
+  switch (mf) {
+    case 1: launch_decode_fp8w<1>(a, plan.max_tiles, plan, abuf, stream); break;
+    case 2: launch_decode_fp8w<2>(a, plan.max_tiles, plan, abuf, stream); break;
+    default: launch_decode_fp8w<4>(a, plan.max_tiles, plan, abuf, stream); break;
+  }
+  return hipGetLastError();
+}
 
 size_t ffn_workspace_bytes(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16) {
   return layout(n_rows, E, n_shared, nseg, d, I, bf16).total;

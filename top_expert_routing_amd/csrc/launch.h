@@ -44,9 +44,15 @@ struct FfnArgs {
   const void* w_down;
   int bf16;  // 1: bf16 operands, 0: fp32
   void* h_sorted;
+  // FP8-weight call only: one fp32 scale per weight row ([E+S][I], [E+S][I], [E+S][d])
+  const float* s_gate = nullptr;
+  const float* s_up = nullptr;
+  const float* s_down = nullptr;
 };
 size_t ffn_workspace_bytes(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16);
 hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream);
+size_t ffn_fp8w_workspace_bytes(int n_rows, int I);
+hipError_t launch_ffn_fp8w(const FfnArgs& a, void* workspace, hipStream_t stream);
 
 // ---- combine ---------------------------------------------------------------
 hipError_t launch_combine(const void* h_sorted, const int* flat_to_sorted, const float* topk_w, int T,

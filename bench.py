@@ -271,6 +271,13 @@ def main():
     if fp8 and s.dtype != "bf16":
         print("--fp8-weights needs a bf16 workload", file=sys.stderr)
         sys.exit(2)
+    if fp8 and s.n_priority > 0:
+        # its one run ended in a GPU memory fault whose cause has not been
+        # found (a host-side model of the FP8 kernel's work items and address
+        # ranges for this routing finds every access in bounds)
+        print("--fp8-weights is not run on workloads with a priority segment: a memory fault in that "
+              "configuration is not explained yet", file=sys.stderr)
+        sys.exit(2)
     # expert weight bytes (fp8: codes plus one fp32 scale per weight row)
     expert_bytes = 3 * s.d * s.I + (2 * s.I + s.d) * 4 if fp8 else 3 * s.d * s.I * esize
     all_w = (s.E + s.S) * expert_bytes

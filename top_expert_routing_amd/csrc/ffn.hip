@@ -529,15 +529,17 @@ __global__ __launch_bounds__(kThreads, kDecodeWavesPerSimd) void ffn_decode_spli
 //     eight values of its token row from LDS (the MFMA sums over its 32 K
 //     values, so any split of the 64 values between the two steps works as
 //     long as both operands use it);
-//   * a chunk is 512 K values (256 for 64-row tiles), so a wave keeps 16 KiB of
-//     weights in flight as in the bf16 kernel; the chunk's token rows are
-//     staged through LDS, double buffered, and shared by the eight waves (two
-//     blocks per CU fit in LDS);
+//   * a chunk is 512 K values for 16-row tiles, so a wave keeps 16 KiB of
+//     weights in flight as in the bf16 kernel; 384 for 32-row tiles (at 512
+//     their accumulators and staging spill registers to scratch, which cost
+//     a sixth of the OLMoE-shaped call) and 256 for 64-row tiles (LDS); the
+//     chunk's token rows are staged through LDS, double buffered, and shared
+//     by the eight waves (two blocks per CU fit in LDS);
 //   * the row scale multiplies the fp32 accumulator before SwiGLU or the store.
 constexpr int kThreads8 = 512;
 constexpr int kWaves8 = kThreads8 / kWave;
 template <int MF>
-constexpr int fp8_kc() { return MF <= 2 ? 512 : 256; }
+constexpr int fp8_kc() { return MF == 1 ? 512 : MF == 2 ? 384 : 256; }
 
 // Eight E4M3 codes (two 32-bit words, lowest byte first) as eight bf16 values.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {

@@ -116,3 +116,37 @@ def test_layer_with_router_parity(name):
                       n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize), tokens=toks)
     y_err = rel_max_err(f64_of(layer.y[torch.from_numpy(toks).to(DEV)]), ref["y"])
     assert y_err <= TOL[s.dtype], y_err
+
+
+@pytest.mark.parametrize("name", ["olmoe_decode", "dsv2_decode_t16", "dsv2_decode_t256"])
+def test_layer_fp8_weights_parity(name):
+    """The layer with FP8 expert weights (E4M3 codes, fp32 row scales): routing
+    bit for bit as with bf16 weights, and the output of sampled tokens against
+    the oracle's gate -> permute -> FP8 FFN -> combine on the same codes."""
+    announce(f"layer {name} with fp8 weights")
+    wl = workloads.make(name, DEV)
+    s = wl.spec
+    q = [moe.quantize_fp8_rows(w) for w in (wl.w_gate, wl.w_up, wl.w_down)]
+    fp8 = (q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1])
+    layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, wl.w_gate, wl.w_up, wl.w_down,
+                         n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize), device=DEV,
+                         fp8_weights=fp8)
+    layer.forward(wl.logits, wl.x)
+    torch.cuda.synchronize()
+    logits, x = np_of(wl.logits), np_of(wl.x)
+    ids, w = O.gate(logits, s.k, bool(s.renormalize))
+    np.testing.assert_array_equal(np_of(layer.topk_ids), ids)
+    p = O.permute(ids, s.E, s.S, s.n_priority, x)
+    toks = _sample_tokens(s.T, s.n_priority)
+    T, k = ids.shape
+    f2s = p["flat_to_sorted"].astype(np.int64)
+    flat = [t * k + j for t in toks for j in range(k)] + [T * k + e * T + t for t in toks for e in range(s.S)]
+    need = np.unique(f2s[np.asarray(flat, dtype=np.int64)])
+    nseg = 2 if s.n_priority > 0 else 1
+    h = O.grouped_ffn_fp8w(p["x_sorted"], p["group_offsets"], s.E, s.S, nseg, *(np_of(t) for t in fp8),
+                           dtype=s.dtype, rows=need)
+    h_err = rel_max_err(f64_of(layer.h_sorted[torch.from_numpy(need).to(DEV)]), h)
+    assert h_err <= TOL[s.dtype], h_err
+    y_ref = O.combine(h, f2s, w, T, k, s.S, tokens=toks, row_of_sorted={int(n): i for i, n in enumerate(need)})
+    y_err = rel_max_err(f64_of(layer.y[torch.from_numpy(toks).to(DEV)]), y_ref)
+    assert y_err <= TOL[s.dtype], y_err

@@ -462,6 +462,10 @@ FP8_CASES = [
     (16, 64, 6, 2, 0, 2048, 1408, "zipf"),      # DSv2-Lite decode shape: 16-row tiles, shared experts
     (96, 16, 4, 0, 0, 144, 208, "random"),      # K tails (144 = 128 + 16) and column tails in both phases
     (300, 8, 2, 1, 20, 256, 192, "random"),     # 64-row tiles (256-wide chunks), priority segment + shared
+    (100, 16, 4, 0, 30, 128, 96, "random"),     # 32-row tiles (384-wide chunks) with a priority segment
+    (64, 512, 8, 2, 0, 64, 48, "random"),       # the most routed experts, two shared, K shorter than a chunk
+    (80, 512, 4, 2, 30, 32, 16, "zipf"),        # 1026 groups (priority segment at E = 512), one column chunk
+    (1, 4, 1, 0, 0, 16, 16, "random"),          # one token, the smallest d and I
 ]
 
 

@@ -493,3 +493,34 @@ def test_grouped_ffn_fp8w_parity(T, E, k, S, P, d, I, kind):
                               qd.to(DEV), sd.to(DEV), h_sorted=_poison((xs.shape[0], d), torch.bfloat16), x_rows=rows)
     torch.cuda.synchronize()
     assert torch.equal(h2, h)
+
+
+def test_ffn_bindings_reject_mismatched_shapes():
+    """The FFN bindings refuse weights, scales, offsets or outputs whose shapes do
+    not match the call's sizes (before anything is enqueued)."""
+    E, S, d, I, N = 4, 1, 32, 48, 10
+    dev = DEV
+    x = torch.zeros((N, d), dtype=torch.bfloat16, device=dev)
+    offs = torch.zeros(E + S + 1, dtype=torch.int32, device=dev)
+    wg = torch.zeros((E + S, I, d), dtype=torch.bfloat16, device=dev)
+    wd = torch.zeros((E + S, d, I), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        moe.grouped_ffn(x, offs, E, S, 1, wg, wg, wg)                     # down has the wrong shape
+    with pytest.raises(ValueError):
+        moe.grouped_ffn(x, offs[:-1], E, S, 1, wg, wg, wd)                # too few offsets
+    with pytest.raises(ValueError):
+        moe.grouped_ffn(x, offs, E, S, 1, wg, wg, wd, h_sorted=torch.empty((N - 1, d), dtype=torch.bfloat16,
+                                                                           device=dev))
+    qg = torch.zeros((E + S, I, d), dtype=torch.uint8, device=dev)
+    qd = torch.zeros((E + S, d, I), dtype=torch.uint8, device=dev)
+    sg = torch.ones((E + S, I), dtype=torch.float32, device=dev)
+    sd = torch.ones((E + S, d), dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError):
+        moe.grouped_ffn_fp8w(x, offs, E, S, 1, qg, sg, qg, sg, qg, sd)    # down codes have the wrong shape
+    with pytest.raises(ValueError):
+        moe.grouped_ffn_fp8w(x, offs, E, S, 1, qg, sg, qg, sg, qd, sg)    # down scales have the wrong shape
+    with pytest.raises(ValueError):
+        moe.grouped_ffn_fp8w(x, offs, E + 1, S, 1, qg, sg, qg, sg, qd, sd)  # E does not match the weights
+    with pytest.raises(ValueError):
+        moe.grouped_ffn_fp8w(x, offs, E, S, 1, qg, sg, qg, sg, qd, sd,
+                             h_sorted=torch.empty((N, d + 16), dtype=torch.bfloat16, device=dev))

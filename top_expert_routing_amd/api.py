@@ -168,6 +168,9 @@ def grouped_ffn(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_s
     dev = x_sorted.device
     if h_sorted is None:
         h_sorted = torch.empty((N, d), dtype=x_sorted.dtype, device=dev)
+    _need(h_sorted, "h_sorted", x_sorted.dtype, 2)
+    if h_sorted.shape != (N, d):
+        raise ValueError(f"h_sorted must be [{N}][{d}]")
     if workspace is None:
         workspace = torch.empty(max(ffn_workspace_bytes(N, E, n_shared, nseg, d, I, x_sorted.dtype), 256),
                                 dtype=torch.uint8, device=dev)
@@ -212,12 +215,24 @@ def grouped_ffn_fp8w(x: torch.Tensor, group_offsets: torch.Tensor, E: int, n_sha
     for t, n in ((s_gate, "s_gate"), (s_up, "s_up"), (s_down, "s_down")):
         _need(t, n, torch.float32, 2)
     _need(group_offsets, "group_offsets", torch.int32, 1)
+    if x_rows is not None:
+        _need(x_rows, "x_rows", torch.int32, 1)
     n_rows = int(x_rows.numel()) if x_rows is not None else x.shape[0]
     d = x.shape[1]
     I = w_gate.shape[1]
+    G = E + n_shared
+    if w_gate.shape != (G, I, d) or w_up.shape != w_gate.shape or w_down.shape != (G, d, I):
+        raise ValueError("expert weight codes must be [E+S][I][d] (gate, up) and [E+S][d][I] (down)")
+    if s_gate.shape != (G, I) or s_up.shape != (G, I) or s_down.shape != (G, d):
+        raise ValueError("row scales must be [E+S][I] (gate, up) and [E+S][d] (down)")
+    if group_offsets.numel() != nseg * E + n_shared + 1:
+        raise ValueError("group_offsets must have nseg*E + n_shared + 1 entries")
     dev = x.device
     if h_sorted is None:
         h_sorted = torch.empty((n_rows, d), dtype=torch.bfloat16, device=dev)
+    _need(h_sorted, "h_sorted", torch.bfloat16, 2)
+    if h_sorted.shape != (n_rows, d):
+        raise ValueError(f"h_sorted must be [{n_rows}][{d}]")
     if workspace is None:
         workspace = torch.empty(max(ffn_fp8w_workspace_bytes(n_rows, I), 256), dtype=torch.uint8, device=dev)
     lib = _lib.load()

@@ -186,7 +186,7 @@ def test_permute_parity(T, E, k, S, P, d, dtype, kind):
 
 
 def test_permute_empty_batch_writes_zero_offsets():
-    out = {"group_offsets": _poison(2 * 8 + 1 + 1, torch.int32),
+    out = {"group_offsets": _poison(8 + 1 + 1, torch.int32),
            "sorted_to_flat": torch.empty(0, dtype=torch.int32, device=DEV),
            "flat_to_sorted": torch.empty(0, dtype=torch.int32, device=DEV)}
     moe.permute(torch.empty((0, 2), dtype=torch.int32, device=DEV), 8, 1, 0, None, out=out)
@@ -524,3 +524,28 @@ def test_ffn_bindings_reject_mismatched_shapes():
     with pytest.raises(ValueError):
         moe.grouped_ffn_fp8w(x, offs, E, S, 1, qg, sg, qg, sg, qd, sd,
                              h_sorted=torch.empty((N, d + 16), dtype=torch.bfloat16, device=dev))
+
+
+def test_bindings_reject_mismatched_outputs():
+    """Caller-supplied outputs of the wrong shape (or inputs whose sizes disagree)
+    are refused before anything is enqueued."""
+    T, E, k, d = 8, 16, 2, 32
+    dev = DEV
+    logits = torch.zeros((T, E), dtype=torch.float32, device=dev)
+    ids = torch.zeros((T, k), dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):
+        moe.gate(logits, k, True, ids, torch.empty((T, k + 1), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        moe.gate(logits, k, True, torch.empty((T - 1, k), dtype=torch.int32, device=dev))
+    with pytest.raises(ValueError):
+        moe.permute(ids, E, x=torch.zeros((T + 1, d), dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        moe.permute(ids, E, out={"group_offsets": torch.empty(E, dtype=torch.int32, device=dev)})
+    with pytest.raises(ValueError):
+        moe.stats(ids.view(1, T, k), E, out={"counts": torch.empty((1, E - 1), dtype=torch.int32, device=dev)})
+    offs = torch.tensor([0, 4, 8], dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):
+        moe.prob_signature(logits.view(1, T, E), offs, torch.empty((2, 1, E + 1), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        moe.router(torch.zeros((T, d), dtype=torch.bfloat16, device=dev),
+                   torch.zeros((E, d), dtype=torch.bfloat16, device=dev), torch.empty((T, E - 1), device=dev))

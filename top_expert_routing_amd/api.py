@@ -44,6 +44,13 @@ def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims")
 
 
+def _out(t: torch.Tensor, name: str, dtype, shape):
+    """A caller-supplied output: a contiguous GPU tensor of exactly this dtype and shape."""
+    _need(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _workspace(fn, args_before_ws, dev) -> torch.Tensor:
     """Query a call's workspace size (NULL workspace) and allocate it."""
     n = ctypes.c_size_t(0)
@@ -62,7 +69,7 @@ def router(x: torch.Tensor, w_router: torch.Tensor, logits: Optional[torch.Tenso
     dev = x.device
     if logits is None:
         logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-    _need(logits, "logits", torch.float32, 2)
+    _out(logits, "logits", torch.float32, (T, E))
     lib = _lib.load()
     check("moe_router", lib.moe_router(_ptr(x), _ptr(w_router), T, d, E, _dtype_code(x), _ptr(logits),
                                        _stream(dev)))
@@ -78,6 +85,8 @@ def gate(logits: torch.Tensor, k: int, renormalize: bool = True,
         topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     if topk_w is None:
         topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _out(topk_ids, "topk_ids", torch.int32, (T, k))
+    _out(topk_w, "topk_w", torch.float32, (T, k))
     lib = _lib.load()
     check("moe_gate", lib.moe_gate(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(topk_ids),
                                    _ptr(topk_w), _stream(dev)))
@@ -107,6 +116,8 @@ def permute(topk_ids: torch.Tensor, E: int, n_shared: int = 0, n_priority: int =
     dt = MOE_BF16
     if x is not None:
         _need(x, "x", None, 2)
+        if x.shape[0] != T:
+            raise ValueError(f"x must have {T} rows, one per token")
         d = x.shape[1]
         dt = _dtype_code(x)
     o = {} if out is None else out
@@ -120,6 +131,11 @@ def permute(topk_ids: torch.Tensor, E: int, n_shared: int = 0, n_priority: int =
         o["sorted_token"] = torch.empty(N, dtype=torch.int32, device=dev)
     if x is not None and "x_sorted" not in o:
         o["x_sorted"] = torch.empty((N, d), dtype=x.dtype, device=dev)
+    _out(o["group_offsets"], "group_offsets", torch.int32, (G + 1,))
+    for key in ("sorted_to_flat", "flat_to_sorted") + (("sorted_token",) if sorted_token else ()):
+        _out(o[key], key, torch.int32, (N,))
+    if x is not None:
+        _out(o["x_sorted"], "x_sorted", x.dtype, (N, d))
     if workspace is None:
         workspace = torch.empty(max(permute_workspace_bytes(T, E, k, n_shared, n_priority), 256),
                                 dtype=torch.uint8, device=dev)
@@ -282,7 +298,7 @@ def stats(topk_ids: torch.Tensor, E: int, req_offsets: Optional[torch.Tensor] = 
         _need(req_offsets, "req_offsets", torch.int32, 1)
         R = req_offsets.numel() - 1
     if idf is not None:
-        _need(idf, "idf", torch.float32, 2)
+        _out(idf, "idf", torch.float32, (L, E))
     o = {} if out is None else out
     o.setdefault("counts", torch.empty((L, E), dtype=torch.int32, device=dev))
     o.setdefault("union_size", torch.empty(L, dtype=torch.int32, device=dev))
@@ -293,6 +309,12 @@ def stats(topk_ids: torch.Tensor, E: int, req_offsets: Optional[torch.Tensor] = 
         o.setdefault("req_counts", torch.empty((R, L, E), dtype=torch.int32, device=dev))
         if signature:
             o.setdefault("signature", torch.empty((R, L, E), dtype=torch.float32, device=dev))
+    shapes = {"counts": ((L, E), torch.int32), "union_size": ((L,), torch.int32),
+              "union_mask": ((L, E), torch.uint8), "affinity": ((L, E, E), torch.int32),
+              "req_counts": ((R, L, E), torch.int32), "signature": ((R, L, E), torch.float32)}
+    for key, (shape, dt) in shapes.items():
+        if key in o and (R > 0 or key not in ("req_counts", "signature")):
+            _out(o[key], key, dt, shape)
     if workspace is None:
         workspace = torch.empty(max(stats_workspace_bytes(L, T, k, E, R), 256), dtype=torch.uint8, device=dev)
     lib = _lib.load()
@@ -315,7 +337,7 @@ def prob_signature(logits: torch.Tensor, req_offsets: torch.Tensor,
     dev = logits.device
     if out is None:
         out = torch.empty((R, L, E), dtype=torch.float32, device=dev)
-    _need(out, "out", torch.float32, 3)
+    _out(out, "out", torch.float32, (R, L, E))
     lib = _lib.load()
     check("moe_prob_signature", lib.moe_prob_signature(_ptr(logits), L, T, E, _ptr(req_offsets), R, _ptr(out),
                                                        _stream(dev)))

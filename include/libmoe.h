@@ -199,6 +199,12 @@ moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t 
  *   accumulated row product.  Runs on the decode-shaped kernel (any group
  *   sizes; meant for decode-sized groups).
  *   Requires d and I multiples of 16; every pointer 16-byte aligned.
+ *   Errors: MOE_ERR_UNSUPPORTED when d or I is not a multiple of 16 or
+ *   E > 512; MOE_ERR_INVALID_ARG for nseg outside {1, 2}, a NULL required
+ *   pointer (the three scale arrays included) or a misaligned one;
+ *   MOE_ERR_WORKSPACE for a workspace below the queried size.  The workspace
+ *   holds the bf16 SwiGLU intermediate [n_rows][I]; its last 4 bytes are
+ *   written 0 by every call with n_rows > 0 (this call has no bounded waits).
  */
 moe_status moe_grouped_ffn_fp8w(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
                                 const int32_t* group_offsets, int32_t n_rows, int32_t E,

@@ -46,7 +46,7 @@ _lib = None
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libmoe.so once.  Raises ImportError if it has not been built.
 
-    torch must be imported first on a GPU machine so that the library binds to the
+    torch must be imported first on a machine with a GPU so that the library binds to the
     same HIP runtime as torch's allocator and streams.
     """
     global _lib

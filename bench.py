@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--fp8-weights", action="store_true",
                     help="expert weights as E4M3 codes with per-row scales (moe_grouped_ffn_fp8w); the CPU "
                          "baseline leg is skipped in this mode")
+    ap.add_argument("--unpacked-weights", action="store_true",
+                    help="keep the [E+S][rows][K] weight layout (moe_grouped_ffn) on decode-sized bf16 "
+                         "workloads; by default their weights are pre-packed once before timing "
+                         "(pack_weights) and the FFN runs moe_grouped_ffn_packed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle leg")
     ap.add_argument("--json-out", default="", help="also append the JSON line to this file")
@@ -271,6 +275,10 @@ def main():
     if fp8 and s.dtype != "bf16":
         print("--fp8-weights needs a bf16 workload", file=sys.stderr)
         sys.exit(2)
+    # decode-sized bf16 batches run on pre-packed weights unless asked otherwise
+    packable = (not fp8 and s.dtype == "bf16" and s.d % 32 == 0 and s.I % 32 == 0 and
+                s.N <= moe.PACKED_MAX_AVG_ROWS * ((2 if s.n_priority else 1) * s.E + s.S))
+    packed = packable and not args.unpacked_weights
     if fp8 and s.n_priority > 0:
         # its one run ended in a GPU memory fault whose cause has not been
         # found (a host-side model of the FP8 kernel's work items and address
@@ -287,9 +295,12 @@ def main():
         base = (q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1])
         wsets = [base] + [tuple(t.clone() for t in base) for _ in range(copies - 1)]
     else:
-        wsets = [(wl.w_gate, wl.w_up, wl.w_down)]
+        base = (wl.w_gate, wl.w_up, wl.w_down)
+        if packed:
+            base = tuple(moe.pack_weights(w) for w in base)
+        wsets = [base]
         for _ in range(copies - 1):
-            wsets.append((wl.w_gate.clone(), wl.w_up.clone(), wl.w_down.clone()))
+            wsets.append(tuple(w.clone() for w in base))
 
     # the gate writes the routing layer's ids straight into layer 0 of the
     # statistics stack
@@ -298,7 +309,8 @@ def main():
     if args.router:
         g = torch.Generator().manual_seed(1234)
         w_router = (torch.randn((s.E, s.d), generator=g) * 0.02).to(wl.torch_dtype).to(dev)
-    layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, wl.w_gate, wl.w_up, wl.w_down,
+    w16 = (wl.w_gate, wl.w_up, wl.w_down) if fp8 else wsets[0]     # the layer's bf16 / fp32 weights
+    layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, *w16, packed_weights=packed,
                          n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize),
                          stats_layers=s.stats_layers, req_offsets=wl.req_offsets, device=dev,
                          topk_ids=stats_ids[0], w_router=w_router, fp8_weights=wsets[0] if fp8 else None)
@@ -390,7 +402,7 @@ def main():
     N = s.N
     ffn_bytes = used_experts * expert_bytes + 2 * N * s.d * esize
     ffn_flops = 2.0 * N * 3 * s.d * s.I
-    ffn_name = "moe_grouped_ffn_fp8w" if fp8 else "moe_grouped_ffn"
+    ffn_name = "moe_grouped_ffn_fp8w" if fp8 else "moe_grouped_ffn_packed" if packed else "moe_grouped_ffn"
     ffn_s = per_call[ffn_name] * 1e-3
     peak_flops = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
     intensity = ffn_flops / ffn_bytes
@@ -403,7 +415,8 @@ def main():
         achieved = ffn_flops / ffn_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_flops, "unit": "TFLOP/s",
                 "frac": round(achieved / peak_flops, 4)}
-    traffic = None if fp8 else traffic_for(args.workload)
+    # the committed counters are for the default mode of each workload
+    traffic = None if fp8 or args.unpacked_weights else traffic_for(args.workload)
     roof["traffic"] = None if traffic is None else round(traffic)
     roof["kernel"] = f"{ffn_name} (gate/up launch + down launch), HIP events over K eager steps"
     roof["algorithmic_bytes"] = int(ffn_bytes)
@@ -421,7 +434,8 @@ def main():
         "config": {"workload": args.workload, "T": s.T, "E": s.E, "k": s.k, "n_shared": s.S, "d": s.d,
                    "I": s.I, "n_priority": s.n_priority, "stats_layers": s.stats_layers,
                    "weight_copies": copies, "union": union, "router": bool(args.router),
-                   "expert_weights": "fp8_e4m3 + fp32 row scales" if fp8 else s.dtype},
+                   "expert_weights": "fp8_e4m3 + fp32 row scales" if fp8 else
+                   f"{s.dtype}, packed 16x32 blocks" if packed else s.dtype},
         "roofline": roof,
         "per_call_us": {n: round(v * 1e3, 2) for n, v in per_call.items()},
         "timing": "eager launches" if args.eager else

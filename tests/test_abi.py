@@ -27,7 +27,7 @@ def _declared():
 
 
 def test_header_declares_the_calls():
-    assert _declared() == sorted(["moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_fp8w",
+    assert _declared() == sorted(["moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_packed", "moe_grouped_ffn_fp8w",
                                   "moe_combine", "moe_stats", "moe_prob_signature", "moe_status_string"])
 
 
@@ -90,6 +90,22 @@ def test_ffn_fp8w_validation_and_query(lib):
     big = ctypes.c_size_t(1 << 30)
     assert f(*args(a17=FAKE, a18=ctypes.byref(big), a11=None)) == INV   # NULL scale
     assert f(*args(a17=FAKE, a18=ctypes.byref(big), a10=FAKE + 8)) == INV   # misaligned weights
+
+
+def test_ffn_packed_validation_and_query(lib):
+    f = lib.moe_grouped_ffn_packed
+    n = ctypes.c_size_t(0)
+    args = lambda **kw: [kw.get(f"a{i}", v) for i, v in enumerate(
+        [FAKE, None, 0, FAKE, 64, 8, 0, 1, 256, 512, FAKE, FAKE, FAKE, FAKE, None, ctypes.byref(n), None])]
+    assert f(*args()) == 0 and n.value >= 64 * 512 * 2            # query (workspace of moe_grouped_ffn)
+    assert f(*args(a8=272)) == UNS                                 # d not a multiple of 32
+    assert f(*args(a9=528)) == UNS                                 # I not a multiple of 32
+    assert f(*args(a4=49 * 8 + 1)) == UNS                          # groups above 48 rows on average
+    assert f(*args(a4=48 * 8)) == 0                                # 48 on average is accepted
+    assert f(*args(a7=3)) == INV                                   # nseg
+    big = ctypes.c_size_t(1 << 30)
+    assert f(*args(a14=FAKE, a15=ctypes.byref(big), a12=None)) == INV       # NULL w_down
+    assert f(*args(a14=FAKE, a15=ctypes.byref(big), a10=FAKE + 8)) == INV   # misaligned weights
 
 
 def test_gate_validation(lib):

@@ -549,3 +549,43 @@ def test_bindings_reject_mismatched_outputs():
     with pytest.raises(ValueError):
         moe.router(torch.zeros((T, d), dtype=torch.bfloat16, device=dev),
                    torch.zeros((E, d), dtype=torch.bfloat16, device=dev), torch.empty((T, E - 1), device=dev))
+
+
+PACKED_CASES = [
+    # (T, E, k, S, P, d, I, kind)
+    (128, 64, 8, 0, 0, 2048, 1024, "random"),   # OLMoE decode shape: 32-row tiles
+    (256, 64, 6, 2, 0, 2048, 1408, "zipf"),     # DSv2-Lite T=256 shape: 64-row tiles, shared experts
+    (16, 64, 6, 2, 0, 2048, 1408, "zipf"),      # DSv2-Lite T=16 shape: split-K kernel
+    (24, 16, 2, 1, 6, 96, 160, "random"),       # split-K with a priority segment and a shared expert
+    (300, 8, 2, 0, 20, 256, 192, "random"),     # 64-row tiles with a priority segment, column tail
+    (4, 512, 4, 256, 2, 64, 32, "random"),      # the largest group count (1280)
+]
+
+
+@pytest.mark.parametrize("T,E,k,S,P,d,I,kind", PACKED_CASES)
+def test_grouped_ffn_packed_parity(T, E, k, S, P, d, I, kind):
+    """Pre-packed weights: within the bf16 tolerance of the oracle on sampled rows,
+    and bit for bit the unpacked call's result (the same products in the same
+    order, only read from other addresses), directly and through the row list."""
+    announce(f"ffn packed T={T} E={E} k={k} S={S} P={P} d={d} I={I} {kind}")
+    wl, ids = _ffn_inputs(T, E, k, S, P, d, I, "bf16", kind, seed=T + E + 3)
+    nseg = 2 if P > 0 else 1
+    p_ref = O.permute(ids.numpy(), E, S, P, np_of(wl.x))
+    N = int(p_ref["group_offsets"][-1])
+    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 48)), [N - 1]]))
+    h_ref = O.grouped_ffn(p_ref["x_sorted"], p_ref["group_offsets"], E, S, nseg, np_of(wl.w_gate),
+                          np_of(wl.w_up), np_of(wl.w_down), "bf16", rows=rows)
+    xs = torch.from_numpy(p_ref["x_sorted"].view(np.int16)).view(torch.bfloat16).to(DEV)
+    offs = torch.from_numpy(p_ref["group_offsets"]).to(DEV)
+    w = [t.to(DEV) for t in (wl.w_gate, wl.w_up, wl.w_down)]
+    wp = [moe.pack_weights(t) for t in w]
+    h_plain = moe.grouped_ffn(xs, offs, E, S, nseg, *w, h_sorted=_poison((N, d), torch.bfloat16))
+    h = moe.grouped_ffn_packed(xs, offs, E, S, nseg, *wp, h_sorted=_poison((N, d), torch.bfloat16))
+    tok = torch.from_numpy(p_ref["sorted_token"]).to(DEV)
+    h2 = moe.grouped_ffn_packed(wl.x.to(DEV), offs, E, S, nseg, *wp, h_sorted=_poison((N, d), torch.bfloat16),
+                                x_rows=tok)
+    torch.cuda.synchronize()
+    err = rel_max_err(f64_of(h[torch.from_numpy(rows).to(DEV)]), h_ref)
+    assert err <= TOL["bf16"], err
+    assert torch.equal(h, h_plain)
+    assert torch.equal(h2, h)

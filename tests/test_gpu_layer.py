@@ -150,3 +150,22 @@ def test_layer_fp8_weights_parity(name):
     y_ref = O.combine(h, f2s, w, T, k, s.S, tokens=toks, row_of_sorted={int(n): i for i, n in enumerate(need)})
     y_err = rel_max_err(f64_of(layer.y[torch.from_numpy(toks).to(DEV)]), y_ref)
     assert y_err <= TOL[s.dtype], y_err
+
+
+@pytest.mark.parametrize("name", ["olmoe_decode", "dsv2_decode_t16", "dsv2_decode_t256"])
+def test_layer_packed_weights_matches_unpacked(name):
+    """The layer on pre-packed weights gives the unpacked layer's outputs bit for
+    bit (that layer is checked against the oracle in test_layer_parity)."""
+    announce(f"layer {name} with packed weights")
+    wl = workloads.make(name, DEV)
+    s = wl.spec
+    kw = dict(n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize), device=DEV)
+    plain = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, wl.w_gate, wl.w_up, wl.w_down, **kw)
+    packed = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, *(moe.pack_weights(w) for w in
+                                                                     (wl.w_gate, wl.w_up, wl.w_down)),
+                          packed_weights=True, **kw)
+    plain.forward(wl.logits, wl.x)
+    packed.forward(wl.logits, wl.x)
+    torch.cuda.synchronize()
+    assert torch.equal(packed.h_sorted, plain.h_sorted)
+    assert torch.equal(packed.y, plain.y)

@@ -199,6 +199,57 @@ def grouped_ffn(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_s
     return h_sorted
 
 
+PACKED_MAX_AVG_ROWS = 48
+
+
+def pack_weights(w: torch.Tensor) -> torch.Tensor:
+    """Expert matrices [..][R][K] in the layout moe_grouped_ffn_packed reads:
+    blocks of 16 rows x 32 K values, block (r/16, k/32) at element offset
+    ((r/16) * (K/32) + k/32) * 512 of each matrix, and W[r][k] at
+    (((k%32)/8) * 16 + r%16) * 8 + k%8 inside its block.  The result keeps the
+    input's shape (and each matrix its place); a one-time weight preparation."""
+    *lead, R, K = w.shape
+    if R % 16 != 0 or K % 32 != 0:
+        raise ValueError("packing needs rows % 16 == 0 and K % 32 == 0")
+    v = w.reshape(*lead, R // 16, 16, K // 32, 4, 8)       # r = 16 rb + r16, k = 32 kb + 8 q + t
+    n = len(lead)
+    return v.permute(*range(n), n, n + 2, n + 3, n + 1, n + 4).contiguous().reshape(w.shape)
+
+
+def grouped_ffn_packed(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_shared: int, nseg: int,
+                       w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                       h_sorted: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       x_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """grouped_ffn for bf16 decode-sized batches with weights from pack_weights."""
+    _need(x_sorted, "x_sorted", torch.bfloat16, 2)
+    _need(group_offsets, "group_offsets", torch.int32, 1)
+    for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(w, name, torch.bfloat16, 3)
+    n_x, d = x_sorted.shape
+    N = n_x
+    if x_rows is not None:
+        _need(x_rows, "x_rows", torch.int32, 1)
+        N = x_rows.numel()
+    I = w_gate.shape[1]
+    if w_gate.shape != (E + n_shared, I, d) or w_up.shape != w_gate.shape or w_down.shape != (E + n_shared, d, I):
+        raise ValueError("expert weight shapes do not match [E+S][I][d] / [E+S][d][I]")
+    if group_offsets.numel() != nseg * E + n_shared + 1:
+        raise ValueError("group_offsets must have nseg*E + n_shared + 1 entries")
+    dev = x_sorted.device
+    if h_sorted is None:
+        h_sorted = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
+    _out(h_sorted, "h_sorted", torch.bfloat16, (N, d))
+    if workspace is None:
+        workspace = torch.empty(max(ffn_workspace_bytes(N, E, n_shared, nseg, d, I, torch.bfloat16), 256),
+                                dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    nbytes = ctypes.c_size_t(workspace.numel())
+    check("moe_grouped_ffn_packed", lib.moe_grouped_ffn_packed(
+        _ptr(x_sorted), _ptr(x_rows), n_x, _ptr(group_offsets), N, E, n_shared, nseg, d, I, _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), _ptr(h_sorted), _ptr(workspace), ctypes.byref(nbytes), _stream(dev)))
+    return h_sorted
+
+
 def ffn_fp8w_workspace_bytes(n_rows, I) -> int:
     lib = _lib.load()
     n = ctypes.c_size_t(0)
@@ -357,11 +408,14 @@ class MoeLayer:
 
     def __init__(self, E, k, d, I, T, dtype, w_gate, w_up, w_down, n_shared=0, n_priority=0,
                  renormalize=True, stats_layers=0, req_offsets=None, device="cuda", topk_ids=None,
-                 fused_gather=True, w_router=None, fp8_weights=None):
+                 fused_gather=True, w_router=None, fp8_weights=None, packed_weights=False):
         dev = torch.device(device)
         # fp8_weights = (codes_gate, scales_gate, codes_up, scales_up, codes_down, scales_down):
         # the FFN runs moe_grouped_ffn_fp8w on them instead of w_gate / w_up / w_down
         self.fp8_weights = fp8_weights
+        # packed_weights: w_gate / w_up / w_down come from pack_weights and the FFN
+        # runs moe_grouped_ffn_packed (bf16, decode-sized batches)
+        self.packed = bool(packed_weights)
         self.w_router = w_router
         self.logits = torch.empty((T, E), dtype=torch.float32, device=dev) if w_router is not None else None
         self.E, self.k, self.d, self.I, self.T = E, k, d, I, T
@@ -416,6 +470,11 @@ class MoeLayer:
             return grouped_ffn_fp8w(src, self.perm["group_offsets"], self.E, self.S, self.nseg, *self.fp8_weights,
                                     h_sorted=self.h_sorted, workspace=self.ffn_ws,
                                     x_rows=self.perm["sorted_token"] if self.fused_gather else None)
+        if self.packed:
+            src = x if self.fused_gather else self.perm["x_sorted"]
+            return grouped_ffn_packed(src, self.perm["group_offsets"], self.E, self.S, self.nseg, self.w_gate,
+                                      self.w_up, self.w_down, self.h_sorted, self.ffn_ws,
+                                      x_rows=self.perm["sorted_token"] if self.fused_gather else None)
         if self.fused_gather:
             return grouped_ffn(x, self.perm["group_offsets"], self.E, self.S, self.nseg, self.w_gate, self.w_up,
                                self.w_down, self.h_sorted, self.ffn_ws, x_rows=self.perm["sorted_token"])
@@ -492,6 +551,11 @@ class MoeLayer:
             return ("moe_grouped_ffn_fp8w", lib.moe_grouped_ffn_fp8w, (
                 src, rows, self.T, offs, self.N, self.E, self.S, self.nseg, self.d, self.I, qg, sg, qu, su, qd, sd,
                 self.h_sorted.data_ptr(), self.ffn_ws.data_ptr(), ctypes.byref(n_ffn), st))
+        if self.packed:
+            return ("moe_grouped_ffn_packed", lib.moe_grouped_ffn_packed, (
+                src, rows, self.T, offs, self.N, self.E, self.S, self.nseg, self.d, self.I, self.w_gate.data_ptr(),
+                self.w_up.data_ptr(), self.w_down.data_ptr(), self.h_sorted.data_ptr(), self.ffn_ws.data_ptr(),
+                ctypes.byref(n_ffn), st))
         return ("moe_grouped_ffn", lib.moe_grouped_ffn, (
             src, rows, self.T, offs, self.N, self.E, self.S, self.nseg, self.d, self.I, self.w_gate.data_ptr(),
             self.w_up.data_ptr(), self.w_down.data_ptr(), dt, self.h_sorted.data_ptr(), self.ffn_ws.data_ptr(),

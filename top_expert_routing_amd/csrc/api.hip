@@ -173,6 +173,50 @@ moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t 
   return hip_status(moe::launch_ffn(a, workspace, stream));
 }
 
+moe_status moe_grouped_ffn_packed(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                                  const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
+                                  int32_t nseg, int32_t d, int32_t I, const void* w_gate, const void* w_up,
+                                  const void* w_down, void* h_sorted, void* workspace, size_t* workspace_bytes,
+                                  hipStream_t stream) {
+  if (n_rows < 0 || E < 1 || n_shared < 0 || (nseg != 1 && nseg != 2) || d < 1 || I < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
+  if (d % 32 != 0 || I % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long G = static_cast<long long>(nseg) * E + n_shared;
+  if (n_rows > MOE_PACKED_MAX_AVG_ROWS * G) return MOE_ERR_UNSUPPORTED;   // GEMM-sized groups
+  if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
+    return MOE_ERR_UNSUPPORTED;
+  bool query;
+  moe_status st = workspace_check(workspace, workspace_bytes,
+                                  moe::ffn_workspace_bytes(n_rows, E, n_shared, nseg, d, I, 1), &query);
+  if (st != MOE_OK || query) return st;
+  if (n_rows == 0) return MOE_OK;
+  if (!x_sorted || !group_offsets || !w_gate || !w_up || !w_down || !h_sorted) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_sorted) || !aligned4(group_offsets) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(h_sorted))
+    return MOE_ERR_INVALID_ARG;
+  if (x_rows && (!aligned4(x_rows) || n_x < 1)) return MOE_ERR_INVALID_ARG;
+  if (x_rows && !fits_int(static_cast<long long>(n_x) * d)) return MOE_ERR_UNSUPPORTED;
+  moe::FfnArgs a;
+  a.x_sorted = x_sorted;
+  a.x_rows = x_rows;
+  a.n_x = x_rows ? n_x : n_rows;
+  a.group_offsets = group_offsets;
+  a.n_rows = n_rows;
+  a.E = E;
+  a.n_shared = n_shared;
+  a.nseg = nseg;
+  a.d = d;
+  a.I = I;
+  a.w_gate = w_gate;
+  a.w_up = w_up;
+  a.w_down = w_down;
+  a.bf16 = 1;
+  a.h_sorted = h_sorted;
+  a.packed = true;
+  return hip_status(moe::launch_ffn(a, workspace, stream));
+}
+
 moe_status moe_grouped_ffn_fp8w(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
                                 const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
                                 int32_t nseg, int32_t d, int32_t I, const void* w_gate, const float* s_gate,

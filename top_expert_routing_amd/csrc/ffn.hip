@@ -239,7 +239,7 @@ template <int MF>
 constexpr int decode_kc() { return MF <= 2 ? 256 : 128; }
 constexpr int kDecodeWavesPerSimd = 4;
 
-template <int MF, int NFC, int PHASE>
+template <int MF, int NFC, int PHASE, bool PK = false>
 __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void ffn_decode_bf16(
     const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
     int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
@@ -268,7 +268,8 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
   for (int j = 0; j < NF; ++j) {
     const int n = min(col0 + (j % NFC) * 16 + l16, Ncols - 1);
     const uint16_t* W = (PHASE == 1 && j >= NFC) ? W1 : W0;
-    bp[j] = W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n) * K + 8 * q;
+    bp[j] = PK ? W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n / 16) * (K / 32) * 512 + lane * 8
+               : W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n) * K + 8 * q;
   }
 
   // A staging: thread handles uint4 slots idx = tid + s*256 of the chunk
@@ -313,7 +314,8 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
       const int kk = kc + 32 * u + 8 * q;
 #pragma unroll
       for (int j = 0; j < NF; ++j)
-        b[u][j] = kk < K ? *reinterpret_cast<const uint4*>(bp[j] + kc + 32 * u) : make_uint4(0, 0, 0, 0);
+        b[u][j] = kk < K ? *reinterpret_cast<const uint4*>(bp[j] + (PK ? (kc + 32 * u) * 16 : kc + 32 * u))
+                         : make_uint4(0, 0, 0, 0);
     }
   };
   auto mma = [&](const uint4 (&b)[U][NF], const uint16_t* as) {
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
 //     the wave's K range.
 //   * The waves add their partial sums through LDS; each stores a share of the
 //     item's 16x16 output blocks (SwiGLU applied in phase 1).
-template <int NFC, int PHASE>
+template <int NFC, int PHASE, bool PK = false>
 __global__ __launch_bounds__(kThreads, kDecodeWavesPerSimd) void ffn_decode_splitk_bf16(
     const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
     int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
@@ -415,7 +417,8 @@ __global__ __launch_bounds__(kThreads, kDecodeWavesPerSimd) void ffn_decode_spli
   for (int j = 0; j < NF; ++j) {
     const int n = min(col0 + (j % NFC) * 16 + l16, Ncols - 1);
     const uint16_t* W = (PHASE == 1 && j >= NFC) ? W1 : W0;
-    bp[j] = W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n) * K + 8 * q;
+    bp[j] = PK ? W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n / 16) * (K / 32) * 512 + lane * 8
+               : W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n) * K + 8 * q;
   }
   f32x4 acc[NF];
 #pragma unroll
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(kThreads, kDecodeWavesPerSimd) void ffn_decode_spli
     for (int u = 0; u < U; ++u) {
       const int ko = koff(mask, kc + 32 * u);
 #pragma unroll
-      for (int j = 0; j < NF; ++j) b[u][j] = *reinterpret_cast<const uint4*>(bp[j] + ko);
+      for (int j = 0; j < NF; ++j) b[u][j] = *reinterpret_cast<const uint4*>(bp[j] + (PK ? ko * 16 : ko));
     }
   };
   auto load_a = [&](auto mask, int kc) {
@@ -1523,33 +1526,34 @@ constexpr int kDecodeNfc2 = 2;
 
 // Groups of at most kSplitKMaxAvg rows on average: the split-K kernel, 16
 // columns per item in phase 1 and 32 in phase 2 (tiles of 16 rows).
+template <bool PK>
 void launch_decode_splitk_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, uint16_t* abuf,
                                hipStream_t stream) {
   constexpr int NFC1 = 1, NFC2 = 2;
   const int nch1 = (a.I + 16 * NFC1 - 1) / (16 * NFC1), nch2 = (a.d + 16 * NFC2 - 1) / (16 * NFC2);
-  hipLaunchKernelGGL((ffn_decode_splitk_bf16<NFC1, 1>), dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((ffn_decode_splitk_bf16<NFC1, 1, PK>), dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
                      static_cast<const uint16_t*>(a.w_up), a.I, plan, abuf);
   PlanArgs plan2 = plan;
   plan2.diag = nullptr;
   plan2.arows = nullptr;
-  hipLaunchKernelGGL((ffn_decode_splitk_bf16<NFC2, 2>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((ffn_decode_splitk_bf16<NFC2, 2, PK>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
                      static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted));
 }
 
-template <int MF>
+template <int MF, bool PK>
 void launch_decode_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, uint16_t* abuf,
                         hipStream_t stream) {
   const int bn1 = kWaves * 16 * kDecodeNfc1, bn2 = kWaves * 16 * kDecodeNfc2;
   const int nch1 = (a.I + bn1 - 1) / bn1, nch2 = (a.d + bn2 - 1) / bn2;
-  hipLaunchKernelGGL((ffn_decode_bf16<MF, kDecodeNfc1, 1>), dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((ffn_decode_bf16<MF, kDecodeNfc1, 1, PK>), dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
                      static_cast<const uint16_t*>(a.w_up), a.I, plan, abuf);
   PlanArgs plan2 = plan;
   plan2.diag = nullptr;
   plan2.arows = nullptr;
-  hipLaunchKernelGGL((ffn_decode_bf16<MF, kDecodeNfc2, 2>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((ffn_decode_bf16<MF, kDecodeNfc2, 2, PK>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
                      static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted));
 }
@@ -1696,16 +1700,28 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
   plan.diag = reinterpret_cast<int*>(ws + L.total - 4);
   plan.arows = a.x_rows;
   plan.n_x = a.n_x;
+  if (a.packed && L.path != Path::kDecode) return hipErrorInvalidValue;
   switch (L.path) {
     case Path::kDecode: {
       uint16_t* abuf = reinterpret_cast<uint16_t*>(ws + L.a_off);
+      if (a.packed) {
+        switch (L.BM / 16) {
+          case 1:
+            if (L.splitk) launch_decode_splitk_bf16<true>(a, L, plan, abuf, stream);
+            else launch_decode_bf16<1, true>(a, L, plan, abuf, stream);
+            break;
+          case 2: launch_decode_bf16<2, true>(a, L, plan, abuf, stream); break;
+          default: launch_decode_bf16<4, true>(a, L, plan, abuf, stream); break;
+        }
+        break;
+      }
       switch (L.BM / 16) {
         case 1:
-          if (L.splitk) launch_decode_splitk_bf16(a, L, plan, abuf, stream);
-          else launch_decode_bf16<1>(a, L, plan, abuf, stream);
+          if (L.splitk) launch_decode_splitk_bf16<false>(a, L, plan, abuf, stream);
+          else launch_decode_bf16<1, false>(a, L, plan, abuf, stream);
           break;
-        case 2: launch_decode_bf16<2>(a, L, plan, abuf, stream); break;
-        default: launch_decode_bf16<4>(a, L, plan, abuf, stream); break;
+        case 2: launch_decode_bf16<2, false>(a, L, plan, abuf, stream); break;
+        default: launch_decode_bf16<4, false>(a, L, plan, abuf, stream); break;
       }
       break;
     }

@@ -48,6 +48,8 @@ struct FfnArgs {
   const float* s_gate = nullptr;
   const float* s_up = nullptr;
   const float* s_down = nullptr;
+  // bf16 weights pre-packed in 16-row x 32-K blocks (moe_grouped_ffn_packed)
+  bool packed = false;
 };
 size_t ffn_workspace_bytes(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16);
 hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream);

@@ -279,6 +279,8 @@ def main():
     packable = (not fp8 and s.dtype == "bf16" and s.d % 32 == 0 and s.I % 32 == 0 and
                 s.N <= moe.PACKED_MAX_AVG_ROWS * ((2 if s.n_priority else 1) * s.E + s.S))
     packed = packable and not args.unpacked_weights
+    # FP8 codes are packed too when d and I are multiples of 64
+    fp8_packed = fp8 and s.d % 64 == 0 and s.I % 64 == 0 and not args.unpacked_weights
     if fp8 and s.n_priority > 0:
         # its one run ended in a GPU memory fault whose cause has not been
         # found (a host-side model of the FP8 kernel's work items and address
@@ -292,6 +294,8 @@ def main():
     copies = args.weight_copies or max(1, int(np.ceil(3 * 2**30 / all_w)))
     if fp8:
         q = [moe.quantize_fp8_rows(w) for w in (wl.w_gate, wl.w_up, wl.w_down)]
+        if fp8_packed:
+            q = [(moe.pack_fp8_codes(c), sc) for c, sc in q]
         base = (q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1])
         wsets = [base] + [tuple(t.clone() for t in base) for _ in range(copies - 1)]
     else:
@@ -310,7 +314,7 @@ def main():
         g = torch.Generator().manual_seed(1234)
         w_router = (torch.randn((s.E, s.d), generator=g) * 0.02).to(wl.torch_dtype).to(dev)
     w16 = (wl.w_gate, wl.w_up, wl.w_down) if fp8 else wsets[0]     # the layer's bf16 / fp32 weights
-    layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, *w16, packed_weights=packed,
+    layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, *w16, packed_weights=packed or fp8_packed,
                          n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize),
                          stats_layers=s.stats_layers, req_offsets=wl.req_offsets, device=dev,
                          topk_ids=stats_ids[0], w_router=w_router, fp8_weights=wsets[0] if fp8 else None)
@@ -402,7 +406,8 @@ def main():
     N = s.N
     ffn_bytes = used_experts * expert_bytes + 2 * N * s.d * esize
     ffn_flops = 2.0 * N * 3 * s.d * s.I
-    ffn_name = "moe_grouped_ffn_fp8w" if fp8 else "moe_grouped_ffn_packed" if packed else "moe_grouped_ffn"
+    ffn_name = ("moe_grouped_ffn_fp8w_packed" if fp8_packed else "moe_grouped_ffn_fp8w") if fp8 else \
+        "moe_grouped_ffn_packed" if packed else "moe_grouped_ffn"
     ffn_s = per_call[ffn_name] * 1e-3
     peak_flops = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
     intensity = ffn_flops / ffn_bytes
@@ -434,7 +439,8 @@ def main():
         "config": {"workload": args.workload, "T": s.T, "E": s.E, "k": s.k, "n_shared": s.S, "d": s.d,
                    "I": s.I, "n_priority": s.n_priority, "stats_layers": s.stats_layers,
                    "weight_copies": copies, "union": union, "router": bool(args.router),
-                   "expert_weights": "fp8_e4m3 + fp32 row scales" if fp8 else
+                   "expert_weights": ("fp8_e4m3 + fp32 row scales" + (", packed 16x64 blocks" if fp8_packed else ""))
+                   if fp8 else
                    f"{s.dtype}, packed 16x32 blocks" if packed else s.dtype},
         "roofline": roof,
         "per_call_us": {n: round(v * 1e3, 2) for n, v in per_call.items()},

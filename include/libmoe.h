@@ -244,6 +244,29 @@ moe_status moe_grouped_ffn_fp8w(const void* x_sorted, const int32_t* x_rows, int
                                 hipStream_t stream);
 
 /*
+ * moe_grouped_ffn_fp8w_packed - moe_grouped_ffn_fp8w on pre-packed codes.
+ * (ExpertPlex page, "Experimental results", models table, as above; the
+ * packing is a one-time weight layout, not a change of the computation.)
+ *
+ *   As moe_grouped_ffn_fp8w, except that each code matrix C [R][K] of an
+ *   expert is stored as blocks of 16 rows x 64 codes (1 KiB): block
+ *   (r / 16, k / 64) at byte offset ((r / 16) * (K / 64) + k / 64) * 1024 of
+ *   the expert's matrix, and C[r][k] at (((k % 64) / 16) * 16 + r % 16) * 16 +
+ *   k % 16 inside it.  Each expert's matrix keeps its R * K bytes at the same
+ *   place as in the unpacked array; the scales are unchanged.  The results
+ *   equal moe_grouped_ffn_fp8w's on the unpacked codes bit for bit.
+ *   Requires d and I multiples of 64 (MOE_ERR_UNSUPPORTED otherwise).
+ */
+moe_status moe_grouped_ffn_fp8w_packed(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                                const int32_t* group_offsets, int32_t n_rows, int32_t E,
+                                int32_t n_shared, int32_t nseg, int32_t d, int32_t I,
+                                const void* w_gate, const float* s_gate,
+                                const void* w_up, const float* s_up,
+                                const void* w_down, const float* s_down,
+                                void* h_sorted, void* workspace, size_t* workspace_bytes,
+                                hipStream_t stream);
+
+/*
  * moe_combine - gate-weighted combine back to token order.
  * (GRACE-MoE page, section 1: the combine exchange.)
  *

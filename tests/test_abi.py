@@ -28,6 +28,7 @@ def _declared():
 
 def test_header_declares_the_calls():
     assert _declared() == sorted(["moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_packed", "moe_grouped_ffn_fp8w",
+                                  "moe_grouped_ffn_fp8w_packed",
                                   "moe_combine", "moe_stats", "moe_prob_signature", "moe_status_string"])
 
 
@@ -90,6 +91,10 @@ def test_ffn_fp8w_validation_and_query(lib):
     big = ctypes.c_size_t(1 << 30)
     assert f(*args(a17=FAKE, a18=ctypes.byref(big), a11=None)) == INV   # NULL scale
     assert f(*args(a17=FAKE, a18=ctypes.byref(big), a10=FAKE + 8)) == INV   # misaligned weights
+    fp = lib.moe_grouped_ffn_fp8w_packed
+    assert fp(*args()) == 0                                        # d = 256, I = 512: multiples of 64
+    assert fp(*args(a8=272)) == UNS                                # d a multiple of 16 but not of 64
+    assert fp(*args(a9=528)) == UNS                                # I a multiple of 16 but not of 64
 
 
 def test_ffn_packed_validation_and_query(lib):

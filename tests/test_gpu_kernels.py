@@ -493,6 +493,14 @@ def test_grouped_ffn_fp8w_parity(T, E, k, S, P, d, I, kind):
                               qd.to(DEV), sd.to(DEV), h_sorted=_poison((xs.shape[0], d), torch.bfloat16), x_rows=rows)
     torch.cuda.synchronize()
     assert torch.equal(h2, h)
+    if d % 64 == 0 and I % 64 == 0:
+        # pre-packed codes: the same products in the same order, so the same bits
+        h3 = moe.grouped_ffn_fp8w(wl.x.to(DEV), offs, E, S, nseg, moe.pack_fp8_codes(qg.to(DEV)), sg.to(DEV),
+                                  moe.pack_fp8_codes(qu.to(DEV)), su.to(DEV), moe.pack_fp8_codes(qd.to(DEV)),
+                                  sd.to(DEV), h_sorted=_poison((xs.shape[0], d), torch.bfloat16), x_rows=rows,
+                                  packed=True)
+        torch.cuda.synchronize()
+        assert torch.equal(h3, h)
 
 
 def test_ffn_bindings_reject_mismatched_shapes():

@@ -150,6 +150,14 @@ def test_layer_fp8_weights_parity(name):
     y_ref = O.combine(h, f2s, w, T, k, s.S, tokens=toks, row_of_sorted={int(n): i for i, n in enumerate(need)})
     y_err = rel_max_err(f64_of(layer.y[torch.from_numpy(toks).to(DEV)]), y_ref)
     assert y_err <= TOL[s.dtype], y_err
+    # the same layer on pre-packed codes: the same bits
+    fp8p = (moe.pack_fp8_codes(fp8[0]), fp8[1], moe.pack_fp8_codes(fp8[2]), fp8[3], moe.pack_fp8_codes(fp8[4]), fp8[5])
+    lp = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, wl.w_gate, wl.w_up, wl.w_down, n_shared=s.S,
+                      n_priority=s.n_priority, renormalize=bool(s.renormalize), device=DEV, fp8_weights=fp8p,
+                      packed_weights=True)
+    lp.forward(wl.logits, wl.x)
+    torch.cuda.synchronize()
+    assert torch.equal(lp.y, layer.y)
 
 
 @pytest.mark.parametrize("name", ["olmoe_decode", "dsv2_decode_t16", "dsv2_decode_t256"])

@@ -47,3 +47,17 @@ def test_shapes_that_do_not_tile_are_refused():
         moe.pack_weights(torch.zeros(1, 24, 32))
     with pytest.raises(ValueError):
         moe.pack_weights(torch.zeros(1, 16, 48))
+
+
+@pytest.mark.parametrize("E,R,K", [(1, 16, 64), (2, 32, 128)])
+def test_fp8_codes_land_at_their_offsets(E, R, K):
+    q = torch.randint(0, 256, (E, R, K), dtype=torch.uint8, generator=torch.Generator().manual_seed(R + K))
+    flat = moe.pack_fp8_codes(q).reshape(E, R * K)
+    for e, r, k in itertools.product(range(E), range(R), range(K)):
+        off = ((r // 16) * (K // 64) + k // 64) * 1024 + (((k % 64) // 16) * 16 + r % 16) * 16 + k % 16
+        assert flat[e, off] == q[e, r, k]
+
+
+def test_fp8_shapes_that_do_not_tile_are_refused():
+    with pytest.raises(ValueError):
+        moe.pack_fp8_codes(torch.zeros(1, 16, 96, dtype=torch.uint8))

@@ -270,12 +270,27 @@ def quantize_fp8_rows(w: torch.Tensor):
     return q.contiguous(), s.contiguous()
 
 
+def pack_fp8_codes(q: torch.Tensor) -> torch.Tensor:
+    """E4M3 code matrices [..][R][K] (uint8) in the layout
+    moe_grouped_ffn_fp8w_packed reads: blocks of 16 rows x 64 codes, block
+    (r/16, k/64) at byte ((r/16) * (K/64) + k/64) * 1024 of each matrix and
+    C[r][k] at (((k%64)/16) * 16 + r%16) * 16 + k%16 inside it; same shape."""
+    *lead, R, K = q.shape
+    if R % 16 != 0 or K % 64 != 0:
+        raise ValueError("packing needs rows % 16 == 0 and K % 64 == 0")
+    v = q.reshape(*lead, R // 16, 16, K // 64, 4, 16)      # r = 16 rb + r16, k = 64 kb + 16 j + t
+    n = len(lead)
+    return v.permute(*range(n), n, n + 2, n + 3, n + 1, n + 4).contiguous().reshape(q.shape)
+
+
 def grouped_ffn_fp8w(x: torch.Tensor, group_offsets: torch.Tensor, E: int, n_shared: int, nseg: int,
                      w_gate: torch.Tensor, s_gate: torch.Tensor, w_up: torch.Tensor, s_up: torch.Tensor,
                      w_down: torch.Tensor, s_down: torch.Tensor, h_sorted: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None, x_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     workspace: Optional[torch.Tensor] = None, x_rows: Optional[torch.Tensor] = None,
+                     packed: bool = False) -> torch.Tensor:
     """The expert FFN with E4M3 weight codes (uint8) and fp32 per-row scales;
-    bf16 token rows, read directly or through `x_rows`."""
+    bf16 token rows, read directly or through `x_rows`.  packed: the codes come
+    from pack_fp8_codes (moe_grouped_ffn_fp8w_packed)."""
     _need(x, "x", torch.bfloat16, 2)
     for t, n in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
         _need(t, n, torch.uint8, 3)
@@ -304,7 +319,8 @@ def grouped_ffn_fp8w(x: torch.Tensor, group_offsets: torch.Tensor, E: int, n_sha
         workspace = torch.empty(max(ffn_fp8w_workspace_bytes(n_rows, I), 256), dtype=torch.uint8, device=dev)
     lib = _lib.load()
     nbytes = ctypes.c_size_t(workspace.numel())
-    check("moe_grouped_ffn_fp8w", lib.moe_grouped_ffn_fp8w(
+    name = "moe_grouped_ffn_fp8w_packed" if packed else "moe_grouped_ffn_fp8w"
+    check(name, getattr(lib, name)(
         _ptr(x), _ptr(x_rows), x.shape[0] if x_rows is not None else 0, _ptr(group_offsets), n_rows, E, n_shared,
         nseg, d, I, _ptr(w_gate), _ptr(s_gate), _ptr(w_up), _ptr(s_up), _ptr(w_down), _ptr(s_down), _ptr(h_sorted),
         _ptr(workspace), ctypes.byref(nbytes), _stream(dev)))
@@ -414,7 +430,8 @@ class MoeLayer:
         # the FFN runs moe_grouped_ffn_fp8w on them instead of w_gate / w_up / w_down
         self.fp8_weights = fp8_weights
         # packed_weights: w_gate / w_up / w_down come from pack_weights and the FFN
-        # runs moe_grouped_ffn_packed (bf16, decode-sized batches)
+        # runs moe_grouped_ffn_packed (bf16, decode-sized batches); with
+        # fp8_weights, the codes come from pack_fp8_codes (moe_grouped_ffn_fp8w_packed)
         self.packed = bool(packed_weights)
         self.w_router = w_router
         self.logits = torch.empty((T, E), dtype=torch.float32, device=dev) if w_router is not None else None
@@ -469,7 +486,8 @@ class MoeLayer:
             src = x if self.fused_gather else self.perm["x_sorted"]
             return grouped_ffn_fp8w(src, self.perm["group_offsets"], self.E, self.S, self.nseg, *self.fp8_weights,
                                     h_sorted=self.h_sorted, workspace=self.ffn_ws,
-                                    x_rows=self.perm["sorted_token"] if self.fused_gather else None)
+                                    x_rows=self.perm["sorted_token"] if self.fused_gather else None,
+                                    packed=self.packed)
         if self.packed:
             src = x if self.fused_gather else self.perm["x_sorted"]
             return grouped_ffn_packed(src, self.perm["group_offsets"], self.E, self.S, self.nseg, self.w_gate,
@@ -548,7 +566,8 @@ class MoeLayer:
         offs = self.perm["group_offsets"].data_ptr()
         if self.fp8_weights is not None:
             qg, sg, qu, su, qd, sd = (t.data_ptr() for t in self.fp8_weights)
-            return ("moe_grouped_ffn_fp8w", lib.moe_grouped_ffn_fp8w, (
+            name = "moe_grouped_ffn_fp8w_packed" if self.packed else "moe_grouped_ffn_fp8w"
+            return (name, getattr(lib, name), (
                 src, rows, self.T, offs, self.N, self.E, self.S, self.nseg, self.d, self.I, qg, sg, qu, su, qd, sd,
                 self.h_sorted.data_ptr(), self.ffn_ws.data_ptr(), ctypes.byref(n_ffn), st))
         if self.packed:

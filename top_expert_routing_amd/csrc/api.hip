@@ -35,6 +35,53 @@ moe_status workspace_check(void* workspace, size_t* workspace_bytes, size_t need
   return MOE_OK;
 }
 
+// moe_grouped_ffn_fp8w and its packed-weight variant
+moe_status ffn_fp8w_call(bool packed, const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                                const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
+                                int32_t nseg, int32_t d, int32_t I, const void* w_gate, const float* s_gate,
+                                const void* w_up, const float* s_up, const void* w_down, const float* s_down,
+                                void* h_sorted, void* workspace, size_t* workspace_bytes, hipStream_t stream) {
+  if (n_rows < 0 || E < 1 || n_shared < 0 || (nseg != 1 && nseg != 2) || d < 1 || I < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
+  if (d % 16 != 0 || I % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (packed && (d % 64 != 0 || I % 64 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
+    return MOE_ERR_UNSUPPORTED;
+  bool query;
+  moe_status st = workspace_check(workspace, workspace_bytes, moe::ffn_fp8w_workspace_bytes(n_rows, I), &query);
+  if (st != MOE_OK || query) return st;
+  if (n_rows == 0) return MOE_OK;
+  if (!x_sorted || !group_offsets || !w_gate || !w_up || !w_down || !s_gate || !s_up || !s_down || !h_sorted)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_sorted) || !aligned4(group_offsets) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(s_gate) || !aligned16(s_up) || !aligned16(s_down) || !aligned16(h_sorted))
+    return MOE_ERR_INVALID_ARG;
+  if (x_rows && (!aligned4(x_rows) || n_x < 1)) return MOE_ERR_INVALID_ARG;
+  if (x_rows && !fits_int(static_cast<long long>(n_x) * d)) return MOE_ERR_UNSUPPORTED;
+  moe::FfnArgs a;
+  a.x_sorted = x_sorted;
+  a.x_rows = x_rows;
+  a.n_x = x_rows ? n_x : n_rows;
+  a.group_offsets = group_offsets;
+  a.n_rows = n_rows;
+  a.E = E;
+  a.n_shared = n_shared;
+  a.nseg = nseg;
+  a.d = d;
+  a.I = I;
+  a.w_gate = w_gate;
+  a.w_up = w_up;
+  a.w_down = w_down;
+  a.bf16 = 1;
+  a.h_sorted = h_sorted;
+  a.s_gate = s_gate;
+  a.s_up = s_up;
+  a.s_down = s_down;
+  a.packed = packed;
+  return hip_status(moe::launch_ffn_fp8w(a, workspace, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -222,43 +269,17 @@ moe_status moe_grouped_ffn_fp8w(const void* x_sorted, const int32_t* x_rows, int
                                 int32_t nseg, int32_t d, int32_t I, const void* w_gate, const float* s_gate,
                                 const void* w_up, const float* s_up, const void* w_down, const float* s_down,
                                 void* h_sorted, void* workspace, size_t* workspace_bytes, hipStream_t stream) {
-  if (n_rows < 0 || E < 1 || n_shared < 0 || (nseg != 1 && nseg != 2) || d < 1 || I < 1)
-    return MOE_ERR_INVALID_ARG;
-  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
-  if (d % 16 != 0 || I % 16 != 0) return MOE_ERR_UNSUPPORTED;
-  if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
-    return MOE_ERR_UNSUPPORTED;
-  bool query;
-  moe_status st = workspace_check(workspace, workspace_bytes, moe::ffn_fp8w_workspace_bytes(n_rows, I), &query);
-  if (st != MOE_OK || query) return st;
-  if (n_rows == 0) return MOE_OK;
-  if (!x_sorted || !group_offsets || !w_gate || !w_up || !w_down || !s_gate || !s_up || !s_down || !h_sorted)
-    return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x_sorted) || !aligned4(group_offsets) || !aligned16(w_gate) || !aligned16(w_up) ||
-      !aligned16(w_down) || !aligned16(s_gate) || !aligned16(s_up) || !aligned16(s_down) || !aligned16(h_sorted))
-    return MOE_ERR_INVALID_ARG;
-  if (x_rows && (!aligned4(x_rows) || n_x < 1)) return MOE_ERR_INVALID_ARG;
-  if (x_rows && !fits_int(static_cast<long long>(n_x) * d)) return MOE_ERR_UNSUPPORTED;
-  moe::FfnArgs a;
-  a.x_sorted = x_sorted;
-  a.x_rows = x_rows;
-  a.n_x = x_rows ? n_x : n_rows;
-  a.group_offsets = group_offsets;
-  a.n_rows = n_rows;
-  a.E = E;
-  a.n_shared = n_shared;
-  a.nseg = nseg;
-  a.d = d;
-  a.I = I;
-  a.w_gate = w_gate;
-  a.w_up = w_up;
-  a.w_down = w_down;
-  a.bf16 = 1;
-  a.h_sorted = h_sorted;
-  a.s_gate = s_gate;
-  a.s_up = s_up;
-  a.s_down = s_down;
-  return hip_status(moe::launch_ffn_fp8w(a, workspace, stream));
+  return ffn_fp8w_call(false, x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I, w_gate, s_gate, w_up,
+                       s_up, w_down, s_down, h_sorted, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_grouped_ffn_fp8w_packed(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                                const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
+                                int32_t nseg, int32_t d, int32_t I, const void* w_gate, const float* s_gate,
+                                const void* w_up, const float* s_up, const void* w_down, const float* s_down,
+                                void* h_sorted, void* workspace, size_t* workspace_bytes, hipStream_t stream) {
+  return ffn_fp8w_call(true, x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I, w_gate, s_gate, w_up,
+                       s_up, w_down, s_down, h_sorted, workspace, workspace_bytes, stream);
 }
 
 moe_status moe_combine(const void* h_sorted, const int32_t* flat_to_sorted, const float* topk_w, int32_t T, int32_t k,

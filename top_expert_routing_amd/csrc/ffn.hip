@@ -553,7 +553,7 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <int MF, int NFC, int PHASE>
+template <int MF, int NFC, int PHASE, bool PK = false>
 __global__ __launch_bounds__(kThreads8, 4) void ffn_decode_fp8w(
     const uint16_t* __restrict__ A, int K, const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
     const float* __restrict__ S0, const float* __restrict__ S1, int Ncols, PlanArgs plan,
@@ -583,7 +583,9 @@ __global__ __launch_bounds__(kThreads8, 4) void ffn_decode_fp8w(
   for (int j = 0; j < NF; ++j) {
     const int n = min(col0 + (j % NFC) * 16 + l16, Ncols - 1);
     const uint8_t* W = (PHASE == 1 && j >= NFC) ? W1 : W0;
-    bp[j] = W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n) * K + 16 * q;
+    // packed: blocks of 16 rows x 64 codes (1 KiB), lane 16 q + l16 at byte 16 * lane
+    bp[j] = PK ? W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n / 16) * (K / 64) * 1024 + lane * 16
+               : W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n) * K + 16 * q;
   }
 
   // token rows of a chunk: thread handles uint4 slots idx = tid + s * 512
@@ -628,7 +630,8 @@ __global__ __launch_bounds__(kThreads8, 4) void ffn_decode_fp8w(
       const int kk = kc + 64 * u + 16 * q;
 #pragma unroll
       for (int j = 0; j < NF; ++j)
-        b[u][j] = kk < K ? *reinterpret_cast<const uint4*>(bp[j] + kc + 64 * u) : make_uint4(0, 0, 0, 0);
+        b[u][j] = kk < K ? *reinterpret_cast<const uint4*>(bp[j] + (PK ? (kc + 64 * u) * 16 : kc + 64 * u))
+                         : make_uint4(0, 0, 0, 0);
     }
   };
   auto mma = [&](const uint4 (&b)[U][NF], const uint16_t* as) {
@@ -1633,18 +1636,18 @@ void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t 
 
 // FP8-weight FFN: both phases on the FP8 decode kernel (groups of any size;
 // it is the decode-shaped kernel, meant for decode-sized groups).
-template <int MF>
+template <int MF, bool PK>
 void launch_decode_fp8w(const FfnArgs& a, int max_tiles, const PlanArgs& plan, uint16_t* abuf,
                         hipStream_t stream) {
   const int bn1 = kWaves8 * 16 * 1, bn2 = kWaves8 * 16 * 2;
   const int nch1 = (a.I + bn1 - 1) / bn1, nch2 = (a.d + bn2 - 1) / bn2;
-  hipLaunchKernelGGL((ffn_decode_fp8w<MF, 1, 1>), dim3(item_grid(max_tiles, nch1)), dim3(kThreads8), 0, stream,
+  hipLaunchKernelGGL((ffn_decode_fp8w<MF, 1, 1, PK>), dim3(item_grid(max_tiles, nch1)), dim3(kThreads8), 0, stream,
                      static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint8_t*>(a.w_gate),
                      static_cast<const uint8_t*>(a.w_up), a.s_gate, a.s_up, a.I, plan, abuf);
   PlanArgs plan2 = plan;
   plan2.diag = nullptr;
   plan2.arows = nullptr;
-  hipLaunchKernelGGL((ffn_decode_fp8w<MF, 2, 2>), dim3(item_grid(max_tiles, nch2)), dim3(kThreads8), 0, stream,
+  hipLaunchKernelGGL((ffn_decode_fp8w<MF, 2, 2, PK>), dim3(item_grid(max_tiles, nch2)), dim3(kThreads8), 0, stream,
                      static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint8_t*>(a.w_down),
                      static_cast<const uint8_t*>(nullptr), a.s_down, static_cast<const float*>(nullptr), a.d, plan2,
                      static_cast<uint16_t*>(a.h_sorted));
@@ -1674,10 +1677,18 @@ hipError_t launch_ffn_fp8w(const FfnArgs& a, void* workspace, hipStream_t stream
   plan.arows = a.x_rows;
   plan.n_x = a.n_x;
   uint16_t* abuf = reinterpret_cast<uint16_t*>(ws);
+  if (a.packed) {
+    switch (mf) {
+      case 1: launch_decode_fp8w<1, true>(a, plan.max_tiles, plan, abuf, stream); break;
+      case 2: launch_decode_fp8w<2, true>(a, plan.max_tiles, plan, abuf, stream); break;
+      default: launch_decode_fp8w<4, true>(a, plan.max_tiles, plan, abuf, stream); break;
+    }
+    return hipGetLastError();
+  }
   switch (mf) {
-    case 1: launch_decode_fp8w<1>(a, plan.max_tiles, plan, abuf, stream); break;
-    case 2: launch_decode_fp8w<2>(a, plan.max_tiles, plan, abuf, stream); break;
-    default: launch_decode_fp8w<4>(a, plan.max_tiles, plan, abuf, stream); break;
+    case 1: launch_decode_fp8w<1, false>(a, plan.max_tiles, plan, abuf, stream); break;
+    case 2: launch_decode_fp8w<2, false>(a, plan.max_tiles, plan, abuf, stream); break;
+    default: launch_decode_fp8w<4, false>(a, plan.max_tiles, plan, abuf, stream); break;
   }
   return hipGetLastError();
 }

@@ -48,7 +48,8 @@ struct FfnArgs {
   const float* s_gate = nullptr;
   const float* s_up = nullptr;
   const float* s_down = nullptr;
-  // bf16 weights pre-packed in 16-row x 32-K blocks (moe_grouped_ffn_packed)
+  // weights pre-packed in 1 KiB blocks of 16 rows: 32 K values for bf16
+  // (moe_grouped_ffn_packed), 64 for FP8 codes (moe_grouped_ffn_fp8w_packed)
   bool packed = false;
 };
 size_t ffn_workspace_bytes(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16);

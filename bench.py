@@ -4,8 +4,10 @@
 A step is one pass of the whole path over one batch: softmax top-k gate ->
 dispatch permutation -> grouped SwiGLU FFN -> combine, plus the expert
 statistics over the workload's layer stack.  Inputs are synthetic, already in
-HBM when the timed region starts.  The default workload is the OLMoE-shaped
-decode step (T=128 tokens, E=64, top-8, d=2048, I=1024, bf16).
+HBM when the timed region starts.  The default workload is the largest one
+that fits one GPU: the GPT-OSS-120B-shaped mixed batch (64 decode tokens ahead
+of a 4096-token prefill chunk, E=128, top-4, d=I=2880, bf16, 6.4 GB of expert
+weights), whose FFN runs as one persistent launch with the decode tiles first.
 
 Expert weights rotate over several copies (one per simulated layer) so that
 each step streams its weights from HBM rather than from the 256 MB last-level
@@ -40,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="olmoe_decode")
+    ap.add_argument("--workload", default="gptoss_mixed")
     ap.add_argument("--weight-copies", type=int, default=0,
                     help="expert-weight copies to rotate over (0: enough to exceed 3 GiB)")
     ap.add_argument("--router", action="store_true",
@@ -142,12 +144,24 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv:
     print(json.dumps(rec["workloads"][workload]))
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s: float, w_router=None):
     """Time the CPU oracle (as it stands) on a bounded sample of the workload
-    (with `w_router`, the sample's logits come from the oracle's router)."""
+    (with `w_router`, the sample's logits come from the oracle's router), once
+    with one BLAS thread and once with all of them."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import moe_oracle as O
 
     def host(t):
@@ -160,27 +174,64 @@ def cpu_baseline(wl, budget_s: float, w_router=None):
     # sample: the first n tokens (whole batch when it is small), whole layer path
     n = s.T if s.T <= 256 else 256
     toks = np.arange(n)
-    t0 = time.perf_counter()
-    done = 0
-    passes = 0
     wr = None if w_router is None else host(w_router)
-    while True:
-        if wr is not None:
-            logits = logits.copy()
-            logits[:n] = O.router(x[:n], wr, s.dtype)
-        O.moe_layer(logits, x, wg, wu, wd, s.k, s.dtype, n_shared=s.S, n_priority=s.n_priority, tokens=toks)
-        ids, _ = O.gate(logits[:n], s.k)
-        O.stats(ids[None], s.E, np.arange(n + 1, dtype=np.int32))
-        done += n
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or passes >= 20 or el * (passes + 1) / passes > 2.5 * budget_s:
-            break
+
+    def timed(budget):
+        t0 = time.perf_counter()
+        done = passes = 0
+        while True:
+            lg = logits
+            if wr is not None:
+                lg = logits.copy()
+                lg[:n] = O.router(x[:n], wr, s.dtype)
+            O.moe_layer(lg, x, wg, wu, wd, s.k, s.dtype, n_shared=s.S, n_priority=s.n_priority, tokens=toks)
+            ids, _ = O.gate(lg[:n], s.k)
+            O.stats(ids[None], s.E, np.arange(n + 1, dtype=np.int32))
+            done += n
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget or passes >= 20 or el * (passes + 1) / passes > 2.5 * budget:
+                return done / el, passes, el
+
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    with threadpool_limits(limits=1, user_api="blas"):
+        v1, p1, e1 = timed(budget_s / 2)
+    vn, pn, en = timed(budget_s / 2)
+    return {"value": round(vn, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n} of {s.T} tokens, whole layer path (gate, permute, FFN on their rows, "
-                      f"combine) plus their statistics{', router first' if wr is not None else ''}, "
-                      f"{passes} pass(es) in {el:.1f} s"}
+                      f"combine) plus their statistics{', router first' if wr is not None else ''}; "
+                      f"{pn} pass(es) in {en:.1f} s with {threads} BLAS threads, {p1} in {e1:.1f} s with 1",
+            "one_thread": {"value": round(v1, 1), "unit": "tokens/s", "cores": 1},
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def decode_segment(layer, wl, s, dev, expert_bytes):
+    """One FFN call of the layer with the per-tile timeline: when the priority
+    (decode) segment's last tile and the whole call's last tile ended, from the
+    call's first tile start.  Against the time the decode segment's distinct
+    experts' weights take to stream at the HBM peak."""
+    import numpy as np
+    import torch
+    import top_expert_routing_amd as moe
+    trace = torch.zeros((1 << 17, 4), dtype=torch.int64, device=dev)
+    moe.grouped_ffn(wl.x, layer.perm["group_offsets"], s.E, s.S, layer.nseg, layer.w_gate, layer.w_up,
+                    layer.w_down, layer.h_sorted, layer.ffn_ws, x_rows=layer.perm["sorted_token"], trace=trace)
+    torch.cuda.synchronize()
+    tr = trace.cpu().numpy().view(np.uint64)
+    rec = tr[tr[:, 1] != 0]
+    if len(rec) == 0:
+        return None
+    prio = ((rec[:, 2] >> 1) & 1) == 1
+    t0 = int(rec[:, 0].min())
+    u_dec = int(np.unique(layer.topk_ids[: s.n_priority].cpu().numpy()).size)
+    return {"completion_us": round((int(rec[prio, 1].max()) - t0) / 100.0, 1) if prio.any() else None,
+            "ffn_us": round((int(rec[:, 1].max()) - t0) / 100.0, 1),
+            "priority_tiles": int(prio.sum()), "tiles": int(len(rec)),
+            "decode_union": u_dec,
+            "hbm_bound_us": round(u_dec * expert_bytes / (PEAK_HBM_GBS * 1e3), 1),
+            "clock": "s_memrealtime, 100 MHz; tile stamps of one traced call (a wait for each tile's stores "
+                     "before its end stamp)"}
 
 
 def signature_recording(s, stats_ids, req_offsets, stream, K, dev, logits_stack=None, block=16):
@@ -282,11 +333,10 @@ def main():
     # FP8 codes are packed too when d and I are multiples of 64
     fp8_packed = fp8 and s.d % 64 == 0 and s.I % 64 == 0 and not args.unpacked_weights
     if fp8 and s.n_priority > 0:
-        # its one run ended in a GPU memory fault whose cause has not been
-        # found (a host-side model of the FP8 kernel's work items and address
-        # ranges for this routing finds every access in bounds)
-        print("--fp8-weights is not run on workloads with a priority segment: a memory fault in that "
-              "configuration is not explained yet", file=sys.stderr)
+        # the library refuses FP8 weights with a priority segment (one run on
+        # this shape ended in a GPU memory fault whose cause is not found)
+        print("--fp8-weights: the library refuses FP8 expert weights with a priority segment "
+              "(MOE_ERR_UNSUPPORTED)", file=sys.stderr)
         sys.exit(2)
     # expert weight bytes (fp8: codes plus one fp32 scale per weight row)
     expert_bytes = 3 * s.d * s.I + (2 * s.I + s.d) * 4 if fp8 else 3 * s.d * s.I * esize
@@ -395,6 +445,9 @@ def main():
         for i in range(K):
             step(i, evs[i])
     torch.cuda.synchronize()
+    diag = int(layer.ffn_ws[-4:].view(torch.int32).item())
+    if diag != 0:
+        raise RuntimeError("the FFN's diagnostic word is set: a wait of the persistent tile queue gave up")
     per_call = {n: 0.0 for n in names}
     for e in evs:
         for j, n in enumerate(names):
@@ -423,13 +476,22 @@ def main():
     # the committed counters are for the default mode of each workload
     traffic = None if fp8 or args.unpacked_weights else traffic_for(args.workload)
     roof["traffic"] = None if traffic is None else round(traffic)
-    roof["kernel"] = f"{ffn_name} (gate/up launch + down launch), HIP events over K eager steps"
+    queue = (not fp8 and not packed and s.dtype == "bf16" and s.n_priority > 0 and s.d % 32 == 0 and
+             s.I % 32 == 0 and s.N // s.G > 48 and os.environ.get("LIBMOE_FFN_QUEUE", "1") != "0")
+    roof["kernel"] = (f"{ffn_name} (" + ("one persistent launch: decode-priority tile queues" if queue else
+                                         "gate/up launch + down launch") + "), HIP events over K eager steps")
     roof["algorithmic_bytes"] = int(ffn_bytes)
     roof["algorithmic_flops"] = int(ffn_flops)
     roof["avg_call_us"] = round(ffn_s * 1e6, 2)
 
+    # the FFN against the other roof as well (MFMA for decode-bound batches,
+    # HBM for compute-bound ones)
+    roof["hbm_frac"] = round(ffn_bytes / ffn_s / 1e9 / PEAK_HBM_GBS, 4)
+    roof["mfma_frac"] = round(ffn_flops / ffn_s / 1e12 / peak_flops, 4)
+
     signature = signature_recording(s, stats_ids, wl.req_offsets, stream, K, dev,
                                     wl.stats_logits.contiguous()) if args.signature else None
+    dseg = decode_segment(layer, wl, s, dev, expert_bytes) if queue else None
 
     tokens_per_s = s.T * K / elapsed
     out = {
@@ -449,6 +511,8 @@ def main():
     }
     if signature is not None:
         out["signature_recording"] = signature
+    if dseg is not None:
+        out["decode_segment"] = dseg
     if not args.no_cpu_baseline and not fp8:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, w_router)
     line = json.dumps(out)

@@ -170,11 +170,15 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t E, int32_t k,
  *   accumulation, the SwiGLU product rounded to bf16 (round to nearest even)
  *   before the down projection.  f32: fp32 throughout.
  *   Requires d % 8 == 0, I % 8 == 0, nseg in {1, 2}, 1 <= E <= 512.
+ *   bf16 batches with a priority segment (nseg == 2) whose groups average
+ *   more than 48 rows and whose d and I are multiples of 32 run both phases
+ *   in one launch of persistent workers that take tiles from device-side
+ *   queues, the priority segment's tiles first ("Adaptive Persistent
+ *   Kernels (APK)"); other batches run two launches (gate/up, then down).
  *   The 4 bytes at offset (queried workspace size - 4) hold a diagnostic
  *   word once the call has completed: 0, or nonzero if a wait of the
- *   persistent tile queue (used for bf16 batches with a priority segment and
- *   large groups) gave up after its bound; the outputs are then not to be
- *   trusted.
+ *   persistent tile queue for a phase-1 tile gave up after its bound (20 ms);
+ *   the outputs are then not to be trusted.
  */
 moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
                            const int32_t* group_offsets,
@@ -183,6 +187,37 @@ moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t 
                            const void* w_gate, const void* w_up, const void* w_down,
                            moe_dtype dtype, void* h_sorted,
                            void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_ffn_traced - moe_grouped_ffn with a per-tile timeline of the
+ * persistent tile queue.
+ * (ExpertPlex page, "Adaptive Persistent Kernels (APK)": a decode tile waits at
+ * most for the tiles already running; the timeline shows when the priority
+ * segment's tiles ran and finished.)
+ *
+ *   Arguments, results and workspace as moe_grouped_ffn, plus
+ *   trace           device buffer of trace_capacity records, 4 uint64 each,
+ *                   16-byte aligned; the caller zero-fills it.
+ *   trace_capacity  records (>= 0; 0: no trace, exactly moe_grouped_ffn).
+ *   Records are written only on the persistent-queue path.  Queue q (of nq =
+ *   8) owns records [q * (trace_capacity / nq), (q + 1) * (trace_capacity /
+ *   nq)); its tile popped at position t writes record q * (trace_capacity /
+ *   nq) + t if t < trace_capacity / nq:
+ *     [0] start and [1] end of the tile, s_memrealtime ticks (100 MHz);
+ *     [2] unit << 32 | column chunk << 8 | kind << 2 | priority << 1 |
+ *         (phase - 1), kind 0 = GEMM tile, 1 = weight-streaming tile;
+ *     [3] queue << 32 | block index.
+ *   A record whose end is 0 was not written.  Tracing adds a wait for the
+ *   tile's stores before its end stamp.
+ *   Errors: MOE_ERR_INVALID_ARG for trace_capacity < 0 or a NULL or
+ *   misaligned trace with trace_capacity > 0; otherwise as moe_grouped_ffn.
+ */
+moe_status moe_grouped_ffn_traced(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                                  const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
+                                  int32_t nseg, int32_t d, int32_t I, const void* w_gate, const void* w_up,
+                                  const void* w_down, moe_dtype dtype, void* h_sorted, void* workspace,
+                                  size_t* workspace_bytes, uint64_t* trace, int32_t trace_capacity,
+                                  hipStream_t stream);
 
 /*
  * moe_grouped_ffn_packed - moe_grouped_ffn (bf16) for decode-sized groups,
@@ -226,9 +261,13 @@ moe_status moe_grouped_ffn_packed(const void* x_sorted, const int32_t* x_rows, i
  *   exact in bf16; products accumulate in fp32 and the scale multiplies the
  *   accumulated row product.  Runs on the decode-shaped kernel (any group
  *   sizes; meant for decode-sized groups).
- *   Requires d and I multiples of 16; every pointer 16-byte aligned.
- *   Errors: MOE_ERR_UNSUPPORTED when d or I is not a multiple of 16 or
- *   E > 512; MOE_ERR_INVALID_ARG for nseg outside {1, 2}, a NULL required
+ *   Requires d and I multiples of 16, nseg == 1; every pointer 16-byte
+ *   aligned.
+ *   Errors: MOE_ERR_UNSUPPORTED when d or I is not a multiple of 16, E > 512
+ *   or nseg == 2 (a priority segment: refused, because one run with FP8
+ *   weights on a GPT-OSS-shaped mixed batch, d = I = 2880 with a priority
+ *   segment, ended in a GPU memory fault whose cause has not been found);
+ *   MOE_ERR_INVALID_ARG for nseg outside {1, 2}, a NULL required
  *   pointer (the three scale arrays included) or a misaligned one;
  *   MOE_ERR_WORKSPACE for a workspace below the queried size.  The workspace
  *   holds the bf16 SwiGLU intermediate [n_rows][I]; its last 4 bytes are

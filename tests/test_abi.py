@@ -27,8 +27,8 @@ def _declared():
 
 
 def test_header_declares_the_calls():
-    assert _declared() == sorted(["moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_packed", "moe_grouped_ffn_fp8w",
-                                  "moe_grouped_ffn_fp8w_packed",
+    assert _declared() == sorted(["moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_traced",
+                                  "moe_grouped_ffn_packed", "moe_grouped_ffn_fp8w", "moe_grouped_ffn_fp8w_packed",
                                   "moe_combine", "moe_stats", "moe_prob_signature", "moe_status_string"])
 
 
@@ -85,6 +85,7 @@ def test_ffn_fp8w_validation_and_query(lib):
     assert f(*args(a8=264)) == UNS                                 # d not a multiple of 16
     assert f(*args(a9=520)) == UNS                                 # I not a multiple of 16
     assert f(*args(a7=3)) == INV                                   # nseg
+    assert f(*args(a7=2)) == UNS                                   # a priority segment is refused
     assert f(*args(a5=513)) == UNS                                 # E > 512
     small = ctypes.c_size_t(16)
     assert f(*args(a17=FAKE, a18=ctypes.byref(small))) == WS       # workspace too small
@@ -174,6 +175,22 @@ def test_ffn_validation_and_query(lib):
     assert st == 0 and need >= 65536 * 768 * 2           # holds the bf16 intermediate
     assert _ffn(lib, N=65536, E=128, d=2048, I=768, nbytes=need - 1)[0] == WS
     assert _ffn(lib, N=0, ws=FAKE)[0] == 0               # no rows: no-op
+
+
+def test_ffn_traced_validation_and_query(lib):
+    f = lib.moe_grouped_ffn_traced
+    n = ctypes.c_size_t(0)
+    args = lambda **kw: [kw.get(f"a{i}", v) for i, v in enumerate(
+        [FAKE, None, 0, FAKE, 4160 * 4, 128, 0, 2, 2880, 2880, FAKE, FAKE, FAKE, 1, FAKE, None, ctypes.byref(n),
+         FAKE, 1024, None])]
+    assert f(*args()) == 0                                          # query
+    st, need = _ffn(lib, N=4160 * 4, E=128, nseg=2, d=2880, I=2880, ws=None, nbytes=0)
+    assert st == 0 and n.value == need                              # the same workspace as moe_grouped_ffn
+    big = ctypes.c_size_t(1 << 40)
+    assert f(*args(a15=FAKE, a16=ctypes.byref(big), a18=-1)) == INV          # negative capacity
+    assert f(*args(a15=FAKE, a16=ctypes.byref(big), a17=None)) == INV        # NULL trace
+    assert f(*args(a15=FAKE, a16=ctypes.byref(big), a17=FAKE + 8)) == INV    # misaligned trace
+    assert f(*args(a15=FAKE, a16=ctypes.byref(big), a8=100)) == UNS          # checks of moe_grouped_ffn apply
 
 
 def test_combine_validation(lib):

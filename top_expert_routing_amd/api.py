@@ -163,10 +163,13 @@ def grouped_ffn(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_s
                 w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
                 h_sorted: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None,
-                x_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
+                x_rows: Optional[torch.Tensor] = None,
+                trace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Grouped SwiGLU FFN.  With `x_rows` ([N] int32, e.g. permute's
     sorted_token) `x_sorted` is the unsorted token matrix and sorted row n
-    reads its row x_rows[n]."""
+    reads its row x_rows[n].  With `trace` ([R][4] int64, zero-filled by the
+    caller) the persistent-queue path records one line per tile
+    (moe_grouped_ffn_traced)."""
     _need(x_sorted, "x_sorted", None, 2)
     _need(group_offsets, "group_offsets", torch.int32, 1)
     for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
@@ -192,10 +195,16 @@ def grouped_ffn(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_s
                                 dtype=torch.uint8, device=dev)
     lib = _lib.load()
     nbytes = ctypes.c_size_t(workspace.numel())
-    check("moe_grouped_ffn", lib.moe_grouped_ffn(
-        _ptr(x_sorted), _ptr(x_rows), n_x, _ptr(group_offsets), N, E, n_shared, nseg, d, I, _ptr(w_gate), _ptr(w_up),
-        _ptr(w_down), _dtype_code(x_sorted), _ptr(h_sorted), _ptr(workspace), ctypes.byref(nbytes),
-        _stream(dev)))
+    args = (_ptr(x_sorted), _ptr(x_rows), n_x, _ptr(group_offsets), N, E, n_shared, nseg, d, I, _ptr(w_gate),
+            _ptr(w_up), _ptr(w_down), _dtype_code(x_sorted), _ptr(h_sorted), _ptr(workspace), ctypes.byref(nbytes))
+    if trace is None:
+        check("moe_grouped_ffn", lib.moe_grouped_ffn(*args, _stream(dev)))
+    else:
+        _need(trace, "trace", torch.int64, 2)
+        if trace.shape[1] != 4:
+            raise ValueError("trace must be [records][4] int64")
+        check("moe_grouped_ffn_traced", lib.moe_grouped_ffn_traced(*args, _ptr(trace), trace.shape[0],
+                                                                   _stream(dev)))
     return h_sorted
 
 

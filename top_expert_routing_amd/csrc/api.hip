@@ -44,6 +44,10 @@ moe_status ffn_fp8w_call(bool packed, const void* x_sorted, const int32_t* x_row
   if (n_rows < 0 || E < 1 || n_shared < 0 || (nseg != 1 && nseg != 2) || d < 1 || I < 1)
     return MOE_ERR_INVALID_ARG;
   if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
+  // A priority segment is refused: one FP8 run on a GPT-OSS-shaped mixed batch
+  // (d = I = 2880, 64-row tiles, priority segment) ended in a GPU memory fault
+  // whose cause has not been found.
+  if (nseg == 2) return MOE_ERR_UNSUPPORTED;
   if (d % 16 != 0 || I % 16 != 0) return MOE_ERR_UNSUPPORTED;
   if (packed && (d % 64 != 0 || I % 64 != 0)) return MOE_ERR_UNSUPPORTED;
   if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
@@ -80,6 +84,51 @@ moe_status ffn_fp8w_call(bool packed, const void* x_sorted, const int32_t* x_row
   a.s_down = s_down;
   a.packed = packed;
   return hip_status(moe::launch_ffn_fp8w(a, workspace, stream));
+}
+
+// moe_grouped_ffn and its traced form
+moe_status ffn_call(const void* x_sorted, const int32_t* x_rows, int32_t n_x, const int32_t* group_offsets,
+                    int32_t n_rows, int32_t E, int32_t n_shared, int32_t nseg, int32_t d, int32_t I,
+                    const void* w_gate, const void* w_up, const void* w_down, moe_dtype dtype, void* h_sorted,
+                    void* workspace, size_t* workspace_bytes, uint64_t* trace, int32_t trace_capacity,
+                    hipStream_t stream) {
+  if (n_rows < 0 || E < 1 || n_shared < 0 || (nseg != 1 && nseg != 2) || d < 1 || I < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
+  if (!known_dtype(dtype) || d % 8 != 0 || I % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
+    return MOE_ERR_UNSUPPORTED;
+  bool query;
+  moe_status st = workspace_check(
+      workspace, workspace_bytes,
+      moe::ffn_workspace_bytes(n_rows, E, n_shared, nseg, d, I, dtype == MOE_BF16 ? 1 : 0), &query);
+  if (st != MOE_OK || query) return st;
+  if (n_rows == 0) return MOE_OK;
+  if (!x_sorted || !group_offsets || !w_gate || !w_up || !w_down || !h_sorted) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_sorted) || !aligned4(group_offsets) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(h_sorted))
+    return MOE_ERR_INVALID_ARG;
+  if (x_rows && (!aligned4(x_rows) || n_x < 1)) return MOE_ERR_INVALID_ARG;
+  if (x_rows && !fits_int(static_cast<long long>(n_x) * d)) return MOE_ERR_UNSUPPORTED;
+  moe::FfnArgs a;
+  a.x_sorted = x_sorted;
+  a.x_rows = x_rows;
+  a.n_x = x_rows ? n_x : n_rows;
+  a.group_offsets = group_offsets;
+  a.n_rows = n_rows;
+  a.E = E;
+  a.n_shared = n_shared;
+  a.nseg = nseg;
+  a.d = d;
+  a.I = I;
+  a.w_gate = w_gate;
+  a.w_up = w_up;
+  a.w_down = w_down;
+  a.bf16 = dtype == MOE_BF16 ? 1 : 0;
+  a.h_sorted = h_sorted;
+  a.trace = reinterpret_cast<unsigned long long*>(trace);
+  a.trace_capacity = trace_capacity;
+  return hip_status(moe::launch_ffn(a, workspace, stream));
 }
 
 }  // namespace
@@ -183,41 +232,20 @@ moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t 
                            int32_t n_shared, int32_t nseg, int32_t d, int32_t I, const void* w_gate,
                            const void* w_up, const void* w_down, moe_dtype dtype, void* h_sorted, void* workspace,
                            size_t* workspace_bytes, hipStream_t stream) {
-  if (n_rows < 0 || E < 1 || n_shared < 0 || (nseg != 1 && nseg != 2) || d < 1 || I < 1)
-    return MOE_ERR_INVALID_ARG;
-  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
-  if (!known_dtype(dtype) || d % 8 != 0 || I % 8 != 0) return MOE_ERR_UNSUPPORTED;
-  if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
-    return MOE_ERR_UNSUPPORTED;
-  bool query;
-  moe_status st = workspace_check(
-      workspace, workspace_bytes,
-      moe::ffn_workspace_bytes(n_rows, E, n_shared, nseg, d, I, dtype == MOE_BF16 ? 1 : 0), &query);
-  if (st != MOE_OK || query) return st;
-  if (n_rows == 0) return MOE_OK;
-  if (!x_sorted || !group_offsets || !w_gate || !w_up || !w_down || !h_sorted) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x_sorted) || !aligned4(group_offsets) || !aligned16(w_gate) || !aligned16(w_up) ||
-      !aligned16(w_down) || !aligned16(h_sorted))
-    return MOE_ERR_INVALID_ARG;
-  if (x_rows && (!aligned4(x_rows) || n_x < 1)) return MOE_ERR_INVALID_ARG;
-  if (x_rows && !fits_int(static_cast<long long>(n_x) * d)) return MOE_ERR_UNSUPPORTED;
-  moe::FfnArgs a;
-  a.x_sorted = x_sorted;
-  a.x_rows = x_rows;
-  a.n_x = x_rows ? n_x : n_rows;
-  a.group_offsets = group_offsets;
-  a.n_rows = n_rows;
-  a.E = E;
-  a.n_shared = n_shared;
-  a.nseg = nseg;
-  a.d = d;
-  a.I = I;
-  a.w_gate = w_gate;
-  a.w_up = w_up;
-  a.w_down = w_down;
-  a.bf16 = dtype == MOE_BF16 ? 1 : 0;
-  a.h_sorted = h_sorted;
-  return hip_status(moe::launch_ffn(a, workspace, stream));
+  return ffn_call(x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I, w_gate, w_up, w_down, dtype,
+                  h_sorted, workspace, workspace_bytes, nullptr, 0, stream);
+}
+
+moe_status moe_grouped_ffn_traced(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                                  const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
+                                  int32_t nseg, int32_t d, int32_t I, const void* w_gate, const void* w_up,
+                                  const void* w_down, moe_dtype dtype, void* h_sorted, void* workspace,
+                                  size_t* workspace_bytes, uint64_t* trace, int32_t trace_capacity,
+                                  hipStream_t stream) {
+  if (trace_capacity < 0 || (trace_capacity > 0 && (!trace || !aligned16(trace)))) return MOE_ERR_INVALID_ARG;
+  return ffn_call(x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I, w_gate, w_up, w_down, dtype,
+                  h_sorted, workspace, workspace_bytes, trace_capacity > 0 ? trace : nullptr, trace_capacity,
+                  stream);
 }
 
 moe_status moe_grouped_ffn_packed(const void* x_sorted, const int32_t* x_rows, int32_t n_x,

@@ -22,6 +22,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "queue_plan.h"
 
 namespace moe {
 
@@ -239,10 +240,17 @@ template <int MF>
 constexpr int decode_kc() { return MF <= 2 ? 256 : 128; }
 constexpr int kDecodeWavesPerSimd = 4;
 
+// LDS staging of one decode tile: two buffers of BM rows x (KC + 8) bf16.
+template <int MF>
+constexpr int decode_lds_elems() { return 2 * 16 * MF * (decode_kc<MF>() + 8); }
+
+// One decode-shaped tile: item `it` (rows it.row(0..rows), output columns
+// it.chunk * 64 * NFC + [0, 64 * NFC)) of expert it.expert.  All kThreads
+// threads call it; `As0` is decode_lds_elems<MF>() bf16 of LDS, free on entry.
 template <int MF, int NFC, int PHASE, bool PK = false>
-__global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void ffn_decode_bf16(
-    const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-    int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
+__device__ __forceinline__ void decode_tile(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x,
+                                            int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+                                            int Ncols, const Item& it, uint16_t* __restrict__ out, uint16_t* As0) {
   constexpr int NF = PHASE == 1 ? 2 * NFC : NFC;
   constexpr int BN = kWaves * 16 * NFC;
   constexpr int BM = 16 * MF;
@@ -251,11 +259,7 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
   constexpr int U = kDecodeKC / 32;
   constexpr int VPR = kDecodeKC / 8;                       // uint4 per staged row
   constexpr int APT = (BM * VPR + kThreads - 1) / kThreads; // uint4 staged per thread
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kDecodeStride];
-
-  const int nch = (Ncols + BN - 1) / BN;
-  const Item it = block_find_item(plan, nch);
-  if (it.rows == 0) return;
+  auto As = [&](int buf) { return As0 + buf * (BM * kDecodeStride); };
   const int rows = it.rows, e = it.expert;
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int l16 = lane & 15, q = lane >> 4;
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
   for (int s = 0; s < APT; ++s) {
     const int idx = threadIdx.x + s * kThreads;
     const int r = idx / VPR;
-    arow[s] = (idx < BM * VPR && r < rows) ? A + a_row(plan.arows, plan.n_x, it.row(r)) * K : nullptr;
+    arow[s] = (idx < BM * VPR && r < rows) ? A + a_row(arows, n_x, it.row(r)) * K : nullptr;
   }
   auto load_a = [&](int c) {
 #pragma unroll
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
     for (int s = 0; s < APT; ++s) {
       const int idx = threadIdx.x + s * kThreads;
       if (idx < BM * VPR)
-        *reinterpret_cast<uint4*>(&As[buf][(idx / VPR) * kDecodeStride + (idx % VPR) * 8]) = stage[s];
+        *reinterpret_cast<uint4*>(As(buf) + (idx / VPR) * kDecodeStride + (idx % VPR) * 8) = stage[s];
     }
   };
 
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
     const bool more = c + 1 < nchunks;
     if (more) load_a(c + 1);
     __syncthreads();                           // chunk c of A is in As[c & 1]
-    mma(b, As[c & 1]);
+    mma(b, As(c & 1));
     if (more) store_a((c + 1) & 1);            // that buffer was last read before this barrier
   }
 
@@ -364,6 +368,17 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
       *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
   }
+}
+
+template <int MF, int NFC, int PHASE, bool PK = false>
+__global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void ffn_decode_bf16(
+    const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+    int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[decode_lds_elems<MF>()];
+  const int nch = (Ncols + kWaves * 16 * NFC - 1) / (kWaves * 16 * NFC);
+  const Item it = block_find_item(plan, nch);
+  if (it.rows == 0) return;
+  decode_tile<MF, NFC, PHASE, PK>(A, plan.arows, plan.n_x, K, W0, W1, Ncols, it, out, As);
 }
 
 // ---- decode-sized tiles of one 16-row slab: K split over the waves ----------------
@@ -1223,183 +1238,213 @@ int gemm_grid() {
   return (b + kXcds - 1) / kXcds * kXcds;
 }
 
-// ---- mixed batches: one persistent launch, per-XCD tile queues ----------------
-// Tile queue with decode priority (ExpertPlex page, "Instance vs module
-// disaggregation" / token-level preemption: a decode request waits at most one
-// tile, never a whole prefill launch).  Both phases run in one launch of
-// persistent blocks (two per CU, 128 x 256 tiles):
-//   * units are the m-tiles of all groups, in group order (the priority
-//     segment's groups first); each XCD owns an eighth of the priority units
-//     and an eighth of the others;
-//   * XCD x's queue is [phase 1 of its priority units] [the first `lag` phase-1
-//     tiles of its other units] [phase 2 of its priority units] [the remaining
-//     phase-1 tiles] [phase 2 of its other units]; within a section tiles go
-//     group by group, column chunk by chunk, m-tile by m-tile;
-//   * a block reads its XCD id from the hardware and pops tiles from that
-//     queue with one atomic add; a phase-2 tile waits until every phase-1 tile
-//     of its unit has raised its flag (one flag per (unit, column chunk)).
-//     The lag keeps the blocks busy with other phase-1 tiles while the
-//     priority units' phase 1 drains.
-// All tiles of a unit run on one XCD, so the intermediate rows pass through
-// that XCD's L2: a phase-1 tile's stores have reached L2 once its vmcnt is
-// zero, before it raises its flag; the waiting block then drops its L1 lines
-// (buffer_inv sc0) before loading them.  Flags are written with agent-scope
-// atomic stores and polled with agent-scope atomic loads, both of which skip
-// the non-coherent caches on this target (the pattern rocPRIM's look-back
-// scan uses on gfx942/gfx950); an L2 read-modify-write counter polled with
-// such loads is not seen by them.  A dependency always points to a tile
-// popped earlier by a running block, so the waits end; each is also bounded
-// (kSpinLimit polls), after which the block sets the diagnostic word (the
-// workspace's last 4 bytes, same store/load pattern) and goes on, and other
-// waits stop at once.
-constexpr int kQueueStride = 32;          // ints between the per-XCD queue heads (128 B)
-constexpr int kCusPerXcd = 32;            // MI355X: 8 XCDs x 32 CUs
-constexpr int kSpinLimit = 1 << 16;       // polls before a wait gives up (far above any tile time)
+// ---- mixed batches: one persistent launch, device-side tile queues --------------
+// ExpertPlex page, "Adaptive Persistent Kernels (APK)": one resident kernel
+// whose workers take tiles from a device-side queue, the urgent decode tiles
+// first, so a decode tile waits at most for the tiles already running and no
+// host relaunch sits between the two phases.  Both phases run in one launch of
+// persistent blocks (two per CU); the tile order is queue_plan.h's:
+//   * sequences (experts; with a priority segment an expert's priority rows
+//     followed by its other rows) of at most kStreamMaxRows rows run on
+//     decode-shaped weight-streaming tiles (64-row units, weights straight from
+//     HBM into MFMA registers), larger ones on 128 x 256 LDS-tiled GEMM tiles
+//     (128-row units), so memory-bound and MFMA-bound tiles share the chip;
+//   * block b takes its tiles from queue b mod nq with one atomic add; queue
+//     order puts the priority units' phase 1 first and their phase 2 after a
+//     lag of one round of the other phase-1 tiles;
+//   * a phase-2 tile of unit u waits until each phase-1 tile of u has raised
+//     its flag (one int per (unit, column chunk)).
+// Memory ordering (HIP / LLVM AMDGPU memory model, agent scope): after a
+// phase-1 tile, every wave executes an agent-scope release fence (its stores
+// of the SwiGLU rows reach the coherence point: buffer_wbl2 sc1, then vmcnt 0),
+// the block barriers, and thread 0 stores the flag with an agent-scope release
+// store.  A phase-2 tile's first wave polls the flags with agent-scope
+// relaxed loads; once all are set it executes an agent-scope acquire fence
+// (buffer_inv sc1) and the block barriers before any wave loads the rows.  The
+// fence pair makes the producer's row stores visible to the consumer on any
+// XCD, so nothing depends on where the hardware places the blocks.
+// Progress: every queue lists all phase-1 tiles a phase-2 tile of it may need
+// before that tile, priority ones at the very front, so each awaited tile has
+// been or will be popped by a block that is not waiting (queue_plan.h; checked
+// for every queue position by a host program built on the same header).
+// Every wait is still bounded: it gives up after kWaitTicks of the 100 MHz
+// real-time counter (or kMaxPolls polls), or at once when another wait gave
+// up; the block then sets the diagnostic word (the workspace's last 4 bytes)
+// and waits no more, so a fault of the protocol costs a bounded delay and a
+// flagged result, never a hang.
+constexpr int kQueueStride = 32;                 // ints between the queue heads (128 B)
+constexpr int kMaxQueues = 8;
+constexpr int kStreamMaxRows = 64;               // sequences of 1..64 rows: weight-streaming tiles
+constexpr int kStreamMF = 4;                     // 64-row stream units
+constexpr unsigned long long kWaitTicks = 2000000ull;   // 20 ms of the 100 MHz counter
+constexpr int kMaxPolls = 1 << 22;
+constexpr int kMaxSeq = MOE_MAX_EXPERTS_DEV + 256;      // routed + shared experts
+constexpr int kSeqPerThread = (kMaxSeq + kThreads - 1) / kThreads;
 
 struct QueueArgs {
+  qplan::Shape shape;
   const int* offs;
-  int G, E, nseg, n_rows, n_prio_groups, nch1, nch2, lag;
-  int nq;       // queues = XCDs of the device (1 when it is a single-XCD partition)
   const int* arows;   // phase-1 A row list (nullptr: sorted rows)
   int n_x;
-  int* heads;   // [kXcds * kQueueStride]
-  int* flags;   // [units][nch1]: phase-1 tile (unit, chunk) done
-  int* error;   // set when a wait gave up
+  int* heads;         // [nq * kQueueStride]
+  int* flags;         // [units_cap][nch1_max]: phase-1 tile (unit, chunk) done
+  int* error;         // diagnostic word, set when a wait gave up
+  unsigned long long* trace;   // optional per-tile records, trace_per_queue per queue
+  int trace_per_queue;
 };
 
-__device__ __forceinline__ int xcc_id() {
-  int x;
-  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
-  return x & 0xf;
-}
+__device__ __forceinline__ unsigned long long realtime() { return __builtin_amdgcn_s_memrealtime(); }
 
 template <class C>
 __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
     const uint16_t* __restrict__ x, int d, const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
     const uint16_t* __restrict__ w_down, int I, QueueArgs q, uint16_t* __restrict__ abuf,
     uint16_t* __restrict__ h) {
-  static_assert(C::NT == kThreads, "the scan below assumes 256 threads");
-  constexpr int BM = C::BM;
-  constexpr int kMaxG = kThreads * kMaxGroupsPerThread;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::RING];
-  __shared__ int fu[kMaxG + 1];         // first unit of each group
-  __shared__ int wsum[kWaves];
-  __shared__ int s_tile;
+  static_assert(C::NT == kThreads, "one block shape for both tile kinds");
+  static_assert(decode_lds_elems<kStreamMF>() * 2 <= C::RING, "stream tiles stage their rows in the GEMM ring");
+  // dynamic LDS: the GEMM operand ring (also the stream tiles' row staging),
+  // then five prefix arrays of nseq + 1 ints: units (fu) and this queue's tile
+  // counts of P1, R1, P2, R2
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+  uint8_t* smem = dyn_lds;
+  const qplan::Shape& sh = q.shape;
+  const int ns = sh.nseq();
+  int* fu = reinterpret_cast<int*>(dyn_lds + C::RING);
+  int* pre = fu + (ns + 1);
+  __shared__ int wsum[kWaves][5];
+  __shared__ int s_tile, s_ok;
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  const int qi = static_cast<int>(blockIdx.x) % sh.nq;
 
-  // units per group, exclusive scan -> fu
   {
-    int cnt[kMaxGroupsPerThread];
-    int sum = 0;
+    int cnt[kSeqPerThread][5];
+    int sum[5] = {0, 0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < kMaxGroupsPerThread; ++i) {
-      const int g = tid * kMaxGroupsPerThread + i;
-      cnt[i] = 0;
-      if (g < q.G) {
-        const int lo = min(max(q.offs[g], 0), q.n_rows), hi = min(max(q.offs[g + 1], 0), q.n_rows);
-        cnt[i] = (max(0, hi - lo) + BM - 1) / BM;
+    for (int i = 0; i < kSeqPerThread; ++i) {
+      const int s = tid * kSeqPerThread + i;
+#pragma unroll
+      for (int c = 0; c < 5; ++c) cnt[i][c] = 0;
+      if (s < ns) {
+        const qplan::SeqUnits u = qplan::seq_units(sh, qplan::seq_rows(sh, q.offs, s));
+        const qplan::SeqCounts c = qplan::seq_counts(sh, s, u, qi);
+        cnt[i][0] = u.units;
+        cnt[i][1] = c.p1;
+        cnt[i][2] = c.r1;
+        cnt[i][3] = c.p2;
+        cnt[i][4] = c.r2;
       }
-      sum += cnt[i];
-    }
-    int incl = sum;
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += y;
+      for (int c = 0; c < 5; ++c) sum[c] += cnt[i][c];
     }
-    if (lane == kWave - 1) wsum[w] = incl;
+    int incl[5];
+#pragma unroll
+    for (int c = 0; c < 5; ++c) {
+      incl[c] = sum[c];
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl[c], o, kWave);
+        if (lane >= o) incl[c] += y;
+      }
+      if (lane == kWave - 1) wsum[w][c] = incl[c];
+    }
     __syncthreads();
-    int run = incl - sum;
-    for (int i = 0; i < w; ++i) run += wsum[i];
 #pragma unroll
-    for (int i = 0; i < kMaxGroupsPerThread; ++i) {
-      const int g = tid * kMaxGroupsPerThread + i;
-      if (g < q.G) fu[g] = run;
-      run += cnt[i];
+    for (int c = 0; c < 5; ++c) {
+      int run = incl[c] - sum[c];
+      for (int i = 0; i < w; ++i) run += wsum[i][c];
+      int* arr = fu + c * (ns + 1);
+#pragma unroll
+      for (int i = 0; i < kSeqPerThread; ++i) {
+        const int s = tid * kSeqPerThread + i;
+        if (s < ns) arr[s] = run;
+        run += cnt[i][c];
+      }
+      if (tid == kThreads - 1) arr[ns] = run;
     }
-    if (tid == kThreads - 1) fu[q.G] = run;
     __syncthreads();
   }
-  const int units = fu[q.G];
-  const int up = fu[q.n_prio_groups];
-  const int xc = xcc_id() % q.nq;
-  const int p_lo = static_cast<int>(1LL * up * xc / q.nq), p_hi = static_cast<int>(1LL * up * (xc + 1) / q.nq);
-  const int r_lo = up + static_cast<int>(1LL * (units - up) * xc / q.nq);
-  const int r_hi = up + static_cast<int>(1LL * (units - up) * (xc + 1) / q.nq);
-  const int s1 = (p_hi - p_lo) * q.nch1, s2 = (p_hi - p_lo) * q.nch2;
-  const int s3 = (r_hi - r_lo) * q.nch1, s4 = (r_hi - r_lo) * q.nch2;
-  const int s3a = min(q.lag, s3);
-  const int total = s1 + s3 + s2 + s4;
+  const qplan::QueueParts qp = qplan::queue_parts(
+      sh, qplan::SeqCounts{pre[ns], pre[(ns + 1) + ns], pre[2 * (ns + 1) + ns], pre[3 * (ns + 1) + ns]});
+  const int total = qp.total();
+  const int nch1max = sh.nch1_max();
+  bool waits = true;                 // false once a wait of this block gave up (block-uniform)
 
   for (;;) {
-    if (tid == 0) s_tile = __hip_atomic_fetch_add(q.heads + xc * kQueueStride, 1, __ATOMIC_RELAXED,
+    if (tid == 0) s_tile = __hip_atomic_fetch_add(q.heads + qi * kQueueStride, 1, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();                 // also: every wave is done with the previous tile's ring
-    int t = s_tile;
+    __syncthreads();                 // also: every wave is done with the previous tile's LDS
+    const int t = s_tile;
     __syncthreads();                 // s_tile read by all before thread 0 overwrites it
     if (t >= total) break;
-    // section -> phase, unit range, index within the section
-    int phase, a, b, i;
-    if (t < s1) {
-      phase = 1, a = p_lo, b = p_hi, i = t;
-    } else if (t < s1 + s3a) {
-      phase = 1, a = r_lo, b = r_hi, i = t - s1;
-    } else if (t < s1 + s3a + s2) {
-      phase = 2, a = p_lo, b = p_hi, i = t - s1 - s3a;
-    } else if (t < s1 + s3 + s2) {
-      phase = 1, a = r_lo, b = r_hi, i = t - s1 - s2;
-    } else {
-      phase = 2, a = r_lo, b = r_hi, i = t - s1 - s3 - s2;
-    }
-    const int nch = phase == 1 ? q.nch1 : q.nch2;
-    // group holding unit a + i / nch: last g with fu[g] <= u
-    const int u = a + i / nch;
-    int lo = 0, hi = q.G;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (fu[mid] <= u) lo = mid; else hi = mid;
-    }
-    const int g = lo;
-    const int sg = max(a, fu[g]), cg = min(b, fu[g + 1]) - sg;
-    const int local = i - nch * (sg - a);
-    const int chunk = local / cg, mt = sg - fu[g] + local % cg;
-    const int unit = fu[g] + mt;
-    const int glo = min(max(q.offs[g], 0), q.n_rows), ghi = min(max(q.offs[g + 1], 0), q.n_rows);
-    const Item it = contiguous_item(glo + mt * BM, min(BM, ghi - glo - mt * BM), expert_of_group(g, q.E, q.nseg), chunk);
-    if (phase == 1) {
-      gemm_tile<1, C>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are in L2
+    const qplan::Slot sl = qplan::slot_of(qp, t);
+    const int* pr = pre + ((sl.phase == 1 ? 0 : 2) + (sl.prio ? 0 : 1)) * (ns + 1);
+    const qplan::Tile tl = qplan::decode_tile(sh, q.offs, pr, fu, qi, sl);
+    const Item it{tl.row0, tl.rows, tl.seq, tl.chunk, tl.split, tl.row1};
+    const unsigned long long t0 = q.trace ? realtime() : 0ull;
+    if (tl.phase == 1) {
+      if (tl.kind == qplan::kGemm)
+        gemm_tile<1, C>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
+      else
+        decode_tile<kStreamMF, 1, 1>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf,
+                                     reinterpret_cast<uint16_t*>(smem));
+      // publish: each wave's row stores reach the coherence point, then the flag
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __syncthreads();
       if (tid == 0)
-        __hip_atomic_store(q.flags + static_cast<size_t>(unit) * q.nch1 + chunk, 1, __ATOMIC_RELAXED,
+        __hip_atomic_store(q.flags + static_cast<size_t>(tl.unit) * nch1max + tl.chunk, 1, __ATOMIC_RELEASE,
                            __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      if (tid < kWave) {
-        // lane c watches the flags of chunks c, c + 64, ...; the wave waits
-        // until all are raised
-        const int* f = q.flags + static_cast<size_t>(unit) * q.nch1;
-        int spins = 0;
-        for (;;) {
-          int mine = 1;
-          for (int c = tid; c < q.nch1; c += kWave)
-            mine &= __hip_atomic_load(f + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-          if (__all(mine)) break;
-          __builtin_amdgcn_s_sleep(2);
-          // give up after kSpinLimit polls, or at once when another wait already did
-          if (++spins > kSpinLimit ||
-              ((spins & 63) == 0 && __hip_atomic_load(q.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-            if (tid == 0) __hip_atomic_store(q.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
+      if (waits) {
+        if (w == 0) {
+          // lane c watches the flags of chunks c, c + 64, ...
+          const int* f = q.flags + static_cast<size_t>(tl.unit) * nch1max;
+          const int nf = sh.nch1[tl.kind];
+          const unsigned long long start = realtime();
+          int ok = 1, polls = 0;
+          for (;;) {
+            int mine = 1;
+            for (int c = lane; c < nf; c += kWave)
+              mine &= __hip_atomic_load(f + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+            if (__all(mine)) break;
+            ++polls;
+            if (((polls & 63) == 0 && __hip_atomic_load(q.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ||
+                polls > kMaxPolls || realtime() - start > kWaitTicks) {
+              ok = 0;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
           }
+          if (ok) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          } else if (lane == 0) {
+            __hip_atomic_store(q.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          if (lane == 0) s_ok = ok;
         }
+        __syncthreads();
+        waits = s_ok != 0;
       }
-      __syncthreads();
-      asm volatile("buffer_inv sc0" ::: "memory");
-      gemm_tile<2, C>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
+      if (tl.kind == qplan::kGemm)
+        gemm_tile<2, C>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
+      else
+        decode_tile<kStreamMF, 2, 2>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h,
+                                     reinterpret_cast<uint16_t*>(smem));
+    }
+    if (q.trace && tid == 0 && t < q.trace_per_queue) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      unsigned long long* r = q.trace + 4 * (static_cast<size_t>(qi) * q.trace_per_queue + t);
+      r[0] = t0;
+      r[1] = realtime();
+      r[2] = (static_cast<unsigned long long>(tl.unit) << 32) | (static_cast<unsigned long long>(tl.chunk) << 8) |
+             (static_cast<unsigned long long>(tl.kind) << 2) | (static_cast<unsigned long long>(tl.prio) << 1) |
+             static_cast<unsigned long long>(tl.phase - 1);
+      r[3] = (static_cast<unsigned long long>(qi) << 32) | blockIdx.x;
     }
   }
 }
 
+// Clears the queue heads, the phase-1 flags and the diagnostic word (a kernel,
+// not a memset, so the call can sit in a captured graph).
 __global__ void ffn_queue_reset(int* p, int n, int* diag) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -1466,9 +1511,12 @@ struct Layout {
 // Small groups (decode) stream weights through the decode kernel; large groups
 // use the LDS-tiled GEMM, whose K steps need d and I to be multiples of 32
 // (otherwise the decode kernel, which takes any multiple of 8, runs them).
+// LIBMOE_FFN_QUEUE=0 runs priority batches on the two-launch GEMM instead of
+// the persistent queue (for comparisons; the results are the same up to the
+// order of nothing: both compute every output from the same products).
 bool queue_path_requested() {
   const char* v = getenv("LIBMOE_FFN_QUEUE");
-  return v != nullptr && v[0] == '1';
+  return v == nullptr || v[0] != '0';
 }
 
 // Up to this many rows per group on average the decode path runs the split-K
@@ -1481,6 +1529,33 @@ int pick_mf(int avg) {
   if (avg <= 8) return 1;
   if (avg <= 24) return 2;
   return 4;
+}
+
+// Tile order of the persistent queue for a call (queue_plan.h): 128-row GEMM
+// units with 128 SwiGLU / 256 output columns per tile, 64-row stream units with
+// 64 / 128 columns per tile.
+qplan::Shape queue_shape(int n_rows, int E, int n_shared, int nseg, int d, int I, int nq, int lag) {
+  qplan::Shape sh;
+  sh.E = E;
+  sh.S = n_shared;
+  sh.nseg = nseg;
+  sh.n_rows = n_rows;
+  sh.stream_max = kStreamMaxRows;
+  sh.bm[qplan::kGemm] = GemmSmall::BM;
+  sh.bm[qplan::kStream] = 16 * kStreamMF;
+  sh.nch1[qplan::kGemm] = (I + GemmSmall::BN / 2 - 1) / (GemmSmall::BN / 2);
+  sh.nch1[qplan::kStream] = (I + kWaves * 16 - 1) / (kWaves * 16);
+  sh.nch2[qplan::kGemm] = (d + GemmSmall::BN - 1) / GemmSmall::BN;
+  sh.nch2[qplan::kStream] = (d + kWaves * 32 - 1) / (kWaves * 32);
+  sh.nq = nq;
+  sh.lag = lag;
+  return sh;
+}
+
+// Units never exceed ceil(n_rows / 64) + one partial unit per sequence.
+int queue_units_cap(const qplan::Shape& sh) {
+  const int bmin = sh.bm[0] < sh.bm[1] ? sh.bm[0] : sh.bm[1];
+  return (sh.n_rows + bmin - 1) / bmin + sh.nseq();
 }
 
 Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16) {
@@ -1496,12 +1571,9 @@ Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16)
     L.BM = 16 * pick_mf(avg);
     L.splitk = static_cast<long long>(n_rows) <= static_cast<long long>(kSplitKMaxAvg) * G;
   } else {
-    // With a priority segment both phases could run in one persistent launch
-    // (ffn_queue_bf16); that path stays off unless LIBMOE_FFN_QUEUE=1 is set:
-    // its phase-2 waits did not see the phase-1 counters complete on MI355X
-    // (the counters are bumped with L2 atomics but polled with cache-bypassing
-    // loads).  The two-launch GEMM still serves the priority segment's tiles
-    // first in each launch.
+    // With a priority segment both phases run in one persistent launch
+    // (ffn_queue_bf16: decode-priority tile queues, stream tiles for small
+    // experts and GEMM tiles for large ones); otherwise two GEMM launches.
     L.path = (nseg > 1 && queue_path_requested()) ? Path::kQueue
              : avg >= kGemmLargeMinAvg                  ? Path::kGemmLarge
                                                         : Path::kGemm;
@@ -1511,12 +1583,14 @@ Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16)
   L.a_off = 0;
   const size_t a_bytes = static_cast<size_t>(n_rows) * I * (bf16 ? 2 : 4);
   L.q_off = (a_bytes + 255) / 256 * 256;
-  // queue heads, per-(unit, chunk) phase-1 flags; the last 4 bytes of the
-  // workspace are the diagnostic word
-  const int nch1_queue = (I + GemmSmall::BN / 2 - 1) / (GemmSmall::BN / 2);
-  L.q_ints = L.path == Path::kQueue
-                 ? static_cast<size_t>(kXcds) * kQueueStride + static_cast<size_t>(L.max_tiles) * nch1_queue
-                 : 0;
+  // persistent queue: the queue heads, then one phase-1 flag per (unit,
+  // column chunk); the last 4 bytes of the workspace are the diagnostic word
+  L.q_ints = 0;
+  if (L.path == Path::kQueue) {
+    const qplan::Shape sh = queue_shape(n_rows, E, n_shared, nseg, d, I, kMaxQueues, 0);
+    L.q_ints = static_cast<size_t>(kMaxQueues) * kQueueStride +
+               static_cast<size_t>(queue_units_cap(sh)) * sh.nch1_max();
+  }
   L.total = L.q_off + (L.q_ints * 4 + 255) / 256 * 256 + 256;
   return L;
 }
@@ -1603,32 +1677,25 @@ int device_cus() {
 
 void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t stream) {
   using C = GemmSmall;
-  constexpr int BN = C::BN;
   int* qbase = reinterpret_cast<int*>(ws + L.q_off);
   const int n = static_cast<int>(L.q_ints);
   int* diag = reinterpret_cast<int*>(ws + L.total - 4);
   hipLaunchKernelGGL(ffn_queue_reset, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, stream, qbase, n,
                      diag);
-  const int cus = device_cus();
-  const int blocks = cus * C::BLOCKS_PER_CU;          // persistent: every block resident
-  const int nq = cus >= kXcds * kCusPerXcd ? kXcds : (cus >= 4 * kCusPerXcd ? 4 : (cus >= 2 * kCusPerXcd ? 2 : 1));
+  const int blocks = device_cus() * C::BLOCKS_PER_CU;     // persistent: two blocks per CU
+  const int nq = blocks >= kMaxQueues ? kMaxQueues : blocks;
   QueueArgs q;
+  q.shape = queue_shape(a.n_rows, a.E, a.n_shared, a.nseg, a.d, a.I, nq, (blocks + nq - 1) / nq);
   q.offs = a.group_offsets;
-  q.G = a.nseg * a.E + a.n_shared;
-  q.E = a.E;
-  q.nseg = a.nseg;
-  q.n_rows = a.n_rows;
-  q.n_prio_groups = a.nseg > 1 ? a.E : 0;   // segment 0 = the priority tokens' routed groups
-  q.nch1 = (a.I + BN / 2 - 1) / (BN / 2);
-  q.nch2 = (a.d + BN - 1) / BN;
-  q.nq = nq;
   q.arows = a.x_rows;
   q.n_x = a.n_x;
-  q.lag = (blocks + nq - 1) / nq;
   q.heads = qbase;
-  q.flags = qbase + kXcds * kQueueStride;
+  q.flags = qbase + kMaxQueues * kQueueStride;
   q.error = diag;
-  hipLaunchKernelGGL((ffn_queue_bf16<C>), dim3(blocks), dim3(C::NT), 0, stream,
+  q.trace = a.trace;
+  q.trace_per_queue = a.trace ? a.trace_capacity / nq : 0;
+  const size_t lds = C::RING + 5 * static_cast<size_t>(q.shape.nseq() + 1) * sizeof(int);
+  hipLaunchKernelGGL((ffn_queue_bf16<C>), dim3(blocks), dim3(C::NT), lds, stream,
                      static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
                      static_cast<const uint16_t*>(a.w_up), static_cast<const uint16_t*>(a.w_down), a.I, q,
                      reinterpret_cast<uint16_t*>(ws + L.a_off), static_cast<uint16_t*>(a.h_sorted));

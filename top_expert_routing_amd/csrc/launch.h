@@ -51,6 +51,10 @@ struct FfnArgs {
   // weights pre-packed in 1 KiB blocks of 16 rows: 32 K values for bf16
   // (moe_grouped_ffn_packed), 64 for FP8 codes (moe_grouped_ffn_fp8w_packed)
   bool packed = false;
+  // per-tile timeline of the persistent queue (moe_grouped_ffn_traced): records
+  // of 4 uint64, nullptr for none
+  unsigned long long* trace = nullptr;
+  int trace_capacity = 0;
 };
 size_t ffn_workspace_bytes(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16);
 hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream);

@@ -2,7 +2,7 @@
 // same header the GPU kernel includes (top_expert_routing_amd/csrc/queue_plan.h).
 //
 // Input (stdin, whitespace separated):
-//   E S nseg n_rows stream_max bm0 bm1 nch1_0 nch1_1 nch2_0 nch2_1 nq lag units_cap
+//   E S nseg n_rows stream_max bm0 bm1 nch1_0 nch1_1 nch2_0 nch2_1 nq lag nk units_cap
 //   G+1 group offsets
 // Checks, for every queue and pop position:
 //   * every (phase, unit, chunk) of every unit appears exactly once over all
@@ -36,9 +36,9 @@ static int fail(const char* why, long long a = 0, long long b = 0) {
 int main() {
   Shape p{};
   int units_cap = 0;
-  if (std::scanf("%d %d %d %d %d %d %d %d %d %d %d %d %d %d", &p.E, &p.S, &p.nseg, &p.n_rows, &p.stream_max,
-                 &p.bm[0], &p.bm[1], &p.nch1[0], &p.nch1[1], &p.nch2[0], &p.nch2[1], &p.nq, &p.lag,
-                 &units_cap) != 14)
+  if (std::scanf("%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d", &p.E, &p.S, &p.nseg, &p.n_rows, &p.stream_max,
+                 &p.bm[0], &p.bm[1], &p.nch1[0], &p.nch1[1], &p.nch2[0], &p.nch2[1], &p.nq, &p.lag, &p.nk,
+                 &units_cap) != 15)
     return fail("bad header");
   const int G = p.nseg * p.E + p.S;
   std::vector<int> offs(G + 1);
@@ -68,11 +68,12 @@ int main() {
 
   // enumerate every queue
   struct Pop { int phase, unit, chunk, prio; };
-  std::vector<std::vector<Pop>> qlist(p.nq);
+  const int nqueues = p.queues();
+  std::vector<std::vector<Pop>> qlist(nqueues);
   std::map<std::tuple<int, int, int>, int> seen;          // (phase, unit, chunk) -> count
   std::vector<std::vector<int>> unit_rows(units);         // rows of each unit (from its phase-1 chunk 0 tile)
   long long tiles = 0;
-  for (int q = 0; q < p.nq; ++q) {
+  for (int q = 0; q < nqueues; ++q) {
     std::vector<int> pre[4];                              // P1, R1, P2, R2 prefixes
     for (auto& v : pre) v.assign(ns + 1, 0);
     SeqCounts sum{0, 0, 0, 0};
@@ -96,6 +97,7 @@ int main() {
       if (tl.split < 0 || tl.split > tl.rows) return fail("split", tl.split, tl.rows);
       if (static_cast<long long>(tl.unit) * p.nch1_max() + tl.chunk >= static_cast<long long>(units_cap) * p.nch1_max())
         return fail("flag index above capacity", tl.unit, tl.chunk);
+      if (p.nk == 2 && tl.kind != q / p.nq) return fail("tile in the other kind's queue", q, tl.kind);
       const bool is_prio_unit = tl.mt < su[tl.seq].tp;
       if (is_prio_unit != (tl.prio != 0)) return fail("priority part holds a wrong unit", tl.unit, tl.prio);
       std::vector<int> rr;
@@ -133,10 +135,10 @@ int main() {
   std::vector<int> done1(units, 0), need1(units, 0);
   for (int s = 0; s < ns; ++s)
     for (int mt = 0; mt < su[s].units; ++mt) need1[fu[s] + mt] = p.nch1[su[s].kind];
-  std::vector<size_t> head(p.nq, 0);
+  std::vector<size_t> head(nqueues, 0);
   for (bool progress = true; progress;) {
     progress = false;
-    for (int q = 0; q < p.nq; ++q) {
+    for (int q = 0; q < nqueues; ++q) {
       while (head[q] < qlist[q].size()) {
         const Pop& x = qlist[q][head[q]];
         if (x.phase == 1) {
@@ -149,7 +151,7 @@ int main() {
       }
     }
   }
-  for (int q = 0; q < p.nq; ++q)
+  for (int q = 0; q < nqueues; ++q)
     if (head[q] != qlist[q].size()) return fail("queue stalls on a wait that never ends", q, head[q]);
   std::printf("ok units=%d tiles=%lld\n", units, tiles);
   return 0;

@@ -437,10 +437,14 @@ def test_grouped_ffn_queue_path(T, E, k, S, P, d, I, kind):
     unit = (info >> 32).astype(np.int64)
     keys = set(zip(phase.tolist(), unit.tolist(), chunk.tolist()))
     assert len(keys) == len(rec), "a tile ran twice"
-    per_q = trace.shape[0] // 8
+    nq = 16                                   # 8 queue groups x 2 tile kinds
+    per_q = trace.shape[0] // nq
     slot = np.nonzero(tr[:, 1] != 0)[0]
     q_of, t_of = slot // per_q, slot % per_q
-    for q in range(8):
+    assert np.array_equal(q_of, (rec[:, 3] >> 32).astype(np.int64)), "record in another queue's slots"
+    kind = ((info >> 2) & 3).astype(np.int64)
+    assert np.all(kind == q_of // 8), "a tile in the other kind's queue"
+    for q in range(nq):
         sel = q_of == q
         if not sel.any():
             continue

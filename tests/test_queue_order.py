@@ -8,7 +8,8 @@ the workspace the host allocates, and with ONE block per queue popping in
 order (a waiting block stalls its whole queue) every queue drains - so no
 phase-2 wait of the kernel can stall on a phase-1 tile that is never popped.
 The shapes mirror the library's: 128-row GEMM units (128 SwiGLU / 256 output
-columns per tile), 64-row stream units (64 / 128 columns), up to 8 queues.
+columns per tile), 64-row stream units (64 / 128 columns), up to 8 queue
+groups, with one queue per group or one per group and tile kind.
 """
 import os
 import shutil
@@ -34,13 +35,13 @@ def checker(tmp_path_factory):
     return exe
 
 
-def _run(exe, offs, E, S, nseg, d, I, stream_max=64, nq=8, lag=64, units_cap=None):
+def _run(exe, offs, E, S, nseg, d, I, stream_max=64, nq=8, lag=64, units_cap=None, nk=2):
     N = int(offs[-1])
     bm = (128, 64)
     nch1 = (-(-I // 128), -(-I // 64))
     nch2 = (-(-d // 256), -(-d // 128))
     cap = -(-N // 64) + E + S if units_cap is None else units_cap
-    hdr = [E, S, nseg, N, stream_max, bm[0], bm[1], nch1[0], nch1[1], nch2[0], nch2[1], nq, lag, cap]
+    hdr = [E, S, nseg, N, stream_max, bm[0], bm[1], nch1[0], nch1[1], nch2[0], nch2[1], nq, lag, nk, cap]
     inp = " ".join(map(str, hdr)) + "\n" + " ".join(map(str, np.asarray(offs).tolist())) + "\n"
     r = subprocess.run([exe], input=inp, capture_output=True, text=True)
     return r.returncode, r.stdout.strip()
@@ -75,11 +76,11 @@ CASES = [
 
 
 @pytest.mark.parametrize("T,E,k,S,P,d,I,kind", CASES)
-@pytest.mark.parametrize("stream_max,nq,lag", [(64, 8, 64), (0, 8, 64), (1 << 30, 8, 0), (64, 1, 1),
-                                               (64, 3, 5), (32, 8, 1 << 20)])
-def test_queue_order(checker, T, E, k, S, P, d, I, kind, stream_max, nq, lag):
+@pytest.mark.parametrize("stream_max,nq,lag,nk", [(64, 8, 64, 2), (64, 8, 64, 1), (0, 8, 64, 2), (1 << 30, 8, 0, 2),
+                                                  (64, 1, 1, 2), (64, 3, 5, 2), (32, 8, 1 << 20, 1)])
+def test_queue_order(checker, T, E, k, S, P, d, I, kind, stream_max, nq, lag, nk):
     offs = _offsets(T, E, k, S, P, kind, seed=T + E)
-    rc, out = _run(checker, offs, E, S, 2 if P else 1, d, I, stream_max, nq, lag)
+    rc, out = _run(checker, offs, E, S, 2 if P else 1, d, I, stream_max, nq, lag, nk=nk)
     assert rc == 0 and out.startswith("ok"), out
 
 
@@ -91,7 +92,9 @@ def test_queue_order_gptoss_shape(checker):
     ids, _ = O.gate(wl.logits.numpy(), s.k)
     offs = O.permute(ids, s.E, s.S, s.n_priority)["group_offsets"]
     for stream_max in (64, 0):
-        rc, out = _run(checker, offs, s.E, s.S, 2, s.d, s.I, stream_max, 8, 64)
+        for nk in (1, 2):
+            rc, out = _run(checker, offs, s.E, s.S, 2, s.d, s.I, stream_max, 8, 64, nk=nk)
+            assert rc == 0 and out.startswith("ok"), out
         assert rc == 0 and out.startswith("ok"), out
 
 

@@ -219,6 +219,19 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
+// Four bf16 outputs (8 bytes).  COHERENT: as an agent-scope atomic store
+// (written through to the device's coherence point, so a consumer on another
+// XCD sees it after its acquire without the producer writing back its L2).
+template <bool COHERENT>
+__device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, float d) {
+  const uint2 v = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+  if constexpr (COHERENT)
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), __builtin_bit_cast(unsigned long long, v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *reinterpret_cast<uint2*>(p) = v;
+}
+
 // ---- decode-sized tiles: weights stream from HBM straight into MFMA registers ----
 // One block of four waves per item (m-tile of <= 16*MF rows, 64*NFC output
 // columns).  Each wave computes every row of the m-tile against its own 16*NFC
@@ -241,20 +254,21 @@ constexpr int decode_kc() { return MF <= 2 ? 256 : 128; }
 constexpr int kDecodeWavesPerSimd = 4;
 
 // LDS staging of one decode tile: two buffers of BM rows x (KC + 8) bf16.
-template <int MF>
-constexpr int decode_lds_elems() { return 2 * 16 * MF * (decode_kc<MF>() + 8); }
+template <int MF, int KC = decode_kc<MF>()>
+constexpr int decode_lds_elems() { return 2 * 16 * MF * (KC + 8); }
 
 // One decode-shaped tile: item `it` (rows it.row(0..rows), output columns
-// it.chunk * 64 * NFC + [0, 64 * NFC)) of expert it.expert.  All kThreads
-// threads call it; `As0` is decode_lds_elems<MF>() bf16 of LDS, free on entry.
-template <int MF, int NFC, int PHASE, bool PK = false>
+// it.chunk * 64 * NFC + [0, 64 * NFC)) of expert it.expert, K in chunks of KC.
+// All kThreads threads call it; `As0` is decode_lds_elems<MF, KC>() bf16 of
+// LDS, free on entry.
+template <int MF, int NFC, int PHASE, bool PK = false, bool COHERENT = false, int KC = decode_kc<MF>()>
 __device__ __forceinline__ void decode_tile(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x,
                                             int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
                                             int Ncols, const Item& it, uint16_t* __restrict__ out, uint16_t* As0) {
   constexpr int NF = PHASE == 1 ? 2 * NFC : NFC;
   constexpr int BN = kWaves * 16 * NFC;
   constexpr int BM = 16 * MF;
-  constexpr int kDecodeKC = decode_kc<MF>();
+  constexpr int kDecodeKC = KC;
   constexpr int kDecodeStride = kDecodeKC + 8;             // bf16 per staged A row (pad 16 B)
   constexpr int U = kDecodeKC / 32;
   constexpr int VPR = kDecodeKC / 8;                       // uint4 per staged row
@@ -365,7 +379,7 @@ __device__ __forceinline__ void decode_tile(const uint16_t* __restrict__ A, cons
       float v[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) v[t] = PHASE == 1 ? silu_mul(acc[i][j][t], acc[i][NFC + j][t]) : acc[i][j][t];
-      *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      store4<COHERENT>(orow + n, v[0], v[1], v[2], v[3]);
     }
   }
 }
@@ -949,6 +963,7 @@ struct TileMath {
   // accumulator block a lane holds token row l32 and output columns
   // 8 (r/4) + 4 hk + r % 4: four consecutive columns per r/4, stored as one
   // 8-byte write (Ncols is a multiple of 32 on this path).
+  template <bool COHERENT = false>
   __device__ __forceinline__ void store(const Item& it, int Ncols, uint16_t* __restrict__ out) const {
     constexpr int OUTC = PHASE == 1 ? BN / 2 : BN;
     const int n0 = it.chunk * OUTC;
@@ -968,7 +983,7 @@ struct TileMath {
 #pragma unroll
           for (int t = 0; t < 4; ++t)
             v[t] = PHASE == 1 ? silu_mul(acc[i][j][4 * q + t], acc[i][NJ / 2 + j][4 * q + t]) : acc[i][j][4 * q + t];
-          *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          store4<COHERENT>(orow + n, v[0], v[1], v[2], v[3]);
         }
       }
     }
@@ -1021,7 +1036,7 @@ __device__ __forceinline__ uint32_t lds_address(const uint8_t* smem) {
 // One tile: the it.rows sorted rows it.row(0..) of A against output column chunk
 // `it.chunk` of expert `it.expert`.  `smem` is the block's operand ring, free
 // on entry (no wave still reads it).
-template <int PHASE, class C>
+template <int PHASE, class C, bool COHERENT = false>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x,
                                           int K, const uint16_t* __restrict__ W0,
                                           const uint16_t* __restrict__ W1, int Ncols, const Item& it,
@@ -1056,7 +1071,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const 
   if (ld.na == C::ADMA) loop(Int<C::ADMA>{});
   else if (ld.na == 1) loop(Int<1>{});
   else loop(Int<0>{});
-  mm.store(it, Ncols, out);
+  mm.template store<COHERENT>(it, Ncols, out);
 }
 
 // One tile per block, blocks dealt by the hardware (two resident per CU, so
@@ -1249,9 +1264,14 @@ int gemm_grid() {
 //     decode-shaped weight-streaming tiles (64-row units, weights straight from
 //     HBM into MFMA registers), larger ones on 128 x 256 LDS-tiled GEMM tiles
 //     (128-row units), so memory-bound and MFMA-bound tiles share the chip;
-//   * block b takes its tiles from queue b mod nq with one atomic add; queue
-//     order puts the priority units' phase 1 first and their phase 2 after a
-//     lag of one round of the other phase-1 tiles;
+//   * the queues come in eight groups (one per XCD's worth of blocks), each
+//     with one queue of GEMM tiles and one of stream tiles; block b belongs to
+//     group b mod 8 and takes tiles with one atomic add from the queue of its
+//     preferred kind (alternating over the blocks, so that the two blocks of
+//     a CU likely run one tile of each kind side by side), then from its
+//     group's other queue once the first is empty; queue order puts the
+//     priority units' phase 1 first and their phase 2 after a lag of one
+//     round of the other phase-1 tiles;
 //   * a phase-2 tile of unit u waits until each phase-1 tile of u has raised
 //     its flag (one int per (unit, column chunk)).
 // Memory ordering (HIP / LLVM AMDGPU memory model, agent scope): after a
@@ -1276,6 +1296,7 @@ constexpr int kQueueStride = 32;                 // ints between the queue heads
 constexpr int kMaxQueues = 8;
 constexpr int kStreamMaxRows = 64;               // sequences of 1..64 rows: weight-streaming tiles
 constexpr int kStreamMF = 4;                     // 64-row stream units
+constexpr int kStreamKC = 256;                   // K per chunk of a stream tile (staging fits the GEMM ring)
 constexpr unsigned long long kWaitTicks = 2000000ull;   // 20 ms of the 100 MHz counter
 constexpr int kMaxPolls = 1 << 22;
 constexpr int kMaxSeq = MOE_MAX_EXPERTS_DEV + 256;      // routed + shared experts
@@ -1286,7 +1307,7 @@ struct QueueArgs {
   const int* offs;
   const int* arows;   // phase-1 A row list (nullptr: sorted rows)
   int n_x;
-  int* heads;         // [nq * kQueueStride]
+  int* heads;         // [nk * nq * kQueueStride]: one head per queue
   int* flags;         // [units_cap][nch1_max]: phase-1 tile (unit, chunk) done
   int* error;         // diagnostic word, set when a wait gave up
   unsigned long long* trace;   // optional per-tile records, trace_per_queue per queue
@@ -1301,44 +1322,61 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
     const uint16_t* __restrict__ w_down, int I, QueueArgs q, uint16_t* __restrict__ abuf,
     uint16_t* __restrict__ h) {
   static_assert(C::NT == kThreads, "one block shape for both tile kinds");
-  static_assert(decode_lds_elems<kStreamMF>() * 2 <= C::RING, "stream tiles stage their rows in the GEMM ring");
+  static_assert(decode_lds_elems<kStreamMF, kStreamKC>() * 2 <= C::RING,
+                "stream tiles stage their rows in the GEMM ring");
+  constexpr int NV = 9;              // per sequence: units, then P1, R1, P2, R2 of each of the block's queues
   // dynamic LDS: the GEMM operand ring (also the stream tiles' row staging),
-  // then five prefix arrays of nseq + 1 ints: units (fu) and this queue's tile
-  // counts of P1, R1, P2, R2
+  // then NV prefix arrays of nseq + 1 ints: units (fu) and, for each of the
+  // block's (up to) two queues, its tile counts of P1, R1, P2, R2
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   uint8_t* smem = dyn_lds;
   const qplan::Shape& sh = q.shape;
   const int ns = sh.nseq();
   int* fu = reinterpret_cast<int*>(dyn_lds + C::RING);
-  int* pre = fu + (ns + 1);
-  __shared__ int wsum[kWaves][5];
+  __shared__ int wsum[kWaves][NV];
   __shared__ int s_tile, s_ok;
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  const int qi = static_cast<int>(blockIdx.x) % sh.nq;
+  // the block's queues: its group's queue of its preferred kind, then the other
+  // kind's (nk == 2).  The preference alternates with bit 0 ^ bit 5 of the
+  // block's slot in its group, so the two blocks a CU holds (slots 2c and 2c+1,
+  // or c and c+32, depending on how the dispatcher fills CUs) differ.
+  const int grp = static_cast<int>(blockIdx.x) % sh.nq, slot = static_cast<int>(blockIdx.x) / sh.nq;
+  const int pref = ((slot ^ (slot >> 5)) & 1) ? qplan::kStream : qplan::kGemm;
+  const int nmine = sh.nk;
+  int myq[2];
+  myq[0] = sh.nk == 2 ? pref * sh.nq + grp : grp;
+  myq[1] = sh.nk == 2 ? (1 - pref) * sh.nq + grp : grp;
 
   {
-    int cnt[kSeqPerThread][5];
-    int sum[5] = {0, 0, 0, 0, 0};
+    int cnt[kSeqPerThread][NV];
+    int sum[NV];
+#pragma unroll
+    for (int c = 0; c < NV; ++c) sum[c] = 0;
 #pragma unroll
     for (int i = 0; i < kSeqPerThread; ++i) {
       const int s = tid * kSeqPerThread + i;
 #pragma unroll
-      for (int c = 0; c < 5; ++c) cnt[i][c] = 0;
+      for (int c = 0; c < NV; ++c) cnt[i][c] = 0;
       if (s < ns) {
         const qplan::SeqUnits u = qplan::seq_units(sh, qplan::seq_rows(sh, q.offs, s));
-        const qplan::SeqCounts c = qplan::seq_counts(sh, s, u, qi);
         cnt[i][0] = u.units;
-        cnt[i][1] = c.p1;
-        cnt[i][2] = c.r1;
-        cnt[i][3] = c.p2;
-        cnt[i][4] = c.r2;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          if (m < nmine) {
+            const qplan::SeqCounts c = qplan::seq_counts(sh, s, u, myq[m]);
+            cnt[i][1 + 4 * m] = c.p1;
+            cnt[i][2 + 4 * m] = c.r1;
+            cnt[i][3 + 4 * m] = c.p2;
+            cnt[i][4 + 4 * m] = c.r2;
+          }
+        }
       }
 #pragma unroll
-      for (int c = 0; c < 5; ++c) sum[c] += cnt[i][c];
+      for (int c = 0; c < NV; ++c) sum[c] += cnt[i][c];
     }
-    int incl[5];
+    int incl[NV];
 #pragma unroll
-    for (int c = 0; c < 5; ++c) {
+    for (int c = 0; c < NV; ++c) {
       incl[c] = sum[c];
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -1349,7 +1387,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
     }
     __syncthreads();
 #pragma unroll
-    for (int c = 0; c < 5; ++c) {
+    for (int c = 0; c < NV; ++c) {
       int run = incl[c] - sum[c];
       for (int i = 0; i < w; ++i) run += wsum[i][c];
       int* arr = fu + c * (ns + 1);
@@ -1363,12 +1401,15 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
     }
     __syncthreads();
   }
-  const qplan::QueueParts qp = qplan::queue_parts(
-      sh, qplan::SeqCounts{pre[ns], pre[(ns + 1) + ns], pre[2 * (ns + 1) + ns], pre[3 * (ns + 1) + ns]});
-  const int total = qp.total();
   const int nch1max = sh.nch1_max();
   bool waits = true;                 // false once a wait of this block gave up (block-uniform)
 
+  for (int m = 0; m < nmine; ++m) {
+  const int qi = myq[m];
+  const int* pre = fu + (1 + 4 * m) * (ns + 1);     // P1, R1, P2, R2 prefixes of queue qi
+  const qplan::QueueParts qp = qplan::queue_parts(
+      sh, qplan::SeqCounts{pre[ns], pre[(ns + 1) + ns], pre[2 * (ns + 1) + ns], pre[3 * (ns + 1) + ns]});
+  const int total = qp.total();
   for (;;) {
     if (tid == 0) s_tile = __hip_atomic_fetch_add(q.heads + qi * kQueueStride, 1, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
@@ -1383,15 +1424,15 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
     const unsigned long long t0 = q.trace ? realtime() : 0ull;
     if (tl.phase == 1) {
       if (tl.kind == qplan::kGemm)
-        gemm_tile<1, C>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
+        gemm_tile<1, C, true>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
       else
-        decode_tile<kStreamMF, 1, 1>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf,
-                                     reinterpret_cast<uint16_t*>(smem));
-      // publish: each wave's row stores reach the coherence point, then the flag
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        decode_tile<kStreamMF, 1, 1, false, true, kStreamKC>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf,
+                                                             reinterpret_cast<uint16_t*>(smem));
+      // publish: every wave's agent-scope row stores have completed, then the flag
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (tid == 0)
-        __hip_atomic_store(q.flags + static_cast<size_t>(tl.unit) * nch1max + tl.chunk, 1, __ATOMIC_RELEASE,
+        __hip_atomic_store(q.flags + static_cast<size_t>(tl.unit) * nch1max + tl.chunk, 1, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     } else {
       if (waits) {
@@ -1427,8 +1468,8 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
       if (tl.kind == qplan::kGemm)
         gemm_tile<2, C>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
       else
-        decode_tile<kStreamMF, 2, 2>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h,
-                                     reinterpret_cast<uint16_t*>(smem));
+        decode_tile<kStreamMF, 2, 2, false, false, kStreamKC>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h,
+                                                              reinterpret_cast<uint16_t*>(smem));
     }
     if (q.trace && tid == 0 && t < q.trace_per_queue) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1440,6 +1481,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
              static_cast<unsigned long long>(tl.phase - 1);
       r[3] = (static_cast<unsigned long long>(qi) << 32) | blockIdx.x;
     }
+  }
   }
 }
 
@@ -1549,6 +1591,11 @@ qplan::Shape queue_shape(int n_rows, int E, int n_shared, int nseg, int d, int I
   sh.nch2[qplan::kStream] = (d + kWaves * 32 - 1) / (kWaves * 32);
   sh.nq = nq;
   sh.lag = lag;
+  // One queue per group for both tile kinds: per-kind queues (nk = 2) keep
+  // about half the blocks on each kind at every instant, but neither kind ran
+  // faster beside the other (GPT-OSS-shaped mixed batch: 2.11 ms against
+  // 2.07 ms, decode segment done at 789 us against 567 us)
+  sh.nk = 1;
   return sh;
 }
 
@@ -1588,7 +1635,7 @@ Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16)
   L.q_ints = 0;
   if (L.path == Path::kQueue) {
     const qplan::Shape sh = queue_shape(n_rows, E, n_shared, nseg, d, I, kMaxQueues, 0);
-    L.q_ints = static_cast<size_t>(kMaxQueues) * kQueueStride +
+    L.q_ints = static_cast<size_t>(2 * kMaxQueues) * kQueueStride +
                static_cast<size_t>(queue_units_cap(sh)) * sh.nch1_max();
   }
   L.total = L.q_off + (L.q_ints * 4 + 255) / 256 * 256 + 256;
@@ -1690,11 +1737,11 @@ void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t 
   q.arows = a.x_rows;
   q.n_x = a.n_x;
   q.heads = qbase;
-  q.flags = qbase + kMaxQueues * kQueueStride;
+  q.flags = qbase + 2 * kMaxQueues * kQueueStride;
   q.error = diag;
   q.trace = a.trace;
-  q.trace_per_queue = a.trace ? a.trace_capacity / nq : 0;
-  const size_t lds = C::RING + 5 * static_cast<size_t>(q.shape.nseq() + 1) * sizeof(int);
+  q.trace_per_queue = a.trace ? a.trace_capacity / q.shape.queues() : 0;
+  const size_t lds = C::RING + 9 * static_cast<size_t>(q.shape.nseq() + 1) * sizeof(int);
   hipLaunchKernelGGL((ffn_queue_bf16<C>), dim3(blocks), dim3(C::NT), lds, stream,
                      static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
                      static_cast<const uint16_t*>(a.w_up), static_cast<const uint16_t*>(a.w_down), a.I, q,

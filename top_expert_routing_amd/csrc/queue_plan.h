@@ -19,19 +19,24 @@
 // bm[kind] rows; phase 1 (gate/up + SwiGLU) cuts the I columns into nch1[kind]
 // chunks, phase 2 (down projection) the d columns into nch2[kind] chunks.
 //
-// Queues.  Chunk j of sequence s in phase p goes to queue
-// (s * nch_p + j) mod nq, with all of that chunk's units, so the units that
-// share a weight slab run on one queue (one XCD's L2) and a large expert's
-// chunks spread over every queue.  Queue q's tiles, in pop order:
+// Queues.  Chunk j of sequence s in phase p goes to queue group
+// x = (s * nch_p + j) mod nq, with all of that chunk's units, so the units that
+// share a weight slab run on one queue group (one XCD's L2) and a large
+// expert's chunks spread over every group.  With nk == 2 each group holds two
+// queues, one per tile kind (queue id kind * nq + x), so that workers can pick
+// a kind and a CU can run a memory-bound and an MFMA-bound tile side by side;
+// with nk == 1 one queue (id x) holds both kinds.  Queue q's tiles, in pop
+// order:
 //   [P1: phase 1 of priority units][R1 head: the first `lag` phase-1 tiles of
 //   the other units][P2: phase 2 of priority units][R1 tail][R2: phase 2 of
 //   the other units]
 // and inside each part sequence by sequence, chunk by chunk, unit by unit.
-// A phase-2 tile of unit u needs the phase-1 tiles of u in every queue.  Each
-// queue lists every phase-1 tile of a kind (priority or not) before any
-// phase-2 tile of that kind, and all P1 tiles are at the front of their
-// queues, so a waited-for tile has always been popped, or will be popped by
-// a block of its queue that is not waiting (see queue_check in the tests).
+// A phase-2 tile of unit u needs the phase-1 tiles of u in every queue group
+// (of u's kind).  Each queue lists every phase-1 tile of a kind (priority or
+// not) before any phase-2 tile of that kind, and all P1 tiles are at the front
+// of their queues, so a waited-for tile has always been popped, or will be
+// popped by a block of its queue that is not waiting (see queue_check in the
+// tests).
 #pragma once
 
 #ifdef __HIPCC__
@@ -51,7 +56,9 @@ struct Shape {
   int bm[2];                // unit rows per kind
   int nch1[2], nch2[2];     // column chunks per kind and phase
   int nq, lag;
+  int nk;                   // 1: one queue per group; 2: one per group and tile kind
   MOE_HD int nseq() const { return E + S; }
+  MOE_HD int queues() const { return nq * nk; }
   MOE_HD int nch1_max() const { return nch1[0] > nch1[1] ? nch1[0] : nch1[1]; }
 };
 
@@ -116,8 +123,10 @@ struct SeqCounts {
 };
 
 MOE_HD SeqCounts seq_counts(const Shape& p, int s, const SeqUnits& u, int q) {
-  const int c1 = chunks_in_queue(first_chunk(s, p.nch1[u.kind], q, p.nq), p.nch1[u.kind], p.nq);
-  const int c2 = chunks_in_queue(first_chunk(s, p.nch2[u.kind], q, p.nq), p.nch2[u.kind], p.nq);
+  if (p.nk == 2 && u.kind != q / p.nq) return SeqCounts{0, 0, 0, 0};   // the other kind's queue
+  const int x = q % p.nq;
+  const int c1 = chunks_in_queue(first_chunk(s, p.nch1[u.kind], x, p.nq), p.nch1[u.kind], p.nq);
+  const int c2 = chunks_in_queue(first_chunk(s, p.nch2[u.kind], x, p.nq), p.nch2[u.kind], p.nq);
   return SeqCounts{u.tp * c1, (u.units - u.tp) * c1, u.tp * c2, (u.units - u.tp) * c2};
 }
 
@@ -186,7 +195,7 @@ MOE_HD Tile decode_tile(const Shape& p, const int* offs, const int* pre, const i
   t.prio = sl.prio;
   t.seq = s;
   t.kind = u.kind;
-  t.chunk = first_chunk(s, nch, q, p.nq) + p.nq * (local / nu);
+  t.chunk = first_chunk(s, nch, q % p.nq, p.nq) + p.nq * (local / nu);
   t.mt = (sl.prio ? 0 : u.tp) + local % nu;
   t.unit = fu[s] + t.mt;
   const int bm = p.bm[u.kind];

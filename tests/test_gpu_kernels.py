@@ -437,13 +437,12 @@ def test_grouped_ffn_queue_path(T, E, k, S, P, d, I, kind):
     unit = (info >> 32).astype(np.int64)
     keys = set(zip(phase.tolist(), unit.tolist(), chunk.tolist()))
     assert len(keys) == len(rec), "a tile ran twice"
-    nq = 16                                   # 8 queue groups x 2 tile kinds
+    nq = 8                                    # one queue per group of blocks, both tile kinds
     per_q = trace.shape[0] // nq
     slot = np.nonzero(tr[:, 1] != 0)[0]
     q_of, t_of = slot // per_q, slot % per_q
     assert np.array_equal(q_of, (rec[:, 3] >> 32).astype(np.int64)), "record in another queue's slots"
-    kind = ((info >> 2) & 3).astype(np.int64)
-    assert np.all(kind == q_of // 8), "a tile in the other kind's queue"
+    assert np.array_equal((rec[:, 3] & 0xFFFFFFFF).astype(np.int64) % nq, q_of), "block took another group's queue"
     for q in range(nq):
         sel = q_of == q
         if not sel.any():

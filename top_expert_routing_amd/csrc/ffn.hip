@@ -1296,7 +1296,7 @@ constexpr int kQueueStride = 32;                 // ints between the queue heads
 constexpr int kMaxQueues = 8;
 constexpr int kStreamMaxRows = 64;               // sequences of 1..64 rows: weight-streaming tiles
 constexpr int kStreamMF = 4;                     // 64-row stream units
-constexpr int kStreamKC = 256;                   // K per chunk of a stream tile (staging fits the GEMM ring)
+constexpr int kStreamKC = 128;                   // K per chunk of a stream tile (staging fits the GEMM ring)
 constexpr unsigned long long kWaitTicks = 2000000ull;   // 20 ms of the 100 MHz counter
 constexpr int kMaxPolls = 1 << 22;
 constexpr int kMaxSeq = MOE_MAX_EXPERTS_DEV + 256;      // routed + shared experts
@@ -1694,7 +1694,7 @@ void launch_gemm_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, u
   const uint16_t* wu = static_cast<const uint16_t*>(a.w_up);
   const uint16_t* wd = static_cast<const uint16_t*>(a.w_down);
   uint16_t* h = static_cast<uint16_t*>(a.h_sorted);
-  if (C::BLOCKS_PER_CU > 1) {
+  if constexpr (C::BLOCKS_PER_CU > 1) {
     hipLaunchKernelGGL((ffn_gemm_bf16<1, C>), dim3(item_grid(L.max_tiles, nch1)), dim3(C::NT), 0, stream, x, a.d, wg,
                        wu, a.I, plan, abuf);
     hipLaunchKernelGGL((ffn_gemm_bf16<2, C>), dim3(item_grid(L.max_tiles, nch2)), dim3(C::NT), 0, stream, abuf, a.I,

@@ -199,8 +199,8 @@ moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t 
  *   trace           device buffer of trace_capacity records, 4 uint64 each,
  *                   16-byte aligned; the caller zero-fills it.
  *   trace_capacity  records (>= 0; 0: no trace, exactly moe_grouped_ffn).
- *   Records are written only on the persistent-queue path, which has nq = 16
- *   queues (8 groups x 2 tile kinds).  Queue q owns records
+ *   Records are written only on the persistent-queue path, which has nq = 8
+ *   queues (block b takes its tiles from queue b mod 8).  Queue q owns records
  *   [q * (trace_capacity / nq), (q + 1) * (trace_capacity / nq)); its tile
  *   popped at position t writes record q * (trace_capacity / nq) + t if
  *   t < trace_capacity / nq:

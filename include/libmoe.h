@@ -41,8 +41,9 @@
  *     bytes it needs in *workspace_bytes, returns MOE_OK and enqueues nothing.
  *     The size depends only on the scalar arguments.  Otherwise
  *     *workspace_bytes is the size of the caller's buffer.
- *   - Calls are reentrant; the library holds no mutable global state.  Two calls
- *     that share a workspace must not overlap in time.
+ *   - Calls are reentrant; apart from moe_grouped_ffn_noalloc's per-device
+ *     scratch array the library holds no mutable global state.  Two calls that
+ *     share a workspace must not overlap in time.
  *   - Expert ids outside [0, E) in an input id array are a precondition
  *     violation: kernels clamp them into range to stay memory safe, the
  *     results are then unspecified.
@@ -219,6 +220,32 @@ moe_status moe_grouped_ffn_traced(const void* x_sorted, const int32_t* x_rows, i
                                   const void* w_down, moe_dtype dtype, void* h_sorted, void* workspace,
                                   size_t* workspace_bytes, uint64_t* trace, int32_t trace_capacity,
                                   hipStream_t stream);
+
+/*
+ * moe_grouped_ffn_noalloc - moe_grouped_ffn with no workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The call allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *
+ *   Arguments and results as moe_grouped_ffn without `workspace` and
+ *   `workspace_bytes`.  The workspace lives in a device array of
+ *   MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ *   until the process ends; its device address is looked up on the first call
+ *   on each device.  All calls on one GPU share that array and it keeps the
+ *   last call's contents (every call writes what it reads first): calls that
+ *   overlap in time on one GPU (for example on two streams) race, so the
+ *   caller orders them.  The diagnostic word of moe_grouped_ffn stays inside
+ *   the array and is not visible to the caller.
+ *   Errors: as moe_grouped_ffn; MOE_ERR_WORKSPACE when the call needs more
+ *   than MOE_NOALLOC_SCRATCH_BYTES of workspace (the SwiGLU intermediate
+ *   n_rows * I values plus a little; decode-sized batches fit), MOE_ERR_HIP
+ *   when the array's address cannot be looked up.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_grouped_ffn_noalloc(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                                   const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
+                                   int32_t nseg, int32_t d, int32_t I, const void* w_gate, const void* w_up,
+                                   const void* w_down, moe_dtype dtype, void* h_sorted, hipStream_t stream);
 
 /*
  * moe_grouped_ffn_packed - moe_grouped_ffn (bf16) for decode-sized groups,

@@ -28,6 +28,7 @@ def _declared():
 
 def test_header_declares_the_calls():
     assert _declared() == sorted(["moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_traced",
+                                  "moe_grouped_ffn_noalloc",
                                   "moe_grouped_ffn_packed", "moe_grouped_ffn_fp8w", "moe_grouped_ffn_fp8w_packed",
                                   "moe_combine", "moe_stats", "moe_prob_signature", "moe_status_string"])
 
@@ -191,6 +192,19 @@ def test_ffn_traced_validation_and_query(lib):
     assert f(*args(a15=FAKE, a16=ctypes.byref(big), a17=None)) == INV        # NULL trace
     assert f(*args(a15=FAKE, a16=ctypes.byref(big), a17=FAKE + 8)) == INV    # misaligned trace
     assert f(*args(a15=FAKE, a16=ctypes.byref(big), a8=100)) == UNS          # checks of moe_grouped_ffn apply
+
+
+def test_ffn_noalloc_validation(lib):
+    """Argument errors and the scratch limit are reported before the library
+    touches a GPU (the CPU here has none)."""
+    f = lib.moe_grouped_ffn_noalloc
+    args = lambda **kw: [kw.get(f"a{i}", v) for i, v in enumerate(
+        [FAKE, None, 0, FAKE, 1024, 64, 0, 1, 2048, 1024, FAKE, FAKE, FAKE, 1, FAKE, None])]
+    assert f(*args(a7=3)) == INV                                     # nseg
+    assert f(*args(a8=100)) == UNS                                   # d not a multiple of 8
+    assert f(*args(a13=5)) == UNS                                    # unknown dtype
+    assert f(*args(a4=65536, a5=128, a8=2048, a9=768)) == WS         # Qwen3-shaped: above the 64 MiB array
+    assert f(*args(a4=0)) == 0                                       # no rows: nothing to do
 
 
 def test_combine_validation(lib):

@@ -208,6 +208,37 @@ def grouped_ffn(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_s
     return h_sorted
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def grouped_ffn_noalloc(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_shared: int, nseg: int,
+                        w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, h_sorted: torch.Tensor,
+                        x_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """grouped_ffn on the library's per-device scratch array
+    (moe_grouped_ffn_noalloc): no workspace, nothing allocated by the call.
+    The caller passes the output; calls on one GPU must not overlap."""
+    _need(x_sorted, "x_sorted", None, 2)
+    _need(group_offsets, "group_offsets", torch.int32, 1)
+    for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(w, name, x_sorted.dtype, 3)
+    n_x, d = x_sorted.shape
+    N = n_x
+    if x_rows is not None:
+        _need(x_rows, "x_rows", torch.int32, 1)
+        N = x_rows.numel()
+    I = w_gate.shape[1]
+    if w_gate.shape != (E + n_shared, I, d) or w_up.shape != w_gate.shape or w_down.shape != (E + n_shared, d, I):
+        raise ValueError("expert weight shapes do not match [E+S][I][d] / [E+S][d][I]")
+    if group_offsets.numel() != nseg * E + n_shared + 1:
+        raise ValueError("group_offsets must have nseg*E + n_shared + 1 entries")
+    _out(h_sorted, "h_sorted", x_sorted.dtype, (N, d))
+    lib = _lib.load()
+    check("moe_grouped_ffn_noalloc", lib.moe_grouped_ffn_noalloc(
+        _ptr(x_sorted), _ptr(x_rows), n_x, _ptr(group_offsets), N, E, n_shared, nseg, d, I, _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), _dtype_code(x_sorted), _ptr(h_sorted), _stream(x_sorted.device)))
+    return h_sorted
+
+
 PACKED_MAX_AVG_ROWS = 48
 
 

@@ -3,10 +3,37 @@
 // reads device memory on the host.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "libmoe.h"
 #include "launch.h"
 
 namespace {
+
+// Scratch of moe_grouped_ffn_noalloc: the FFN workspace (SwiGLU intermediate,
+// tile-queue flags, diagnostic word) in a device array that every GPU the
+// library runs on holds until the process ends.  In host code `scratch` only
+// names the symbol; its device address is looked up once per device (with that
+// device current) and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// This device's copy of `scratch`.
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return MOE_ERR_HIP;
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 constexpr long long kIntMax = 0x7fffffffLL;
 
@@ -246,6 +273,25 @@ moe_status moe_grouped_ffn_traced(const void* x_sorted, const int32_t* x_rows, i
   return ffn_call(x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I, w_gate, w_up, w_down, dtype,
                   h_sorted, workspace, workspace_bytes, trace_capacity > 0 ? trace : nullptr, trace_capacity,
                   stream);
+}
+
+moe_status moe_grouped_ffn_noalloc(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                                   const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
+                                   int32_t nseg, int32_t d, int32_t I, const void* w_gate, const void* w_up,
+                                   const void* w_down, moe_dtype dtype, void* h_sorted, hipStream_t stream) {
+  // the scalar checks of moe_grouped_ffn, and the workspace this call needs
+  size_t need = 0;
+  moe_status st = ffn_call(x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I, w_gate, w_up,
+                           w_down, dtype, h_sorted, nullptr, &need, nullptr, 0, stream);
+  if (st != MOE_OK) return st;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  if (n_rows == 0) return MOE_OK;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MOE_OK) return st;
+  size_t have = MOE_NOALLOC_SCRATCH_BYTES;
+  return ffn_call(x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I, w_gate, w_up, w_down, dtype,
+                  h_sorted, ws, &have, nullptr, 0, stream);
 }
 
 moe_status moe_grouped_ffn_packed(const void* x_sorted, const int32_t* x_rows, int32_t n_x,

@@ -21,6 +21,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "item_plan.h"
 #include "launch.h"
 #include "queue_plan.h"
 
@@ -46,7 +47,6 @@ constexpr int kWaves = kThreads / kWave;
 // priority segment's items start first on every XCD.
 constexpr int kMaxGroups = 2 * 512 + 256;   // nseg * E + shared experts, at most
 constexpr int kMaxGroupsPerThread = (kMaxGroups + kThreads - 1) / kThreads;   // for 256 threads
-constexpr int kXcds = 8;                    // MI355X: 8 XCDs, workgroups dealt round-robin
 
 struct PlanArgs {
   const int* offs;
@@ -92,62 +92,6 @@ __device__ __forceinline__ size_t a_row_of(const int* arows, int n_x, int n, int
   return arows ? static_cast<size_t>(min(max(raw, 0), n_x - 1)) : static_cast<size_t>(n);
 }
 
-// A tile's rows: tile row r < split is sorted row row0 + r, a later one is
-// row1 + (r - split) (two ranges when a priority group and the same expert's
-// other rows share a tile; one range otherwise, split == rows).
-struct Item {
-  int row0, rows, expert, chunk;   // rows == 0: no work for this block
-  int split, row1;
-  __device__ __forceinline__ int row(int r) const { return r < split ? row0 + r : row1 + (r - split); }
-};
-
-__device__ __forceinline__ Item contiguous_item(int row0, int rows, int expert, int chunk) {
-  return Item{row0, rows, expert, chunk, rows, row0 + rows};
-}
-
-// Column chunks of group g that XCD x holds: j = first, first + 8, ... < nch.
-__device__ __forceinline__ int xcd_first_chunk(int g, int nch, int x) {
-  return static_cast<int>((static_cast<long long>(x) - static_cast<long long>(g) * nch) & (kXcds - 1));
-}
-__device__ __forceinline__ int xcd_chunks(int first, int nch) {
-  return first < nch ? (nch - 1 - first) / kXcds + 1 : 0;
-}
-
-// The rows a group's tiles cover: `na` rows from row `a0`, then `nb` rows from
-// row `b0`, cut into m-tiles of BM; the group owns tiles [t0, t0 + nt).
-struct GroupRows {
-  int a0, na, b0, nb, t0, nt;
-};
-
-// With a priority segment (nseg == 2), expert e's priority rows P and its
-// other rows R are tiled as one sequence P ++ R: group e (priority segment)
-// owns the tiles that hold a row of P - so its first tile carries the first
-// rows of R too, and the expert's weights stream once for both when R is
-// small - and group E + e owns the remaining tiles.  Every priority row is
-// still in the priority part of the list.  Otherwise a group is its own rows.
-__device__ __forceinline__ GroupRows group_rows(const PlanArgs& p, int g) {
-  auto lo = [&](int i) { return min(max(p.offs[i], 0), p.n_rows); };
-  GroupRows r;
-  if (p.nseg == 2 && g < 2 * p.E) {
-    const int e = g < p.E ? g : g - p.E;
-    r.a0 = lo(e);
-    r.na = max(0, lo(e + 1) - r.a0);
-    r.b0 = lo(p.E + e);
-    r.nb = max(0, lo(p.E + e + 1) - r.b0);
-    const int tp = (r.na + p.BM - 1) / p.BM;
-    r.t0 = g < p.E ? 0 : tp;
-    r.nt = g < p.E ? tp : (r.na + r.nb + p.BM - 1) / p.BM - tp;
-  } else {
-    r.a0 = lo(g);
-    r.na = max(0, lo(g + 1) - r.a0);
-    r.b0 = r.a0 + r.na;
-    r.nb = 0;
-    r.t0 = 0;
-    r.nt = (r.na + p.BM - 1) / p.BM;
-  }
-  return r;
-}
-
 // Must be called by all NT threads of the block.
 template <int NT = kThreads>
 __device__ Item block_find_item(const PlanArgs& p, int nch) {
@@ -166,8 +110,8 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
     const int g = tid * GPT + q;
     gr[q] = GroupRows{0, 0, 0, 0, 0, 0};
     if (g < p.G) {
-      gr[q] = group_rows(p, g);
-      s += gr[q].nt * xcd_chunks(xcd_first_chunk(g, nch, x), nch);
+      gr[q] = group_rows(p.offs, p.n_rows, p.E, p.nseg, p.BM, g);
+      s += group_items(gr[q], g, nch, x);
     }
   }
   int incl = s;
@@ -188,29 +132,13 @@ __device__ Item block_find_item(const PlanArgs& p, int nch) {
       const int g = tid * GPT + q;
       if (g >= p.G) break;
       const GroupRows& r = gr[q];
-      const int first = xcd_first_chunk(g, nch, x);
-      const int n = r.nt * xcd_chunks(first, nch);
-      if (slot >= t && slot < t + n) {
-        const int local = slot - t;
-        const int j = first + kXcds * (local / r.nt);
-        const int a = (r.t0 + local % r.nt) * p.BM;                  // first row of the tile in the sequence
-        const int rows = min(p.BM, r.na + r.nb - a);
-        const int split = min(max(r.na - a, 0), rows);
-        found = Item{r.a0 + a, rows, expert_of_group(g, p.E, p.nseg), j, split, r.b0 + max(a - r.na, 0)};
-      }
+      const int n = group_items(r, g, nch, x);
+      if (slot >= t && slot < t + n) found = group_item(r, g, nch, x, slot - t, p.BM, p.E, p.nseg);
       t += n;
     }
   }
   __syncthreads();
   return found;
-}
-
-// Grid size that covers every possible item of a call: XCD x holds at most
-// ceil(nch / 8) chunks of each group, so at most max_tiles * ceil(nch / 8)
-// items.
-inline int item_grid(int max_tiles, int nch) {
-  const long long per_xcd = static_cast<long long>(max_tiles) * ((nch + kXcds - 1) / kXcds);
-  return static_cast<int>(per_xcd * kXcds);
 }
 
 // silu(g) * u for the bf16 kernels (their result is rounded to bf16, so the
@@ -604,7 +532,6 @@ __global__ __launch_bounds__(kThreads8, 4) void ffn_decode_fp8w(
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int l16 = lane & 15, q = lane >> 4;
   const int col0 = it.chunk * BN + wave * 16 * NFC;
-  const size_t wstride = static_cast<size_t>(Ncols) * K;   // bytes per expert matrix
   const int nchunks = (K + KC - 1) / KC;
 
   const uint8_t* bp[NF];
@@ -613,8 +540,7 @@ __global__ __launch_bounds__(kThreads8, 4) void ffn_decode_fp8w(
     const int n = min(col0 + (j % NFC) * 16 + l16, Ncols - 1);
     const uint8_t* W = (PHASE == 1 && j >= NFC) ? W1 : W0;
     // packed: blocks of 16 rows x 64 codes (1 KiB), lane 16 q + l16 at byte 16 * lane
-    bp[j] = PK ? W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n / 16) * (K / 64) * 1024 + lane * 16
-               : W + static_cast<size_t>(e) * wstride + static_cast<size_t>(n) * K + 16 * q;
+    bp[j] = W + fp8_code_offset(e, n, K, Ncols, lane, 0, PK);
   }
 
   // token rows of a chunk: thread handles uint4 slots idx = tid + s * 512
@@ -659,7 +585,7 @@ __global__ __launch_bounds__(kThreads8, 4) void ffn_decode_fp8w(
       const int kk = kc + 64 * u + 16 * q;
 #pragma unroll
       for (int j = 0; j < NF; ++j)
-        b[u][j] = kk < K ? *reinterpret_cast<const uint4*>(bp[j] + (PK ? (kc + 64 * u) * 16 : kc + 64 * u))
+        b[u][j] = kk < K ? *reinterpret_cast<const uint4*>(bp[j] + fp8_code_step(kc + 64 * u, PK))
                          : make_uint4(0, 0, 0, 0);
     }
   };

@@ -189,7 +189,8 @@ constexpr int decode_lds_elems() { return 2 * 16 * MF * (KC + 8); }
 // it.chunk * 64 * NFC + [0, 64 * NFC)) of expert it.expert, K in chunks of KC.
 // All kThreads threads call it; `As0` is decode_lds_elems<MF, KC>() bf16 of
 // LDS, free on entry.
-template <int MF, int NFC, int PHASE, bool PK = false, bool COHERENT = false, int KC = decode_kc<MF>()>
+template <int MF, int NFC, int PHASE, bool PK = false, bool COHERENT = false, int KC = decode_kc<MF>(),
+          bool DB = false>
 __device__ __forceinline__ void decode_tile(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x,
                                             int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
                                             int Ncols, const Item& it, uint16_t* __restrict__ out, uint16_t* As0) {
@@ -281,14 +282,34 @@ __device__ __forceinline__ void decode_tile(const uint16_t* __restrict__ A, cons
 
   load_a(0);
   store_a(0);
-  for (int c = 0; c < nchunks; ++c) {
-    uint4 b[U][NF];
-    load_b(b, c);
-    const bool more = c + 1 < nchunks;
-    if (more) load_a(c + 1);
-    __syncthreads();                           // chunk c of A is in As[c & 1]
-    mma(b, As(c & 1));
-    if (more) store_a((c + 1) & 1);            // that buffer was last read before this barrier
+  if constexpr (DB) {
+    // weight registers double buffered: chunk c + 1's loads are in flight while
+    // chunk c is multiplied (for callers with few waves per CU)
+    uint4 b0[U][NF], b1[U][NF];
+    load_b(b0, 0);
+    for (int c = 0; c < nchunks; c += 2) {
+      if (c + 1 < nchunks) load_b(b1, c + 1);
+      if (c + 1 < nchunks) load_a(c + 1);
+      __syncthreads();                         // chunk c of A is in As[c & 1]
+      mma(b0, As(0));
+      if (c + 1 < nchunks) store_a(1);
+      if (c + 1 >= nchunks) break;
+      if (c + 2 < nchunks) load_b(b0, c + 2);
+      if (c + 2 < nchunks) load_a(c + 2);
+      __syncthreads();                         // chunk c + 1 of A is in As[1]
+      mma(b1, As(1));
+      if (c + 2 < nchunks) store_a(0);
+    }
+  } else {
+    for (int c = 0; c < nchunks; ++c) {
+      uint4 b[U][NF];
+      load_b(b, c);
+      const bool more = c + 1 < nchunks;
+      if (more) load_a(c + 1);
+      __syncthreads();                         // chunk c of A is in As[c & 1]
+      mma(b, As(c & 1));
+      if (more) store_a((c + 1) & 1);          // that buffer was last read before this barrier
+    }
   }
 
   // The MFMA computes (weight rows) x (token rows)^T: in each 16x16 block a
@@ -1190,14 +1211,9 @@ int gemm_grid() {
 //     decode-shaped weight-streaming tiles (64-row units, weights straight from
 //     HBM into MFMA registers), larger ones on 128 x 256 LDS-tiled GEMM tiles
 //     (128-row units), so memory-bound and MFMA-bound tiles share the chip;
-//   * the queues come in eight groups (one per XCD's worth of blocks), each
-//     with one queue of GEMM tiles and one of stream tiles; block b belongs to
-//     group b mod 8 and takes tiles with one atomic add from the queue of its
-//     preferred kind (alternating over the blocks, so that the two blocks of
-//     a CU likely run one tile of each kind side by side), then from its
-//     group's other queue once the first is empty; queue order puts the
-//     priority units' phase 1 first and their phase 2 after a lag of one
-//     round of the other phase-1 tiles;
+//   * block b takes its tiles from queue b mod 8 with one atomic add; queue
+//     order puts the priority units' phase 1 first and their phase 2 after a
+//     lag of one round of the other phase-1 tiles;
 //   * a phase-2 tile of unit u waits until each phase-1 tile of u has raised
 //     its flag (one int per (unit, column chunk)).
 // Memory ordering (HIP / LLVM AMDGPU memory model, agent scope): after a
@@ -1242,36 +1258,36 @@ struct QueueArgs {
 
 __device__ __forceinline__ unsigned long long realtime() { return __builtin_amdgcn_s_memrealtime(); }
 
-template <class C>
-__global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
+// Configuration of the persistent queue kernel: GEMM tiles (128 x 256,
+// GemmSmall's ring) for large experts and 64-row weight-streaming tiles for the
+// rest, two blocks per CU, row-major weights.
+struct QueueMixed {
+  using C = GemmSmall;
+  static constexpr int BPC = C::BLOCKS_PER_CU, SMF = kStreamMF, SKC = kStreamKC;
+  static constexpr bool GEMM = true, DB = true, PK = false;
+  static constexpr int RING = C::RING;
+};
+
+template <class QC>
+__global__ __launch_bounds__(kThreads, QC::BPC) void ffn_queue_bf16(
     const uint16_t* __restrict__ x, int d, const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
     const uint16_t* __restrict__ w_down, int I, QueueArgs q, uint16_t* __restrict__ abuf,
     uint16_t* __restrict__ h) {
+  using C = typename QC::C;
   static_assert(C::NT == kThreads, "one block shape for both tile kinds");
-  static_assert(decode_lds_elems<kStreamMF, kStreamKC>() * 2 <= C::RING,
-                "stream tiles stage their rows in the GEMM ring");
-  constexpr int NV = 9;              // per sequence: units, then P1, R1, P2, R2 of each of the block's queues
-  // dynamic LDS: the GEMM operand ring (also the stream tiles' row staging),
-  // then NV prefix arrays of nseq + 1 ints: units (fu) and, for each of the
-  // block's (up to) two queues, its tile counts of P1, R1, P2, R2
+  static_assert(decode_lds_elems<QC::SMF, QC::SKC>() * 2 <= QC::RING, "stream tiles stage their rows in the ring");
+  constexpr int NV = 5;              // per sequence: units, then this queue's P1, R1, P2, R2 tile counts
+  // dynamic LDS: the ring (GEMM operands; also the stream tiles' row staging),
+  // then NV prefix arrays of nseq + 1 ints
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   uint8_t* smem = dyn_lds;
   const qplan::Shape& sh = q.shape;
   const int ns = sh.nseq();
-  int* fu = reinterpret_cast<int*>(dyn_lds + C::RING);
+  int* fu = reinterpret_cast<int*>(dyn_lds + QC::RING);
   __shared__ int wsum[kWaves][NV];
   __shared__ int s_tile, s_ok;
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  // the block's queues: its group's queue of its preferred kind, then the other
-  // kind's (nk == 2).  The preference alternates with bit 0 ^ bit 5 of the
-  // block's slot in its group, so the two blocks a CU holds (slots 2c and 2c+1,
-  // or c and c+32, depending on how the dispatcher fills CUs) differ.
-  const int grp = static_cast<int>(blockIdx.x) % sh.nq, slot = static_cast<int>(blockIdx.x) / sh.nq;
-  const int pref = ((slot ^ (slot >> 5)) & 1) ? qplan::kStream : qplan::kGemm;
-  const int nmine = sh.nk;
-  int myq[2];
-  myq[0] = sh.nk == 2 ? pref * sh.nq + grp : grp;
-  myq[1] = sh.nk == 2 ? (1 - pref) * sh.nq + grp : grp;
+  const int qi = static_cast<int>(blockIdx.x) % sh.nq;   // block b takes its tiles from queue b mod nq
 
   {
     int cnt[kSeqPerThread][NV];
@@ -1285,17 +1301,12 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
       for (int c = 0; c < NV; ++c) cnt[i][c] = 0;
       if (s < ns) {
         const qplan::SeqUnits u = qplan::seq_units(sh, qplan::seq_rows(sh, q.offs, s));
+        const qplan::SeqCounts c = qplan::seq_counts(sh, s, u, qi);
         cnt[i][0] = u.units;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          if (m < nmine) {
-            const qplan::SeqCounts c = qplan::seq_counts(sh, s, u, myq[m]);
-            cnt[i][1 + 4 * m] = c.p1;
-            cnt[i][2 + 4 * m] = c.r1;
-            cnt[i][3 + 4 * m] = c.p2;
-            cnt[i][4 + 4 * m] = c.r2;
-          }
-        }
+        cnt[i][1] = c.p1;
+        cnt[i][2] = c.r1;
+        cnt[i][3] = c.p2;
+        cnt[i][4] = c.r2;
       }
 #pragma unroll
       for (int c = 0; c < NV; ++c) sum[c] += cnt[i][c];
@@ -1329,10 +1340,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
   }
   const int nch1max = sh.nch1_max();
   bool waits = true;                 // false once a wait of this block gave up (block-uniform)
-
-  for (int m = 0; m < nmine; ++m) {
-  const int qi = myq[m];
-  const int* pre = fu + (1 + 4 * m) * (ns + 1);     // P1, R1, P2, R2 prefixes of queue qi
+  const int* pre = fu + (ns + 1);    // P1, R1, P2, R2 prefixes of queue qi
   const qplan::QueueParts qp = qplan::queue_parts(
       sh, qplan::SeqCounts{pre[ns], pre[(ns + 1) + ns], pre[2 * (ns + 1) + ns], pre[3 * (ns + 1) + ns]});
   const int total = qp.total();
@@ -1349,11 +1357,12 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
     const Item it{tl.row0, tl.rows, tl.seq, tl.chunk, tl.split, tl.row1};
     const unsigned long long t0 = q.trace ? realtime() : 0ull;
     if (tl.phase == 1) {
-      if (tl.kind == qplan::kGemm)
-        gemm_tile<1, C, true>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
-      else
-        decode_tile<kStreamMF, 1, 1, false, true, kStreamKC>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf,
-                                                             reinterpret_cast<uint16_t*>(smem));
+      if (QC::GEMM && tl.kind == qplan::kGemm) {
+        if constexpr (QC::GEMM) gemm_tile<1, C, true>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
+      } else {
+        decode_tile<QC::SMF, 1, 1, QC::PK, true, QC::SKC, QC::DB>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf,
+                                                                   reinterpret_cast<uint16_t*>(smem));
+      }
       // publish: every wave's agent-scope row stores have completed, then the flag
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -1391,11 +1400,12 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
         __syncthreads();
         waits = s_ok != 0;
       }
-      if (tl.kind == qplan::kGemm)
-        gemm_tile<2, C>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
-      else
-        decode_tile<kStreamMF, 2, 2, false, false, kStreamKC>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h,
-                                                              reinterpret_cast<uint16_t*>(smem));
+      if (QC::GEMM && tl.kind == qplan::kGemm) {
+        if constexpr (QC::GEMM) gemm_tile<2, C>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
+      } else {
+        decode_tile<QC::SMF, 2, 2, QC::PK, false, QC::SKC, QC::DB>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h,
+                                                                    reinterpret_cast<uint16_t*>(smem));
+      }
     }
     if (q.trace && tid == 0 && t < q.trace_per_queue) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1407,7 +1417,6 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_queue_bf16(
              static_cast<unsigned long long>(tl.phase - 1);
       r[3] = (static_cast<unsigned long long>(qi) << 32) | blockIdx.x;
     }
-  }
   }
 }
 
@@ -1517,10 +1526,11 @@ qplan::Shape queue_shape(int n_rows, int E, int n_shared, int nseg, int d, int I
   sh.nch2[qplan::kStream] = (d + kWaves * 32 - 1) / (kWaves * 32);
   sh.nq = nq;
   sh.lag = lag;
-  // One queue per group for both tile kinds: per-kind queues (nk = 2) keep
-  // about half the blocks on each kind at every instant, but neither kind ran
-  // faster beside the other (GPT-OSS-shaped mixed batch: 2.11 ms against
-  // 2.07 ms, decode segment done at 789 us against 567 us)
+  // One queue per group for both tile kinds (the kernel takes one queue per
+  // block): per-kind queues (nk = 2) keep about half the blocks on each kind at
+  // every instant, but neither kind ran faster beside the other (GPT-OSS-shaped
+  // mixed batch: 2.11 ms against 2.07 ms, decode segment done at 789 us
+  // against 567 us)
   sh.nk = 1;
   return sh;
 }
@@ -1543,6 +1553,12 @@ Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16)
     L.path = Path::kDecode;
     L.BM = 16 * pick_mf(avg);
     L.splitk = static_cast<long long>(n_rows) <= static_cast<long long>(kSplitKMaxAvg) * G;
+    // Decode-sized batches keep two launches: the persistent queue with
+    // stream tiles only (both phases in one launch, 16/32/64-row units, four
+    // or two blocks per CU) was slower on every decode shape measured
+    // (OLMoE-shaped FFN 161 -> 194 us, DSv2-Lite T=128 176 -> 215 us): per tile
+    // it adds a queue pop, a completion wait before the flag and written-through
+    // intermediate rows, against tiles of a few tens of microseconds.
   } else {
     // With a priority segment both phases run in one persistent launch
     // (ffn_queue_bf16: decode-priority tile queues, stream tiles for small
@@ -1648,14 +1664,14 @@ int device_cus() {
   return cached[slot];
 }
 
+template <class QC>
 void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t stream) {
-  using C = GemmSmall;
   int* qbase = reinterpret_cast<int*>(ws + L.q_off);
   const int n = static_cast<int>(L.q_ints);
   int* diag = reinterpret_cast<int*>(ws + L.total - 4);
   hipLaunchKernelGGL(ffn_queue_reset, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, stream, qbase, n,
                      diag);
-  const int blocks = device_cus() * C::BLOCKS_PER_CU;     // persistent: two blocks per CU
+  const int blocks = device_cus() * QC::BPC;              // persistent: QC::BPC blocks per CU
   const int nq = blocks >= kMaxQueues ? kMaxQueues : blocks;
   QueueArgs q;
   q.shape = queue_shape(a.n_rows, a.E, a.n_shared, a.nseg, a.d, a.I, nq, (blocks + nq - 1) / nq);
@@ -1667,8 +1683,8 @@ void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t 
   q.error = diag;
   q.trace = a.trace;
   q.trace_per_queue = a.trace ? a.trace_capacity / q.shape.queues() : 0;
-  const size_t lds = C::RING + 9 * static_cast<size_t>(q.shape.nseq() + 1) * sizeof(int);
-  hipLaunchKernelGGL((ffn_queue_bf16<C>), dim3(blocks), dim3(C::NT), lds, stream,
+  const size_t lds = QC::RING + 5 * static_cast<size_t>(q.shape.nseq() + 1) * sizeof(int);
+  hipLaunchKernelGGL((ffn_queue_bf16<QC>), dim3(blocks), dim3(kThreads), lds, stream,
                      static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
                      static_cast<const uint16_t*>(a.w_up), static_cast<const uint16_t*>(a.w_down), a.I, q,
                      reinterpret_cast<uint16_t*>(ws + L.a_off), static_cast<uint16_t*>(a.h_sorted));
@@ -1783,7 +1799,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
       launch_gemm_bf16<GemmLarge>(a, L, plan, reinterpret_cast<uint16_t*>(ws + L.a_off), stream);
       break;
     case Path::kQueue:
-      launch_queue_bf16(a, L, ws, stream);
+      launch_queue_bf16<QueueMixed>(a, L, ws, stream);
       break;
     case Path::kF32: {
       float* abuf = reinterpret_cast<float*>(ws + L.a_off);

@@ -55,9 +55,9 @@ def parse():
                     help="expert weights as E4M3 codes with per-row scales (moe_grouped_ffn_fp8w); the CPU "
                          "baseline leg is skipped in this mode")
     ap.add_argument("--unpacked-weights", action="store_true",
-                    help="keep the [E+S][rows][K] weight layout (moe_grouped_ffn) on decode-sized bf16 "
-                         "workloads; by default their weights are pre-packed once before timing "
-                         "(pack_weights) and the FFN runs moe_grouped_ffn_packed")
+                    help="keep the [E+S][rows][K] weight layout (moe_grouped_ffn) on bf16 workloads; by "
+                         "default their weights are pre-packed once before timing (pack_weights) and the FFN "
+                         "runs moe_grouped_ffn_packed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle leg")
     ap.add_argument("--json-out", default="", help="also append the JSON line to this file")
@@ -326,9 +326,8 @@ def main():
     if fp8 and s.dtype != "bf16":
         print("--fp8-weights needs a bf16 workload", file=sys.stderr)
         sys.exit(2)
-    # decode-sized bf16 batches run on pre-packed weights unless asked otherwise
-    packable = (not fp8 and s.dtype == "bf16" and s.d % 32 == 0 and s.I % 32 == 0 and
-                s.N <= moe.PACKED_MAX_AVG_ROWS * ((2 if s.n_priority else 1) * s.E + s.S))
+    # bf16 batches run on pre-packed weights unless asked otherwise
+    packable = not fp8 and s.dtype == "bf16" and s.d % 32 == 0 and s.I % 32 == 0
     packed = packable and not args.unpacked_weights
     # FP8 codes are packed too when d and I are multiples of 64
     fp8_packed = fp8 and s.d % 64 == 0 and s.I % 64 == 0 and not args.unpacked_weights
@@ -476,7 +475,7 @@ def main():
     # the committed counters are for the default mode of each workload
     traffic = None if fp8 or args.unpacked_weights else traffic_for(args.workload)
     roof["traffic"] = None if traffic is None else round(traffic)
-    queue = (not fp8 and not packed and s.dtype == "bf16" and s.n_priority > 0 and s.d % 32 == 0 and
+    queue = (not fp8 and s.dtype == "bf16" and s.n_priority > 0 and s.d % 32 == 0 and
              s.I % 32 == 0 and s.N // s.G > 48 and os.environ.get("LIBMOE_FFN_QUEUE", "1") != "0")
     roof["kernel"] = (f"{ffn_name} (" + ("one persistent launch: decode-priority tile queues" if queue else
                                          "gate/up launch + down launch") + "), HIP events over K eager steps")

@@ -248,27 +248,27 @@ moe_status moe_grouped_ffn_noalloc(const void* x_sorted, const int32_t* x_rows, 
                                    const void* w_down, moe_dtype dtype, void* h_sorted, hipStream_t stream);
 
 /*
- * moe_grouped_ffn_packed - moe_grouped_ffn (bf16) for decode-sized groups,
- * with the expert weights pre-packed so that each weight load instruction of
- * the weight-streaming kernels reads 1 KiB of contiguous memory.
+ * moe_grouped_ffn_packed - moe_grouped_ffn (bf16) on expert weights pre-packed
+ * so that each weight load instruction reads 1 KiB of contiguous memory: the
+ * weight-streaming kernels load it into MFMA registers, the GEMM kernels copy
+ * it into LDS as is.
  * (ExpertPlex page, "Instance vs module disaggregation": the expert FFN; the
  * packing is a one-time weight layout, not a change of the computation.)
  *
- *   Arguments, results, numerics and the diagnostic word as moe_grouped_ffn
- *   with dtype MOE_BF16, except the weight layout.  A weight matrix W [R][K]
- *   (gate and up: R = I, K = d; down: R = d, K = I) of expert e is stored as
- *   blocks of 16 rows x 32 K values, block (r / 16, k / 32) at element offset
- *   ((r / 16) * (K / 32) + k / 32) * 512 of the expert's matrix, and inside a
- *   block W[r][k] at (((k % 32) / 8) * 16 + r % 16) * 8 + k % 8.  Each
- *   expert's matrix keeps its R * K elements at the same place as in the
- *   unpacked [E+S][R][K] array.
- *   Requires d and I multiples of 32 and n_rows <= MOE_PACKED_MAX_AVG_ROWS *
- *   (nseg * E + n_shared) (decode-sized groups; larger batches run on the
- *   GEMM kernels of moe_grouped_ffn with unpacked weights).
- *   Errors: MOE_ERR_UNSUPPORTED for the two conditions above or E > 512;
- *   otherwise as moe_grouped_ffn.  The workspace size is moe_grouped_ffn's.
+ *   Arguments, results, numerics, kernels chosen and the diagnostic word as
+ *   moe_grouped_ffn with dtype MOE_BF16, except the weight layout.  A weight
+ *   matrix W [R][K] (gate and up: R = I, K = d; down: R = d, K = I) of expert
+ *   e is stored as blocks of 16 rows x 32 K values, block (r / 16, k / 32) at
+ *   element offset ((r / 16) * (K / 32) + k / 32) * 512 of the expert's
+ *   matrix, and inside a block W[r][k] at (((k % 32) / 8) * 16 + r % 16) * 8 +
+ *   k % 8.  Each expert's matrix keeps its R * K elements at the same place as
+ *   in the unpacked [E+S][R][K] array.  The results equal moe_grouped_ffn's
+ *   on the unpacked weights bit for bit.
+ *   Requires d and I multiples of 32.
+ *   Errors: MOE_ERR_UNSUPPORTED when d or I is not a multiple of 32 or
+ *   E > 512; otherwise as moe_grouped_ffn.  The workspace size is
+ *   moe_grouped_ffn's.
  */
-#define MOE_PACKED_MAX_AVG_ROWS 48
 moe_status moe_grouped_ffn_packed(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
                                   const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
                                   int32_t nseg, int32_t d, int32_t I, const void* w_gate, const void* w_up,

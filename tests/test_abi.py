@@ -107,8 +107,7 @@ def test_ffn_packed_validation_and_query(lib):
     assert f(*args()) == 0 and n.value >= 64 * 512 * 2            # query (workspace of moe_grouped_ffn)
     assert f(*args(a8=272)) == UNS                                 # d not a multiple of 32
     assert f(*args(a9=528)) == UNS                                 # I not a multiple of 32
-    assert f(*args(a4=49 * 8 + 1)) == UNS                          # groups above 48 rows on average
-    assert f(*args(a4=48 * 8)) == 0                                # 48 on average is accepted
+    assert f(*args(a4=49 * 8 + 1)) == 0                            # GEMM-sized groups: the GEMM kernels read it too
     assert f(*args(a7=3)) == INV                                   # nseg
     big = ctypes.c_size_t(1 << 30)
     assert f(*args(a14=FAKE, a15=ctypes.byref(big), a12=None)) == INV       # NULL w_down

@@ -645,6 +645,11 @@ PACKED_CASES = [
     (24, 16, 2, 1, 6, 96, 160, "random"),       # split-K with a priority segment and a shared expert
     (300, 8, 2, 0, 20, 256, 192, "random"),     # 64-row tiles with a priority segment, column tail
     (4, 512, 4, 256, 2, 64, 32, "random"),      # the largest group count (1280)
+    # GEMM-sized groups: the GEMM kernels copy the packed blocks into LDS
+    (300, 8, 2, 0, 0, 256, 192, "random"),      # 128 x 256 tiles, column tail in I
+    (2000, 8, 2, 0, 0, 256, 320, "random"),     # 256 x 256 persistent tiles, column tail in I
+    (4160, 128, 4, 0, 64, 256, 320, "zipf"),    # priority segment: the persistent queue (GEMM + stream tiles)
+    (1300, 512, 4, 256, 10, 64, 32, "random"),  # the largest group count on the queue
 ]
 
 

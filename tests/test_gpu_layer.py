@@ -169,7 +169,8 @@ def test_layer_fp8_weights_parity(name):
     assert torch.equal(lp.y, layer.y)
 
 
-@pytest.mark.parametrize("name", ["olmoe_decode", "dsv2_decode_t16", "dsv2_decode_t256"])
+@pytest.mark.parametrize("name", ["olmoe_decode", "dsv2_decode_t16", "dsv2_decode_t256", "qwen3_prefill",
+                                  "gptoss_mixed"])
 def test_layer_packed_weights_matches_unpacked(name):
     """The layer on pre-packed weights gives the unpacked layer's outputs bit for
     bit (that layer is checked against the oracle in test_layer_parity)."""

@@ -239,9 +239,6 @@ def grouped_ffn_noalloc(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: 
     return h_sorted
 
 
-PACKED_MAX_AVG_ROWS = 48
-
-
 def pack_weights(w: torch.Tensor) -> torch.Tensor:
     """Expert matrices [..][R][K] in the layout moe_grouped_ffn_packed reads:
     blocks of 16 rows x 32 K values, block (r/16, k/32) at element offset
@@ -260,7 +257,7 @@ def grouped_ffn_packed(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: i
                        w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
                        h_sorted: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                        x_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """grouped_ffn for bf16 decode-sized batches with weights from pack_weights."""
+    """grouped_ffn (bf16, any batch size) with weights from pack_weights."""
     _need(x_sorted, "x_sorted", torch.bfloat16, 2)
     _need(group_offsets, "group_offsets", torch.int32, 1)
     for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):

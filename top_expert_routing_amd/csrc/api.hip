@@ -303,8 +303,6 @@ moe_status moe_grouped_ffn_packed(const void* x_sorted, const int32_t* x_rows, i
     return MOE_ERR_INVALID_ARG;
   if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
   if (d % 32 != 0 || I % 32 != 0) return MOE_ERR_UNSUPPORTED;
-  const long long G = static_cast<long long>(nseg) * E + n_shared;
-  if (n_rows > MOE_PACKED_MAX_AVG_ROWS * G) return MOE_ERR_UNSUPPORTED;   // GEMM-sized groups
   if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
     return MOE_ERR_UNSUPPORTED;
   bool query;

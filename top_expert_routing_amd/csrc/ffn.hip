@@ -751,7 +751,13 @@ __device__ __forceinline__ void wait_ahead_barrier(int ahead) {
 // rows 16 (wave + NW q) .. +15; lane -> row + lane / 4, slot lane % 4, fetching
 // chunk slot ^ swz(row).  Rows past the tile's valid rows / columns read a
 // valid row instead (their results are never stored).
-template <int PHASE, class C>
+// PKB: the weights are pre-packed (pack_weights: blocks of 16 rows x 32 K,
+// 1 KiB each, (row block, K block) order; inside a block lane 16 q + r's 16
+// bytes are W[r][8q .. 8q+7]).  A K-step of 16 weight rows is then one
+// contiguous KiB, which one DMA instruction copies as is: in LDS the block's
+// row r, chunk c sits at byte c * 256 + r * 16 (no swizzle needed: a 16-lane
+// group of an operand read covers 256 contiguous bytes).
+template <int PHASE, class C, bool PKB = false>
 struct TileLoader {
   const uint16_t* asrc[C::ADMA];
   const uint16_t* bsrc[C::BDMA];
@@ -785,14 +791,26 @@ struct TileLoader {
     }
 #pragma unroll
     for (int q = 0; q < C::BDMA; ++q) {
-      const int r = 16 * (wave + C::NW * q) + dr;
-      int n = n0 + r;
-      const uint16_t* W = W0;
-      if (PHASE == 1 && r >= OUTC) {
-        n -= OUTC;
-        W = W1;
+      if constexpr (PKB) {
+        const int rb = 16 * (wave + C::NW * q);         // first tile row of this instruction
+        int nb = n0 + rb;
+        const uint16_t* W = W0;
+        if (PHASE == 1 && rb >= OUTC) {
+          nb -= OUTC;
+          W = W1;
+        }
+        nb = min(nb, Ncols - 16);                        // blocks past the rows are read but never stored
+        bsrc[q] = W + eoff + static_cast<size_t>(nb / 16) * (K / 32) * 512 + lane * 8;
+      } else {
+        const int r = 16 * (wave + C::NW * q) + dr;
+        int n = n0 + r;
+        const uint16_t* W = W0;
+        if (PHASE == 1 && r >= OUTC) {
+          n -= OUTC;
+          W = W1;
+        }
+        bsrc[q] = W + eoff + static_cast<size_t>(min(n, Ncols - 1)) * K + 8 * ((lane & 3) ^ gemm_swz(r));
       }
-      bsrc[q] = W + eoff + static_cast<size_t>(min(n, Ncols - 1)) * K + 8 * ((lane & 3) ^ gemm_swz(r));
     }
   }
 
@@ -808,7 +826,7 @@ struct TileLoader {
     for (int q = 0; q < C::ADMA; ++q)
       if (!skip_a || q < na) dma_b128(asrc[q] + k, st + q * C::NW * 1024);
 #pragma unroll
-    for (int q = 0; q < C::BDMA; ++q) dma_b128(bsrc[q] + k, st + C::A_BYTES + q * C::NW * 1024);
+    for (int q = 0; q < C::BDMA; ++q) dma_b128(bsrc[q] + (PKB ? kt * 512 : k), st + C::A_BYTES + q * C::NW * 1024);
   }
 };
 
@@ -826,7 +844,7 @@ struct Int {
   static constexpr int value = V;
 };
 
-template <int PHASE, class C>
+template <int PHASE, class C, bool PKB = false>
 struct TileMath {
   static constexpr int MI = C::MI, NJ = C::NJ, WM = C::WM, WN = C::WN, BN = C::BN;
   static_assert(PHASE == 2 || NJ % 2 == 0, "phase 1 pairs gate and up blocks");
@@ -834,7 +852,7 @@ struct TileMath {
   static_assert(C::ADMA >= 1 && C::BDMA >= 1, "tile too small for its waves");
   static_assert(C::STAGES >= 2, "the ring needs two buffers");
   int boff[NJ];
-  int aoff, loff[2];
+  int aoff, loff[2], loffb[2];
   int wm, wn, l32, hk;
   int nv;                 // this wave's slabs holding valid rows (wave-uniform)
   f32x16 acc[MI][NJ];
@@ -854,7 +872,10 @@ struct TileMath {
     aoff = 32 * wm * kGemmRowBytes;
     nv = MI;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) loff[s] = l32 * kGemmRowBytes + 16 * ((2 * s + hk) ^ gemm_swz(l32));
+    for (int s = 0; s < 2; ++s) {
+      loff[s] = l32 * kGemmRowBytes + 16 * ((2 * s + hk) ^ gemm_swz(l32));
+      loffb[s] = PKB ? (l32 / 16) * 1024 + (2 * s + hk) * 256 + (l32 % 16) * 16 : loff[s];
+    }
   }
 
   __device__ __forceinline__ void zero() {
@@ -883,7 +904,7 @@ struct TileMath {
       for (int i = 0; i < NV; ++i)
         af[i] = *reinterpret_cast<const bf16x8*>(st + aoff + 32 * WM * i * kGemmRowBytes + loff[s]);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(st + boff[j] + loff[s]);
+      for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(st + boff[j] + loffb[s]);
 #pragma unroll
       for (int i = 0; i < NV; ++i)
 #pragma unroll
@@ -983,15 +1004,15 @@ __device__ __forceinline__ uint32_t lds_address(const uint8_t* smem) {
 // One tile: the it.rows sorted rows it.row(0..) of A against output column chunk
 // `it.chunk` of expert `it.expert`.  `smem` is the block's operand ring, free
 // on entry (no wave still reads it).
-template <int PHASE, class C, bool COHERENT = false>
+template <int PHASE, class C, bool COHERENT = false, bool PKB = false>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x,
                                           int K, const uint16_t* __restrict__ W0,
                                           const uint16_t* __restrict__ W1, int Ncols, const Item& it,
                                           uint16_t* __restrict__ out, uint8_t* smem) {
   constexpr int STAGES = C::STAGES;
-  TileLoader<PHASE, C> ld;
+  TileLoader<PHASE, C, PKB> ld;
   ld.init(A, arows, n_x, K, W0, W1, Ncols, it);
-  TileMath<PHASE, C> mm;
+  TileMath<PHASE, C, PKB> mm;
   mm.init();
   mm.set_rows(it.rows);
   mm.zero();
@@ -1023,7 +1044,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const 
 
 // One tile per block, blocks dealt by the hardware (two resident per CU, so
 // one block's start-up overlaps the other's work).
-template <int PHASE, class C>
+template <int PHASE, class C, bool PKB>
 __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
     int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
@@ -1031,7 +1052,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_bf16(
   constexpr int OUTC = PHASE == 1 ? C::BN / 2 : C::BN;
   const Item it = block_find_item<C::NT>(plan, (Ncols + OUTC - 1) / OUTC);
   if (it.rows == 0) return;
-  gemm_tile<PHASE, C>(A, plan.arows, plan.n_x, K, W0, W1, Ncols, it, out, smem);
+  gemm_tile<PHASE, C, false, PKB>(A, plan.arows, plan.n_x, K, W0, W1, Ncols, it, out, smem);
 }
 
 // ---- persistent GEMM launch: each block walks a list of tiles ----------------
@@ -1044,7 +1065,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_bf16(
 // items' K-steps as one stream through the ring, so the next tile's first
 // K-steps load while the current tile finishes and stores: no per-tile
 // prologue bubble, no block launch per tile.
-template <int PHASE, class C>
+template <int PHASE, class C, bool PKB>
 __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_bf16(
     const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
     int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
@@ -1153,7 +1174,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_b
   const int total = n_my * nk;                         // K-steps of all my tiles, in order
   const uint32_t lds0 = lds_address(smem);
   // issue side: next K-step to load is step ikt of my tile ir, into ring slot islot
-  TileLoader<PHASE, C> ld;
+  TileLoader<PHASE, C, PKB> ld;
   int ir = 0, ikt = 0, islot = 0;
   auto issue_next = [&]() {
     if (ikt == 0) ld.init(A, plan.arows, plan.n_x, K, W0, W1, Ncols, decode(ir));
@@ -1164,7 +1185,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_b
       ++ir;
     }
   };
-  TileMath<PHASE, C> mm;
+  TileMath<PHASE, C, PKB> mm;
   mm.init();
   Item cur{};
 #pragma unroll
@@ -1261,10 +1282,11 @@ __device__ __forceinline__ unsigned long long realtime() { return __builtin_amdg
 // Configuration of the persistent queue kernel: GEMM tiles (128 x 256,
 // GemmSmall's ring) for large experts and 64-row weight-streaming tiles for the
 // rest, two blocks per CU, row-major weights.
+template <bool PKV>
 struct QueueMixed {
   using C = GemmSmall;
   static constexpr int BPC = C::BLOCKS_PER_CU, SMF = kStreamMF, SKC = kStreamKC;
-  static constexpr bool GEMM = true, DB = true, PK = false;
+  static constexpr bool GEMM = true, DB = true, PK = PKV;
   static constexpr int RING = C::RING;
 };
 
@@ -1358,7 +1380,7 @@ __global__ __launch_bounds__(kThreads, QC::BPC) void ffn_queue_bf16(
     const unsigned long long t0 = q.trace ? realtime() : 0ull;
     if (tl.phase == 1) {
       if (QC::GEMM && tl.kind == qplan::kGemm) {
-        if constexpr (QC::GEMM) gemm_tile<1, C, true>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
+        if constexpr (QC::GEMM) gemm_tile<1, C, true, QC::PK>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
       } else {
         decode_tile<QC::SMF, 1, 1, QC::PK, true, QC::SKC, QC::DB>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf,
                                                                    reinterpret_cast<uint16_t*>(smem));
@@ -1401,7 +1423,7 @@ __global__ __launch_bounds__(kThreads, QC::BPC) void ffn_queue_bf16(
         waits = s_ok != 0;
       }
       if (QC::GEMM && tl.kind == qplan::kGemm) {
-        if constexpr (QC::GEMM) gemm_tile<2, C>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
+        if constexpr (QC::GEMM) gemm_tile<2, C, false, QC::PK>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
       } else {
         decode_tile<QC::SMF, 2, 2, QC::PK, false, QC::SKC, QC::DB>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h,
                                                                     reinterpret_cast<uint16_t*>(smem));
@@ -1624,7 +1646,7 @@ void launch_decode_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan,
                      static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted));
 }
 
-template <class C>
+template <class C, bool PKB>
 void launch_gemm_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, uint16_t* abuf, hipStream_t stream) {
   constexpr int BN = C::BN;
   const int nch1 = (a.I + BN / 2 - 1) / (BN / 2), nch2 = (a.d + BN - 1) / BN;
@@ -1637,15 +1659,15 @@ void launch_gemm_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, u
   const uint16_t* wd = static_cast<const uint16_t*>(a.w_down);
   uint16_t* h = static_cast<uint16_t*>(a.h_sorted);
   if constexpr (C::BLOCKS_PER_CU > 1) {
-    hipLaunchKernelGGL((ffn_gemm_bf16<1, C>), dim3(item_grid(L.max_tiles, nch1)), dim3(C::NT), 0, stream, x, a.d, wg,
+    hipLaunchKernelGGL((ffn_gemm_bf16<1, C, PKB>), dim3(item_grid(L.max_tiles, nch1)), dim3(C::NT), 0, stream, x, a.d, wg,
                        wu, a.I, plan, abuf);
-    hipLaunchKernelGGL((ffn_gemm_bf16<2, C>), dim3(item_grid(L.max_tiles, nch2)), dim3(C::NT), 0, stream, abuf, a.I,
+    hipLaunchKernelGGL((ffn_gemm_bf16<2, C, PKB>), dim3(item_grid(L.max_tiles, nch2)), dim3(C::NT), 0, stream, abuf, a.I,
                        wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, h);
   } else {
     const size_t lds = C::RING + C::NW * kEpiBytes + 8 * static_cast<size_t>(plan.G + 1);
-    hipLaunchKernelGGL((ffn_gemm_persistent_bf16<1, C>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, x, a.d, wg,
+    hipLaunchKernelGGL((ffn_gemm_persistent_bf16<1, C, PKB>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, x, a.d, wg,
                        wu, a.I, plan, abuf);
-    hipLaunchKernelGGL((ffn_gemm_persistent_bf16<2, C>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, abuf, a.I,
+    hipLaunchKernelGGL((ffn_gemm_persistent_bf16<2, C, PKB>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, abuf, a.I,
                        wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, h);
   }
 }
@@ -1767,7 +1789,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
   plan.diag = reinterpret_cast<int*>(ws + L.total - 4);
   plan.arows = a.x_rows;
   plan.n_x = a.n_x;
-  if (a.packed && L.path != Path::kDecode) return hipErrorInvalidValue;
+  if (a.packed && L.path == Path::kF32) return hipErrorInvalidValue;
   switch (L.path) {
     case Path::kDecode: {
       uint16_t* abuf = reinterpret_cast<uint16_t*>(ws + L.a_off);
@@ -1793,13 +1815,16 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
       break;
     }
     case Path::kGemm:
-      launch_gemm_bf16<GemmSmall>(a, L, plan, reinterpret_cast<uint16_t*>(ws + L.a_off), stream);
+      if (a.packed) launch_gemm_bf16<GemmSmall, true>(a, L, plan, reinterpret_cast<uint16_t*>(ws + L.a_off), stream);
+      else launch_gemm_bf16<GemmSmall, false>(a, L, plan, reinterpret_cast<uint16_t*>(ws + L.a_off), stream);
       break;
     case Path::kGemmLarge:
-      launch_gemm_bf16<GemmLarge>(a, L, plan, reinterpret_cast<uint16_t*>(ws + L.a_off), stream);
+      if (a.packed) launch_gemm_bf16<GemmLarge, true>(a, L, plan, reinterpret_cast<uint16_t*>(ws + L.a_off), stream);
+      else launch_gemm_bf16<GemmLarge, false>(a, L, plan, reinterpret_cast<uint16_t*>(ws + L.a_off), stream);
       break;
     case Path::kQueue:
-      launch_queue_bf16<QueueMixed>(a, L, ws, stream);
+      if (a.packed) launch_queue_bf16<QueueMixed<true>>(a, L, ws, stream);
+      else launch_queue_bf16<QueueMixed<false>>(a, L, ws, stream);
       break;
     case Path::kF32: {
       float* abuf = reinterpret_cast<float*>(ws + L.a_off);

@@ -107,7 +107,8 @@ def _counter_per_dispatch(csv_path: str, counter: str, name_part: str):
 
 
 def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str):
-    """FFN phase kernels are two dispatches per call; the copy calibration runs
+    """An FFN call is two dispatches: the gate/up and down launches, or the
+    queue reset and the persistent queue launch.  The copy calibration runs
     three 1 GiB copies (each reads and writes 2**30 bytes)."""
     fk, fn = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", "ffn_")
     wk, wn = _counter_per_dispatch(write_csv, "WRITE_SIZE", "ffn_")
@@ -115,6 +116,10 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv:
     cw, cwn = _counter_per_dispatch(copy_write_csv, "WRITE_SIZE", "copyBuffer")
     if not (fn and wn and cfn and cwn) or fn % 2 or wn % 2:
         raise SystemExit("unexpected dispatch counts in the counter CSVs")
+    _, qf = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", "ffn_queue_bf16")
+    _, qw = _counter_per_dispatch(write_csv, "WRITE_SIZE", "ffn_queue_bf16")
+    if (qf and 2 * qf != fn) or (qw and 2 * qw != wn):
+        raise SystemExit("queue launches without their reset in the counter CSVs")
     copy_kib = 3 * 2**30 / 1024.0
     try:
         with open(TRAFFIC_FILE) as f:
@@ -127,7 +132,7 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv:
         "ffn_source_sha256_16": ffn_source_hash(),
         "fetch_scale": round(copy_kib / cf, 4),
         "write_scale": round(copy_kib / cw, 4),
-        "note": "KiB per moe_grouped_ffn call (two dispatches) from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE; "
+        "note": "KiB per FFN call (two dispatches: both phase launches, or queue reset + queue launch) from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE; "
                 "scales = bytes a 1 GiB copy moves / what the same counter reports for it",
     })
     rec.setdefault("workloads", {})[workload] = {
@@ -206,7 +211,7 @@ def cpu_baseline(wl, budget_s: float, w_router=None):
             "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
-def decode_segment(layer, wl, s, dev, expert_bytes):
+def decode_segment(layer, wl, s, dev, expert_bytes, packed):
     """One FFN call of the layer with the per-tile timeline: when the priority
     (decode) segment's last tile and the whole call's last tile ended, from the
     call's first tile start.  Against the time the decode segment's distinct
@@ -215,8 +220,9 @@ def decode_segment(layer, wl, s, dev, expert_bytes):
     import torch
     import top_expert_routing_amd as moe
     trace = torch.zeros((1 << 17, 4), dtype=torch.int64, device=dev)
-    moe.grouped_ffn(wl.x, layer.perm["group_offsets"], s.E, s.S, layer.nseg, layer.w_gate, layer.w_up,
-                    layer.w_down, layer.h_sorted, layer.ffn_ws, x_rows=layer.perm["sorted_token"], trace=trace)
+    ffn = moe.grouped_ffn_packed if packed else moe.grouped_ffn
+    ffn(wl.x, layer.perm["group_offsets"], s.E, s.S, layer.nseg, layer.w_gate, layer.w_up, layer.w_down,
+        layer.h_sorted, layer.ffn_ws, x_rows=layer.perm["sorted_token"], trace=trace)
     torch.cuda.synchronize()
     tr = trace.cpu().numpy().view(np.uint64)
     rec = tr[tr[:, 1] != 0]
@@ -490,7 +496,7 @@ def main():
 
     signature = signature_recording(s, stats_ids, wl.req_offsets, stream, K, dev,
                                     wl.stats_logits.contiguous()) if args.signature else None
-    dseg = decode_segment(layer, wl, s, dev, expert_bytes) if queue else None
+    dseg = decode_segment(layer, wl, s, dev, expert_bytes, packed) if queue else None
 
     tokens_per_s = s.T * K / elapsed
     out = {

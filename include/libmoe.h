@@ -199,7 +199,11 @@ moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t 
  *   Arguments, results and workspace as moe_grouped_ffn, plus
  *   trace           device buffer of trace_capacity records, 4 uint64 each,
  *                   16-byte aligned; the caller zero-fills it.
- *   trace_capacity  records (>= 0; 0: no trace, exactly moe_grouped_ffn).
+ *   trace_capacity  records (>= 0; 0: no trace, exactly moe_grouped_ffn or
+ *                   moe_grouped_ffn_packed).
+ *   weights_packed  0: w_gate, w_up, w_down in moe_grouped_ffn's layout and
+ *                   `dtype`; 1: in moe_grouped_ffn_packed's layout (dtype must
+ *                   be MOE_BF16, d and I multiples of 32).
  *   Records are written only on the persistent-queue path, which has nq = 8
  *   queues (block b takes its tiles from queue b mod 8).  Queue q owns records
  *   [q * (trace_capacity / nq), (q + 1) * (trace_capacity / nq)); its tile
@@ -211,15 +215,17 @@ moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t 
  *     [3] queue << 32 | block index.
  *   A record whose end is 0 was not written.  Tracing adds a wait for the
  *   tile's stores before its end stamp.
- *   Errors: MOE_ERR_INVALID_ARG for trace_capacity < 0 or a NULL or
- *   misaligned trace with trace_capacity > 0; otherwise as moe_grouped_ffn.
+ *   Errors: MOE_ERR_INVALID_ARG for trace_capacity < 0, a NULL or misaligned
+ *   trace with trace_capacity > 0, or weights_packed not 0 or 1;
+ *   MOE_ERR_UNSUPPORTED for packed weights with another dtype or with d or I
+ *   not multiples of 32; otherwise as moe_grouped_ffn.
  */
 moe_status moe_grouped_ffn_traced(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
                                   const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
                                   int32_t nseg, int32_t d, int32_t I, const void* w_gate, const void* w_up,
                                   const void* w_down, moe_dtype dtype, void* h_sorted, void* workspace,
                                   size_t* workspace_bytes, uint64_t* trace, int32_t trace_capacity,
-                                  hipStream_t stream);
+                                  int32_t weights_packed, hipStream_t stream);
 
 /*
  * moe_grouped_ffn_noalloc - moe_grouped_ffn with no workspace argument, for

@@ -182,7 +182,7 @@ def test_ffn_traced_validation_and_query(lib):
     n = ctypes.c_size_t(0)
     args = lambda **kw: [kw.get(f"a{i}", v) for i, v in enumerate(
         [FAKE, None, 0, FAKE, 4160 * 4, 128, 0, 2, 2880, 2880, FAKE, FAKE, FAKE, 1, FAKE, None, ctypes.byref(n),
-         FAKE, 1024, None])]
+         FAKE, 1024, 0, None])]
     assert f(*args()) == 0                                          # query
     st, need = _ffn(lib, N=4160 * 4, E=128, nseg=2, d=2880, I=2880, ws=None, nbytes=0)
     assert st == 0 and n.value == need                              # the same workspace as moe_grouped_ffn
@@ -191,6 +191,10 @@ def test_ffn_traced_validation_and_query(lib):
     assert f(*args(a15=FAKE, a16=ctypes.byref(big), a17=None)) == INV        # NULL trace
     assert f(*args(a15=FAKE, a16=ctypes.byref(big), a17=FAKE + 8)) == INV    # misaligned trace
     assert f(*args(a15=FAKE, a16=ctypes.byref(big), a8=100)) == UNS          # checks of moe_grouped_ffn apply
+    assert f(*args(a15=FAKE, a16=ctypes.byref(big), a19=2)) == INV           # weights_packed is 0 or 1
+    assert f(*args(a19=1)) == 0                                              # packed weights: same query
+    assert f(*args(a15=FAKE, a16=ctypes.byref(big), a19=1, a13=0)) == UNS    # packed weights are bf16 only
+    assert f(*args(a15=FAKE, a16=ctypes.byref(big), a19=1, a8=2888)) == UNS  # packed: d % 32 != 0
 
 
 def test_ffn_noalloc_validation(lib):

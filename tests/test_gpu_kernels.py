@@ -386,16 +386,17 @@ QUEUE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
 @pytest.mark.parametrize("T,E,k,S,P,d,I,kind", QUEUE_CASES)
-def test_grouped_ffn_queue_path(T, E, k, S, P, d, I, kind):
+def test_grouped_ffn_queue_path(T, E, k, S, P, d, I, kind, packed):
     """The persistent single-launch FFN (device-side tile queues, priority
-    tiles first): every row within the bf16 tolerance of the oracle, the
-    diagnostic word 0, the same bits as the two-launch GEMM path, and a
-    per-tile timeline in which every tile ran once, the priority units' phase-1
-    tiles were popped first in each queue, and every phase-2 tile ended after
-    every phase-1 tile of its unit."""
+    tiles first), on row-major and on pre-packed weights: every row within the
+    bf16 tolerance of the oracle, the diagnostic word 0, the two-launch path
+    within the tolerance too, and a per-tile timeline in which every tile ran
+    once, the priority units' phase-1 tiles were popped first in each queue,
+    and every phase-2 tile ended after every phase-1 tile of its unit."""
     import os
-    announce(f"ffn queue T={T} E={E} k={k} S={S} P={P} d={d} I={I} {kind}")
+    announce(f"ffn queue T={T} E={E} k={k} S={S} P={P} d={d} I={I} {kind} packed={packed}")
     wl, ids = _ffn_inputs(T, E, k, S, P, d, I, "bf16", kind, seed=T + E + 11)
     p_ref = O.permute(ids.numpy(), E, S, P, np_of(wl.x))
     N = int(p_ref["group_offsets"][-1])
@@ -404,19 +405,21 @@ def test_grouped_ffn_queue_path(T, E, k, S, P, d, I, kind):
     offs = torch.from_numpy(p_ref["group_offsets"]).to(DEV)
     rows = torch.from_numpy(p_ref["sorted_token"]).to(DEV)
     w = [t.to(DEV) for t in (wl.w_gate, wl.w_up, wl.w_down)]
+    if packed:
+        w = [moe.pack_weights(t) for t in w]
+    ffn = moe.grouped_ffn_packed if packed else moe.grouped_ffn
     x = wl.x.to(DEV)
     nbytes = moe.ffn_workspace_bytes(N, E, S, 2, d, I)
     ws = torch.full((nbytes,), 0x5a, dtype=torch.uint8, device=DEV)
     trace = torch.zeros((1 << 16, 4), dtype=torch.int64, device=DEV)
-    h = moe.grouped_ffn(x, offs, E, S, 2, *w, h_sorted=_poison((N, d), torch.bfloat16), workspace=ws,
-                        x_rows=rows, trace=trace)
+    h = ffn(x, offs, E, S, 2, *w, h_sorted=_poison((N, d), torch.bfloat16), workspace=ws, x_rows=rows, trace=trace)
     torch.cuda.synchronize()
     assert int(ws[-4:].view(torch.int32).item()) == 0, "a tile-queue wait gave up"
     err = rel_max_err(f64_of(h), h_ref)
     assert err <= TOL["bf16"], err
     os.environ["LIBMOE_FFN_QUEUE"] = "0"
     try:
-        h2 = moe.grouped_ffn(x, offs, E, S, 2, *w, h_sorted=_poison((N, d), torch.bfloat16), x_rows=rows)
+        h2 = ffn(x, offs, E, S, 2, *w, h_sorted=_poison((N, d), torch.bfloat16), x_rows=rows)
         torch.cuda.synchronize()
     finally:
         os.environ.pop("LIBMOE_FFN_QUEUE", None)

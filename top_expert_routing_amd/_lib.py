@@ -30,7 +30,7 @@ SIGNATURES = {
     "moe_permute": [_p, _i32, _i32, _i32, _i32, _i32, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _sz, _p],
     "moe_grouped_ffn": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _sz, _p],
     "moe_grouped_ffn_traced": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _sz,
-                               _p, _i32, _p],
+                               _p, _i32, _i32, _p],
     "moe_grouped_ffn_noalloc": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p],
     "moe_grouped_ffn_packed": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p],
     "moe_combine": [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p],

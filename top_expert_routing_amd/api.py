@@ -200,12 +200,16 @@ def grouped_ffn(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_s
     if trace is None:
         check("moe_grouped_ffn", lib.moe_grouped_ffn(*args, _stream(dev)))
     else:
-        _need(trace, "trace", torch.int64, 2)
-        if trace.shape[1] != 4:
-            raise ValueError("trace must be [records][4] int64")
-        check("moe_grouped_ffn_traced", lib.moe_grouped_ffn_traced(*args, _ptr(trace), trace.shape[0],
+        _need_trace(trace)
+        check("moe_grouped_ffn_traced", lib.moe_grouped_ffn_traced(*args, _ptr(trace), trace.shape[0], 0,
                                                                    _stream(dev)))
     return h_sorted
+
+
+def _need_trace(trace: torch.Tensor):
+    _need(trace, "trace", torch.int64, 2)
+    if trace.shape[1] != 4:
+        raise ValueError("trace must be [records][4] int64")
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -256,8 +260,10 @@ def pack_weights(w: torch.Tensor) -> torch.Tensor:
 def grouped_ffn_packed(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_shared: int, nseg: int,
                        w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
                        h_sorted: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                       x_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """grouped_ffn (bf16, any batch size) with weights from pack_weights."""
+                       x_rows: Optional[torch.Tensor] = None,
+                       trace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """grouped_ffn (bf16, any batch size) with weights from pack_weights;
+    `trace` as in grouped_ffn (moe_grouped_ffn_traced with packed weights)."""
     _need(x_sorted, "x_sorted", torch.bfloat16, 2)
     _need(group_offsets, "group_offsets", torch.int32, 1)
     for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
@@ -281,9 +287,16 @@ def grouped_ffn_packed(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: i
                                 dtype=torch.uint8, device=dev)
     lib = _lib.load()
     nbytes = ctypes.c_size_t(workspace.numel())
-    check("moe_grouped_ffn_packed", lib.moe_grouped_ffn_packed(
-        _ptr(x_sorted), _ptr(x_rows), n_x, _ptr(group_offsets), N, E, n_shared, nseg, d, I, _ptr(w_gate),
-        _ptr(w_up), _ptr(w_down), _ptr(h_sorted), _ptr(workspace), ctypes.byref(nbytes), _stream(dev)))
+    if trace is None:
+        check("moe_grouped_ffn_packed", lib.moe_grouped_ffn_packed(
+            _ptr(x_sorted), _ptr(x_rows), n_x, _ptr(group_offsets), N, E, n_shared, nseg, d, I, _ptr(w_gate),
+            _ptr(w_up), _ptr(w_down), _ptr(h_sorted), _ptr(workspace), ctypes.byref(nbytes), _stream(dev)))
+    else:
+        _need_trace(trace)
+        check("moe_grouped_ffn_traced", lib.moe_grouped_ffn_traced(
+            _ptr(x_sorted), _ptr(x_rows), n_x, _ptr(group_offsets), N, E, n_shared, nseg, d, I, _ptr(w_gate),
+            _ptr(w_up), _ptr(w_down), _dtype_code(x_sorted), _ptr(h_sorted), _ptr(workspace), ctypes.byref(nbytes),
+            _ptr(trace), trace.shape[0], 1, _stream(dev)))
     return h_sorted
 
 

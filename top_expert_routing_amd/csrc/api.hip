@@ -118,11 +118,12 @@ moe_status ffn_call(const void* x_sorted, const int32_t* x_rows, int32_t n_x, co
                     int32_t n_rows, int32_t E, int32_t n_shared, int32_t nseg, int32_t d, int32_t I,
                     const void* w_gate, const void* w_up, const void* w_down, moe_dtype dtype, void* h_sorted,
                     void* workspace, size_t* workspace_bytes, uint64_t* trace, int32_t trace_capacity,
-                    hipStream_t stream) {
+                    bool packed, hipStream_t stream) {
   if (n_rows < 0 || E < 1 || n_shared < 0 || (nseg != 1 && nseg != 2) || d < 1 || I < 1)
     return MOE_ERR_INVALID_ARG;
   if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
   if (!known_dtype(dtype) || d % 8 != 0 || I % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (packed && (dtype != MOE_BF16 || d % 32 != 0 || I % 32 != 0)) return MOE_ERR_UNSUPPORTED;
   if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
     return MOE_ERR_UNSUPPORTED;
   bool query;
@@ -155,6 +156,7 @@ moe_status ffn_call(const void* x_sorted, const int32_t* x_rows, int32_t n_x, co
   a.h_sorted = h_sorted;
   a.trace = reinterpret_cast<unsigned long long*>(trace);
   a.trace_capacity = trace_capacity;
+  a.packed = packed;
   return hip_status(moe::launch_ffn(a, workspace, stream));
 }
 
@@ -260,7 +262,7 @@ moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t 
                            const void* w_up, const void* w_down, moe_dtype dtype, void* h_sorted, void* workspace,
                            size_t* workspace_bytes, hipStream_t stream) {
   return ffn_call(x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I, w_gate, w_up, w_down, dtype,
-                  h_sorted, workspace, workspace_bytes, nullptr, 0, stream);
+                  h_sorted, workspace, workspace_bytes, nullptr, 0, false, stream);
 }
 
 moe_status moe_grouped_ffn_traced(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
@@ -268,11 +270,12 @@ moe_status moe_grouped_ffn_traced(const void* x_sorted, const int32_t* x_rows, i
                                   int32_t nseg, int32_t d, int32_t I, const void* w_gate, const void* w_up,
                                   const void* w_down, moe_dtype dtype, void* h_sorted, void* workspace,
                                   size_t* workspace_bytes, uint64_t* trace, int32_t trace_capacity,
-                                  hipStream_t stream) {
+                                  int32_t weights_packed, hipStream_t stream) {
   if (trace_capacity < 0 || (trace_capacity > 0 && (!trace || !aligned16(trace)))) return MOE_ERR_INVALID_ARG;
+  if (weights_packed != 0 && weights_packed != 1) return MOE_ERR_INVALID_ARG;
   return ffn_call(x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I, w_gate, w_up, w_down, dtype,
                   h_sorted, workspace, workspace_bytes, trace_capacity > 0 ? trace : nullptr, trace_capacity,
-                  stream);
+                  weights_packed == 1, stream);
 }
 
 moe_status moe_grouped_ffn_noalloc(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
@@ -282,7 +285,7 @@ moe_status moe_grouped_ffn_noalloc(const void* x_sorted, const int32_t* x_rows, 
   // the scalar checks of moe_grouped_ffn, and the workspace this call needs
   size_t need = 0;
   moe_status st = ffn_call(x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I, w_gate, w_up,
-                           w_down, dtype, h_sorted, nullptr, &need, nullptr, 0, stream);
+                           w_down, dtype, h_sorted, nullptr, &need, nullptr, 0, false, stream);
   if (st != MOE_OK) return st;
   if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
   if (n_rows == 0) return MOE_OK;
@@ -291,7 +294,7 @@ moe_status moe_grouped_ffn_noalloc(const void* x_sorted, const int32_t* x_rows, 
   if (st != MOE_OK) return st;
   size_t have = MOE_NOALLOC_SCRATCH_BYTES;
   return ffn_call(x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I, w_gate, w_up, w_down, dtype,
-                  h_sorted, ws, &have, nullptr, 0, stream);
+                  h_sorted, ws, &have, nullptr, 0, false, stream);
 }
 
 moe_status moe_grouped_ffn_packed(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
@@ -299,41 +302,8 @@ moe_status moe_grouped_ffn_packed(const void* x_sorted, const int32_t* x_rows, i
                                   int32_t nseg, int32_t d, int32_t I, const void* w_gate, const void* w_up,
                                   const void* w_down, void* h_sorted, void* workspace, size_t* workspace_bytes,
                                   hipStream_t stream) {
-  if (n_rows < 0 || E < 1 || n_shared < 0 || (nseg != 1 && nseg != 2) || d < 1 || I < 1)
-    return MOE_ERR_INVALID_ARG;
-  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
-  if (d % 32 != 0 || I % 32 != 0) return MOE_ERR_UNSUPPORTED;
-  if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
-    return MOE_ERR_UNSUPPORTED;
-  bool query;
-  moe_status st = workspace_check(workspace, workspace_bytes,
-                                  moe::ffn_workspace_bytes(n_rows, E, n_shared, nseg, d, I, 1), &query);
-  if (st != MOE_OK || query) return st;
-  if (n_rows == 0) return MOE_OK;
-  if (!x_sorted || !group_offsets || !w_gate || !w_up || !w_down || !h_sorted) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x_sorted) || !aligned4(group_offsets) || !aligned16(w_gate) || !aligned16(w_up) ||
-      !aligned16(w_down) || !aligned16(h_sorted))
-    return MOE_ERR_INVALID_ARG;
-  if (x_rows && (!aligned4(x_rows) || n_x < 1)) return MOE_ERR_INVALID_ARG;
-  if (x_rows && !fits_int(static_cast<long long>(n_x) * d)) return MOE_ERR_UNSUPPORTED;
-  moe::FfnArgs a;
-  a.x_sorted = x_sorted;
-  a.x_rows = x_rows;
-  a.n_x = x_rows ? n_x : n_rows;
-  a.group_offsets = group_offsets;
-  a.n_rows = n_rows;
-  a.E = E;
-  a.n_shared = n_shared;
-  a.nseg = nseg;
-  a.d = d;
-  a.I = I;
-  a.w_gate = w_gate;
-  a.w_up = w_up;
-  a.w_down = w_down;
-  a.bf16 = 1;
-  a.h_sorted = h_sorted;
-  a.packed = true;
-  return hip_status(moe::launch_ffn(a, workspace, stream));
+  return ffn_call(x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I, w_gate, w_up, w_down,
+                  MOE_BF16, h_sorted, workspace, workspace_bytes, nullptr, 0, true, stream);
 }
 
 moe_status moe_grouped_ffn_fp8w(const void* x_sorted, const int32_t* x_rows, int32_t n_x,

@@ -1237,15 +1237,22 @@ int gemm_grid() {
 //     lag of one round of the other phase-1 tiles;
 //   * a phase-2 tile of unit u waits until each phase-1 tile of u has raised
 //     its flag (one int per (unit, column chunk)).
-// Memory ordering (HIP / LLVM AMDGPU memory model, agent scope): after a
-// phase-1 tile, every wave executes an agent-scope release fence (its stores
-// of the SwiGLU rows reach the coherence point: buffer_wbl2 sc1, then vmcnt 0),
-// the block barriers, and thread 0 stores the flag with an agent-scope release
-// store.  A phase-2 tile's first wave polls the flags with agent-scope
-// relaxed loads; once all are set it executes an agent-scope acquire fence
-// (buffer_inv sc1) and the block barriers before any wave loads the rows.  The
-// fence pair makes the producer's row stores visible to the consumer on any
-// XCD, so nothing depends on where the hardware places the blocks.
+// Memory ordering (gfx950 under the LLVM AMDGPU memory model, agent scope).
+// A phase-1 tile writes its SwiGLU rows with agent-scope atomic stores
+// (global_store ... sc1: written through the XCD's L2, so none of them leaves a
+// dirty line there); every wave then waits for its stores to complete
+// (s_waitcnt vmcnt(0)), the block barriers, and thread 0 stores the flag with an
+// agent-scope atomic store.  These are the machine steps of an agent-scope
+// release: the release fence's L2 write-back (buffer_wbl2 sc1) finds nothing to
+// write back after write-through stores, and its wait is that vmcnt(0).  A
+// phase-2 tile's first wave polls the flags with agent-scope atomic loads
+// (global_load ... sc1, never served from a stale L2 line); once all are set it
+// executes an agent-scope acquire fence (buffer_inv sc1: the XCD's L2 and the
+// CU's L1 drop lines that another XCD may have written) and the block
+// barriers before any wave loads the rows.  The rows are thus visible to the
+// consumer on any XCD, whatever the hardware's placement of the blocks.  The
+// argument is at the instruction level: in the language's model the flag store
+// is relaxed, and the release is the write-through plus the completion wait.
 // Progress: every queue lists all phase-1 tiles a phase-2 tile of it may need
 // before that tile, priority ones at the very front, so each awaited tile has
 // been or will be popped by a block that is not waiting (queue_plan.h; checked

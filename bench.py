@@ -241,13 +241,15 @@ def decode_segment(layer, wl, s, dev, expert_bytes, packed):
 
 
 def signature_recording(s, stats_ids, req_offsets, stream, K, dev, logits_stack=None, block=16):
-    """Per-KV-block expert counts over the statistics layer stack (moe_stats
-    with block offsets) and their copy into pinned host memory, timed with HIP
-    events on `stream` over K repetitions.  The ELDR page ("Overhead"
-    paragraph of its evidence section) times the same two steps on MI300X:
-    0.48 ms for the on-GPU scatter and 0.21 ms for the signature's D2H staging
-    per request.  With `logits_stack` ([L][T][E]) it also times the continuous
-    (softmax-probability) request signature over the same layers."""
+    """Per-KV-block expert counts over the statistics layer stack and their
+    copy into pinned host memory, timed with HIP events on `stream` over K
+    repetitions, two ways: recorded at the gate (moe_gate_record for each
+    layer, against moe_gate alone) and by moe_stats with block offsets from
+    the stacked ids; the staging is moe_stage_to_host.  The ELDR page
+    ("Overhead" paragraph of its evidence section) times the same two steps on
+    MI300X: 0.48 ms for the on-GPU scatter and 0.21 ms for the signature's D2H
+    staging per request.  With `logits_stack` ([L][T][E]) it also times the
+    continuous (softmax-probability) request signature over the same layers."""
     import torch
     import top_expert_routing_amd as moe
     offs = list(range(0, s.T, block)) + [s.T]
@@ -257,26 +259,42 @@ def signature_recording(s, stats_ids, req_offsets, stream, K, dev, logits_stack=
     R = req_offsets.numel() - 1 if req_offsets is not None else nb
     out = {}
     ws = torch.empty(max(moe.stats_workspace_bytes(L, s.T, s.k, s.E, nb), 256), dtype=torch.uint8, device=dev)
+    rec_g = torch.empty((nb, L, s.E), dtype=torch.int32, device=dev)
+    ids = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+
+    def gates(record):
+        for l in range(L):
+            if record:
+                moe.gate_record(logits_stack[l], s.k, block, l, rec_g, True, ids, wts)
+            else:
+                moe.gate(logits_stack[l], s.k, True, ids, wts)
+
     with torch.cuda.stream(stream):
         moe.stats(stats_ids, s.E, boffs, affinity=False, signature=False, out=out, workspace=ws)
+        gates(True)
     host = torch.empty(out["req_counts"].shape, dtype=torch.int32, pin_memory=True)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     with torch.cuda.stream(stream):
         for i in range(K):
             ev[i][0].record(stream)
-            moe.stats(stats_ids, s.E, boffs, affinity=False, signature=False, out=out, workspace=ws)
+            gates(False)
             ev[i][1].record(stream)
-            host.copy_(out["req_counts"], non_blocking=True)
+            gates(True)
             ev[i][2].record(stream)
+            moe.stats(stats_ids, s.E, boffs, affinity=False, signature=False, out=out, workspace=ws)
+            ev[i][3].record(stream)
+            moe.stage_to_host(rec_g, host)
+            ev[i][4].record(stream)
     torch.cuda.synchronize()
-    rec = sum(e[0].elapsed_time(e[1]) for e in ev) / K * 1e3
-    d2h = sum(e[1].elapsed_time(e[2]) for e in ev) / K * 1e3
-    if not torch.equal(host, out["req_counts"].cpu()):
-        raise RuntimeError("staged block counts differ from the device copy")
+    ms = [sum(e[a].elapsed_time(e[a + 1]) for e in ev) / K * 1e3 for a in range(4)]
+    gate_us, gate_rec_us, stats_us, d2h = ms
+    if not torch.equal(host, out["req_counts"].cpu()) or not torch.equal(rec_g, out["req_counts"]):
+        raise RuntimeError("block counts recorded at the gate, by moe_stats and on the host differ")
     # the continuous alternative the page compares against: per-request sums of
     # softmax probabilities from the recorded layers' logits
     prob = None
-    if logits_stack is not None and req_offsets is not None:
+    if req_offsets is not None:
         psig = torch.empty((R, L, s.E), dtype=torch.float32, device=dev)
         pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
         with torch.cuda.stream(stream):
@@ -287,9 +305,12 @@ def signature_recording(s, stats_ids, req_offsets, stream, K, dev, logits_stack=
                 pe[i][1].record(stream)
         torch.cuda.synchronize()
         prob = round(sum(a.elapsed_time(b) for a, b in pe) / K * 1e3, 2)
+    rec = gate_rec_us - gate_us
     return {"kv_block_tokens": block, "blocks": nb, "requests": R, "layers": L,
-            "record_us": round(rec, 2), "d2h_us": round(d2h, 2), "d2h_bytes": host.numel() * 4,
-            "per_request_us": round((rec + d2h) / max(R, 1), 3), "prob_signature_us": prob,
+            "gate_us": round(gate_us, 2), "gate_record_us": round(gate_rec_us, 2),
+            "record_at_gate_us": round(rec, 2), "record_by_stats_us": round(stats_us, 2),
+            "d2h_us": round(d2h, 2), "d2h_bytes": host.numel() * 4,
+            "per_request_us": round((max(rec, 0.0) + d2h) / max(R, 1), 3), "prob_signature_us": prob,
             "pages_mi300x_per_request_us": {"scatter": 480.0, "d2h_staging": 210.0}}
 
 

@@ -111,6 +111,52 @@ moe_status moe_gate(const float* logits, int32_t T, int32_t E, int32_t k,
                     hipStream_t stream);
 
 /*
+ * moe_gate_record - moe_gate that also records the batch's expert activations
+ * per KV block for one layer of a recorded layer stack.
+ * (ELDR page, "Core idea / structure / operation": during prefill the expert
+ * activations are recorded at KV-block granularity, and a request's signature
+ * is built from its blocks' counts.)
+ *
+ *   logits, T, E, k, renormalize, topk_ids, topk_w: as moe_gate, with the
+ *                same results bit for bit.
+ *   block_tokens tokens per KV block (>= 1): block b holds tokens
+ *                [b * block_tokens, min(T, (b + 1) * block_tokens)); there are
+ *                nb = ceil(T / block_tokens) blocks.
+ *   layer, L     0 <= layer < L: the row of the record this call fills.
+ *   block_counts [nb][L][E] int32: row (b, layer) is written in full, zeros
+ *                included: entry e = number of top-k slots of the block's
+ *                tokens that chose expert e (moe_stats' req_counts for block
+ *                offsets).  Rows of other layers are not touched, so L calls
+ *                with layer = 0 .. L-1 fill the whole record; nothing needs
+ *                clearing first.
+ *   Errors: MOE_ERR_INVALID_ARG for block_tokens < 1, L < 1, layer outside
+ *   [0, L), a NULL or misaligned block_counts (T > 0), and moe_gate's
+ *   argument errors; otherwise as moe_gate.
+ */
+moe_status moe_gate_record(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renormalize,
+                           int32_t* topk_ids, float* topk_w, int32_t block_tokens, int32_t layer, int32_t L,
+                           int32_t* block_counts, hipStream_t stream);
+
+/*
+ * moe_stage_to_host - enqueue the copy of `bytes` bytes of device memory into
+ * pinned host memory on `stream` (ELDR page, "Core idea / structure /
+ * operation" and its overhead measurements: the recorded signatures are
+ * staged from the GPU to the host).
+ *
+ *   src       device memory (for example moe_gate_record's block_counts or
+ *             moe_stats' signature), read by the copy.
+ *   dst_host  page-locked host memory the caller allocated (hipHostMalloc, or
+ *             a pinned torch tensor); written when the copy runs, so the caller
+ *             waits on the stream (or an event recorded after the call) before
+ *             reading it.  Nothing is allocated.
+ *   Errors: MOE_ERR_INVALID_ARG for a NULL pointer with bytes > 0, a
+ *   destination that is not page-locked host memory (a pageable buffer would
+ *   turn the copy synchronous), or a source that is not device memory;
+ *   MOE_ERR_HIP if the copy cannot be enqueued.  bytes = 0 enqueues nothing.
+ */
+moe_status moe_stage_to_host(const void* src, void* dst_host, size_t bytes, hipStream_t stream);
+
+/*
  * moe_permute - dispatch as a stable counting sort of token->expert
  * assignments into contiguous per-expert groups (histogram, prefix scan,
  * scatter, row gather).  (GRACE-MoE page, section 1: the dispatch exchange.)

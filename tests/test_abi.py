@@ -27,7 +27,8 @@ def _declared():
 
 
 def test_header_declares_the_calls():
-    assert _declared() == sorted(["moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_traced",
+    assert _declared() == sorted(["moe_router", "moe_gate", "moe_gate_record", "moe_stage_to_host", "moe_permute",
+                                  "moe_grouped_ffn", "moe_grouped_ffn_traced",
                                   "moe_grouped_ffn_noalloc",
                                   "moe_grouped_ffn_packed", "moe_grouped_ffn_fp8w", "moe_grouped_ffn_fp8w_packed",
                                   "moe_combine", "moe_stats", "moe_prob_signature", "moe_status_string"])
@@ -124,6 +125,28 @@ def test_gate_validation(lib):
     assert g(None, 4, 8, 2, 1, FAKE, FAKE, None) == INV          # NULL logits
     assert g(FAKE + 2, 4, 8, 2, 1, FAKE, FAKE, None) == INV      # misaligned
     assert g(None, 0, 8, 2, 1, None, None, None) == 0            # T = 0 is a no-op
+
+
+def test_gate_record_validation(lib):
+    g = lib.moe_gate_record
+    ok = [FAKE, 64, 8, 2, 1, FAKE, FAKE, 16, 0, 1, FAKE, None]
+    a = lambda **kw: [kw.get(f"a{i}", v) for i, v in enumerate(ok)]
+    assert g(*a(a3=9)) == INV                  # k > E (moe_gate's checks apply)
+    assert g(*a(a7=0)) == INV                  # block_tokens < 1
+    assert g(*a(a9=0)) == INV                  # L < 1
+    assert g(*a(a8=1)) == INV                  # layer >= L
+    assert g(*a(a8=-1)) == INV                 # layer < 0
+    assert g(*a(a10=None)) == INV              # NULL block_counts
+    assert g(*a(a10=FAKE + 2)) == INV          # misaligned block_counts
+    assert g(*a(a2=513)) == UNS                # E > 512
+    assert g(*a(a1=0, a0=None, a5=None, a6=None, a10=None)) == 0     # T = 0 is a no-op
+
+
+def test_stage_to_host_validation(lib):
+    s = lib.moe_stage_to_host
+    assert s(None, None, 0, None) == 0                               # nothing to copy
+    assert s(None, FAKE, 64, None) == INV
+    assert s(FAKE, None, 64, None) == INV
 
 
 def _perm(lib, T=4, E=8, k=2, S=0, P=0, x=FAKE, dt=1, d=64, ws=FAKE, nbytes=1 << 30, **kw):

@@ -127,6 +127,65 @@ def test_gate_config_logits_bit_exact():
             assert np.abs(np_of(w).astype(np.float64) - w_ref).max() <= GATE_W_ATOL
 
 
+GATE_RECORD_CASES = [
+    # (T, E, k, renormalize, kind, block_tokens, L)
+    (1000, 64, 6, 1, "normal", 16, 2),      # KV blocks of 16, ragged last block
+    (37, 512, 8, 1, "ties", 7, 3),          # E = 512, an odd block size, ties
+    (64, 8, 2, 1, "normal", 1, 1),          # one token per block
+    (50, 32, 4, 0, "zeros_nan", 64, 1),     # one block longer than the batch
+    (300, 96, 3, 1, "ties", 33, 2),         # E not a multiple of 64
+    (200, 130, 130, 1, "normal", 40, 1),    # k = E: every block's row counts its tokens
+]
+
+
+@pytest.mark.parametrize("T,E,k,renorm,kind,bt,L", GATE_RECORD_CASES)
+def test_gate_record_parity(T, E, k, renorm, kind, bt, L):
+    """moe_gate_record: ids and weights bit-identical to moe_gate's, and the
+    KV-block record equal to the oracle's request counts over block offsets,
+    every row of every layer written (the buffer starts poisoned)."""
+    announce(f"gate_record T={T} E={E} k={k} bt={bt} L={L} {kind}")
+    nb = -(-T // bt)
+    lgs = [_gate_logits(T, E, kind, seed=T * 7 + E + l) for l in range(L)]
+    rec = _poison((nb, L, E), torch.int32)
+    ids_all = []
+    for l, lg in enumerate(lgs):
+        ids = _poison((T, k), torch.int32)
+        w = _poison((T, k), torch.float32)
+        moe.gate_record(lg.to(DEV), k, bt, l, rec, bool(renorm), ids, w)
+        ids0, w0 = moe.gate(lg.to(DEV), k, bool(renorm))
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ids0) and torch.equal(w.view(torch.int32), w0.view(torch.int32))
+        ids_ref, _ = O.gate(lg.numpy(), k, bool(renorm))
+        np.testing.assert_array_equal(np_of(ids), ids_ref)
+        ids_all.append(ids_ref)
+    boffs = np.minimum(np.arange(nb + 1, dtype=np.int64) * bt, T).astype(np.int32)
+    ref = O.stats(np.stack(ids_all), E, boffs)["req_counts"]          # [nb][L][E]
+    np.testing.assert_array_equal(np_of(rec), ref)
+
+
+def test_gate_record_touches_only_its_layer():
+    T, E, k, bt, L = 100, 64, 4, 16, 3
+    lg = _gate_logits(T, E, "normal", seed=5).to(DEV)
+    rec = torch.full((-(-T // bt), L, E), -7, dtype=torch.int32, device=DEV)
+    moe.gate_record(lg, k, bt, 1, rec)
+    torch.cuda.synchronize()
+    assert bool((rec[:, 0] == -7).all()) and bool((rec[:, 2] == -7).all())
+    assert int(rec[:, 1].sum().item()) == T * k
+
+
+def test_stage_to_host():
+    """The record staged into pinned host memory with moe_stage_to_host equals
+    the device copy; a pageable destination is refused."""
+    announce("stage_to_host")
+    src = torch.randint(-1000, 1000, (512, 8, 128), dtype=torch.int32, device=DEV)
+    dst = torch.empty(src.shape, dtype=torch.int32, pin_memory=True)
+    moe.stage_to_host(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src.cpu())
+    with pytest.raises(moe.MoeError):
+        moe.stage_to_host(src, torch.empty(src.shape, dtype=torch.int32))
+
+
 def test_gate_empty_batch():
     ids = torch.empty((0, 2), dtype=torch.int32, device=DEV)
     w = torch.empty((0, 2), dtype=torch.float32, device=DEV)

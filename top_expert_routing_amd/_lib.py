@@ -14,8 +14,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
                 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
 
 # every symbol include/libmoe.h declares
-EXPORTS = ("moe_router", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_traced",
-           "moe_grouped_ffn_noalloc",
+EXPORTS = ("moe_router", "moe_gate", "moe_gate_record", "moe_stage_to_host", "moe_permute", "moe_grouped_ffn",
+           "moe_grouped_ffn_traced", "moe_grouped_ffn_noalloc",
            "moe_grouped_ffn_packed", "moe_grouped_ffn_fp8w",
            "moe_grouped_ffn_fp8w_packed", "moe_combine",
            "moe_stats", "moe_prob_signature", "moe_status_string")
@@ -27,6 +27,8 @@ _sz = ctypes.POINTER(ctypes.c_size_t)
 SIGNATURES = {
     "moe_router": [_p, _p, _i32, _i32, _i32, _i32, _p, _p],
     "moe_gate": [_p, _i32, _i32, _i32, _i32, _p, _p, _p],
+    "moe_gate_record": [_p, _i32, _i32, _i32, _i32, _p, _p, _i32, _i32, _i32, _p, _p],
+    "moe_stage_to_host": [_p, _p, ctypes.c_size_t, _p],
     "moe_permute": [_p, _i32, _i32, _i32, _i32, _i32, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _sz, _p],
     "moe_grouped_ffn": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _sz, _p],
     "moe_grouped_ffn_traced": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _sz,

@@ -93,6 +93,48 @@ def gate(logits: torch.Tensor, k: int, renormalize: bool = True,
     return topk_ids, topk_w
 
 
+def gate_record(logits: torch.Tensor, k: int, block_tokens: int, layer: int, block_counts: torch.Tensor,
+                renormalize: bool = True, topk_ids: Optional[torch.Tensor] = None,
+                topk_w: Optional[torch.Tensor] = None):
+    """gate() that also fills row `layer` of the KV-block record block_counts
+    [ceil(T / block_tokens)][L][E] int32 (moe_gate_record)."""
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    dev = logits.device
+    if block_tokens < 1:
+        raise ValueError("block_tokens must be >= 1")
+    nb = -(-T // block_tokens)
+    _need(block_counts, "block_counts", torch.int32, 3)
+    L = block_counts.shape[1]
+    _out(block_counts, "block_counts", torch.int32, (nb, L, E))
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _out(topk_ids, "topk_ids", torch.int32, (T, k))
+    _out(topk_w, "topk_w", torch.float32, (T, k))
+    lib = _lib.load()
+    check("moe_gate_record", lib.moe_gate_record(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(topk_ids),
+                                                 _ptr(topk_w), block_tokens, layer, L, _ptr(block_counts),
+                                                 _stream(dev)))
+    return topk_ids, topk_w
+
+
+def stage_to_host(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """Enqueue the copy of GPU tensor `src` into the pinned host tensor `dst`
+    (same dtype and shape) on the current stream (moe_stage_to_host); read
+    `dst` after synchronising that stream."""
+    _need(src, "src")
+    if dst.is_cuda or not dst.is_contiguous():
+        raise ValueError("dst must be a contiguous host tensor")
+    if dst.dtype != src.dtype or dst.shape != src.shape:
+        raise ValueError("dst must match src in dtype and shape")
+    lib = _lib.load()
+    check("moe_stage_to_host", lib.moe_stage_to_host(_ptr(src), ctypes.c_void_p(dst.data_ptr()),
+                                                     src.numel() * src.element_size(), _stream(src.device)))
+    return dst
+
+
 def permute_workspace_bytes(T, E, k, n_shared=0, n_priority=0) -> int:
     lib = _lib.load()
     n = ctypes.c_size_t(0)

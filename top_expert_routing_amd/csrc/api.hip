@@ -199,6 +199,40 @@ moe_status moe_gate(const float* logits, int32_t T, int32_t E, int32_t k, int32_
   return hip_status(moe::launch_gate(logits, T, E, k, renormalize, topk_ids, topk_w, stream));
 }
 
+moe_status moe_gate_record(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renormalize,
+                           int32_t* topk_ids, float* topk_w, int32_t block_tokens, int32_t layer, int32_t L,
+                           int32_t* block_counts, hipStream_t stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (renormalize != 0 && renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (block_tokens < 1 || L < 1 || layer < 0 || layer >= L) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if (!fits_int(static_cast<long long>(T) * E)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w || !block_counts) return MOE_ERR_INVALID_ARG;
+  if (!aligned4(logits) || !aligned4(topk_ids) || !aligned4(topk_w) || !aligned4(block_counts))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_gate_record(logits, T, E, k, renormalize, topk_ids, topk_w, block_tokens, layer, L,
+                                            block_counts, stream));
+}
+
+moe_status moe_stage_to_host(const void* src, void* dst_host, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return MOE_OK;
+  if (!src || !dst_host) return MOE_ERR_INVALID_ARG;
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, dst_host) != hipSuccess) {
+    (void)hipGetLastError();   // pageable memory is an argument error, not a sticky one
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (a.type != hipMemoryTypeHost) return MOE_ERR_INVALID_ARG;
+  hipPointerAttribute_t b{};
+  if (hipPointerGetAttributes(&b, src) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (b.type != hipMemoryTypeDevice) return MOE_ERR_INVALID_ARG;
+  return hip_status(hipMemcpyAsync(dst_host, src, bytes, hipMemcpyDeviceToHost, stream));
+}
+
 moe_status moe_router(const void* x, const void* w_router, int32_t T, int32_t d, int32_t E, moe_dtype dtype,
                       float* logits, hipStream_t stream) {
   if (T < 0 || E < 1 || d < 1) return MOE_ERR_INVALID_ARG;

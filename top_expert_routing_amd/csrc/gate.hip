@@ -47,13 +47,12 @@ __device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
   return max(max(a, b), max(c, d));
 }
 
+// The gate of token t on one wave (every lane active).  With `hist` (LDS),
+// each chosen expert's counter is also incremented once per slot.
 template <int P>
-__global__ __launch_bounds__(kWave * kWavesPerBlock) void gate_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int renormalize,
-    int* __restrict__ topk_ids, float* __restrict__ topk_w) {
+__device__ __forceinline__ void gate_token(const float* __restrict__ logits, int t, int E, int k, int renormalize,
+                                           int* __restrict__ topk_ids, float* __restrict__ topk_w, int* hist) {
   const int lane = lane_id();
-  const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (t >= T) return;    // whole waves leave: every lane of a live wave is active
   const float* row = logits + static_cast<size_t>(t) * E;
 
   uint32_t key[P], orig[P];
@@ -125,8 +124,43 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void gate_kernel(
     if (slot < k) {
       topk_ids[static_cast<size_t>(t) * k + slot] = cid[i];
       topk_w[static_cast<size_t>(t) * k + slot] = static_cast<float>(z[i] / denom);
+      if (hist) atomicAdd(hist + cid[i], 1);
     }
   }
+}
+
+template <int P>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void gate_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renormalize,
+    int* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (t >= T) return;    // whole waves leave: every lane of a live wave is active
+  gate_token<P>(logits, t, E, k, renormalize, topk_ids, topk_w, nullptr);
+}
+
+// Gate plus KV-block recording (ELDR page, "Core idea / structure /
+// operation": expert activations recorded per KV block during prefill).  One
+// block per KV block of `bt` tokens, min(bt, 16) waves taking its tokens in
+// turn; the block's expert histogram lives in LDS and is written out whole
+// (zeros included) as row (b, layer) of block_counts [nblocks][L][E], so no
+// global atomics and no clearing pass are needed, and the counts are exact.
+constexpr int kRecordMaxWaves = 16;
+
+template <int P>
+__global__ __launch_bounds__(kWave * kRecordMaxWaves) void gate_record_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renormalize, int* __restrict__ topk_ids,
+    float* __restrict__ topk_w, int bt, int layer, int L, int* __restrict__ block_counts) {
+  __shared__ int hist[P * kWave];
+  const int nw = blockDim.x >> 6, w = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const long long t0 = static_cast<long long>(blockIdx.x) * bt;
+  const long long t1 = min(static_cast<long long>(T), t0 + bt);
+  for (long long t = t0 + w; t < t1; t += nw)
+    gate_token<P>(logits, static_cast<int>(t), E, k, renormalize, topk_ids, topk_w, hist);
+  __syncthreads();
+  int* out = block_counts + (static_cast<size_t>(blockIdx.x) * L + layer) * E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = hist[e];
 }
 
 }  // namespace
@@ -142,6 +176,26 @@ hipError_t launch_gate(const float* logits, int T, int E, int k, int renormalize
     hipLaunchKernelGGL(gate_kernel<4>, grid, block, 0, stream, logits, T, E, k, renormalize, topk_ids, topk_w);
   else
     hipLaunchKernelGGL(gate_kernel<8>, grid, block, 0, stream, logits, T, E, k, renormalize, topk_ids, topk_w);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_record(const float* logits, int T, int E, int k, int renormalize, int* topk_ids,
+                              float* topk_w, int block_tokens, int layer, int L, int* block_counts,
+                              hipStream_t stream) {
+  const int nblocks = static_cast<int>((static_cast<long long>(T) + block_tokens - 1) / block_tokens);
+  dim3 grid(nblocks), block(kWave * (block_tokens < kRecordMaxWaves ? block_tokens : kRecordMaxWaves));
+  if (E <= 64)
+    hipLaunchKernelGGL(gate_record_kernel<1>, grid, block, 0, stream, logits, T, E, k, renormalize, topk_ids, topk_w,
+                       block_tokens, layer, L, block_counts);
+  else if (E <= 128)
+    hipLaunchKernelGGL(gate_record_kernel<2>, grid, block, 0, stream, logits, T, E, k, renormalize, topk_ids, topk_w,
+                       block_tokens, layer, L, block_counts);
+  else if (E <= 256)
+    hipLaunchKernelGGL(gate_record_kernel<4>, grid, block, 0, stream, logits, T, E, k, renormalize, topk_ids, topk_w,
+                       block_tokens, layer, L, block_counts);
+  else
+    hipLaunchKernelGGL(gate_record_kernel<8>, grid, block, 0, stream, logits, T, E, k, renormalize, topk_ids, topk_w,
+                       block_tokens, layer, L, block_counts);
   return hipGetLastError();
 }
 

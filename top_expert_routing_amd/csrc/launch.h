@@ -11,6 +11,9 @@ namespace moe {
 
 hipError_t launch_gate(const float* logits, int T, int E, int k, int renormalize, int* topk_ids,
                        float* topk_w, hipStream_t stream);
+hipError_t launch_gate_record(const float* logits, int T, int E, int k, int renormalize, int* topk_ids,
+                              float* topk_w, int block_tokens, int layer, int L, int* block_counts,
+                              hipStream_t stream);
 
 // ---- router projection -------------------------------------------------------
 hipError_t launch_router(const void* x, const void* w_router, int T, int d, int E, int bf16, float* logits,

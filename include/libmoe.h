@@ -256,8 +256,8 @@ moe_status moe_grouped_ffn(const void* x_sorted, const int32_t* x_rows, int32_t 
  *   popped at position t writes record q * (trace_capacity / nq) + t if
  *   t < trace_capacity / nq:
  *     [0] start and [1] end of the tile, s_memrealtime ticks (100 MHz);
- *     [2] unit << 32 | column chunk << 8 | kind << 2 | priority << 1 |
- *         (phase - 1), kind 0 = GEMM tile, 1 = weight-streaming tile;
+ *     [2] unit << 32 | column chunk << 8 | priority << 1 | (phase - 1)
+ *         (a unit is 128 sorted rows of one expert);
  *     [3] queue << 32 | block index.
  *   A record whose end is 0 was not written.  Tracing adds a wait for the
  *   tile's stores before its end stamp.

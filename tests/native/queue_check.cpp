@@ -2,15 +2,15 @@
 // same header the GPU kernel includes (top_expert_routing_amd/csrc/queue_plan.h).
 //
 // Input (stdin, whitespace separated):
-//   E S nseg n_rows stream_max bm0 bm1 nch1_0 nch1_1 nch2_0 nch2_1 nq lag nk units_cap
+//   E S nseg n_rows bm nch1 nch2 nq lag units_cap
 //   G+1 group offsets
 // Checks, for every queue and pop position:
 //   * every (phase, unit, chunk) of every unit appears exactly once over all
-//     queues (phase 1: chunk < nch1[kind], phase 2: chunk < nch2[kind]);
+//     queues (phase 1: chunk < nch1, phase 2: chunk < nch2);
 //   * the units of a sequence cover its rows A ++ B exactly once, in order,
 //     and every tile row lies in [0, n_rows);
 //   * unit ids and flag indices stay below the capacity the host allocates
-//     (units_cap * max(nch1));
+//     (units_cap * nch1);
 //   * with ONE block per queue (the hardest case: a waiting block stalls its
 //     whole queue) processing pops in order, where a phase-1 tile completes
 //     when popped and a phase-2 tile only once every phase-1 tile of its unit
@@ -36,10 +36,10 @@ static int fail(const char* why, long long a = 0, long long b = 0) {
 int main() {
   Shape p{};
   int units_cap = 0;
-  if (std::scanf("%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d", &p.E, &p.S, &p.nseg, &p.n_rows, &p.stream_max,
-                 &p.bm[0], &p.bm[1], &p.nch1[0], &p.nch1[1], &p.nch2[0], &p.nch2[1], &p.nq, &p.lag, &p.nk,
-                 &units_cap) != 15)
+  if (std::scanf("%d %d %d %d %d %d %d %d %d %d", &p.E, &p.S, &p.nseg, &p.n_rows, &p.bm, &p.nch1, &p.nch2, &p.nq,
+                 &p.lag, &units_cap) != 10)
     return fail("bad header");
+  if (p.bm < 1 || p.nch1 < 1 || p.nch2 < 1 || p.nq < 1 || p.lag < 0) return fail("bad shape");
   const int G = p.nseg * p.E + p.S;
   std::vector<int> offs(G + 1);
   for (int i = 0; i <= G; ++i)
@@ -68,7 +68,7 @@ int main() {
 
   // enumerate every queue
   struct Pop { int phase, unit, chunk, prio; };
-  const int nqueues = p.queues();
+  const int nqueues = p.nq;
   std::vector<std::vector<Pop>> qlist(nqueues);
   std::map<std::tuple<int, int, int>, int> seen;          // (phase, unit, chunk) -> count
   std::vector<std::vector<int>> unit_rows(units);         // rows of each unit (from its phase-1 chunk 0 tile)
@@ -90,14 +90,13 @@ int main() {
       const Slot sl = slot_of(qp, t);
       const int* pr = pre[(sl.phase == 1 ? 0 : 2) + (sl.prio ? 0 : 1)].data();
       const Tile tl = decode_tile(p, offs.data(), pr, fu.data(), q, sl);
-      const int nch = tl.phase == 1 ? p.nch1[tl.kind] : p.nch2[tl.kind];
+      const int nch = tl.phase == 1 ? p.nch1 : p.nch2;
       if (tl.chunk < 0 || tl.chunk >= nch) return fail("chunk out of range", tl.chunk, nch);
       if (tl.unit < 0 || tl.unit >= units) return fail("unit out of range", tl.unit, units);
-      if (tl.rows <= 0 || tl.rows > p.bm[tl.kind]) return fail("tile rows", tl.rows, p.bm[tl.kind]);
+      if (tl.rows <= 0 || tl.rows > p.bm) return fail("tile rows", tl.rows, p.bm);
       if (tl.split < 0 || tl.split > tl.rows) return fail("split", tl.split, tl.rows);
-      if (static_cast<long long>(tl.unit) * p.nch1_max() + tl.chunk >= static_cast<long long>(units_cap) * p.nch1_max())
+      if (static_cast<long long>(tl.unit) * p.nch1 + tl.chunk >= static_cast<long long>(units_cap) * p.nch1)
         return fail("flag index above capacity", tl.unit, tl.chunk);
-      if (p.nk == 2 && tl.kind != q / p.nq) return fail("tile in the other kind's queue", q, tl.kind);
       const bool is_prio_unit = tl.mt < su[tl.seq].tp;
       if (is_prio_unit != (tl.prio != 0)) return fail("priority part holds a wrong unit", tl.unit, tl.prio);
       std::vector<int> rr;
@@ -116,9 +115,9 @@ int main() {
   for (int s = 0; s < ns; ++s)
     for (int mt = 0; mt < su[s].units; ++mt) {
       const int u = fu[s] + mt;
-      for (int j = 0; j < p.nch1[su[s].kind]; ++j)
+      for (int j = 0; j < p.nch1; ++j)
         if (seen[{1, u, j}] != 1) return fail("phase-1 tile missing", u, j);
-      for (int j = 0; j < p.nch2[su[s].kind]; ++j)
+      for (int j = 0; j < p.nch2; ++j)
         if (seen[{2, u, j}] != 1) return fail("phase-2 tile missing", u, j);
     }
   if (static_cast<long long>(seen.size()) != tiles) return fail("stray tiles", seen.size(), tiles);
@@ -134,7 +133,7 @@ int main() {
   // one block per queue, pops in order
   std::vector<int> done1(units, 0), need1(units, 0);
   for (int s = 0; s < ns; ++s)
-    for (int mt = 0; mt < su[s].units; ++mt) need1[fu[s] + mt] = p.nch1[su[s].kind];
+    for (int mt = 0; mt < su[s].units; ++mt) need1[fu[s] + mt] = p.nch1;
   std::vector<size_t> head(nqueues, 0);
   for (bool progress = true; progress;) {
     progress = false;

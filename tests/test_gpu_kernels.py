@@ -439,7 +439,7 @@ QUEUE_CASES = [
     # (T, E, k, S, P, d, I, kind): priority segment, groups averaging > 48 rows,
     # so both phases run in the one persistent launch
     (600, 8, 2, 0, 50, 256, 320, "random"),       # GEMM units only, column tail in I
-    (4160, 128, 4, 0, 64, 256, 320, "zipf"),      # GPT-OSS-like routing: stream and GEMM units mixed
+    (4160, 128, 4, 0, 64, 256, 320, "zipf"),      # GPT-OSS-like routing: many one-unit experts, a few large
     (2000, 64, 4, 2, 300, 128, 96, "zipf"),       # shared experts, many priority units
     (1300, 512, 4, 256, 10, 64, 32, "random"),    # 768 sequences: one block per CU fits in LDS
 ]

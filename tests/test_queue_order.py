@@ -7,9 +7,9 @@ queues, the units tile each expert's rows exactly, flag indices stay inside
 the workspace the host allocates, and with ONE block per queue popping in
 order (a waiting block stalls its whole queue) every queue drains - so no
 phase-2 wait of the kernel can stall on a phase-1 tile that is never popped.
-The shapes mirror the library's: 128-row GEMM units (128 SwiGLU / 256 output
-columns per tile), 64-row stream units (64 / 128 columns), up to 8 queue
-groups, with one queue per group or one per group and tile kind.
+The shapes mirror the library's: 128-row units, 128 SwiGLU / 256 output
+columns per tile, 8 queues and a lag of one round of blocks (64), plus other
+unit heights, queue counts and lags.
 """
 import os
 import shutil
@@ -35,13 +35,11 @@ def checker(tmp_path_factory):
     return exe
 
 
-def _run(exe, offs, E, S, nseg, d, I, stream_max=64, nq=8, lag=64, units_cap=None, nk=2):
+def _run(exe, offs, E, S, nseg, d, I, bm=128, nq=8, lag=64, units_cap=None):
     N = int(offs[-1])
-    bm = (128, 64)
-    nch1 = (-(-I // 128), -(-I // 64))
-    nch2 = (-(-d // 256), -(-d // 128))
-    cap = -(-N // 64) + E + S if units_cap is None else units_cap
-    hdr = [E, S, nseg, N, stream_max, bm[0], bm[1], nch1[0], nch1[1], nch2[0], nch2[1], nq, lag, nk, cap]
+    nch1, nch2 = -(-I // 128), -(-d // 256)
+    cap = -(-N // bm) + E + S if units_cap is None else units_cap
+    hdr = [E, S, nseg, N, bm, nch1, nch2, nq, lag, cap]
     inp = " ".join(map(str, hdr)) + "\n" + " ".join(map(str, np.asarray(offs).tolist())) + "\n"
     r = subprocess.run([exe], input=inp, capture_output=True, text=True)
     return r.returncode, r.stdout.strip()
@@ -76,11 +74,11 @@ CASES = [
 
 
 @pytest.mark.parametrize("T,E,k,S,P,d,I,kind", CASES)
-@pytest.mark.parametrize("stream_max,nq,lag,nk", [(64, 8, 64, 2), (64, 8, 64, 1), (0, 8, 64, 2), (1 << 30, 8, 0, 2),
-                                                  (64, 1, 1, 2), (64, 3, 5, 2), (32, 8, 1 << 20, 1)])
-def test_queue_order(checker, T, E, k, S, P, d, I, kind, stream_max, nq, lag, nk):
+@pytest.mark.parametrize("bm,nq,lag", [(128, 8, 64), (128, 8, 0), (64, 8, 64), (128, 1, 1), (128, 3, 5),
+                                       (16, 8, 1 << 20)])
+def test_queue_order(checker, T, E, k, S, P, d, I, kind, bm, nq, lag):
     offs = _offsets(T, E, k, S, P, kind, seed=T + E)
-    rc, out = _run(checker, offs, E, S, 2 if P else 1, d, I, stream_max, nq, lag, nk=nk)
+    rc, out = _run(checker, offs, E, S, 2 if P else 1, d, I, bm, nq, lag)
     assert rc == 0 and out.startswith("ok"), out
 
 
@@ -91,10 +89,8 @@ def test_queue_order_gptoss_shape(checker):
     s = wl.spec
     ids, _ = O.gate(wl.logits.numpy(), s.k)
     offs = O.permute(ids, s.E, s.S, s.n_priority)["group_offsets"]
-    for stream_max in (64, 0):
-        for nk in (1, 2):
-            rc, out = _run(checker, offs, s.E, s.S, 2, s.d, s.I, stream_max, 8, 64, nk=nk)
-            assert rc == 0 and out.startswith("ok"), out
+    for lag in (64, 0):
+        rc, out = _run(checker, offs, s.E, s.S, 2, s.d, s.I, 128, 8, lag)
         assert rc == 0 and out.startswith("ok"), out
 
 

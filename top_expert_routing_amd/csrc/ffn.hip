@@ -182,22 +182,21 @@ constexpr int decode_kc() { return MF <= 2 ? 256 : 128; }
 constexpr int kDecodeWavesPerSimd = 4;
 
 // LDS staging of one decode tile: two buffers of BM rows x (KC + 8) bf16.
-template <int MF, int KC = decode_kc<MF>()>
-constexpr int decode_lds_elems() { return 2 * 16 * MF * (KC + 8); }
+template <int MF>
+constexpr int decode_lds_elems() { return 2 * 16 * MF * (decode_kc<MF>() + 8); }
 
 // One decode-shaped tile: item `it` (rows it.row(0..rows), output columns
-// it.chunk * 64 * NFC + [0, 64 * NFC)) of expert it.expert, K in chunks of KC.
-// All kThreads threads call it; `As0` is decode_lds_elems<MF, KC>() bf16 of
-// LDS, free on entry.
-template <int MF, int NFC, int PHASE, bool PK = false, bool COHERENT = false, int KC = decode_kc<MF>(),
-          bool DB = false>
+// it.chunk * 64 * NFC + [0, 64 * NFC)) of expert it.expert, K in chunks of
+// decode_kc<MF>().  All kThreads threads call it; `As0` is decode_lds_elems<MF>()
+// bf16 of LDS, free on entry.
+template <int MF, int NFC, int PHASE, bool PK = false>
 __device__ __forceinline__ void decode_tile(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x,
                                             int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
                                             int Ncols, const Item& it, uint16_t* __restrict__ out, uint16_t* As0) {
   constexpr int NF = PHASE == 1 ? 2 * NFC : NFC;
   constexpr int BN = kWaves * 16 * NFC;
   constexpr int BM = 16 * MF;
-  constexpr int kDecodeKC = KC;
+  constexpr int kDecodeKC = decode_kc<MF>();
   constexpr int kDecodeStride = kDecodeKC + 8;             // bf16 per staged A row (pad 16 B)
   constexpr int U = kDecodeKC / 32;
   constexpr int VPR = kDecodeKC / 8;                       // uint4 per staged row
@@ -282,34 +281,14 @@ __device__ __forceinline__ void decode_tile(const uint16_t* __restrict__ A, cons
 
   load_a(0);
   store_a(0);
-  if constexpr (DB) {
-    // weight registers double buffered: chunk c + 1's loads are in flight while
-    // chunk c is multiplied (for callers with few waves per CU)
-    uint4 b0[U][NF], b1[U][NF];
-    load_b(b0, 0);
-    for (int c = 0; c < nchunks; c += 2) {
-      if (c + 1 < nchunks) load_b(b1, c + 1);
-      if (c + 1 < nchunks) load_a(c + 1);
-      __syncthreads();                         // chunk c of A is in As[c & 1]
-      mma(b0, As(0));
-      if (c + 1 < nchunks) store_a(1);
-      if (c + 1 >= nchunks) break;
-      if (c + 2 < nchunks) load_b(b0, c + 2);
-      if (c + 2 < nchunks) load_a(c + 2);
-      __syncthreads();                         // chunk c + 1 of A is in As[1]
-      mma(b1, As(1));
-      if (c + 2 < nchunks) store_a(0);
-    }
-  } else {
-    for (int c = 0; c < nchunks; ++c) {
-      uint4 b[U][NF];
-      load_b(b, c);
-      const bool more = c + 1 < nchunks;
-      if (more) load_a(c + 1);
-      __syncthreads();                         // chunk c of A is in As[c & 1]
-      mma(b, As(c & 1));
-      if (more) store_a((c + 1) & 1);          // that buffer was last read before this barrier
-    }
+  for (int c = 0; c < nchunks; ++c) {
+    uint4 b[U][NF];
+    load_b(b, c);
+    const bool more = c + 1 < nchunks;
+    if (more) load_a(c + 1);
+    __syncthreads();                         // chunk c of A is in As[c & 1]
+    mma(b, As(c & 1));
+    if (more) store_a((c + 1) & 1);          // that buffer was last read before this barrier
   }
 
   // The MFMA computes (weight rows) x (token rows)^T: in each 16x16 block a
@@ -328,7 +307,7 @@ __device__ __forceinline__ void decode_tile(const uint16_t* __restrict__ A, cons
       float v[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) v[t] = PHASE == 1 ? silu_mul(acc[i][j][t], acc[i][NFC + j][t]) : acc[i][j][t];
-      store4<COHERENT>(orow + n, v[0], v[1], v[2], v[3]);
+      store4<false>(orow + n, v[0], v[1], v[2], v[3]);
     }
   }
 }
@@ -1226,17 +1205,19 @@ int gemm_grid() {
 // whose workers take tiles from a device-side queue, the urgent decode tiles
 // first, so a decode tile waits at most for the tiles already running and no
 // host relaunch sits between the two phases.  Both phases run in one launch of
-// persistent blocks (two per CU); the tile order is queue_plan.h's:
-//   * sequences (experts; with a priority segment an expert's priority rows
-//     followed by its other rows) of at most kStreamMaxRows rows run on
-//     decode-shaped weight-streaming tiles (64-row units, weights straight from
-//     HBM into MFMA registers), larger ones on 128 x 256 LDS-tiled GEMM tiles
-//     (128-row units), so memory-bound and MFMA-bound tiles share the chip;
+// persistent blocks (two per CU) on 128 x 256 LDS-tiled GEMM tiles (128-row
+// units); the tile order is queue_plan.h's:
+//   * sequences are experts (with a priority segment an expert's priority rows
+//     followed by its other rows), cut into 128-row units;
 //   * block b takes its tiles from queue b mod 8 with one atomic add; queue
 //     order puts the priority units' phase 1 first and their phase 2 after a
 //     lag of one round of the other phase-1 tiles;
 //   * a phase-2 tile of unit u waits until each phase-1 tile of u has raised
 //     its flag (one int per (unit, column chunk)).
+// (Weight-streaming tiles for the experts of <= 64 rows, the decode kernel's
+// tile body, ran beside the GEMM tiles in an earlier form of this kernel: on
+// the GPT-OSS-shaped mixed batch the call took 1.82 ms against 1.78 ms with
+// GEMM tiles only, and the decode segment finished no sooner.)
 // Memory ordering (gfx950 under the LLVM AMDGPU memory model, agent scope).
 // A phase-1 tile writes its SwiGLU rows with agent-scope atomic stores
 // (global_store ... sc1: written through the XCD's L2, so none of them leaves a
@@ -1264,9 +1245,6 @@ int gemm_grid() {
 // flagged result, never a hang.
 constexpr int kQueueStride = 32;                 // ints between the queue heads (128 B)
 constexpr int kMaxQueues = 8;
-constexpr int kStreamMaxRows = 64;               // sequences of 1..64 rows: weight-streaming tiles
-constexpr int kStreamMF = 4;                     // 64-row stream units
-constexpr int kStreamKC = 128;                   // K per chunk of a stream tile (staging fits the GEMM ring)
 constexpr unsigned long long kWaitTicks = 2000000ull;   // 20 ms of the 100 MHz counter
 constexpr int kMaxPolls = 1 << 22;
 constexpr int kMaxSeq = MOE_MAX_EXPERTS_DEV + 256;      // routed + shared experts
@@ -1277,8 +1255,8 @@ struct QueueArgs {
   const int* offs;
   const int* arows;   // phase-1 A row list (nullptr: sorted rows)
   int n_x;
-  int* heads;         // [nk * nq * kQueueStride]: one head per queue
-  int* flags;         // [units_cap][nch1_max]: phase-1 tile (unit, chunk) done
+  int* heads;         // [nq * kQueueStride]: one head per queue
+  int* flags;         // [units_cap][nch1]: phase-1 tile (unit, chunk) done
   int* error;         // diagnostic word, set when a wait gave up
   unsigned long long* trace;   // optional per-tile records, trace_per_queue per queue
   int trace_per_queue;
@@ -1286,14 +1264,14 @@ struct QueueArgs {
 
 __device__ __forceinline__ unsigned long long realtime() { return __builtin_amdgcn_s_memrealtime(); }
 
-// Configuration of the persistent queue kernel: GEMM tiles (128 x 256,
-// GemmSmall's ring) for large experts and 64-row weight-streaming tiles for the
-// rest, two blocks per CU, row-major weights.
+// Configuration of the persistent queue kernel: 128 x 256 GEMM tiles
+// (GemmSmall's ring), two blocks per CU, row-major (PK false) or pre-packed
+// weights.
 template <bool PKV>
-struct QueueMixed {
+struct QueueGemm {
   using C = GemmSmall;
-  static constexpr int BPC = C::BLOCKS_PER_CU, SMF = kStreamMF, SKC = kStreamKC;
-  static constexpr bool GEMM = true, DB = true, PK = PKV;
+  static constexpr int BPC = C::BLOCKS_PER_CU;
+  static constexpr bool PK = PKV;
   static constexpr int RING = C::RING;
 };
 
@@ -1303,11 +1281,10 @@ __global__ __launch_bounds__(kThreads, QC::BPC) void ffn_queue_bf16(
     const uint16_t* __restrict__ w_down, int I, QueueArgs q, uint16_t* __restrict__ abuf,
     uint16_t* __restrict__ h) {
   using C = typename QC::C;
-  static_assert(C::NT == kThreads, "one block shape for both tile kinds");
-  static_assert(decode_lds_elems<QC::SMF, QC::SKC>() * 2 <= QC::RING, "stream tiles stage their rows in the ring");
+  static_assert(C::NT == kThreads, "queue blocks have the GEMM tile's shape");
   constexpr int NV = 5;              // per sequence: units, then this queue's P1, R1, P2, R2 tile counts
-  // dynamic LDS: the ring (GEMM operands; also the stream tiles' row staging),
-  // then NV prefix arrays of nseq + 1 ints
+  // dynamic LDS: the ring (GEMM operands), then NV prefix arrays of nseq + 1
+  // ints
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   uint8_t* smem = dyn_lds;
   const qplan::Shape& sh = q.shape;
@@ -1367,7 +1344,7 @@ __global__ __launch_bounds__(kThreads, QC::BPC) void ffn_queue_bf16(
     }
     __syncthreads();
   }
-  const int nch1max = sh.nch1_max();
+  const int nch1 = sh.nch1;
   bool waits = true;                 // false once a wait of this block gave up (block-uniform)
   const int* pre = fu + (ns + 1);    // P1, R1, P2, R2 prefixes of queue qi
   const qplan::QueueParts qp = qplan::queue_parts(
@@ -1386,24 +1363,19 @@ __global__ __launch_bounds__(kThreads, QC::BPC) void ffn_queue_bf16(
     const Item it{tl.row0, tl.rows, tl.seq, tl.chunk, tl.split, tl.row1};
     const unsigned long long t0 = q.trace ? realtime() : 0ull;
     if (tl.phase == 1) {
-      if (QC::GEMM && tl.kind == qplan::kGemm) {
-        if constexpr (QC::GEMM) gemm_tile<1, C, true, QC::PK>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
-      } else {
-        decode_tile<QC::SMF, 1, 1, QC::PK, true, QC::SKC, QC::DB>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf,
-                                                                   reinterpret_cast<uint16_t*>(smem));
-      }
+      gemm_tile<1, C, true, QC::PK>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
       // publish: every wave's agent-scope row stores have completed, then the flag
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (tid == 0)
-        __hip_atomic_store(q.flags + static_cast<size_t>(tl.unit) * nch1max + tl.chunk, 1, __ATOMIC_RELAXED,
+        __hip_atomic_store(q.flags + static_cast<size_t>(tl.unit) * nch1 + tl.chunk, 1, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     } else {
       if (waits) {
         if (w == 0) {
           // lane c watches the flags of chunks c, c + 64, ...
-          const int* f = q.flags + static_cast<size_t>(tl.unit) * nch1max;
-          const int nf = sh.nch1[tl.kind];
+          const int* f = q.flags + static_cast<size_t>(tl.unit) * nch1;
+          const int nf = nch1;
           const unsigned long long start = realtime();
           int ok = 1, polls = 0;
           for (;;) {
@@ -1429,12 +1401,7 @@ __global__ __launch_bounds__(kThreads, QC::BPC) void ffn_queue_bf16(
         __syncthreads();
         waits = s_ok != 0;
       }
-      if (QC::GEMM && tl.kind == qplan::kGemm) {
-        if constexpr (QC::GEMM) gemm_tile<2, C, false, QC::PK>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
-      } else {
-        decode_tile<QC::SMF, 2, 2, QC::PK, false, QC::SKC, QC::DB>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h,
-                                                                    reinterpret_cast<uint16_t*>(smem));
-      }
+      gemm_tile<2, C, false, QC::PK>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
     }
     if (q.trace && tid == 0 && t < q.trace_per_queue) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1442,7 +1409,7 @@ __global__ __launch_bounds__(kThreads, QC::BPC) void ffn_queue_bf16(
       r[0] = t0;
       r[1] = realtime();
       r[2] = (static_cast<unsigned long long>(tl.unit) << 32) | (static_cast<unsigned long long>(tl.chunk) << 8) |
-             (static_cast<unsigned long long>(tl.kind) << 2) | (static_cast<unsigned long long>(tl.prio) << 1) |
+             (static_cast<unsigned long long>(tl.prio) << 1) |
              static_cast<unsigned long long>(tl.phase - 1);
       r[3] = (static_cast<unsigned long long>(qi) << 32) | blockIdx.x;
     }
@@ -1546,29 +1513,16 @@ qplan::Shape queue_shape(int n_rows, int E, int n_shared, int nseg, int d, int I
   sh.S = n_shared;
   sh.nseg = nseg;
   sh.n_rows = n_rows;
-  sh.stream_max = kStreamMaxRows;
-  sh.bm[qplan::kGemm] = GemmSmall::BM;
-  sh.bm[qplan::kStream] = 16 * kStreamMF;
-  sh.nch1[qplan::kGemm] = (I + GemmSmall::BN / 2 - 1) / (GemmSmall::BN / 2);
-  sh.nch1[qplan::kStream] = (I + kWaves * 16 - 1) / (kWaves * 16);
-  sh.nch2[qplan::kGemm] = (d + GemmSmall::BN - 1) / GemmSmall::BN;
-  sh.nch2[qplan::kStream] = (d + kWaves * 32 - 1) / (kWaves * 32);
+  sh.bm = GemmSmall::BM;
+  sh.nch1 = (I + GemmSmall::BN / 2 - 1) / (GemmSmall::BN / 2);
+  sh.nch2 = (d + GemmSmall::BN - 1) / GemmSmall::BN;
   sh.nq = nq;
   sh.lag = lag;
-  // One queue per group for both tile kinds (the kernel takes one queue per
-  // block): per-kind queues (nk = 2) keep about half the blocks on each kind at
-  // every instant, but neither kind ran faster beside the other (GPT-OSS-shaped
-  // mixed batch: 2.11 ms against 2.07 ms, decode segment done at 789 us
-  // against 567 us)
-  sh.nk = 1;
   return sh;
 }
 
-// Units never exceed ceil(n_rows / 64) + one partial unit per sequence.
-int queue_units_cap(const qplan::Shape& sh) {
-  const int bmin = sh.bm[0] < sh.bm[1] ? sh.bm[0] : sh.bm[1];
-  return (sh.n_rows + bmin - 1) / bmin + sh.nseq();
-}
+// Units never exceed ceil(n_rows / bm) + one partial unit per sequence.
+int queue_units_cap(const qplan::Shape& sh) { return (sh.n_rows + sh.bm - 1) / sh.bm + sh.nseq(); }
 
 Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16) {
   Layout L;
@@ -1606,8 +1560,7 @@ Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16)
   L.q_ints = 0;
   if (L.path == Path::kQueue) {
     const qplan::Shape sh = queue_shape(n_rows, E, n_shared, nseg, d, I, kMaxQueues, 0);
-    L.q_ints = static_cast<size_t>(2 * kMaxQueues) * kQueueStride +
-               static_cast<size_t>(queue_units_cap(sh)) * sh.nch1_max();
+    L.q_ints = static_cast<size_t>(kMaxQueues) * kQueueStride + static_cast<size_t>(queue_units_cap(sh)) * sh.nch1;
   }
   L.total = L.q_off + (L.q_ints * 4 + 255) / 256 * 256 + 256;
   return L;
@@ -1708,10 +1661,10 @@ void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t 
   q.arows = a.x_rows;
   q.n_x = a.n_x;
   q.heads = qbase;
-  q.flags = qbase + 2 * kMaxQueues * kQueueStride;
+  q.flags = qbase + kMaxQueues * kQueueStride;
   q.error = diag;
   q.trace = a.trace;
-  q.trace_per_queue = a.trace ? a.trace_capacity / q.shape.queues() : 0;
+  q.trace_per_queue = a.trace ? a.trace_capacity / q.shape.nq : 0;
   const size_t lds = QC::RING + 5 * static_cast<size_t>(q.shape.nseq() + 1) * sizeof(int);
   hipLaunchKernelGGL((ffn_queue_bf16<QC>), dim3(blocks), dim3(kThreads), lds, stream,
                      static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
@@ -1830,8 +1783,8 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
       else launch_gemm_bf16<GemmLarge, false>(a, L, plan, reinterpret_cast<uint16_t*>(ws + L.a_off), stream);
       break;
     case Path::kQueue:
-      if (a.packed) launch_queue_bf16<QueueMixed<true>>(a, L, ws, stream);
-      else launch_queue_bf16<QueueMixed<false>>(a, L, ws, stream);
+      if (a.packed) launch_queue_bf16<QueueGemm<true>>(a, L, ws, stream);
+      else launch_queue_bf16<QueueGemm<false>>(a, L, ws, stream);
       break;
     case Path::kF32: {
       float* abuf = reinterpret_cast<float*>(ws + L.a_off);

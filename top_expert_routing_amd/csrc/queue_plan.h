@@ -9,34 +9,26 @@
 // Sequences.  Sequence s is expert s.  With a priority segment (nseg == 2) a
 // routed expert's rows are its priority group's rows A followed by its other
 // group's rows B, tiled as one sequence A ++ B, so the expert's weights stream
-// once for both; the units (m-tiles) holding a row of A are its priority
-// units.  A shared expert (s >= E) is its one group; without a priority
-// segment every sequence is its one group.
+// once for both; the units (m-tiles of bm rows) holding a row of A are its
+// priority units.  A shared expert (s >= E) is its one group; without a
+// priority segment every sequence is its one group.  Phase 1 (gate/up +
+// SwiGLU) cuts the I columns into nch1 chunks, phase 2 (down projection) the d
+// columns into nch2 chunks.
 //
-// Tile kinds.  A sequence of at most `stream_max` rows runs on weight-streaming
-// tiles (kind 1: few rows, the weights go straight from HBM into MFMA
-// registers); a larger one on LDS-tiled GEMM tiles (kind 0).  A unit is
-// bm[kind] rows; phase 1 (gate/up + SwiGLU) cuts the I columns into nch1[kind]
-// chunks, phase 2 (down projection) the d columns into nch2[kind] chunks.
-//
-// Queues.  Chunk j of sequence s in phase p goes to queue group
-// x = (s * nch_p + j) mod nq, with all of that chunk's units, so the units that
-// share a weight slab run on one queue group (one XCD's L2) and a large
-// expert's chunks spread over every group.  With nk == 2 each group holds two
-// queues, one per tile kind (queue id kind * nq + x), so that workers can pick
-// a kind and a CU can run a memory-bound and an MFMA-bound tile side by side;
-// with nk == 1 one queue (id x) holds both kinds.  Queue q's tiles, in pop
-// order:
+// Queues.  Chunk j of sequence s in phase p goes to queue
+// (s * nch_p + j) mod nq, with all of that chunk's units, so the units that
+// share a weight slab run from one queue (one XCD's L2 when the hardware deals
+// a queue's blocks to one XCD) and a large expert's chunks spread over every
+// queue.  Queue q's tiles, in pop order:
 //   [P1: phase 1 of priority units][R1 head: the first `lag` phase-1 tiles of
 //   the other units][P2: phase 2 of priority units][R1 tail][R2: phase 2 of
 //   the other units]
 // and inside each part sequence by sequence, chunk by chunk, unit by unit.
-// A phase-2 tile of unit u needs the phase-1 tiles of u in every queue group
-// (of u's kind).  Each queue lists every phase-1 tile of a kind (priority or
-// not) before any phase-2 tile of that kind, and all P1 tiles are at the front
-// of their queues, so a waited-for tile has always been popped, or will be
-// popped by a block of its queue that is not waiting (see queue_check in the
-// tests).
+// A phase-2 tile of unit u needs the phase-1 tiles of u from every queue.
+// Each queue lists every phase-1 tile it holds before any phase-2 tile of the
+// same part, and all P1 tiles are at the front of their queues, so a
+// waited-for tile has always been popped, or will be popped by a block of its
+// queue that is not waiting (see queue_check in the tests).
 #pragma once
 
 #ifdef __HIPCC__
@@ -48,18 +40,12 @@
 namespace moe {
 namespace qplan {
 
-constexpr int kStream = 1, kGemm = 0;
-
 struct Shape {
   int E, S, nseg, n_rows;
-  int stream_max;           // sequences of 1..stream_max rows use stream tiles
-  int bm[2];                // unit rows per kind
-  int nch1[2], nch2[2];     // column chunks per kind and phase
+  int bm;                   // unit rows
+  int nch1, nch2;           // column chunks per phase
   int nq, lag;
-  int nk;                   // 1: one queue per group; 2: one per group and tile kind
   MOE_HD int nseq() const { return E + S; }
-  MOE_HD int queues() const { return nq * nk; }
-  MOE_HD int nch1_max() const { return nch1[0] > nch1[1] ? nch1[0] : nch1[1]; }
 };
 
 MOE_HD int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -90,22 +76,15 @@ MOE_HD SeqRows seq_rows(const Shape& p, const int* offs, int s) {
   return r;
 }
 
-MOE_HD int seq_kind(const Shape& p, int rows) {
-  return (rows > 0 && rows <= p.stream_max) ? kStream : kGemm;
-}
-
 // Units of a sequence and how many of them are priority units.
 struct SeqUnits {
-  int kind, units, tp;
+  int units, tp;
 };
 
 MOE_HD SeqUnits seq_units(const Shape& p, const SeqRows& r) {
   SeqUnits u;
-  const int rows = r.na + r.nb;
-  u.kind = seq_kind(p, rows);
-  const int bm = p.bm[u.kind];
-  u.units = (rows + bm - 1) / bm;
-  u.tp = (r.prio + bm - 1) / bm;
+  u.units = (r.na + r.nb + p.bm - 1) / p.bm;
+  u.tp = (r.prio + p.bm - 1) / p.bm;
   return u;
 }
 
@@ -123,10 +102,8 @@ struct SeqCounts {
 };
 
 MOE_HD SeqCounts seq_counts(const Shape& p, int s, const SeqUnits& u, int q) {
-  if (p.nk == 2 && u.kind != q / p.nq) return SeqCounts{0, 0, 0, 0};   // the other kind's queue
-  const int x = q % p.nq;
-  const int c1 = chunks_in_queue(first_chunk(s, p.nch1[u.kind], x, p.nq), p.nch1[u.kind], p.nq);
-  const int c2 = chunks_in_queue(first_chunk(s, p.nch2[u.kind], x, p.nq), p.nch2[u.kind], p.nq);
+  const int c1 = chunks_in_queue(first_chunk(s, p.nch1, q, p.nq), p.nch1, p.nq);
+  const int c2 = chunks_in_queue(first_chunk(s, p.nch2, q, p.nq), p.nch2, p.nq);
   return SeqCounts{u.tp * c1, (u.units - u.tp) * c1, u.tp * c2, (u.units - u.tp) * c2};
 }
 
@@ -171,11 +148,11 @@ MOE_HD int last_le(const int* pre, int n, int i) {
   return lo;
 }
 
-// A decoded tile: sequence, kind, chunk, unit within the sequence and its
-// global unit id (fu[s] + mt), and its rows: tile row r < split is sorted row
+// A decoded tile: sequence, chunk, unit within the sequence and its global
+// unit id (fu[s] + mt), and its rows: tile row r < split is sorted row
 // row0 + r, a later one row1 + (r - split).
 struct Tile {
-  int phase, prio, seq, kind, chunk, mt, unit;
+  int phase, prio, seq, chunk, mt, unit;
   int row0, rows, split, row1;
 };
 
@@ -187,21 +164,19 @@ MOE_HD Tile decode_tile(const Shape& p, const int* offs, const int* pre, const i
   const int s = last_le(pre, ns, sl.i);
   const SeqRows r = seq_rows(p, offs, s);
   const SeqUnits u = seq_units(p, r);
-  const int nch = sl.phase == 1 ? p.nch1[u.kind] : p.nch2[u.kind];
+  const int nch = sl.phase == 1 ? p.nch1 : p.nch2;
   const int nu = sl.prio ? u.tp : u.units - u.tp;      // units of this part (> 0 here)
   const int local = sl.i - pre[s];
   Tile t;
   t.phase = sl.phase;
   t.prio = sl.prio;
   t.seq = s;
-  t.kind = u.kind;
-  t.chunk = first_chunk(s, nch, q % p.nq, p.nq) + p.nq * (local / nu);
+  t.chunk = first_chunk(s, nch, q, p.nq) + p.nq * (local / nu);
   t.mt = (sl.prio ? 0 : u.tp) + local % nu;
   t.unit = fu[s] + t.mt;
-  const int bm = p.bm[u.kind];
-  const int a = t.mt * bm;                              // first row of the unit in A ++ B
+  const int a = t.mt * p.bm;                            // first row of the unit in A ++ B
   const int rows = r.na + r.nb - a;
-  t.rows = rows < bm ? rows : bm;
+  t.rows = rows < p.bm ? rows : p.bm;
   t.row0 = r.a0 + a;
   t.split = clampi(r.na - a, 0, t.rows);
   t.row1 = r.b0 + (a > r.na ? a - r.na : 0);

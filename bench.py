@@ -58,6 +58,9 @@ def parse():
                     help="keep the [E+S][rows][K] weight layout (moe_grouped_ffn) on bf16 workloads; by "
                          "default their weights are pre-packed once before timing (pack_weights) and the FFN "
                          "runs moe_grouped_ffn_packed")
+    ap.add_argument("--fused-combine", action="store_true",
+                    help="run the FFN and the combine as one moe_grouped_ffn_combine call (the combine folded "
+                         "into the down projection; bf16 decode-sized batches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle leg")
     ap.add_argument("--json-out", default="", help="also append the JSON line to this file")
@@ -393,7 +396,8 @@ def main():
     layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, *w16, packed_weights=packed or fp8_packed,
                          n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize),
                          stats_layers=s.stats_layers, req_offsets=wl.req_offsets, device=dev,
-                         topk_ids=stats_ids[0], w_router=w_router, fp8_weights=wsets[0] if fp8 else None)
+                         topk_ids=stats_ids[0], w_router=w_router, fp8_weights=wsets[0] if fp8 else None,
+                         fused_combine=args.fused_combine)
     for l in range(1, s.stats_layers):      # the other layers' ids, produced before timing
         moe.gate(wl.stats_logits[l].contiguous(), s.k, True, stats_ids[l],
                  torch.empty((s.T, s.k), device=dev))
@@ -486,6 +490,7 @@ def main():
     ffn_bytes = used_experts * expert_bytes + 2 * N * s.d * esize
     ffn_flops = 2.0 * N * 3 * s.d * s.I
     ffn_name = ("moe_grouped_ffn_fp8w_packed" if fp8_packed else "moe_grouped_ffn_fp8w") if fp8 else \
+        "moe_grouped_ffn_combine" if args.fused_combine else \
         "moe_grouped_ffn_packed" if packed else "moe_grouped_ffn"
     ffn_s = per_call[ffn_name] * 1e-3
     peak_flops = PEAK_F32_TFLOPS if s.dtype == "f32" else PEAK_BF16_TFLOPS
@@ -500,11 +505,13 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_flops, "unit": "TFLOP/s",
                 "frac": round(achieved / peak_flops, 4)}
     # the committed counters are for the default mode of each workload
-    traffic = None if fp8 or args.unpacked_weights else traffic_for(args.workload)
+    traffic = None if fp8 or args.unpacked_weights or args.fused_combine else traffic_for(args.workload)
     roof["traffic"] = None if traffic is None else round(traffic)
     queue = (not fp8 and s.dtype == "bf16" and s.n_priority > 0 and s.d % 32 == 0 and
              s.I % 32 == 0 and s.N // s.G > 48 and os.environ.get("LIBMOE_FFN_QUEUE", "1") != "0")
     roof["kernel"] = (f"{ffn_name} (" + ("one persistent launch: decode-priority tile queues" if queue else
+                                         "gate/up launch + down launch with the combine in its epilogue + "
+                                         "conversion launch" if args.fused_combine else
                                          "gate/up launch + down launch") + "), HIP events over K eager steps")
     roof["algorithmic_bytes"] = int(ffn_bytes)
     roof["algorithmic_flops"] = int(ffn_flops)

@@ -274,6 +274,44 @@ moe_status moe_grouped_ffn_traced(const void* x_sorted, const int32_t* x_rows, i
                                   int32_t weights_packed, hipStream_t stream);
 
 /*
+ * moe_grouped_ffn_combine - moe_grouped_ffn followed by moe_combine, with the
+ * combine folded into the down projection's epilogue: no h_sorted round trip
+ * and no separate combine launch.  (GRACE-MoE page, section 1: every MoE layer
+ * dispatches tokens to their experts and gathers the results back;
+ * ExpertPlex page, "Adaptive Persistent Kernels (APK)": per-batch launch cost.)
+ *
+ *   x_sorted, x_rows, n_x, group_offsets, n_rows, E, n_shared, nseg, d, I,
+ *   w_gate, w_up, w_down: as moe_grouped_ffn with dtype MOE_BF16, or as
+ *                  moe_grouped_ffn_packed when weights_packed = 1.
+ *   sorted_to_flat [n_rows] int32 and topk_w [T][k] fp32: moe_permute's and
+ *                  moe_gate's outputs for the same batch; n_rows must equal
+ *                  T * (k + n_shared).
+ *   y              [T][d] bf16, written: y[t] = sum over t's routed slots j of
+ *                  topk_w[t][j] * h[row of (t, j)] + sum over shared experts
+ *                  of h[row of (s, t)], where h is the FFN output rounded to
+ *                  bf16 (as moe_grouped_ffn stores it).  The terms are added
+ *                  in fp32 with atomic adds, in no fixed order, and rounded to
+ *                  bf16 once; so y can differ from moe_combine's in the last
+ *                  bits and from one call to the next.
+ *   workspace      [T][d] fp32 sums (rounded up to 256 bytes), then
+ *                  moe_grouped_ffn's workspace; the diagnostic word is its
+ *                  last 4 bytes as for moe_grouped_ffn.
+ *   Only batches that run on the decode-shaped kernels are supported (groups
+ *   averaging at most 48 rows; see moe_grouped_ffn), where the launch and the
+ *   h round trip weigh most; others get MOE_ERR_UNSUPPORTED.
+ *   Errors: MOE_ERR_INVALID_ARG for n_rows != T * (k + n_shared), k < 1,
+ *   weights_packed not 0 or 1, NULL or misaligned pointers (y and workspace
+ *   16-byte aligned); MOE_ERR_UNSUPPORTED for the shapes above and
+ *   moe_grouped_ffn's unsupported cases; MOE_ERR_WORKSPACE as usual.
+ */
+moe_status moe_grouped_ffn_combine(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                                   const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
+                                   int32_t nseg, int32_t d, int32_t I, const void* w_gate, const void* w_up,
+                                   const void* w_down, int32_t weights_packed, const int32_t* sorted_to_flat,
+                                   const float* topk_w, int32_t T, int32_t k, void* y, void* workspace,
+                                   size_t* workspace_bytes, hipStream_t stream);
+
+/*
  * moe_grouped_ffn_noalloc - moe_grouped_ffn with no workspace argument, for
  * callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.  The call allocates

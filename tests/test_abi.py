@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_declares_the_calls():
     assert _declared() == sorted(["moe_router", "moe_gate", "moe_gate_record", "moe_stage_to_host", "moe_permute",
-                                  "moe_grouped_ffn", "moe_grouped_ffn_traced",
+                                  "moe_grouped_ffn", "moe_grouped_ffn_traced", "moe_grouped_ffn_combine",
                                   "moe_grouped_ffn_noalloc",
                                   "moe_grouped_ffn_packed", "moe_grouped_ffn_fp8w", "moe_grouped_ffn_fp8w_packed",
                                   "moe_combine", "moe_stats", "moe_prob_signature", "moe_status_string"])
@@ -218,6 +218,27 @@ def test_ffn_traced_validation_and_query(lib):
     assert f(*args(a19=1)) == 0                                              # packed weights: same query
     assert f(*args(a15=FAKE, a16=ctypes.byref(big), a19=1, a13=0)) == UNS    # packed weights are bf16 only
     assert f(*args(a15=FAKE, a16=ctypes.byref(big), a19=1, a8=2888)) == UNS  # packed: d % 32 != 0
+
+
+def test_ffn_combine_validation(lib):
+    """The fused FFN + combine: argument errors, shape support and the
+    workspace query, all before any GPU work."""
+    f = lib.moe_grouped_ffn_combine
+    n = ctypes.c_size_t(0)
+    base = [FAKE, FAKE, 128, FAKE, 1024, 64, 0, 1, 2048, 1024, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 128, 8, FAKE, None,
+            ctypes.byref(n), None]
+    a = lambda **kw: [kw.get(f"a{i}", v) for i, v in enumerate(base)]
+    assert f(*a()) == 0 and n.value > 128 * 2048 * 4                # query: the fp32 sums + the FFN workspace
+    big = ctypes.c_size_t(1 << 40)
+    assert f(*a(a19=FAKE, a20=ctypes.byref(big), a4=1000)) == INV    # n_rows != T * (k + n_shared)
+    assert f(*a(a19=FAKE, a20=ctypes.byref(big), a13=2)) == INV      # weights_packed not 0/1
+    assert f(*a(a19=FAKE, a20=ctypes.byref(big), a17=0)) == INV      # k < 1
+    assert f(*a(a19=FAKE, a20=ctypes.byref(big), a18=None)) == INV   # NULL y
+    assert f(*a(a19=FAKE, a20=ctypes.byref(big), a18=FAKE + 8)) == INV   # misaligned y
+    assert f(*a(a19=FAKE, a20=ctypes.byref(big), a13=1, a8=2056)) == UNS  # packed: d % 32 != 0
+    assert f(*a(a4=65536, a5=128, a8=2048, a9=768, a16=8192, a17=8)) == UNS   # prefill-sized groups
+    assert f(*a(a19=FAKE, a20=ctypes.byref(ctypes.c_size_t(16)))) == WS
+    assert f(*a(a4=0, a16=0, a19=FAKE, a20=ctypes.byref(big))) == 0  # empty batch: nothing to do
 
 
 def test_ffn_noalloc_validation(lib):

@@ -522,6 +522,65 @@ def test_grouped_ffn_queue_path(T, E, k, S, P, d, I, kind, packed):
         assert e > end1[u], "a phase-2 tile ended before a phase-1 tile of its unit"
 
 
+COMBINE_CASES = [
+    # (T, E, k, S, P, d, I): decode-shaped batches (groups averaging <= 48 rows)
+    (16, 64, 6, 2, 0, 256, 128),      # groups of ~2 rows: the split-K kernel
+    (96, 16, 4, 1, 0, 136, 200),      # 32-row tiles, d and I not multiples of 32, a column tail
+    (100, 16, 4, 0, 30, 128, 96),     # priority segment: two row ranges per tile
+    (300, 32, 4, 0, 0, 256, 192),     # 64-row tiles
+    (128, 64, 8, 0, 0, 2048, 1024),   # OLMoE decode shape
+]
+
+
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
+@pytest.mark.parametrize("T,E,k,S,P,d,I", COMBINE_CASES)
+def test_grouped_ffn_combine_parity(T, E, k, S, P, d, I, packed):
+    """moe_grouped_ffn_combine (the combine folded into the down projection):
+    every token of y within the bf16 tolerance of the oracle's FFN + combine
+    and of the two-call GPU path, twice on one workspace (the second call
+    starts from its own cleared sums)."""
+    if packed and (d % 32 or I % 32):
+        pytest.skip("packed weights need d and I multiples of 32")
+    announce(f"ffn+combine T={T} E={E} k={k} S={S} P={P} d={d} I={I} packed={packed}")
+    wl, ids = _ffn_inputs(T, E, k, S, P, d, I, "bf16", "random", seed=T + E + 5)
+    nseg = 2 if P > 0 else 1
+    g = torch.Generator().manual_seed(T * 3 + k)
+    w = torch.rand((T, k), generator=g) + 0.05
+    w = (w / w.sum(dim=1, keepdim=True)).to(torch.float32)
+    p_ref = O.permute(ids.numpy(), E, S, P, np_of(wl.x))
+    h_ref = O.grouped_ffn(p_ref["x_sorted"], p_ref["group_offsets"], E, S, nseg, np_of(wl.w_gate),
+                          np_of(wl.w_up), np_of(wl.w_down), "bf16")
+    y_ref = O.combine(h_ref, p_ref["flat_to_sorted"], w.numpy(), T, k, S)
+    wts = [t.to(DEV) for t in (wl.w_gate, wl.w_up, wl.w_down)]
+    if packed:
+        wts = [moe.pack_weights(t) for t in wts]
+    x = wl.x.to(DEV)
+    offs = torch.from_numpy(p_ref["group_offsets"]).to(DEV)
+    rows = torch.from_numpy(p_ref["sorted_token"]).to(DEV)
+    s2f = torch.from_numpy(p_ref["sorted_to_flat"]).to(DEV)
+    f2s = torch.from_numpy(p_ref["flat_to_sorted"]).to(DEV)
+    wd = w.to(DEV)
+    nbytes = moe.ffn_combine_workspace_bytes(T * (k + S), E, S, nseg, d, I, T, k, packed)
+    ws = torch.full((nbytes,), 0x5a, dtype=torch.uint8, device=DEV)
+    for rep in range(2):
+        y = moe.grouped_ffn_combine(x, offs, E, S, nseg, *wts, s2f, wd, y=_poison((T, d), torch.bfloat16),
+                                    workspace=ws, x_rows=rows, packed=packed)
+        torch.cuda.synchronize()
+        assert int(ws[-4:].view(torch.int32).item()) == 0
+        err = rel_max_err(f64_of(y), y_ref)
+        assert err <= TOL["bf16"], (rep, err)
+    ffn = moe.grouped_ffn_packed if packed else moe.grouped_ffn
+    h = ffn(x, offs, E, S, nseg, *wts, x_rows=rows)
+    y2 = moe.combine(h, f2s, wd, S)
+    torch.cuda.synchronize()
+    assert rel_max_err(f64_of(y), f64_of(y2)) <= TOL["bf16"]
+
+
+def test_grouped_ffn_combine_refuses_prefill_batches():
+    with pytest.raises(moe.MoeError):
+        moe.ffn_combine_workspace_bytes(65536, 128, 0, 1, 2048, 768, 8192, 8)
+
+
 # ------------------------------------------------------------------ KV-block signature recording
 def test_kv_block_recording_and_host_staging():
     """Expert counts per 16-token KV block over the Qwen3-shaped 8-layer id stack,

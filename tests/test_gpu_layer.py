@@ -98,6 +98,35 @@ def test_layer_parity(name):
     assert y_err <= TOL[s.dtype], y_err
 
 
+@pytest.mark.parametrize("name", ["olmoe_decode", "dsv2_decode_t16", "dsv2_decode_t256"])
+def test_layer_fused_combine_parity(name):
+    """The layer with the combine folded into the down projection
+    (MoeLayer(fused_combine=True), packed weights): every token of y within the
+    bf16 tolerance of the oracle."""
+    announce(f"layer {name} fused combine")
+    wl = workloads.make(name, DEV)
+    s = wl.spec
+    layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype,
+                         *(moe.pack_weights(w) for w in (wl.w_gate, wl.w_up, wl.w_down)),
+                         n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize), device=DEV,
+                         packed_weights=True, fused_combine=True)
+    layer.y.view(torch.uint8).fill_(0xFF)
+    layer.forward(wl.logits, wl.x)
+    torch.cuda.synchronize()
+    logits = np_of(wl.logits)
+    ids_ref, w_ref = O.gate(logits, s.k, bool(s.renormalize))
+    x = np_of(wl.x)
+    p_x = O.permute(ids_ref, s.E, s.S, s.n_priority, x)
+    h_ref = O.grouped_ffn(p_x["x_sorted"], p_x["group_offsets"], s.E, s.S, layer.nseg, np_of(wl.w_gate),
+                          np_of(wl.w_up), np_of(wl.w_down), s.dtype)
+    y_ref = O.combine(h_ref, p_x["flat_to_sorted"], w_ref, s.T, s.k, s.S)
+    y_gpu = f64_of(layer.y)
+    assert not np.isnan(y_gpu).any(), "tokens left unwritten"
+    y_err = rel_max_err(y_gpu, y_ref)
+    announce(f"layer {name} fused combine: y err {y_err:.2e} over {s.T} tokens")
+    assert y_err <= TOL[s.dtype], y_err
+
+
 @pytest.mark.parametrize("name", ["tiny", "olmoe_decode"])
 def test_layer_with_router_parity(name):
     """The layer with the router projection in front of the gate: logits within

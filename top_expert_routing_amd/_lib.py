@@ -15,7 +15,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 
 # every symbol include/libmoe.h declares
 EXPORTS = ("moe_router", "moe_gate", "moe_gate_record", "moe_stage_to_host", "moe_permute", "moe_grouped_ffn",
-           "moe_grouped_ffn_traced", "moe_grouped_ffn_noalloc",
+           "moe_grouped_ffn_traced", "moe_grouped_ffn_noalloc", "moe_grouped_ffn_combine",
            "moe_grouped_ffn_packed", "moe_grouped_ffn_fp8w",
            "moe_grouped_ffn_fp8w_packed", "moe_combine",
            "moe_stats", "moe_prob_signature", "moe_status_string")
@@ -33,6 +33,8 @@ SIGNATURES = {
     "moe_grouped_ffn": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _sz, _p],
     "moe_grouped_ffn_traced": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _sz,
                                _p, _i32, _i32, _p],
+    "moe_grouped_ffn_combine": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _i32,
+                                _i32, _p, _p, _sz, _p],
     "moe_grouped_ffn_noalloc": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p],
     "moe_grouped_ffn_packed": [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p],
     "moe_combine": [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p],

@@ -254,6 +254,61 @@ def _need_trace(trace: torch.Tensor):
         raise ValueError("trace must be [records][4] int64")
 
 
+def ffn_combine_workspace_bytes(N, E, n_shared, nseg, d, I, T, k, packed=False) -> int:
+    """Workspace of moe_grouped_ffn_combine (raises MoeError for a batch it
+    does not serve)."""
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    check("moe_grouped_ffn_combine", lib.moe_grouped_ffn_combine(
+        None, None, 0, None, N, E, n_shared, nseg, d, I, None, None, None, int(bool(packed)), None, None, T, k,
+        None, None, ctypes.byref(n), None))
+    return int(n.value)
+
+
+def grouped_ffn_combine(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: int, n_shared: int, nseg: int,
+                        w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                        sorted_to_flat: torch.Tensor, topk_w: torch.Tensor, y: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, x_rows: Optional[torch.Tensor] = None,
+                        packed: bool = False) -> torch.Tensor:
+    """grouped_ffn then combine in one call, the combine folded into the down
+    projection (moe_grouped_ffn_combine; bf16, decode-sized batches).  With
+    `packed` the weights come from pack_weights."""
+    _need(x_sorted, "x_sorted", torch.bfloat16, 2)
+    _need(group_offsets, "group_offsets", torch.int32, 1)
+    for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(w, name, torch.bfloat16, 3)
+    _need(sorted_to_flat, "sorted_to_flat", torch.int32, 1)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    n_x, d = x_sorted.shape
+    N = sorted_to_flat.numel()
+    if x_rows is not None:
+        _need(x_rows, "x_rows", torch.int32, 1)
+        if x_rows.numel() != N:
+            raise ValueError("x_rows and sorted_to_flat must have one entry per sorted row")
+    elif n_x != N:
+        raise ValueError("x_sorted must have one row per sorted row")
+    T, k = topk_w.shape
+    I = w_gate.shape[1]
+    if w_gate.shape != (E + n_shared, I, d) or w_up.shape != w_gate.shape or w_down.shape != (E + n_shared, d, I):
+        raise ValueError("expert weight shapes do not match [E+S][I][d] / [E+S][d][I]")
+    if group_offsets.numel() != nseg * E + n_shared + 1:
+        raise ValueError("group_offsets must have nseg*E + n_shared + 1 entries")
+    dev = x_sorted.device
+    if y is None:
+        y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    _out(y, "y", torch.bfloat16, (T, d))
+    if workspace is None:
+        workspace = torch.empty(max(ffn_combine_workspace_bytes(N, E, n_shared, nseg, d, I, T, k, packed), 256),
+                                dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    nbytes = ctypes.c_size_t(workspace.numel())
+    check("moe_grouped_ffn_combine", lib.moe_grouped_ffn_combine(
+        _ptr(x_sorted), _ptr(x_rows), n_x, _ptr(group_offsets), N, E, n_shared, nseg, d, I, _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), int(bool(packed)), _ptr(sorted_to_flat), _ptr(topk_w), T, k, _ptr(y),
+        _ptr(workspace), ctypes.byref(nbytes), _stream(dev)))
+    return y
+
+
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -516,7 +571,7 @@ class MoeLayer:
 
     def __init__(self, E, k, d, I, T, dtype, w_gate, w_up, w_down, n_shared=0, n_priority=0,
                  renormalize=True, stats_layers=0, req_offsets=None, device="cuda", topk_ids=None,
-                 fused_gather=True, w_router=None, fp8_weights=None, packed_weights=False):
+                 fused_gather=True, w_router=None, fp8_weights=None, packed_weights=False, fused_combine=False):
         dev = torch.device(device)
         # fp8_weights = (codes_gate, scales_gate, codes_up, scales_up, codes_down, scales_down):
         # the FFN runs moe_grouped_ffn_fp8w on them instead of w_gate / w_up / w_down
@@ -525,6 +580,11 @@ class MoeLayer:
         # runs moe_grouped_ffn_packed (bf16, decode-sized batches); with
         # fp8_weights, the codes come from pack_fp8_codes (moe_grouped_ffn_fp8w_packed)
         self.packed = bool(packed_weights)
+        # fused_combine: the FFN and the combine run as one moe_grouped_ffn_combine
+        # call (bf16 decode-sized batches; h_sorted is then not written)
+        self.fused_combine = bool(fused_combine)
+        if self.fused_combine and (fp8_weights is not None or dtype != torch.bfloat16):
+            raise ValueError("fused_combine serves bf16 expert weights only")
         self.w_router = w_router
         self.logits = torch.empty((T, E), dtype=torch.float32, device=dev) if w_router is not None else None
         self.E, self.k, self.d, self.I, self.T = E, k, d, I, T
@@ -551,8 +611,12 @@ class MoeLayer:
         self.perm_ws = torch.empty(max(permute_workspace_bytes(T, E, k, n_shared, n_priority), 256),
                                    dtype=torch.uint8, device=dev)
         self.h_sorted = torch.empty((N, d), dtype=dtype, device=dev)
-        ws_bytes = ffn_fp8w_workspace_bytes(N, I) if fp8_weights is not None else \
-            ffn_workspace_bytes(N, E, n_shared, self.nseg, d, I, dtype)
+        if self.fused_combine:
+            ws_bytes = ffn_combine_workspace_bytes(N, E, n_shared, self.nseg, d, I, T, k, self.packed)
+        elif fp8_weights is not None:
+            ws_bytes = ffn_fp8w_workspace_bytes(N, I)
+        else:
+            ws_bytes = ffn_workspace_bytes(N, E, n_shared, self.nseg, d, I, dtype)
         self.ffn_ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.y = torch.empty((T, d), dtype=dtype, device=dev)
         self.stats_out = None
@@ -572,6 +636,13 @@ class MoeLayer:
     def permute(self, x):
         return permute(self.topk_ids, self.E, self.S, self.P, None if self.fused_gather else x, out=self.perm,
                        workspace=self.perm_ws)
+
+    def ffn_combine(self, x):
+        src = x if self.fused_gather else self.perm["x_sorted"]
+        return grouped_ffn_combine(src, self.perm["group_offsets"], self.E, self.S, self.nseg, self.w_gate,
+                                   self.w_up, self.w_down, self.perm["sorted_to_flat"], self.topk_w, self.y,
+                                   self.ffn_ws, x_rows=self.perm["sorted_token"] if self.fused_gather else None,
+                                   packed=self.packed)
 
     def ffn(self, x):
         if self.fp8_weights is not None:
@@ -631,11 +702,21 @@ class MoeLayer:
                                               self.perm["sorted_token"].data_ptr(),
                                               None if fused else self.perm["x_sorted"].data_ptr(),
                                               self.perm_ws.data_ptr(), ctypes.byref(n_perm), st)),
-            self._ffn_call(lib, x, fused, dt, n_ffn, st),
-            ("moe_combine", lib.moe_combine, (self.h_sorted.data_ptr(), self.perm["flat_to_sorted"].data_ptr(),
-                                              self.topk_w.data_ptr(), T, k, self.S, self.d, dt, self.y.data_ptr(),
-                                              st)),
         ]
+        if self.fused_combine:
+            src = x.data_ptr() if fused else self.perm["x_sorted"].data_ptr()
+            calls.append(("moe_grouped_ffn_combine", lib.moe_grouped_ffn_combine, (
+                src, self.perm["sorted_token"].data_ptr() if fused else None, T, self.perm["group_offsets"].data_ptr(),
+                self.N, E, self.S, self.nseg, self.d, self.I, self.w_gate.data_ptr(), self.w_up.data_ptr(),
+                self.w_down.data_ptr(), int(self.packed), self.perm["sorted_to_flat"].data_ptr(),
+                self.topk_w.data_ptr(), T, k, self.y.data_ptr(), self.ffn_ws.data_ptr(), ctypes.byref(n_ffn), st)))
+        else:
+            calls += [
+                self._ffn_call(lib, x, fused, dt, n_ffn, st),
+                ("moe_combine", lib.moe_combine, (self.h_sorted.data_ptr(), self.perm["flat_to_sorted"].data_ptr(),
+                                                  self.topk_w.data_ptr(), T, k, self.S, self.d, dt,
+                                                  self.y.data_ptr(), st)),
+            ]
         if stats_ids is not None and self.stats_out is not None:
             o = self.stats(stats_ids)          # allocates the outputs once
             L = stats_ids.shape[0]
@@ -687,8 +768,11 @@ class MoeLayer:
                 self.stats(stats_ids)
             side = False
         self.permute(x)
-        self.ffn(x)
-        self.combine()
+        if self.fused_combine:
+            self.ffn_combine(x)
+        else:
+            self.ffn(x)
+            self.combine()
         if side:
             self.stats(stats_ids)
         elif stats_ids is not None and self.stats_out is not None:

@@ -331,6 +331,61 @@ moe_status moe_grouped_ffn_noalloc(const void* x_sorted, const int32_t* x_rows, 
                   h_sorted, ws, &have, nullptr, 0, false, stream);
 }
 
+moe_status moe_grouped_ffn_combine(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
+                                   const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
+                                   int32_t nseg, int32_t d, int32_t I, const void* w_gate, const void* w_up,
+                                   const void* w_down, int32_t weights_packed, const int32_t* sorted_to_flat,
+                                   const float* topk_w, int32_t T, int32_t k, void* y, void* workspace,
+                                   size_t* workspace_bytes, hipStream_t stream) {
+  if (n_rows < 0 || E < 1 || n_shared < 0 || (nseg != 1 && nseg != 2) || d < 1 || I < 1 || T < 0 || k < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (weights_packed != 0 && weights_packed != 1) return MOE_ERR_INVALID_ARG;
+  if (static_cast<long long>(T) * (k + n_shared) != n_rows) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED || k > E) return MOE_ERR_UNSUPPORTED;
+  if (d % 8 != 0 || I % 8 != 0 || (weights_packed && (d % 32 != 0 || I % 32 != 0))) return MOE_ERR_UNSUPPORTED;
+  if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
+    return MOE_ERR_UNSUPPORTED;
+  if (n_rows > 0 && !moe::ffn_fused_combine_supported(n_rows, E, n_shared, nseg, d, I)) return MOE_ERR_UNSUPPORTED;
+  // workspace: the [T][d] fp32 combine sums, then moe_grouped_ffn's workspace
+  const size_t ysum = (static_cast<size_t>(T) * d * 4 + 255) / 256 * 256;
+  bool query;
+  moe_status st = workspace_check(workspace, workspace_bytes,
+                                  ysum + moe::ffn_workspace_bytes(n_rows, E, n_shared, nseg, d, I, 1), &query);
+  if (st != MOE_OK || query) return st;
+  if (n_rows == 0) return MOE_OK;
+  if (!x_sorted || !group_offsets || !w_gate || !w_up || !w_down || !sorted_to_flat || !topk_w || !y)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_sorted) || !aligned4(group_offsets) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned4(sorted_to_flat) || !aligned4(topk_w) || !aligned16(y) || !aligned16(workspace))
+    return MOE_ERR_INVALID_ARG;
+  if (x_rows && (!aligned4(x_rows) || n_x < 1)) return MOE_ERR_INVALID_ARG;
+  if (x_rows && !fits_int(static_cast<long long>(n_x) * d)) return MOE_ERR_UNSUPPORTED;
+  moe::FfnArgs a;
+  a.x_sorted = x_sorted;
+  a.x_rows = x_rows;
+  a.n_x = x_rows ? n_x : n_rows;
+  a.group_offsets = group_offsets;
+  a.n_rows = n_rows;
+  a.E = E;
+  a.n_shared = n_shared;
+  a.nseg = nseg;
+  a.d = d;
+  a.I = I;
+  a.w_gate = w_gate;
+  a.w_up = w_up;
+  a.w_down = w_down;
+  a.bf16 = 1;
+  a.h_sorted = nullptr;
+  a.packed = weights_packed == 1;
+  a.y32 = static_cast<float*>(workspace);
+  a.y = y;
+  a.s2f = sorted_to_flat;
+  a.topk_w = topk_w;
+  a.T = T;
+  a.k = k;
+  return hip_status(moe::launch_ffn(a, static_cast<char*>(workspace) + ysum, stream));
+}
+
 moe_status moe_grouped_ffn_packed(const void* x_sorted, const int32_t* x_rows, int32_t n_x,
                                   const int32_t* group_offsets, int32_t n_rows, int32_t E, int32_t n_shared,
                                   int32_t nseg, int32_t d, int32_t I, const void* w_gate, const void* w_up,

@@ -54,7 +54,45 @@ struct PlanArgs {
   int* diag;          // diagnostic word, cleared by block 0 (nullptr: leave it)
   const int* arows;   // A row of sorted row n (nullptr: row n itself)
   int n_x;            // rows of A when arows is given
+  float* zero = nullptr;   // zero_n4 float4s the launch's blocks clear (the fused combine's sums)
+  int zero_n4 = 0;
 };
+
+// The combine folded into the down projection's epilogue (GRACE-MoE page,
+// section 1: the gather back to the tokens after the experts): sorted row n's
+// output row, rounded to bf16 like h_sorted, is scaled by its gate weight and
+// added into y32[token] with fp32 atomics.  Routed rows: flat index
+// f = s2f[n] < T*k, token f / k, weight topk_w[f]; shared rows: token
+// (f - T*k) mod T, weight 1.
+struct CombineArgs {
+  const int* s2f;
+  const float* topk_w;
+  int T, k;
+  float* y32;         // [T][d] fp32, zero before the down projection
+};
+
+__device__ __forceinline__ void clear_span(const PlanArgs& plan) {
+  if (!plan.zero) return;
+  float4* z = reinterpret_cast<float4*>(plan.zero);
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < plan.zero_n4; i += gridDim.x * blockDim.x)
+    z[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__device__ __forceinline__ float bf16_rne(float v) {
+  return __uint_as_float((pack_bf16x2(v, 0.f) & 0xffffu) << 16);
+}
+
+// Adds the four columns n..n+3 of sorted row `row` (bf16-rounded, times its
+// gate weight) into its token's row of the combine sums.
+__device__ __forceinline__ void combine_add4(const CombineArgs& c, int row, int Ncols, int n, const float (&v)[4]) {
+  const int f = c.s2f[row];
+  const int tk = c.T * c.k;
+  const int tok = f < tk ? f / c.k : (f - tk) % c.T;
+  const float w = f < tk ? c.topk_w[f] : 1.0f;
+  float* y = c.y32 + static_cast<size_t>(tok) * Ncols + n;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) atomicAdd(y + t, w * bf16_rne(v[t]));
+}
 
 // Row of the A matrix that sorted row n reads (the row gather folded into the
 // loads when a row list is given; clamped so a bad entry stays in bounds).
@@ -189,10 +227,11 @@ constexpr int decode_lds_elems() { return 2 * 16 * MF * (decode_kc<MF>() + 8); }
 // it.chunk * 64 * NFC + [0, 64 * NFC)) of expert it.expert, K in chunks of
 // decode_kc<MF>().  All kThreads threads call it; `As0` is decode_lds_elems<MF>()
 // bf16 of LDS, free on entry.
-template <int MF, int NFC, int PHASE, bool PK = false>
+template <int MF, int NFC, int PHASE, bool PK = false, bool CMB = false>
 __device__ __forceinline__ void decode_tile(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x,
                                             int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-                                            int Ncols, const Item& it, uint16_t* __restrict__ out, uint16_t* As0) {
+                                            int Ncols, const Item& it, uint16_t* __restrict__ out, uint16_t* As0,
+                                            const CombineArgs& cmb) {
   constexpr int NF = PHASE == 1 ? 2 * NFC : NFC;
   constexpr int BN = kWaves * 16 * NFC;
   constexpr int BM = 16 * MF;
@@ -307,20 +346,24 @@ __device__ __forceinline__ void decode_tile(const uint16_t* __restrict__ A, cons
       float v[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) v[t] = PHASE == 1 ? silu_mul(acc[i][j][t], acc[i][NFC + j][t]) : acc[i][j][t];
-      store4<false>(orow + n, v[0], v[1], v[2], v[3]);
+      if constexpr (CMB)
+        combine_add4(cmb, it.row(m), Ncols, n, v);
+      else
+        store4<false>(orow + n, v[0], v[1], v[2], v[3]);
     }
   }
 }
 
-template <int MF, int NFC, int PHASE, bool PK = false>
+template <int MF, int NFC, int PHASE, bool PK = false, bool CMB = false>
 __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void ffn_decode_bf16(
     const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-    int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
+    int Ncols, PlanArgs plan, uint16_t* __restrict__ out, CombineArgs cmb) {
   __shared__ __attribute__((aligned(16))) uint16_t As[decode_lds_elems<MF>()];
+  clear_span(plan);
   const int nch = (Ncols + kWaves * 16 * NFC - 1) / (kWaves * 16 * NFC);
   const Item it = block_find_item(plan, nch);
   if (it.rows == 0) return;
-  decode_tile<MF, NFC, PHASE, PK>(A, plan.arows, plan.n_x, K, W0, W1, Ncols, it, out, As);
+  decode_tile<MF, NFC, PHASE, PK, CMB>(A, plan.arows, plan.n_x, K, W0, W1, Ncols, it, out, As, cmb);
 }
 
 // ---- decode-sized tiles of one 16-row slab: K split over the waves ----------------
@@ -347,16 +390,17 @@ __global__ __launch_bounds__(kThreads, MF <= 2 ? kDecodeWavesPerSimd : 2) void f
 //     the wave's K range.
 //   * The waves add their partial sums through LDS; each stores a share of the
 //     item's 16x16 output blocks (SwiGLU applied in phase 1).
-template <int NFC, int PHASE, bool PK = false>
+template <int NFC, int PHASE, bool PK = false, bool CMB = false>
 __global__ __launch_bounds__(kThreads, kDecodeWavesPerSimd) void ffn_decode_splitk_bf16(
     const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-    int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
+    int Ncols, PlanArgs plan, uint16_t* __restrict__ out, CombineArgs cmb) {
   constexpr int NF = PHASE == 1 ? 2 * NFC : NFC;
   constexpr int BN = 16 * NFC;
   constexpr int U = 4;
   constexpr int KB = 32 * U;                          // K per batch
   __shared__ f32x4 part[kWaves][NF][kWave];           // partial sums, 16 B per lane per block
 
+  clear_span(plan);
   const int nch = (Ncols + BN - 1) / BN;
   const Item it = block_find_item(plan, nch);
   if (it.rows == 0) return;
@@ -470,9 +514,22 @@ __global__ __launch_bounds__(kThreads, kDecodeWavesPerSimd) void ffn_decode_spli
     float v[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) v[t] = PHASE == 1 ? silu_mul(g[t], u[t]) : g[t];
-    uint16_t* orow = out + static_cast<size_t>(it.row(l16)) * Ncols;
-    *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    if constexpr (CMB) {
+      combine_add4(cmb, it.row(l16), Ncols, n, v);
+    } else {
+      uint16_t* orow = out + static_cast<size_t>(it.row(l16)) * Ncols;
+      *reinterpret_cast<uint2*>(orow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
   }
+}
+
+// The fused combine's last step: y = bf16(y32), eight values per thread.
+__global__ void ffn_combine_finalize(const float* __restrict__ y32, uint16_t* __restrict__ y, int n8) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const float4 a = reinterpret_cast<const float4*>(y32)[2 * i], b = reinterpret_cast<const float4*>(y32)[2 * i + 1];
+  reinterpret_cast<uint4*>(y)[i] = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                                              pack_bf16x2(b.z, b.w));
 }
 
 // ---- decode-sized tiles with FP8 weights ---------------------------------------
@@ -1574,20 +1631,41 @@ constexpr int kDecodeNfc2 = 2;
 
 // Groups of at most kSplitKMaxAvg rows on average: the split-K kernel, 16
 // columns per item in phase 1 and 32 in phase 2 (tiles of 16 rows).
+// Phase-1 plan and combine arguments of a call: with the fused combine
+// (a.y32 set) the phase-1 blocks clear the combine sums and the down
+// projection adds into them.
+PlanArgs phase1_plan(const FfnArgs& a, const PlanArgs& plan) {
+  PlanArgs p = plan;
+  if (a.y32) {
+    p.zero = a.y32;
+    p.zero_n4 = static_cast<int>(static_cast<long long>(a.T) * a.d / 4);
+  }
+  return p;
+}
+
+CombineArgs combine_args(const FfnArgs& a) { return CombineArgs{a.s2f, a.topk_w, a.T, a.k, a.y32}; }
+
 template <bool PK>
 void launch_decode_splitk_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, uint16_t* abuf,
                                hipStream_t stream) {
   constexpr int NFC1 = 1, NFC2 = 2;
   const int nch1 = (a.I + 16 * NFC1 - 1) / (16 * NFC1), nch2 = (a.d + 16 * NFC2 - 1) / (16 * NFC2);
+  const CombineArgs cmb = combine_args(a);
   hipLaunchKernelGGL((ffn_decode_splitk_bf16<NFC1, 1, PK>), dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
-                     static_cast<const uint16_t*>(a.w_up), a.I, plan, abuf);
+                     static_cast<const uint16_t*>(a.w_up), a.I, phase1_plan(a, plan), abuf, cmb);
   PlanArgs plan2 = plan;
   plan2.diag = nullptr;
   plan2.arows = nullptr;
-  hipLaunchKernelGGL((ffn_decode_splitk_bf16<NFC2, 2, PK>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
-                     stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
-                     static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted));
+  if (a.y32)
+    hipLaunchKernelGGL((ffn_decode_splitk_bf16<NFC2, 2, PK, true>), dim3(item_grid(L.max_tiles, nch2)),
+                       dim3(kThreads), 0, stream, static_cast<const uint16_t*>(abuf), a.I,
+                       static_cast<const uint16_t*>(a.w_down), static_cast<const uint16_t*>(nullptr), a.d, plan2,
+                       static_cast<uint16_t*>(nullptr), cmb);
+  else
+    hipLaunchKernelGGL((ffn_decode_splitk_bf16<NFC2, 2, PK>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
+                       stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
+                       static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted), cmb);
 }
 
 template <int MF, bool PK>
@@ -1595,15 +1673,22 @@ void launch_decode_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan,
                         hipStream_t stream) {
   const int bn1 = kWaves * 16 * kDecodeNfc1, bn2 = kWaves * 16 * kDecodeNfc2;
   const int nch1 = (a.I + bn1 - 1) / bn1, nch2 = (a.d + bn2 - 1) / bn2;
+  const CombineArgs cmb = combine_args(a);
   hipLaunchKernelGGL((ffn_decode_bf16<MF, kDecodeNfc1, 1, PK>), dim3(item_grid(L.max_tiles, nch1)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
-                     static_cast<const uint16_t*>(a.w_up), a.I, plan, abuf);
+                     static_cast<const uint16_t*>(a.w_up), a.I, phase1_plan(a, plan), abuf, cmb);
   PlanArgs plan2 = plan;
   plan2.diag = nullptr;
   plan2.arows = nullptr;
-  hipLaunchKernelGGL((ffn_decode_bf16<MF, kDecodeNfc2, 2, PK>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads), 0,
-                     stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
-                     static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted));
+  if (a.y32)
+    hipLaunchKernelGGL((ffn_decode_bf16<MF, kDecodeNfc2, 2, PK, true>), dim3(item_grid(L.max_tiles, nch2)),
+                       dim3(kThreads), 0, stream, static_cast<const uint16_t*>(abuf), a.I,
+                       static_cast<const uint16_t*>(a.w_down), static_cast<const uint16_t*>(nullptr), a.d, plan2,
+                       static_cast<uint16_t*>(nullptr), cmb);
+  else
+    hipLaunchKernelGGL((ffn_decode_bf16<MF, kDecodeNfc2, 2, PK>), dim3(item_grid(L.max_tiles, nch2)), dim3(kThreads),
+                       0, stream, static_cast<const uint16_t*>(abuf), a.I, static_cast<const uint16_t*>(a.w_down),
+                       static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted), cmb);
 }
 
 template <class C, bool PKB>
@@ -1750,6 +1835,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
   plan.arows = a.x_rows;
   plan.n_x = a.n_x;
   if (a.packed && L.path == Path::kF32) return hipErrorInvalidValue;
+  if (a.y32 && L.path != Path::kDecode) return hipErrorInvalidValue;
   switch (L.path) {
     case Path::kDecode: {
       uint16_t* abuf = reinterpret_cast<uint16_t*>(ws + L.a_off);
@@ -1801,7 +1887,16 @@ hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream) {
       break;
     }
   }
+  if (a.y32) {
+    const int n8 = static_cast<int>(static_cast<long long>(a.T) * a.d / 8);
+    hipLaunchKernelGGL(ffn_combine_finalize, dim3((n8 + kThreads - 1) / kThreads), dim3(kThreads), 0, stream, a.y32,
+                       static_cast<uint16_t*>(a.y), n8);
+  }
   return hipGetLastError();
+}
+
+bool ffn_fused_combine_supported(int n_rows, int E, int n_shared, int nseg, int d, int I) {
+  return layout(n_rows, E, n_shared, nseg, d, I, 1).path == Path::kDecode;
 }
 
 }  // namespace moe

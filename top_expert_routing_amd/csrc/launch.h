@@ -58,8 +58,18 @@ struct FfnArgs {
   // of 4 uint64, nullptr for none
   unsigned long long* trace = nullptr;
   int trace_capacity = 0;
+  // combine folded into the down projection (moe_grouped_ffn_combine): y32 is
+  // the [T][d] fp32 sums in the workspace, y the [T][d] bf16 result; nullptr
+  // for the plain call
+  float* y32 = nullptr;
+  void* y = nullptr;
+  const int* s2f = nullptr;
+  const float* topk_w = nullptr;
+  int T = 0, k = 0;
 };
 size_t ffn_workspace_bytes(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16);
+// moe_grouped_ffn_combine: batches on the decode-shaped kernels only
+bool ffn_fused_combine_supported(int n_rows, int E, int n_shared, int nseg, int d, int I);
 hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream);
 size_t ffn_fp8w_workspace_bytes(int n_rows, int I);
 hipError_t launch_ffn_fp8w(const FfnArgs& a, void* workspace, hipStream_t stream);

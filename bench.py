@@ -362,8 +362,9 @@ def main():
     # FP8 codes are packed too when d and I are multiples of 64
     fp8_packed = fp8 and s.d % 64 == 0 and s.I % 64 == 0 and not args.unpacked_weights
     if fp8 and s.n_priority > 0:
-        # the library refuses FP8 weights with a priority segment (one run on
-        # this shape ended in a GPU memory fault whose cause is not found)
+        # the library refuses FP8 weights with a priority segment: two runs of
+        # this benchmark on the GPT-OSS-shaped batch ended in a GPU memory fault
+        # (once with each FP8 FFN kernel), cause not found
         print("--fp8-weights: the library refuses FP8 expert weights with a priority segment "
               "(MOE_ERR_UNSUPPORTED)", file=sys.stderr)
         sys.exit(2)

@@ -98,6 +98,8 @@ def test_ffn_fp8w_validation_and_query(lib):
     assert fp(*args()) == 0                                        # d = 256, I = 512: multiples of 64
     assert fp(*args(a8=272)) == UNS                                # d a multiple of 16 but not of 64
     assert fp(*args(a9=528)) == UNS                                # I a multiple of 16 but not of 64
+    assert fp(*args(a7=2)) == UNS                                  # a priority segment is refused
+    assert fp(*args(a7=2, a4=8192)) == UNS                         # ... also at GEMM sizes
 
 
 def test_ffn_packed_validation_and_query(lib):

@@ -659,6 +659,66 @@ FP8_CASES = [
 ]
 
 
+FP8_GEMM_CASES = [
+    # (T, E, k, S, P, d, I, kind): packed codes, groups averaging > 48 rows ->
+    # the 256 x 256 GEMM on FP8 codes
+    (600, 8, 2, 0, 0, 256, 320, "random"),     # partial m-tiles, a half column chunk in phase 1
+    (2048, 16, 4, 0, 0, 512, 256, "random"),   # ~512 rows per expert: two full m-tiles each
+    (1500, 8, 3, 1, 0, 192, 448, "random"),    # a shared expert of 1500 rows, K = 192 (three code blocks)
+    (3000, 32, 2, 0, 0, 128, 128, "zipf"),     # one hot expert, many nearly empty ones
+    (600, 8, 2, 0, 50, 256, 320, "random"),    # a priority segment: refused (see below)
+]
+
+
+@pytest.mark.parametrize("T,E,k,S,P,d,I,kind", FP8_GEMM_CASES)
+def test_grouped_ffn_fp8w_gemm_parity(T, E, k, S, P, d, I, kind):
+    """FP8 codes on the GEMM (pre-packed codes, prefill-sized groups): every
+    row within the bf16 tolerance of the oracle's FP8 FFN, directly and through
+    the row list, and of the decode-shaped FP8 kernel on row-major codes."""
+    announce(f"ffn fp8 gemm T={T} E={E} k={k} S={S} P={P} d={d} I={I} {kind}")
+    wl, ids = _ffn_inputs(T, E, k, S, P, d, I, "bf16", kind, seed=T + E + 9)
+    nseg = 2 if P > 0 else 1
+    q = [moe.quantize_fp8_rows(w) for w in (wl.w_gate, wl.w_up, wl.w_down)]
+    p_ref = O.permute(ids.numpy(), E, S, P, np_of(wl.x))
+    if nseg == 2:
+        # FP8 weights with a priority segment are refused before anything is
+        # enqueued (two GPU memory faults of FP8 benchmark runs on the
+        # GPT-OSS-shaped batch, cause not found)
+        offs = torch.from_numpy(p_ref["group_offsets"]).to(DEV)
+        codes = [moe.pack_fp8_codes(c.to(DEV)) if i % 2 == 0 else c.to(DEV)
+                 for i, c in enumerate(t for pair in q for t in pair)]
+        with pytest.raises(moe.MoeError) as ei:
+            moe.grouped_ffn_fp8w(wl.x.to(DEV), offs, E, S, nseg, *codes,
+                                 x_rows=torch.from_numpy(p_ref["sorted_token"]).to(DEV), packed=True)
+        assert ei.value.status == 2          # MOE_ERR_UNSUPPORTED
+        return
+    h_ref = O.grouped_ffn_fp8w(p_ref["x_sorted"], p_ref["group_offsets"], E, S, nseg, q[0][0].numpy(),
+                               q[0][1].numpy(), q[1][0].numpy(), q[1][1].numpy(), q[2][0].numpy(), q[2][1].numpy(),
+                               "bf16")
+    offs = torch.from_numpy(p_ref["group_offsets"]).to(DEV)
+    rows = torch.from_numpy(p_ref["sorted_token"]).to(DEV)
+    packed = []
+    for c, sc in q:
+        packed += [moe.pack_fp8_codes(c.to(DEV)), sc.to(DEV)]
+    N = int(p_ref["group_offsets"][-1])
+    nbytes = moe.ffn_fp8w_workspace_bytes(N, I)
+    ws = torch.full((max(nbytes, 256),), 0x5a, dtype=torch.uint8, device=DEV)
+    h = moe.grouped_ffn_fp8w(wl.x.to(DEV), offs, E, S, nseg, *packed, h_sorted=_poison((N, d), torch.bfloat16),
+                             workspace=ws, x_rows=rows, packed=True)
+    torch.cuda.synchronize()
+    assert int(ws[nbytes - 4:nbytes].view(torch.int32).item()) == 0
+    err = rel_max_err(f64_of(h), h_ref)
+    assert err <= TOL["bf16"], err
+    xs = torch.from_numpy(p_ref["x_sorted"].view(np.int16)).view(torch.bfloat16).to(DEV)
+    h2 = moe.grouped_ffn_fp8w(xs, offs, E, S, nseg, *packed, h_sorted=_poison((N, d), torch.bfloat16), packed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(h2, h)
+    rowmajor = [t.to(DEV) for pair in q for t in pair]
+    h3 = moe.grouped_ffn_fp8w(wl.x.to(DEV), offs, E, S, nseg, *rowmajor, x_rows=rows)
+    torch.cuda.synchronize()
+    assert rel_max_err(f64_of(h3), f64_of(h)) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("T,E,k,S,P,d,I,kind", FP8_CASES)
 def test_grouped_ffn_fp8w_parity(T, E, k, S, P, d, I, kind):
     announce(f"ffn fp8 T={T} E={E} k={k} S={S} P={P} d={d} I={I} {kind}")

@@ -156,6 +156,46 @@ def test_layer_with_router_parity(name):
     assert y_err <= TOL[s.dtype], y_err
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["qwen3_prefill", pytest.param("gptoss_mixed", marks=pytest.mark.skip(
+    reason="FP8 weights with a priority segment are refused: a benchmark run on this shape faulted the GPU "
+           "(cause not found)"))])
+def test_layer_fp8_gemm_parity(name):
+    """The prefill-sized layer on pre-packed FP8 codes, which runs the FFN on
+    the GEMM kernel: every sorted row of h and every token of y within the bf16
+    tolerance of the oracle's FP8 FFN and combine (buffers poisoned first)."""
+    announce(f"layer {name} with fp8 weights on the GEMM")
+    wl = workloads.make(name, DEV)
+    s = wl.spec
+    q = [moe.quantize_fp8_rows(w) for w in (wl.w_gate, wl.w_up, wl.w_down)]
+    fp8p = (moe.pack_fp8_codes(q[0][0]), q[0][1], moe.pack_fp8_codes(q[1][0]), q[1][1], moe.pack_fp8_codes(q[2][0]),
+            q[2][1])
+    layer = moe.MoeLayer(s.E, s.k, s.d, s.I, s.T, wl.torch_dtype, wl.w_gate, wl.w_up, wl.w_down,
+                         n_shared=s.S, n_priority=s.n_priority, renormalize=bool(s.renormalize), device=DEV,
+                         fp8_weights=fp8p, packed_weights=True)
+    for buf in (layer.h_sorted, layer.y):
+        buf.view(torch.uint8).fill_(0xFF)
+    layer.forward(wl.logits, wl.x)
+    torch.cuda.synchronize()
+    logits, x = np_of(wl.logits), np_of(wl.x)
+    ids, w = O.gate(logits, s.k, bool(s.renormalize))
+    np.testing.assert_array_equal(np_of(layer.topk_ids), ids)
+    p = O.permute(ids, s.E, s.S, s.n_priority, x)
+    nseg = 2 if s.n_priority > 0 else 1
+    h_ref = O.grouped_ffn_fp8w(p["x_sorted"], p["group_offsets"], s.E, s.S, nseg,
+                               *(np_of(t) for pair in q for t in pair), dtype=s.dtype)
+    h_gpu = f64_of(layer.h_sorted)
+    assert not np.isnan(h_gpu).any(), "sorted rows left unwritten"
+    h_err = rel_max_err(h_gpu, h_ref)
+    y_ref = O.combine(h_ref, p["flat_to_sorted"], w, s.T, s.k, s.S)
+    y_gpu = f64_of(layer.y)
+    assert not np.isnan(y_gpu).any(), "tokens left unwritten"
+    y_err = rel_max_err(y_gpu, y_ref)
+    announce(f"layer {name} fp8 gemm: h err {h_err:.2e}, y err {y_err:.2e}")
+    assert h_err <= TOL[s.dtype], h_err
+    assert y_err <= TOL[s.dtype], y_err
+
+
 @pytest.mark.parametrize("name", ["olmoe_decode", "dsv2_decode_t16", "dsv2_decode_t256"])
 def test_layer_fp8_weights_parity(name):
     """The layer with FP8 expert weights (E4M3 codes, fp32 row scales): routing

@@ -10,4 +10,4 @@ from .api import (router, gate, gate_record, stage_to_host, permute, grouped_ffn
                   grouped_ffn_combine, ffn_combine_workspace_bytes,
                   NOALLOC_SCRATCH_BYTES, grouped_ffn_packed, pack_weights, grouped_ffn_fp8w, quantize_fp8_rows,
                   pack_fp8_codes, combine, stats, prob_signature, MoeLayer,
-                  permute_workspace_bytes, ffn_workspace_bytes, stats_workspace_bytes)
+                  permute_workspace_bytes, ffn_workspace_bytes, ffn_fp8w_workspace_bytes, stats_workspace_bytes)

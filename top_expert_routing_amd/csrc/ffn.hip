@@ -734,19 +734,24 @@ constexpr int kGemmRowBytes = kGemmBK * 2;
 constexpr int kEpiPitch = 80;                 // bytes per row of a wave's 32x32 bf16 epilogue block (64 + 16 pad)
 constexpr int kEpiBytes = 32 * kEpiPitch;     // per wave
 
-template <int MI_, int NJ_, int WM_, int WN_, int STAGES_, int BPC_>
+// F8: the weights are E4M3 codes (one byte each) pre-packed by
+// pack_fp8_codes, so a K-step moves 32 bytes per weight row instead of 64.
+template <int MI_, int NJ_, int WM_, int WN_, int STAGES_, int BPC_, bool F8_ = false>
 struct GemmCfg {
   static constexpr int MI = MI_, NJ = NJ_, WM = WM_, WN = WN_, STAGES = STAGES_, BLOCKS_PER_CU = BPC_;
+  static constexpr bool F8 = F8_;
   static constexpr int NW = WM * WN, NT = kWave * NW;
   static constexpr int BM = 32 * MI * WM, BN = 32 * NJ * WN;
-  static constexpr int A_BYTES = BM * kGemmRowBytes, B_BYTES = BN * kGemmRowBytes;
+  static constexpr int A_BYTES = BM * kGemmRowBytes, B_BYTES = BN * (F8 ? kGemmBK : kGemmRowBytes);
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int RING = STAGES * STAGE;               // LDS bytes of the operand ring
   static constexpr int ADMA = BM / 16 / NW;                 // 1 KiB DMA instructions per wave per K-step
-  static constexpr int BDMA = BN / 16 / NW;
+  static constexpr int BDMA = B_BYTES / 1024 / NW;
 };
 using GemmSmall = GemmCfg<2, 4, 2, 2, 3, 2>;   // 128 x 256
 using GemmLarge = GemmCfg<2, 4, 4, 2, 4, 1>;   // 256 x 256
+// 256 x 256 on FP8 codes: a stage is 24 KiB, so five fit (four K-steps in flight)
+using GemmLargeF8 = GemmCfg<2, 4, 4, 2, 5, 1, true>;
 constexpr int kGemmLargeMinAvg = 256;
 
 __device__ __forceinline__ int gemm_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
@@ -793,10 +798,20 @@ __device__ __forceinline__ void wait_ahead_barrier(int ahead) {
 // contiguous KiB, which one DMA instruction copies as is: in LDS the block's
 // row r, chunk c sits at byte c * 256 + r * 16 (no swizzle needed: a 16-lane
 // group of an operand read covers 256 contiguous bytes).
+// C::F8: the weights are E4M3 codes packed by pack_fp8_codes (blocks of 16
+// rows x 64 codes, 1 KiB, (row block, K block) order; inside a block codes
+// [16 kq, 16 kq + 16) of row r at byte (16 kq + r) * 16).  A K-step of 32
+// codes is half a block (kq = 2 (kt % 2) + 0, 1: 512 contiguous bytes), so an
+// instruction copies the halves of two row blocks: lanes 0-31 rows rb..rb+15,
+// lanes 32-63 rows rb+16..rb+31.  In LDS the instruction's 1 KiB holds, per
+// row block b (512 bytes each), codes [16 s, 16 s + 16) of row r at byte
+// b * 512 + (16 s + r) * 16.
 template <int PHASE, class C, bool PKB = false>
 struct TileLoader {
   const uint16_t* asrc[C::ADMA];
   const uint16_t* bsrc[C::BDMA];
+  const uint8_t* bsrc8[C::BDMA];
+  const float* ssrc;   // C::F8: this lane's 16 bytes of the tile's weight-row scales
   int na;   // this wave's A instructions whose first row is valid (wave-uniform): 0..ADMA
 
   // A DMA instructions wave `wave` issues per K-step for a tile of `rows` rows
@@ -809,7 +824,8 @@ struct TileLoader {
 
   __device__ __forceinline__ void init(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x, int K,
                                        const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int Ncols,
-                                       const Item& it) {
+                                       const Item& it, const float* __restrict__ S0 = nullptr,
+                                       const float* __restrict__ S1 = nullptr) {
     constexpr int OUTC = PHASE == 1 ? C::BN / 2 : C::BN;
     const int wave = threadIdx.x >> 6, lane = lane_id(), dr = lane >> 2;
     const int n0 = it.chunk * OUTC;
@@ -827,7 +843,24 @@ struct TileLoader {
     }
 #pragma unroll
     for (int q = 0; q < C::BDMA; ++q) {
-      if constexpr (PKB) {
+      if constexpr (C::F8) {
+        // W0 / W1 hold bytes here (E4M3 codes); 32 tile rows per instruction
+        const int rb = 32 * (wave + C::NW * q);
+        int nb = n0 + rb + 16 * (lane >> 5);
+        const uint8_t* W = reinterpret_cast<const uint8_t*>(W0);
+        if (PHASE == 1 && rb >= OUTC) {
+          nb -= OUTC;
+          W = reinterpret_cast<const uint8_t*>(W1);
+        }
+        nb = min(nb, Ncols - 16);                        // blocks past the rows are read but never stored
+        bsrc8[q] = W + eoff + static_cast<size_t>(nb / 16) * (K / 64) * 1024 + (lane & 31) * 16;
+        // scales of the tile's weight rows, 1 KiB: phase 1 lanes 0-31 the 128
+        // gate rows, lanes 32-63 the 128 up rows; phase 2 the 256 down rows
+        // (columns past Ncols read the last four, never used)
+        const int c = PHASE == 1 ? 4 * (lane & 31) : 4 * lane;
+        const float* S = (PHASE == 1 && lane >= 32) ? S1 : S0;
+        ssrc = S + static_cast<size_t>(it.expert) * Ncols + min(n0 + c, Ncols - 4);
+      } else if constexpr (PKB) {
         const int rb = 16 * (wave + C::NW * q);         // first tile row of this instruction
         int nb = n0 + rb;
         const uint16_t* W = W0;
@@ -850,6 +883,10 @@ struct TileLoader {
     }
   }
 
+  // C::F8: the tile's scales into 1 KiB of LDS at byte address `dst` (one
+  // instruction; the caller's waits on later K-steps cover it).
+  __device__ __forceinline__ void issue_scales(uint32_t dst) const { dma_b128(ssrc, dst); }
+
   // K-step kt of this tile into ring slot `slot` (lds0: LDS byte address of the ring).
   // With skip_a, A instructions whose rows all lie past the tile's rows are
   // not issued (their LDS rows keep stale data, whose results are never
@@ -862,7 +899,12 @@ struct TileLoader {
     for (int q = 0; q < C::ADMA; ++q)
       if (!skip_a || q < na) dma_b128(asrc[q] + k, st + q * C::NW * 1024);
 #pragma unroll
-    for (int q = 0; q < C::BDMA; ++q) dma_b128(bsrc[q] + (PKB ? kt * 512 : k), st + C::A_BYTES + q * C::NW * 1024);
+    for (int q = 0; q < C::BDMA; ++q) {
+      if constexpr (C::F8)
+        dma_b128(bsrc8[q] + (kt >> 1) * 1024 + (kt & 1) * 512, st + C::A_BYTES + q * C::NW * 1024);
+      else
+        dma_b128(bsrc[q] + (PKB ? kt * 512 : k), st + C::A_BYTES + q * C::NW * 1024);
+    }
   }
 };
 
@@ -903,14 +945,15 @@ struct TileMath {
     for (int j = 0; j < NJ; ++j) {
       const int rb = PHASE == 1 ? (j < NJ / 2 ? 0 : BN / 2) + (BN / 2 / WN) * wn + 32 * (j % (NJ / 2))
                                 : (BN / WN) * wn + 32 * j;
-      boff[j] = C::A_BYTES + rb * kGemmRowBytes;
+      boff[j] = C::A_BYTES + (C::F8 ? (rb / 32) * 1024 : rb * kGemmRowBytes);
     }
     aoff = 32 * wm * kGemmRowBytes;
     nv = MI;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       loff[s] = l32 * kGemmRowBytes + 16 * ((2 * s + hk) ^ gemm_swz(l32));
-      loffb[s] = PKB ? (l32 / 16) * 1024 + (2 * s + hk) * 256 + (l32 % 16) * 16 : loff[s];
+      loffb[s] = C::F8 ? (l32 / 16) * 512 + (16 * s + l32 % 16) * 16 + 8 * hk
+                 : PKB ? (l32 / 16) * 1024 + (2 * s + hk) * 256 + (l32 % 16) * 16 : loff[s];
     }
   }
 
@@ -930,6 +973,29 @@ struct TileMath {
     nv = __builtin_amdgcn_readfirstlane(min(MI, max(0, (slabs - wm + WM - 1) / WM)));
   }
 
+  // FP8 weights: multiply each accumulator by its weight row's scale, from
+  // the tile's scales in LDS (TileLoader::issue_scales: phase 1 gate rows at
+  // [0, BN/2) and up rows at [BN/2, BN), phase 2 rows at [0, BN)), before the
+  // epilogue's SwiGLU or store.
+  __device__ __forceinline__ void apply_scales(const float* sc) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c0 = PHASE == 1 ? (j < NJ / 2 ? 0 : BN / 2) + (BN / 2 / WN) * wn + 32 * (j % (NJ / 2)) + 4 * hk
+                                : (BN / WN) * wn + 32 * j + 4 * hk;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(sc + c0 + 8 * q);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          acc[i][j][4 * q + 0] *= v.x;
+          acc[i][j][4 * q + 1] *= v.y;
+          acc[i][j][4 * q + 2] *= v.z;
+          acc[i][j][4 * q + 3] *= v.w;
+        }
+      }
+    }
+  }
+
   template <int NV>
   __device__ __forceinline__ void kstep_n(const uint8_t* st) {
     if constexpr (NV == 0) return;                // no valid rows: nothing to read or multiply
@@ -940,7 +1006,15 @@ struct TileMath {
       for (int i = 0; i < NV; ++i)
         af[i] = *reinterpret_cast<const bf16x8*>(st + aoff + 32 * WM * i * kGemmRowBytes + loff[s]);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(st + boff[j] + loffb[s]);
+      for (int j = 0; j < NJ; ++j) {
+        if constexpr (C::F8) {
+          // eight codes of this lane's weight row, converted exactly to bf16
+          const uint2 c = *reinterpret_cast<const uint2*>(st + boff[j] + loffb[s]);
+          bf[j] = fp8x8_to_bf16(c.x, c.y);
+        } else {
+          bf[j] = *reinterpret_cast<const bf16x8*>(st + boff[j] + loffb[s]);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < NV; ++i)
 #pragma unroll
@@ -1101,10 +1175,15 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_bf16(
 // items' K-steps as one stream through the ring, so the next tile's first
 // K-steps load while the current tile finishes and stores: no per-tile
 // prologue bubble, no block launch per tile.
+// With C::F8, W0 / W1 point to E4M3 codes packed by pack_fp8_codes and S0 /
+// S1 to their row scales ([E+S][Ncols] fp32; S0 for the gate or down rows,
+// S1 for the up rows); the scales multiply the accumulators before the
+// epilogue.
 template <int PHASE, class C, bool PKB>
 __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_bf16(
     const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-    int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
+    int Ncols, PlanArgs plan, uint16_t* __restrict__ out, const float* __restrict__ S0,
+    const float* __restrict__ S1) {
   constexpr int NT = C::NT, STAGES = C::STAGES, BM = C::BM;
   constexpr int GPT = (kMaxGroups + NT - 1) / NT;
   constexpr int OUTC = PHASE == 1 ? C::BN / 2 : C::BN;
@@ -1117,6 +1196,8 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_b
   uint8_t* wst = dyn_lds + C::RING + (threadIdx.x >> 6) * kEpiBytes;   // this wave's epilogue block
   int* fu = reinterpret_cast<int*>(dyn_lds + C::RING + C::NW * kEpiBytes);
   int* gl = fu + plan.G + 1;
+  // C::F8: two 1 KiB scale buffers (tile parity) after the ring and the epilogue blocks
+  __shared__ __attribute__((aligned(16))) float scl[C::F8 ? 2 * 256 : 1];
   __shared__ int wsum[NT / kWave];
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
   if (tid == 0 && blockIdx.x == 0 && plan.diag) *plan.diag = 0;
@@ -1213,7 +1294,14 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_b
   TileLoader<PHASE, C, PKB> ld;
   int ir = 0, ikt = 0, islot = 0;
   auto issue_next = [&]() {
-    if (ikt == 0) ld.init(A, plan.arows, plan.n_x, K, W0, W1, Ncols, decode(ir));
+    if (ikt == 0) {
+      ld.init(A, plan.arows, plan.n_x, K, W0, W1, Ncols, decode(ir), S0, S1);
+      // one wave loads the tile's scales; its extra load only makes its later
+      // waits stricter, and the barrier after the wait that covers it makes
+      // the scales visible to every wave long before the epilogue
+      if constexpr (C::F8)
+        if (w == 0) ld.issue_scales(lds_address(reinterpret_cast<const uint8_t*>(scl + (ir & 1) * 256)));
+    }
     ld.issue(ikt, islot, lds0);
     islot = islot + 1 == STAGES ? 0 : islot + 1;
     if (++ikt == nk) {
@@ -1244,6 +1332,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_persistent_b
         cslot = cslot + 1 == STAGES ? 0 : cslot + 1;
       }
     });
+    if constexpr (C::F8) mm.apply_scales(scl + (cr & 1) * 256);
     mm.store_staged(cur, Ncols, out, wst);
   }
 }
@@ -1711,9 +1800,10 @@ void launch_gemm_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, u
   } else {
     const size_t lds = C::RING + C::NW * kEpiBytes + 8 * static_cast<size_t>(plan.G + 1);
     hipLaunchKernelGGL((ffn_gemm_persistent_bf16<1, C, PKB>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, x, a.d, wg,
-                       wu, a.I, plan, abuf);
+                       wu, a.I, plan, abuf, static_cast<const float*>(nullptr), static_cast<const float*>(nullptr));
     hipLaunchKernelGGL((ffn_gemm_persistent_bf16<2, C, PKB>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, abuf, a.I,
-                       wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, h);
+                       wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, h, static_cast<const float*>(nullptr),
+                       static_cast<const float*>(nullptr));
   }
 }
 
@@ -1783,6 +1873,40 @@ size_t ffn_fp8w_workspace_bytes(int n_rows, int I) {
   return (static_cast<size_t>(n_rows) * I * 2 + 255) / 256 * 256 + 256;
 }
 
+// FP8 codes on the 256 x 256 persistent GEMM (both phases), for batches whose
+// groups average more than kFp8GemmMinAvg rows and whose codes are packed.
+constexpr int kFp8GemmMinAvg = 48;
+
+void launch_gemm_fp8w(const FfnArgs& a, const PlanArgs& plan0, uint16_t* abuf, hipStream_t stream) {
+  using C = GemmLargeF8;
+  PlanArgs plan = plan0;
+  plan.BM = C::BM;
+  plan.max_tiles = (a.n_rows + C::BM - 1) / C::BM + plan.G;
+  PlanArgs plan2 = plan;
+  plan2.diag = nullptr;
+  plan2.arows = nullptr;
+  const size_t lds = C::RING + C::NW * kEpiBytes + 8 * static_cast<size_t>(plan.G + 1);
+  // the kernel reads the codes through its weight pointers as bytes
+  const uint16_t* wg = static_cast<const uint16_t*>(a.w_gate);
+  const uint16_t* wu = static_cast<const uint16_t*>(a.w_up);
+  const uint16_t* wd = static_cast<const uint16_t*>(a.w_down);
+  hipLaunchKernelGGL((ffn_gemm_persistent_bf16<1, C, false>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream,
+                     static_cast<const uint16_t*>(a.x_sorted), a.d, wg, wu, a.I, plan, abuf, a.s_gate, a.s_up);
+  hipLaunchKernelGGL((ffn_gemm_persistent_bf16<2, C, false>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, abuf, a.I,
+                     wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted),
+                     a.s_down, static_cast<const float*>(nullptr));
+}
+
+// Needs K >= 128 in both phases (at least four K-steps per tile: a tile's
+// scale buffer is refilled only after the tile after it has started) and
+// 16-byte aligned scales (they are copied to LDS in 16-byte pieces).
+bool fp8w_uses_gemm(int n_rows, int G, int d, int I, bool packed, const void* s_gate, const void* s_up,
+                    const void* s_down) {
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  return packed && d % 64 == 0 && I % 64 == 0 && d >= 128 && I >= 128 && al16(s_gate) && al16(s_up) &&
+         al16(s_down) && (G > 0 ? n_rows / G : n_rows) > kFp8GemmMinAvg;
+}
+
 hipError_t launch_ffn_fp8w(const FfnArgs& a, void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   const size_t total = ffn_fp8w_workspace_bytes(a.n_rows, a.I);
@@ -1800,6 +1924,10 @@ hipError_t launch_ffn_fp8w(const FfnArgs& a, void* workspace, hipStream_t stream
   plan.arows = a.x_rows;
   plan.n_x = a.n_x;
   uint16_t* abuf = reinterpret_cast<uint16_t*>(ws);
+  if (fp8w_uses_gemm(a.n_rows, G, a.d, a.I, a.packed, a.s_gate, a.s_up, a.s_down)) {
+    launch_gemm_fp8w(a, plan, abuf, stream);
+    return hipGetLastError();
+  }
   if (a.packed) {
     switch (mf) {
       case 1: launch_decode_fp8w<1, true>(a, plan.max_tiles, plan, abuf, stream); break;

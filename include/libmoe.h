@@ -378,13 +378,15 @@ moe_status moe_grouped_ffn_packed(const void* x_sorted, const int32_t* x_rows, i
  *   Weight row r of expert e is fp8(w[e][r][:]) * s[e][r].  E4M3 values are
  *   exact in bf16; products accumulate in fp32 and the scale multiplies the
  *   accumulated row product.  Runs on the decode-shaped kernel (any group
- *   sizes; meant for decode-sized groups).
+ *   sizes; meant for decode-sized groups; moe_grouped_ffn_fp8w_packed runs
+ *   prefill-sized batches on a GEMM).
  *   Requires d and I multiples of 16, nseg == 1; every pointer 16-byte
  *   aligned.
  *   Errors: MOE_ERR_UNSUPPORTED when d or I is not a multiple of 16, E > 512
- *   or nseg == 2 (a priority segment: refused, because one run with FP8
- *   weights on a GPT-OSS-shaped mixed batch, d = I = 2880 with a priority
- *   segment, ended in a GPU memory fault whose cause has not been found);
+ *   or nseg == 2 (a priority segment: refused, because two benchmark runs
+ *   with FP8 weights on a GPT-OSS-shaped mixed batch, d = I = 2880 with a
+ *   priority segment, ended in a GPU memory fault, one with each FP8 FFN
+ *   kernel, whose cause has not been found);
  *   MOE_ERR_INVALID_ARG for nseg outside {1, 2}, a NULL required
  *   pointer (the three scale arrays included) or a misaligned one;
  *   MOE_ERR_WORKSPACE for a workspace below the queried size.  The workspace
@@ -410,8 +412,14 @@ moe_status moe_grouped_ffn_fp8w(const void* x_sorted, const int32_t* x_rows, int
  *   (r / 16, k / 64) at byte offset ((r / 16) * (K / 64) + k / 64) * 1024 of
  *   the expert's matrix, and C[r][k] at (((k % 64) / 16) * 16 + r % 16) * 16 +
  *   k % 16 inside it.  Each expert's matrix keeps its R * K bytes at the same
- *   place as in the unpacked array; the scales are unchanged.  The results
- *   equal moe_grouped_ffn_fp8w's on the unpacked codes bit for bit.
+ *   place as in the unpacked array; the scales are unchanged.
+ *   Batches whose groups average at most 48 rows run on the decode-shaped
+ *   kernel and equal moe_grouped_ffn_fp8w's results on the unpacked codes bit
+ *   for bit.  Larger groups, with d and I at least 128 and 16-byte aligned
+ *   scale arrays, run both phases on a 256 x 256 LDS-tiled GEMM that converts
+ *   the codes to bf16 as it reads them (exact) and applies the row scales to
+ *   the fp32 sums; its results differ from the decode-shaped kernel's only in
+ *   the order of the fp32 sums.
  *   Requires d and I multiples of 64 (MOE_ERR_UNSUPPORTED otherwise).
  */
 moe_status moe_grouped_ffn_fp8w_packed(const void* x_sorted, const int32_t* x_rows, int32_t n_x,

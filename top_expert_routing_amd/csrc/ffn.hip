@@ -5,17 +5,18 @@
 // weights of every distinct expert the batch selected - and only those.
 //
 // Work is cut into tiles (group, block of rows, block of output columns).  The
-// tile list is built on the device from group_offsets (empty groups give no
-// tiles, so unused experts' weights are never read), then two launches run
-// the phases:
+// tiles are enumerated on the device from group_offsets (empty groups give no
+// tiles, so unused experts' weights are never read) and run the two phases:
 //   phase 1  a[n][i] = silu(xs[n] . W_gate[e][i]) * (xs[n] . W_up[e][i])  -> bf16
 //   phase 2  h[n][o] = a[n] . W_down[e][o]
-// Both are C = A B^T with A and B contiguous along K, which is exactly the
-// operand layout of v_mfma_f32_16x16x32_bf16: each lane holds 8 consecutive K
-// values of one row of A and of one row of B.  The token rows (A) of a tile
-// are staged in LDS and shared by the four waves; the weight rows (B) are
-// used by exactly one wave, so they stream straight from HBM into registers
-// with 16-byte loads and no LDS round trip.
+// either as two launches, or (mixed batches with a priority segment) in one
+// persistent launch whose phase-2 tiles wait for their rows' phase-1 tiles.
+// Both phases are C = A B^T with A and B contiguous along K, the operand
+// layout of the bf16 MFMAs: each lane holds 8 consecutive K values of one row
+// of A and of one row of B.  Decode-sized tiles stage the few token rows (A)
+// in LDS and stream the weight rows (B), each used by one wave, straight from
+// HBM into registers; prefill-sized tiles bring both operands into an LDS
+// ring with LDS-DMA loads.
 #include <stdlib.h>
 
 #include <type_traits>

@@ -523,8 +523,15 @@ def main():
     roof["hbm_frac"] = round(ffn_bytes / ffn_s / 1e9 / PEAK_HBM_GBS, 4)
     roof["mfma_frac"] = round(ffn_flops / ffn_s / 1e12 / peak_flops, 4)
 
-    signature = signature_recording(s, stats_ids, wl.req_offsets, stream, K, dev,
-                                    wl.stats_logits.contiguous()) if args.signature else None
+    signature = None
+    if args.signature:
+        # the recorded layers' logits; layer 0 is the routing layer, whose gate
+        # read the router's logits when the router runs in front
+        rec_logits = wl.stats_logits.contiguous()
+        if layer.logits is not None:
+            rec_logits = rec_logits.clone()
+            rec_logits[0].copy_(layer.logits)
+        signature = signature_recording(s, stats_ids, wl.req_offsets, stream, K, dev, rec_logits)
     dseg = decode_segment(layer, wl, s, dev, expert_bytes, packed) if queue else None
 
     tokens_per_s = s.T * K / elapsed

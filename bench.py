@@ -361,13 +361,6 @@ def main():
     packed = packable and not args.unpacked_weights
     # FP8 codes are packed too when d and I are multiples of 64
     fp8_packed = fp8 and s.d % 64 == 0 and s.I % 64 == 0 and not args.unpacked_weights
-    if fp8 and s.n_priority > 0:
-        # the library refuses FP8 weights with a priority segment: two runs of
-        # this benchmark on the GPT-OSS-shaped batch ended in a GPU memory fault
-        # (once with each FP8 FFN kernel), cause not found
-        print("--fp8-weights: the library refuses FP8 expert weights with a priority segment "
-              "(MOE_ERR_UNSUPPORTED)", file=sys.stderr)
-        sys.exit(2)
     # expert weight bytes (fp8: codes plus one fp32 scale per weight row)
     expert_bytes = 3 * s.d * s.I + (2 * s.I + s.d) * 4 if fp8 else 3 * s.d * s.I * esize
     all_w = (s.E + s.S) * expert_bytes
@@ -430,6 +423,13 @@ def main():
             if ev is not None:
                 ev[j][1].record(stream)
 
+    # Everything above ran on the default stream and returned before the GPU
+    # finished: the weight preparation frees large temporaries whose kernels are
+    # still queued, and the layer's buffers may reuse that memory.  The steps run
+    # on `stream`, which is not ordered after those kernels, so wait for them
+    # here (otherwise a late write of a freed temporary can land in the layer's
+    # index buffers while the steps use them).
+    torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             step(i)

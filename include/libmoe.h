@@ -380,13 +380,9 @@ moe_status moe_grouped_ffn_packed(const void* x_sorted, const int32_t* x_rows, i
  *   accumulated row product.  Runs on the decode-shaped kernel (any group
  *   sizes; meant for decode-sized groups; moe_grouped_ffn_fp8w_packed runs
  *   prefill-sized batches on a GEMM).
- *   Requires d and I multiples of 16, nseg == 1; every pointer 16-byte
- *   aligned.
- *   Errors: MOE_ERR_UNSUPPORTED when d or I is not a multiple of 16, E > 512
- *   or nseg == 2 (a priority segment: refused, because two benchmark runs
- *   with FP8 weights on a GPT-OSS-shaped mixed batch, d = I = 2880 with a
- *   priority segment, ended in a GPU memory fault, one with each FP8 FFN
- *   kernel, whose cause has not been found);
+ *   Requires d and I multiples of 16; every pointer 16-byte aligned.
+ *   Errors: MOE_ERR_UNSUPPORTED when d or I is not a multiple of 16 or
+ *   E > 512;
  *   MOE_ERR_INVALID_ARG for nseg outside {1, 2}, a NULL required
  *   pointer (the three scale arrays included) or a misaligned one;
  *   MOE_ERR_WORKSPACE for a workspace below the queried size.  The workspace

@@ -87,7 +87,7 @@ def test_ffn_fp8w_validation_and_query(lib):
     assert f(*args(a8=264)) == UNS                                 # d not a multiple of 16
     assert f(*args(a9=520)) == UNS                                 # I not a multiple of 16
     assert f(*args(a7=3)) == INV                                   # nseg
-    assert f(*args(a7=2)) == UNS                                   # a priority segment is refused
+    assert f(*args(a7=2)) == 0                                     # a priority segment: same query
     assert f(*args(a5=513)) == UNS                                 # E > 512
     small = ctypes.c_size_t(16)
     assert f(*args(a17=FAKE, a18=ctypes.byref(small))) == WS       # workspace too small
@@ -98,8 +98,8 @@ def test_ffn_fp8w_validation_and_query(lib):
     assert fp(*args()) == 0                                        # d = 256, I = 512: multiples of 64
     assert fp(*args(a8=272)) == UNS                                # d a multiple of 16 but not of 64
     assert fp(*args(a9=528)) == UNS                                # I a multiple of 16 but not of 64
-    assert fp(*args(a7=2)) == UNS                                  # a priority segment is refused
-    assert fp(*args(a7=2, a4=8192)) == UNS                         # ... also at GEMM sizes
+    assert fp(*args(a7=2)) == 0                                    # a priority segment, decode-sized groups
+    assert fp(*args(a7=2, a4=8192)) == 0                           # ... and GEMM-sized ones
 
 
 def test_ffn_packed_validation_and_query(lib):

@@ -35,6 +35,7 @@ def test_graph_replays_match_eager(name):
     x = wl.x.clone()
     stream = torch.cuda.Stream()
     side = torch.cuda.Stream()
+    torch.cuda.synchronize()      # the default stream's set-up is done before `stream` uses its buffers
     with torch.cuda.stream(stream):
         layer.forward(logits, x, stats_ids, stats_stream=side)     # warm-up, allocates stats outputs
     torch.cuda.synchronize()

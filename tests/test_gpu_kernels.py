@@ -666,7 +666,8 @@ FP8_GEMM_CASES = [
     (2048, 16, 4, 0, 0, 512, 256, "random"),   # ~512 rows per expert: two full m-tiles each
     (1500, 8, 3, 1, 0, 192, 448, "random"),    # a shared expert of 1500 rows, K = 192 (three code blocks)
     (3000, 32, 2, 0, 0, 128, 128, "zipf"),     # one hot expert, many nearly empty ones
-    (600, 8, 2, 0, 50, 256, 320, "random"),    # a priority segment: refused (see below)
+    (600, 8, 2, 0, 50, 256, 320, "random"),    # a priority segment (its groups are tiles of their own)
+    (2000, 64, 4, 2, 300, 128, 192, "zipf"),   # priority segment, two shared experts, Zipf routing
 ]
 
 
@@ -680,18 +681,6 @@ def test_grouped_ffn_fp8w_gemm_parity(T, E, k, S, P, d, I, kind):
     nseg = 2 if P > 0 else 1
     q = [moe.quantize_fp8_rows(w) for w in (wl.w_gate, wl.w_up, wl.w_down)]
     p_ref = O.permute(ids.numpy(), E, S, P, np_of(wl.x))
-    if nseg == 2:
-        # FP8 weights with a priority segment are refused before anything is
-        # enqueued (two GPU memory faults of FP8 benchmark runs on the
-        # GPT-OSS-shaped batch, cause not found)
-        offs = torch.from_numpy(p_ref["group_offsets"]).to(DEV)
-        codes = [moe.pack_fp8_codes(c.to(DEV)) if i % 2 == 0 else c.to(DEV)
-                 for i, c in enumerate(t for pair in q for t in pair)]
-        with pytest.raises(moe.MoeError) as ei:
-            moe.grouped_ffn_fp8w(wl.x.to(DEV), offs, E, S, nseg, *codes,
-                                 x_rows=torch.from_numpy(p_ref["sorted_token"]).to(DEV), packed=True)
-        assert ei.value.status == 2          # MOE_ERR_UNSUPPORTED
-        return
     h_ref = O.grouped_ffn_fp8w(p_ref["x_sorted"], p_ref["group_offsets"], E, S, nseg, q[0][0].numpy(),
                                q[0][1].numpy(), q[1][0].numpy(), q[1][1].numpy(), q[2][0].numpy(), q[2][1].numpy(),
                                "bf16")
@@ -728,15 +717,6 @@ def test_grouped_ffn_fp8w_parity(T, E, k, S, P, d, I, kind):
     qu, su = moe.quantize_fp8_rows(wl.w_up)
     qd, sd = moe.quantize_fp8_rows(wl.w_down)
     p_ref = O.permute(ids.numpy(), E, S, P, np_of(wl.x))
-    if nseg == 2:
-        # a priority segment is refused before anything is enqueued (an
-        # unexplained GPU memory fault on a GPT-OSS-shaped FP8 batch)
-        offs = torch.from_numpy(p_ref["group_offsets"]).to(DEV)
-        with pytest.raises(moe.MoeError) as ei:
-            moe.grouped_ffn_fp8w(wl.x.to(DEV), offs, E, S, nseg, qg.to(DEV), sg.to(DEV), qu.to(DEV), su.to(DEV),
-                                 qd.to(DEV), sd.to(DEV), x_rows=torch.from_numpy(p_ref["sorted_token"]).to(DEV))
-        assert ei.value.status == 2          # MOE_ERR_UNSUPPORTED
-        return
     h_ref = O.grouped_ffn_fp8w(p_ref["x_sorted"], p_ref["group_offsets"], E, S, nseg, qg.numpy(), sg.numpy(),
                                qu.numpy(), su.numpy(), qd.numpy(), sd.numpy(), "bf16")
     xs = torch.from_numpy(p_ref["x_sorted"].view(np.int16)).view(torch.bfloat16).to(DEV)
@@ -753,13 +733,18 @@ def test_grouped_ffn_fp8w_parity(T, E, k, S, P, d, I, kind):
     torch.cuda.synchronize()
     assert torch.equal(h2, h)
     if d % 64 == 0 and I % 64 == 0:
-        # pre-packed codes: the same products in the same order, so the same bits
         h3 = moe.grouped_ffn_fp8w(wl.x.to(DEV), offs, E, S, nseg, moe.pack_fp8_codes(qg.to(DEV)), sg.to(DEV),
                                   moe.pack_fp8_codes(qu.to(DEV)), su.to(DEV), moe.pack_fp8_codes(qd.to(DEV)),
                                   sd.to(DEV), h_sorted=_poison((xs.shape[0], d), torch.bfloat16), x_rows=rows,
                                   packed=True)
         torch.cuda.synchronize()
-        assert torch.equal(h3, h)
+        G = nseg * E + S
+        if xs.shape[0] // G > 48 and d >= 128 and I >= 128:
+            # prefill-sized groups on packed codes run on the FP8 GEMM: other sum order
+            assert rel_max_err(f64_of(h3), h_ref) <= TOL["bf16"]
+        else:
+            # pre-packed codes on the same kernel: the same products in the same order, so the same bits
+            assert torch.equal(h3, h)
 
 
 def test_ffn_bindings_reject_mismatched_shapes():

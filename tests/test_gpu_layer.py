@@ -157,9 +157,7 @@ def test_layer_with_router_parity(name):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["qwen3_prefill", pytest.param("gptoss_mixed", marks=pytest.mark.skip(
-    reason="FP8 weights with a priority segment are refused: a benchmark run on this shape faulted the GPU "
-           "(cause not found)"))])
+@pytest.mark.parametrize("name", ["qwen3_prefill", "gptoss_mixed"])
 def test_layer_fp8_gemm_parity(name):
     """The prefill-sized layer on pre-packed FP8 codes, which runs the FFN on
     the GEMM kernel: every sorted row of h and every token of y within the bf16

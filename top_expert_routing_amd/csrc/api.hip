@@ -71,12 +71,6 @@ moe_status ffn_fp8w_call(bool packed, const void* x_sorted, const int32_t* x_row
   if (n_rows < 0 || E < 1 || n_shared < 0 || (nseg != 1 && nseg != 2) || d < 1 || I < 1)
     return MOE_ERR_INVALID_ARG;
   if (E > MOE_MAX_EXPERTS || n_shared > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
-  // A priority segment is refused.  Two benchmark runs with FP8 weights on a
-  // GPT-OSS-shaped mixed batch (d = I = 2880, priority segment) ended in a GPU
-  // memory fault, one with the FFN on the decode-shaped FP8 kernel and one on
-  // the FP8 GEMM, although the FP8 GEMM passed full-row parity on that shape in
-  // a layer test; the cause has not been found.
-  if (nseg == 2) return MOE_ERR_UNSUPPORTED;
   if (d % 16 != 0 || I % 16 != 0) return MOE_ERR_UNSUPPORTED;
   if (packed && (d % 64 != 0 || I % 64 != 0)) return MOE_ERR_UNSUPPORTED;
   if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))

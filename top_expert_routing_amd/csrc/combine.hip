@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
       wt[jj] = 0.0f;
       if (j < nrow) {
         const int flat = j < k ? t * k + j : T * k + (j - k) * T + t;
-        row[jj] = f2s[flat];
+        row[jj] = min(max(f2s[flat], 0), nrow * T - 1);   // a bad entry stays inside h
         wt[jj] = j < k ? w[static_cast<size_t>(t) * k + j] : 1.0f;
       }
     }

@@ -68,7 +68,7 @@ struct PlanArgs {
 struct CombineArgs {
   const int* s2f;
   const float* topk_w;
-  int T, k;
+  int T, k, n;        // n = T * (k + shared experts) sorted rows
   float* y32;         // [T][d] fp32, zero before the down projection
 };
 
@@ -86,7 +86,7 @@ __device__ __forceinline__ float bf16_rne(float v) {
 // Adds the four columns n..n+3 of sorted row `row` (bf16-rounded, times its
 // gate weight) into its token's row of the combine sums.
 __device__ __forceinline__ void combine_add4(const CombineArgs& c, int row, int Ncols, int n, const float (&v)[4]) {
-  const int f = c.s2f[row];
+  const int f = min(max(c.s2f[row], 0), c.n - 1);     // a bad entry stays inside y32
   const int tk = c.T * c.k;
   const int tok = f < tk ? f / c.k : (f - tk) % c.T;
   const float w = f < tk ? c.topk_w[f] : 1.0f;
@@ -1733,7 +1733,7 @@ PlanArgs phase1_plan(const FfnArgs& a, const PlanArgs& plan) {
   return p;
 }
 
-CombineArgs combine_args(const FfnArgs& a) { return CombineArgs{a.s2f, a.topk_w, a.T, a.k, a.y32}; }
+CombineArgs combine_args(const FfnArgs& a) { return CombineArgs{a.s2f, a.topk_w, a.T, a.k, a.n_rows, a.y32}; }
 
 template <bool PK>
 void launch_decode_splitk_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, uint16_t* abuf,

@@ -753,6 +753,8 @@ using GemmSmall = GemmCfg<2, 4, 2, 2, 3, 2>;   // 128 x 256
 using GemmLarge = GemmCfg<2, 4, 4, 2, 4, 1>;   // 256 x 256
 // 256 x 256 on FP8 codes: a stage is 24 KiB, so five fit (four K-steps in flight)
 using GemmLargeF8 = GemmCfg<2, 4, 4, 2, 5, 1, true>;
+// 128 x 256 on FP8 codes: a stage is 16 KiB, four per block, two blocks per CU
+using GemmSmallF8 = GemmCfg<2, 4, 2, 2, 4, 2, true>;
 constexpr int kGemmLargeMinAvg = 256;
 
 __device__ __forceinline__ int gemm_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
@@ -1114,21 +1116,30 @@ __device__ __forceinline__ uint32_t lds_address(const uint8_t* smem) {
 
 // One tile: the it.rows sorted rows it.row(0..) of A against output column chunk
 // `it.chunk` of expert `it.expert`.  `smem` is the block's operand ring, free
-// on entry (no wave still reads it).
+// on entry (no wave still reads it).  C::F8: W0 / W1 hold packed E4M3 codes,
+// S0 / S1 their row scales, and `scl` is 1 KiB of LDS for the tile's scales
+// (free on entry too).
 template <int PHASE, class C, bool COHERENT = false, bool PKB = false>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const int* __restrict__ arows, int n_x,
                                           int K, const uint16_t* __restrict__ W0,
                                           const uint16_t* __restrict__ W1, int Ncols, const Item& it,
-                                          uint16_t* __restrict__ out, uint8_t* smem) {
+                                          uint16_t* __restrict__ out, uint8_t* smem,
+                                          const float* __restrict__ S0 = nullptr,
+                                          const float* __restrict__ S1 = nullptr, float* scl = nullptr) {
   constexpr int STAGES = C::STAGES;
   TileLoader<PHASE, C, PKB> ld;
-  ld.init(A, arows, n_x, K, W0, W1, Ncols, it);
+  ld.init(A, arows, n_x, K, W0, W1, Ncols, it, S0, S1);
   TileMath<PHASE, C, PKB> mm;
   mm.init();
   mm.set_rows(it.rows);
   mm.zero();
   const uint32_t lds0 = lds_address(smem);
   const int nk = K / kGemmBK;
+  // C::F8: wave 0 loads the tile's scales first; its extra load only makes its
+  // waits stricter, and the first K-step's wait and barrier make the scales
+  // visible to every wave
+  if constexpr (C::F8)
+    if ((threadIdx.x >> 6) == 0) ld.issue_scales(lds_address(reinterpret_cast<const uint8_t*>(scl)));
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nk) ld.template issue<true>(s, s, lds0);
@@ -1150,6 +1161,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const 
   if (ld.na == C::ADMA) loop(Int<C::ADMA>{});
   else if (ld.na == 1) loop(Int<1>{});
   else loop(Int<0>{});
+  if constexpr (C::F8) mm.apply_scales(scl);
   mm.template store<COHERENT>(it, Ncols, out);
 }
 
@@ -1158,12 +1170,14 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A, const 
 template <int PHASE, class C, bool PKB>
 __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-    int Ncols, PlanArgs plan, uint16_t* __restrict__ out) {
+    int Ncols, PlanArgs plan, uint16_t* __restrict__ out, const float* __restrict__ S0,
+    const float* __restrict__ S1) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::RING];
+  __shared__ __attribute__((aligned(16))) float scl[C::F8 ? 256 : 1];
   constexpr int OUTC = PHASE == 1 ? C::BN / 2 : C::BN;
   const Item it = block_find_item<C::NT>(plan, (Ncols + OUTC - 1) / OUTC);
   if (it.rows == 0) return;
-  gemm_tile<PHASE, C, false, PKB>(A, plan.arows, plan.n_x, K, W0, W1, Ncols, it, out, smem);
+  gemm_tile<PHASE, C, false, PKB>(A, plan.arows, plan.n_x, K, W0, W1, Ncols, it, out, smem, S0, S1, scl);
 }
 
 // ---- persistent GEMM launch: each block walks a list of tiles ----------------
@@ -1795,9 +1809,10 @@ void launch_gemm_bf16(const FfnArgs& a, const Layout& L, const PlanArgs& plan, u
   uint16_t* h = static_cast<uint16_t*>(a.h_sorted);
   if constexpr (C::BLOCKS_PER_CU > 1) {
     hipLaunchKernelGGL((ffn_gemm_bf16<1, C, PKB>), dim3(item_grid(L.max_tiles, nch1)), dim3(C::NT), 0, stream, x, a.d, wg,
-                       wu, a.I, plan, abuf);
+                       wu, a.I, plan, abuf, static_cast<const float*>(nullptr), static_cast<const float*>(nullptr));
     hipLaunchKernelGGL((ffn_gemm_bf16<2, C, PKB>), dim3(item_grid(L.max_tiles, nch2)), dim3(C::NT), 0, stream, abuf, a.I,
-                       wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, h);
+                       wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, h, static_cast<const float*>(nullptr),
+                       static_cast<const float*>(nullptr));
   } else {
     const size_t lds = C::RING + C::NW * kEpiBytes + 8 * static_cast<size_t>(plan.G + 1);
     hipLaunchKernelGGL((ffn_gemm_persistent_bf16<1, C, PKB>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, x, a.d, wg,
@@ -1878,24 +1893,41 @@ size_t ffn_fp8w_workspace_bytes(int n_rows, int I) {
 // groups average more than kFp8GemmMinAvg rows and whose codes are packed.
 constexpr int kFp8GemmMinAvg = 48;
 
+// Groups averaging kGemmLargeMinAvg rows or more: the persistent 256 x 256
+// kernel; smaller ones: one 128 x 256 tile per block, two blocks per CU.
 void launch_gemm_fp8w(const FfnArgs& a, const PlanArgs& plan0, uint16_t* abuf, hipStream_t stream) {
-  using C = GemmLargeF8;
+  const int avg = plan0.G > 0 ? a.n_rows / plan0.G : a.n_rows;
+  const bool large = avg >= kGemmLargeMinAvg;
+  const int BM = large ? GemmLargeF8::BM : GemmSmallF8::BM;
   PlanArgs plan = plan0;
-  plan.BM = C::BM;
-  plan.max_tiles = (a.n_rows + C::BM - 1) / C::BM + plan.G;
+  plan.BM = BM;
+  plan.max_tiles = (a.n_rows + BM - 1) / BM + plan.G;
   PlanArgs plan2 = plan;
   plan2.diag = nullptr;
   plan2.arows = nullptr;
-  const size_t lds = C::RING + C::NW * kEpiBytes + 8 * static_cast<size_t>(plan.G + 1);
-  // the kernel reads the codes through its weight pointers as bytes
+  // the kernels read the codes through their weight pointers as bytes
+  const uint16_t* x = static_cast<const uint16_t*>(a.x_sorted);
   const uint16_t* wg = static_cast<const uint16_t*>(a.w_gate);
   const uint16_t* wu = static_cast<const uint16_t*>(a.w_up);
   const uint16_t* wd = static_cast<const uint16_t*>(a.w_down);
-  hipLaunchKernelGGL((ffn_gemm_persistent_bf16<1, C, false>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream,
-                     static_cast<const uint16_t*>(a.x_sorted), a.d, wg, wu, a.I, plan, abuf, a.s_gate, a.s_up);
-  hipLaunchKernelGGL((ffn_gemm_persistent_bf16<2, C, false>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, abuf, a.I,
-                     wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, static_cast<uint16_t*>(a.h_sorted),
-                     a.s_down, static_cast<const float*>(nullptr));
+  uint16_t* h = static_cast<uint16_t*>(a.h_sorted);
+  if (large) {
+    using C = GemmLargeF8;
+    const size_t lds = C::RING + C::NW * kEpiBytes + 8 * static_cast<size_t>(plan.G + 1);
+    hipLaunchKernelGGL((ffn_gemm_persistent_bf16<1, C, false>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, x,
+                       a.d, wg, wu, a.I, plan, abuf, a.s_gate, a.s_up);
+    hipLaunchKernelGGL((ffn_gemm_persistent_bf16<2, C, false>), dim3(gemm_grid<C>()), dim3(C::NT), lds, stream, abuf,
+                       a.I, wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, h, a.s_down,
+                       static_cast<const float*>(nullptr));
+  } else {
+    using C = GemmSmallF8;
+    const int nch1 = (a.I + C::BN / 2 - 1) / (C::BN / 2), nch2 = (a.d + C::BN - 1) / C::BN;
+    hipLaunchKernelGGL((ffn_gemm_bf16<1, C, false>), dim3(item_grid(plan.max_tiles, nch1)), dim3(C::NT), 0, stream, x,
+                       a.d, wg, wu, a.I, plan, abuf, a.s_gate, a.s_up);
+    hipLaunchKernelGGL((ffn_gemm_bf16<2, C, false>), dim3(item_grid(plan.max_tiles, nch2)), dim3(C::NT), 0, stream,
+                       abuf, a.I, wd, static_cast<const uint16_t*>(nullptr), a.d, plan2, h, a.s_down,
+                       static_cast<const float*>(nullptr));
+  }
 }
 
 // Needs K >= 128 in both phases (at least four K-steps per tile: a tile's

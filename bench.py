@@ -508,8 +508,12 @@ def main():
     # the committed counters are for the default mode of each workload
     traffic = None if fp8 or args.unpacked_weights or args.fused_combine else traffic_for(args.workload)
     roof["traffic"] = None if traffic is None else round(traffic)
-    queue = (not fp8 and s.dtype == "bf16" and s.n_priority > 0 and s.d % 32 == 0 and
-             s.I % 32 == 0 and s.N // s.G > 48 and os.environ.get("LIBMOE_FFN_QUEUE", "1") != "0")
+    # the library's path choice for batches with a priority segment: bf16
+    # prefill-sized groups, or packed FP8 codes on 128-row GEMM tiles
+    avg = s.N // s.G
+    queue = (s.n_priority > 0 and os.environ.get("LIBMOE_FFN_QUEUE", "1") != "0" and
+             ((not fp8 and s.dtype == "bf16" and s.d % 32 == 0 and s.I % 32 == 0 and avg > 48) or
+              (fp8_packed and s.d >= 128 and s.I >= 128 and 48 < avg < 256)))
     roof["kernel"] = (f"{ffn_name} (" + ("one persistent launch: decode-priority tile queues" if queue else
                                          "gate/up launch + down launch with the combine in its epilogue + "
                                          "conversion launch" if args.fused_combine else

@@ -690,7 +690,7 @@ def test_grouped_ffn_fp8w_gemm_parity(T, E, k, S, P, d, I, kind):
     for c, sc in q:
         packed += [moe.pack_fp8_codes(c.to(DEV)), sc.to(DEV)]
     N = int(p_ref["group_offsets"][-1])
-    nbytes = moe.ffn_fp8w_workspace_bytes(N, I)
+    nbytes = moe.ffn_fp8w_workspace_bytes(N, I, E, S, nseg, d, packed=True)
     ws = torch.full((max(nbytes, 256),), 0x5a, dtype=torch.uint8, device=DEV)
     h = moe.grouped_ffn_fp8w(wl.x.to(DEV), offs, E, S, nseg, *packed, h_sorted=_poison((N, d), torch.bfloat16),
                              workspace=ws, x_rows=rows, packed=True)

@@ -397,12 +397,14 @@ def grouped_ffn_packed(x_sorted: torch.Tensor, group_offsets: torch.Tensor, E: i
     return h_sorted
 
 
-def ffn_fp8w_workspace_bytes(n_rows, I) -> int:
+def ffn_fp8w_workspace_bytes(n_rows, I, E=1, n_shared=0, nseg=1, d=64, packed=False) -> int:
+    """Workspace of the FP8-weight FFN (the SwiGLU intermediate, plus the
+    persistent queue's state for the batches that may run on it)."""
     lib = _lib.load()
     n = ctypes.c_size_t(0)
-    check("moe_grouped_ffn_fp8w", lib.moe_grouped_ffn_fp8w(None, None, 0, None, n_rows, 1, 0, 1, 16, I, None, None,
-                                                           None, None, None, None, None, None, ctypes.byref(n),
-                                                           None))
+    name = "moe_grouped_ffn_fp8w_packed" if packed else "moe_grouped_ffn_fp8w"
+    check(name, getattr(lib, name)(None, None, 0, None, n_rows, E, n_shared, nseg, d, I, None, None, None, None,
+                                   None, None, None, None, ctypes.byref(n), None))
     return int(n.value)
 
 
@@ -463,7 +465,8 @@ def grouped_ffn_fp8w(x: torch.Tensor, group_offsets: torch.Tensor, E: int, n_sha
     if h_sorted.shape != (n_rows, d):
         raise ValueError(f"h_sorted must be [{n_rows}][{d}]")
     if workspace is None:
-        workspace = torch.empty(max(ffn_fp8w_workspace_bytes(n_rows, I), 256), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(ffn_fp8w_workspace_bytes(n_rows, I, E, n_shared, nseg, d, packed), 256),
+                                dtype=torch.uint8, device=dev)
     lib = _lib.load()
     nbytes = ctypes.c_size_t(workspace.numel())
     name = "moe_grouped_ffn_fp8w_packed" if packed else "moe_grouped_ffn_fp8w"
@@ -614,7 +617,7 @@ class MoeLayer:
         if self.fused_combine:
             ws_bytes = ffn_combine_workspace_bytes(N, E, n_shared, self.nseg, d, I, T, k, self.packed)
         elif fp8_weights is not None:
-            ws_bytes = ffn_fp8w_workspace_bytes(N, I)
+            ws_bytes = ffn_fp8w_workspace_bytes(N, I, E, n_shared, self.nseg, d, self.packed)
         else:
             ws_bytes = ffn_workspace_bytes(N, E, n_shared, self.nseg, d, I, dtype)
         self.ffn_ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)

@@ -76,7 +76,8 @@ moe_status ffn_fp8w_call(bool packed, const void* x_sorted, const int32_t* x_row
   if (!fits_int(static_cast<long long>(n_rows) * d) || !fits_int(static_cast<long long>(n_rows) * I))
     return MOE_ERR_UNSUPPORTED;
   bool query;
-  moe_status st = workspace_check(workspace, workspace_bytes, moe::ffn_fp8w_workspace_bytes(n_rows, I), &query);
+  moe_status st = workspace_check(workspace, workspace_bytes,
+                                  moe::ffn_fp8w_workspace_bytes(n_rows, E, n_shared, nseg, d, I, packed), &query);
   if (st != MOE_OK || query) return st;
   if (n_rows == 0) return MOE_OK;
   if (!x_sorted || !group_offsets || !w_gate || !w_up || !w_down || !s_gate || !s_up || !s_down || !h_sorted)

@@ -1421,16 +1421,19 @@ struct QueueArgs {
   int* error;         // diagnostic word, set when a wait gave up
   unsigned long long* trace;   // optional per-tile records, trace_per_queue per queue
   int trace_per_queue;
+  const float* s_gate;         // FP8 codes (QC::C::F8): weight-row scales
+  const float* s_up;
+  const float* s_down;
 };
 
 __device__ __forceinline__ unsigned long long realtime() { return __builtin_amdgcn_s_memrealtime(); }
 
-// Configuration of the persistent queue kernel: 128 x 256 GEMM tiles
-// (GemmSmall's ring), two blocks per CU, row-major (PK false) or pre-packed
-// weights.
-template <bool PKV>
+// Configuration of the persistent queue kernel: 128 x 256 GEMM tiles, two
+// blocks per CU, on bf16 weights (GemmSmall's ring; row-major with PK false
+// or pre-packed) or on packed FP8 codes (GemmSmallF8).
+template <bool PKV, class CV = GemmSmall>
 struct QueueGemm {
-  using C = GemmSmall;
+  using C = CV;
   static constexpr int BPC = C::BLOCKS_PER_CU;
   static constexpr bool PK = PKV;
   static constexpr int RING = C::RING;
@@ -1453,6 +1456,7 @@ __global__ __launch_bounds__(kThreads, QC::BPC) void ffn_queue_bf16(
   int* fu = reinterpret_cast<int*>(dyn_lds + QC::RING);
   __shared__ int wsum[kWaves][NV];
   __shared__ int s_tile, s_ok;
+  __shared__ __attribute__((aligned(16))) float scl[C::F8 ? 256 : 1];   // FP8: the tile's row scales
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
   const int qi = static_cast<int>(blockIdx.x) % sh.nq;   // block b takes its tiles from queue b mod nq
 
@@ -1524,7 +1528,7 @@ __global__ __launch_bounds__(kThreads, QC::BPC) void ffn_queue_bf16(
     const Item it{tl.row0, tl.rows, tl.seq, tl.chunk, tl.split, tl.row1};
     const unsigned long long t0 = q.trace ? realtime() : 0ull;
     if (tl.phase == 1) {
-      gemm_tile<1, C, true, QC::PK>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem);
+      gemm_tile<1, C, true, QC::PK>(x, q.arows, q.n_x, d, w_gate, w_up, I, it, abuf, smem, q.s_gate, q.s_up, scl);
       // publish: every wave's agent-scope row stores have completed, then the flag
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -1562,7 +1566,7 @@ __global__ __launch_bounds__(kThreads, QC::BPC) void ffn_queue_bf16(
         __syncthreads();
         waits = s_ok != 0;
       }
-      gemm_tile<2, C, false, QC::PK>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem);
+      gemm_tile<2, C, false, QC::PK>(abuf, nullptr, 0, I, w_down, nullptr, d, it, h, smem, q.s_down, nullptr, scl);
     }
     if (q.trace && tid == 0 && t < q.trace_per_queue) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1705,8 +1709,8 @@ Layout layout(int n_rows, int E, int n_shared, int nseg, int d, int I, int bf16)
     // intermediate rows, against tiles of a few tens of microseconds.
   } else {
     // With a priority segment both phases run in one persistent launch
-    // (ffn_queue_bf16: decode-priority tile queues, stream tiles for small
-    // experts and GEMM tiles for large ones); otherwise two GEMM launches.
+    // (ffn_queue_bf16: decode-priority tile queues of GEMM tiles); otherwise
+    // two GEMM launches.
     L.path = (nseg > 1 && queue_path_requested()) ? Path::kQueue
              : avg >= kGemmLargeMinAvg                  ? Path::kGemmLarge
                                                         : Path::kGemm;
@@ -1856,6 +1860,9 @@ void launch_queue_bf16(const FfnArgs& a, const Layout& L, char* ws, hipStream_t 
   q.error = diag;
   q.trace = a.trace;
   q.trace_per_queue = a.trace ? a.trace_capacity / q.shape.nq : 0;
+  q.s_gate = a.s_gate;
+  q.s_up = a.s_up;
+  q.s_down = a.s_down;
   const size_t lds = QC::RING + 5 * static_cast<size_t>(q.shape.nseq() + 1) * sizeof(int);
   hipLaunchKernelGGL((ffn_queue_bf16<QC>), dim3(blocks), dim3(kThreads), lds, stream,
                      static_cast<const uint16_t*>(a.x_sorted), a.d, static_cast<const uint16_t*>(a.w_gate),
@@ -1884,9 +1891,33 @@ void launch_decode_fp8w(const FfnArgs& a, int max_tiles, const PlanArgs& plan, u
 
 }  // namespace
 
-size_t ffn_fp8w_workspace_bytes(int n_rows, int I) {
-  // SwiGLU intermediate [n_rows][I] bf16, then the diagnostic word at the end
-  return (static_cast<size_t>(n_rows) * I * 2 + 255) / 256 * 256 + 256;
+// FP8 workspace: the SwiGLU intermediate [n_rows][I] bf16, then (batches the
+// persistent queue may take) the queue heads and phase-1 flags, then the
+// diagnostic word at the end.  The layout depends on the shapes only; whether
+// the queue runs also needs 16-byte aligned scales (fp8w_uses_gemm).
+bool fp8w_queue_shape(int n_rows, int E, int n_shared, int nseg, int d, int I, bool packed) {
+  const int G = nseg * E + n_shared;
+  return nseg > 1 && queue_path_requested() &&
+         fp8w_uses_gemm(n_rows, G, d, I, packed, nullptr, nullptr, nullptr) &&
+         (G > 0 ? n_rows / G : n_rows) < kGemmLargeMinAvg;
+}
+
+Layout fp8w_layout(int n_rows, int E, int n_shared, int nseg, int d, int I, bool packed) {
+  Layout L{};
+  L.path = fp8w_queue_shape(n_rows, E, n_shared, nseg, d, I, packed) ? Path::kQueue : Path::kDecode;
+  L.a_off = 0;
+  L.q_off = (static_cast<size_t>(n_rows) * I * 2 + 255) / 256 * 256;
+  L.q_ints = 0;
+  if (L.path == Path::kQueue) {
+    const qplan::Shape sh = queue_shape(n_rows, E, n_shared, nseg, d, I, kMaxQueues, 0);
+    L.q_ints = static_cast<size_t>(kMaxQueues) * kQueueStride + static_cast<size_t>(queue_units_cap(sh)) * sh.nch1;
+  }
+  L.total = L.q_off + (L.q_ints * 4 + 255) / 256 * 256 + 256;
+  return L;
+}
+
+size_t ffn_fp8w_workspace_bytes(int n_rows, int E, int n_shared, int nseg, int d, int I, bool packed) {
+  return fp8w_layout(n_rows, E, n_shared, nseg, d, I, packed).total;
 }
 
 // FP8 codes on the 256 x 256 persistent GEMM (both phases), for batches whose
@@ -1942,7 +1973,8 @@ bool fp8w_uses_gemm(int n_rows, int G, int d, int I, bool packed, const void* s_
 
 hipError_t launch_ffn_fp8w(const FfnArgs& a, void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
-  const size_t total = ffn_fp8w_workspace_bytes(a.n_rows, a.I);
+  const Layout L = fp8w_layout(a.n_rows, a.E, a.n_shared, a.nseg, a.d, a.I, a.packed);
+  const size_t total = L.total;
   const int G = a.nseg * a.E + a.n_shared;
   const int mf = pick_mf(G > 0 ? a.n_rows / G : a.n_rows);
   PlanArgs plan;
@@ -1958,7 +1990,9 @@ hipError_t launch_ffn_fp8w(const FfnArgs& a, void* workspace, hipStream_t stream
   plan.n_x = a.n_x;
   uint16_t* abuf = reinterpret_cast<uint16_t*>(ws);
   if (fp8w_uses_gemm(a.n_rows, G, a.d, a.I, a.packed, a.s_gate, a.s_up, a.s_down)) {
-    launch_gemm_fp8w(a, plan, abuf, stream);
+    // a priority segment: both phases in the persistent queue (decode tiles first)
+    if (L.path == Path::kQueue) launch_queue_bf16<QueueGemm<false, GemmSmallF8>>(a, L, ws, stream);
+    else launch_gemm_fp8w(a, plan, abuf, stream);
     return hipGetLastError();
   }
   if (a.packed) {

@@ -71,7 +71,7 @@ size_t ffn_workspace_bytes(int n_rows, int E, int n_shared, int nseg, int d, int
 // moe_grouped_ffn_combine: batches on the decode-shaped kernels only
 bool ffn_fused_combine_supported(int n_rows, int E, int n_shared, int nseg, int d, int I);
 hipError_t launch_ffn(const FfnArgs& a, void* workspace, hipStream_t stream);
-size_t ffn_fp8w_workspace_bytes(int n_rows, int I);
+size_t ffn_fp8w_workspace_bytes(int n_rows, int E, int n_shared, int nseg, int d, int I, bool packed);
 // FP8 batches that run on the GEMM kernel (packed codes, groups averaging more
 // than 48 rows, d and I multiples of 64 and at least 128, 16-byte aligned scales)
 bool fp8w_uses_gemm(int n_rows, int G, int d, int I, bool packed, const void* s_gate, const void* s_up,

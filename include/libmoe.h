@@ -412,10 +412,15 @@ moe_status moe_grouped_ffn_fp8w(const void* x_sorted, const int32_t* x_rows, int
  *   Batches whose groups average at most 48 rows run on the decode-shaped
  *   kernel and equal moe_grouped_ffn_fp8w's results on the unpacked codes bit
  *   for bit.  Larger groups, with d and I at least 128 and 16-byte aligned
- *   scale arrays, run both phases on a 256 x 256 LDS-tiled GEMM that converts
- *   the codes to bf16 as it reads them (exact) and applies the row scales to
- *   the fp32 sums; its results differ from the decode-shaped kernel's only in
- *   the order of the fp32 sums.
+ *   scale arrays, run both phases on an LDS-tiled GEMM (256 x 256 tiles for
+ *   groups of 256 rows or more on average, 128 x 256 below) that converts the
+ *   codes to bf16 as it reads them (exact) and applies the row scales to the
+ *   fp32 sums; its results differ from the decode-shaped kernel's only in the
+ *   order of the fp32 sums.  On the 128 x 256 tiles a batch with a priority
+ *   segment (nseg == 2) runs both phases in the persistent tile queues of
+ *   moe_grouped_ffn (priority tiles first), and the workspace's last 4 bytes
+ *   are its diagnostic word as for moe_grouped_ffn.  The queried workspace
+ *   size depends on the batch shape (n_rows, E, n_shared, nseg, d, I).
  *   Requires d and I multiples of 64 (MOE_ERR_UNSUPPORTED otherwise).
  */
 moe_status moe_grouped_ffn_fp8w_packed(const void* x_sorted, const int32_t* x_rows, int32_t n_x,

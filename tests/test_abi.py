@@ -102,6 +102,38 @@ def test_ffn_fp8w_validation_and_query(lib):
     assert fp(*args(a7=2, a4=8192)) == 0                           # ... and GEMM-sized ones
 
 
+def test_ffn_fp8w_packed_workspace_follows_the_path(lib, monkeypatch):
+    """The packed FP8 call reserves the persistent queue's heads and phase-1
+    flags (the same layout as the bf16 call's) exactly when a batch with a
+    priority segment runs in the queue: packed codes, groups of 49-255 rows
+    on average, d and I multiples of 64 and at least 128.  Otherwise the
+    workspace is the bf16 SwiGLU intermediate plus the diagnostic word."""
+    def fp8(packed, n_rows, nseg, d=256, I=512, E=8):
+        n = ctypes.c_size_t(0)
+        f = lib.moe_grouped_ffn_fp8w_packed if packed else lib.moe_grouped_ffn_fp8w
+        assert f(FAKE, None, 0, FAKE, n_rows, E, 0, nseg, d, I, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                 ctypes.byref(n), None) == 0
+        return n.value
+
+    def bf16(n_rows, nseg, d=256, I=512, E=8):
+        n = ctypes.c_size_t(0)
+        assert lib.moe_grouped_ffn_packed(FAKE, None, 0, FAKE, n_rows, E, 0, nseg, d, I, FAKE, FAKE, FAKE, FAKE,
+                                          None, ctypes.byref(n), None) == 0
+        return n.value
+
+    plain = lambda n_rows, I=512: (n_rows * I * 2 + 255) // 256 * 256 + 256
+    G2 = 2 * 8
+    queue_rows = 100 * G2                          # 100 rows per group on average
+    assert fp8(True, queue_rows, 2) == bf16(queue_rows, 2) > plain(queue_rows)
+    assert fp8(True, queue_rows, 1) == plain(queue_rows)          # no priority segment: two launches
+    assert fp8(False, queue_rows, 2) == plain(queue_rows)         # row-major codes: decode-shaped kernel
+    assert fp8(True, 300 * G2, 2) == plain(300 * G2)              # 256-row tiles: two launches
+    assert fp8(True, 40 * G2, 2) == plain(40 * G2)                # decode-sized groups
+    assert fp8(True, queue_rows, 2, d=64) == plain(queue_rows)    # K below 128 in phase 2
+    monkeypatch.setenv("LIBMOE_FFN_QUEUE", "0")
+    assert fp8(True, queue_rows, 2) == bf16(queue_rows, 2) == plain(queue_rows)
+
+
 def test_ffn_packed_validation_and_query(lib):
     f = lib.moe_grouped_ffn_packed
     n = ctypes.c_size_t(0)
